@@ -1,0 +1,62 @@
+"""CPU float64 oracle for RoPE-4D joint self-attention -- TEST INFRASTRUCTURE.
+
+This package is the checker, not the product.  Only the test suite, the smoke
+check of the entry module and the CPU-baseline leg of the benchmark may import
+it.  It shares no code with the HIP library: the only thing both sides consume
+is the seeded input generator in ``workloads``, which holds none of the
+method's arithmetic.
+
+What it computes, per batch entry b and head h (sources: "Flux.3 Image Klein
+arrives in Diffusers with a modular architecture", bytechap.com, section "How
+it works" -- joint blocks in which every token attends to every other token,
+and a rotary embedding over the four axes time step, height, width and
+sequence length; "FLUX.3 Image Klein open weights ...", kimiseek.app, section
+"Limitations and unconfirmed points" -- one prompt per call and the prompt
+padding is attended, so there is no mask):
+
+  1. upcast the stored inputs exactly to float64 (bf16 bits, or e4m3 code times
+     its per-tensor descale);
+  2. rotate Q and K with RoPE-4D at each token's own (t, h, w, l) position;
+  3. s_ij = <q'_i, k'_j> / sqrt(D) over all i, j (no mask, not causal);
+  4. p_ij = softmax_j(s_ij);
+  5. o_i = sum_j p_ij v_j.
+
+Readings of points the pages leave open (each is also listed in the design
+notes): theta = 10000 with the frequency schedule theta^(-2j/d_a) per axis;
+D split into four equal blocks in the order t, h, w, l; rotation on
+interleaved channel pairs (2j, 2j+1) as (x cos - y sin, x sin + y cos);
+softmax scale 1/sqrt(D); positions shared by every batch entry.
+
+Modules:
+  rope4d     -- the rotary embedding (pinned: orthogonality, norm, identity at
+                p = 0, relative-position property, brute force)
+  joint_attention -- the attention definition above, plus exact storage decoders
+                (pinned: brute force, scaled_dot_product_attention at p = 0,
+                softmax invariants)
+  brute      -- pure-Python scalar loops for tiny shapes (the brute-force pin)
+  fp8        -- OCP E4M3FN decoding (pinned: all 256 codes against the
+                format's definition and torch.float8_e4m3fn)
+"""
+
+from .joint_attention import (
+    attention,
+    attention_inputs_rows,
+    attention_rows,
+    bf16_to_f64,
+    decode_inputs,
+    rel_l2,
+)
+from .fp8 import e4m3_decode
+from .rope4d import rope4d, rope_frequencies
+
+__all__ = [
+    "attention",
+    "attention_inputs_rows",
+    "attention_rows",
+    "bf16_to_f64",
+    "decode_inputs",
+    "e4m3_decode",
+    "rel_l2",
+    "rope4d",
+    "rope_frequencies",
+]
