@@ -1,0 +1,186 @@
+#!/usr/bin/env python3
+"""Benchmark of the RoPE-4D joint-attention forward on one MI355X.
+
+One step = one call of the attention library on one batch of the 2048x2048
+text-to-image workload with CFG (cond + uncond batched): B=2, S=16,896
+(512 text + 128x128 image tokens), H=24, D=128, bf16 in/out, inputs resident
+in HBM before timing.  Throughput is attention TFLOP/s = 4*B*H*S^2*D / t.
+
+Prints ONE JSON line.  Fields beyond the common ones:
+  roofline      -- the attention kernel against dense bf16 MFMA peak, with the
+                   HBM traffic measured by rocprofv3 counters when the stored
+                   measurement matches the current kernel sources;
+  cpu_baseline  -- the fp64 CPU oracle timed on a bounded sample of the same
+                   workload (a seeded subset of query rows), scaled to TFLOP/s;
+  fp8           -- the FP8 E4M3 variant on the 2048x2048 edit workload
+                   (S = 33,280), against dense fp8 MFMA peak.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "joint-attention TFLOP/s + % MFMA peak at 2048² (16,896 tok, 24 heads×128)"
+PEAK_BF16 = 2516.6      # dense bf16 MFMA, TFLOP/s (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_FP8 = 5033.2       # dense fp8 MFMA, TFLOP/s
+KERNEL_SOURCES = ["klein_device.hpp", "attn_fwd_bf16.hip"]
+KERNEL_SOURCES_FP8 = ["klein_device.hpp", "attn_fwd_fp8.hip"]
+
+
+def sources_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "joint_attention_rope_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kind, names):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kind}.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_hash") != sources_hash(names):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def to_device(inp, dev):
+    """Seeded host inputs -> GPU tensors holding exactly the generator's bits."""
+    import numpy as np
+    import torch
+    if inp.descale is None:
+        conv = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        conv = lambda a: torch.from_numpy(a).to(dev)
+    return conv(inp.q), conv(inp.k), conv(inp.v), torch.from_numpy(inp.pos).to(dev)
+
+
+def time_gpu(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps          # ms per launch
+
+
+def cpu_baseline(inp, cfg, target_s=15.0):
+    """Time the fp64 oracle on a seeded sample of query rows of batch entry 0,
+    all heads; scale its rate to TFLOP/s with the same 4*S*D flops per row."""
+    import numpy as np
+    import oracle
+    from workloads import Inputs
+    workers = min(16, len(os.sched_getaffinity(0)))
+    sub = Inputs(cfg, inp.q[:1], inp.k[:1], inp.v[:1], inp.pos, inp.descale)
+    rng = np.random.default_rng(12345)
+    rows = np.sort(rng.choice(cfg.S, size=64, replace=False))
+    t0 = time.perf_counter()
+    oracle.attention_inputs_rows(sub, rows, workers=workers)
+    t_cal = time.perf_counter() - t0
+    n = int(min(cfg.S, max(64, 64 * target_s / max(t_cal, 1e-3))))
+    rows = np.sort(rng.choice(cfg.S, size=n, replace=False))
+    t0 = time.perf_counter()
+    oracle.attention_inputs_rows(sub, rows, workers=workers)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * n * cfg.S * cfg.D * cfg.H
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"{n} seeded query rows x {cfg.H} heads of batch entry 0 "
+                  f"(all {cfg.S} keys each), float64 NumPy, {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the attention shards by batch entry and head with no exchange; "
+              "see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import joint_attention_rope_amd as kl
+    from workloads import get_config, make_inputs
+
+    dev = "cuda:0"
+    cfg = get_config(4)
+    inp = make_inputs(cfg)
+    q, k, v, pos = to_device(inp, dev)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    ms = time_gpu(lambda: kl.klein_rope4d_attn_fwd(q, k, v, pos, out), args.steps,
+                  args.warmup, torch)
+    tflops = cfg.flops / (ms * 1e-3) / 1e12
+    traffic = stored_traffic("attn_fwd_bf16_2048px_t2i_cfg", KERNEL_SOURCES)
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V; uncond text tokens zeroed)",
+        "config": {"workload": "2048x2048 text-to-image with CFG: B=2, S=16896 "
+                               "(512 text + 128x128 image), H=24, D=128, bf16",
+                   "global_batch": cfg.B, "seq_len": cfg.S, "heads": cfg.H,
+                   "head_dim": cfg.D, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16, 4),
+                     "traffic": traffic},
+    }
+    del q, k, v, out
+    if not args.no_fp8:
+        try:
+            cfg5 = get_config(5)
+            inp5 = make_inputs(cfg5)
+            q5, k5, v5, p5 = to_device(inp5, dev)
+            o5 = torch.empty(q5.shape, dtype=torch.bfloat16, device=dev)
+            ms5 = time_gpu(lambda: kl.klein_rope4d_attn_fwd_fp8(q5, k5, v5, p5, o5, *inp5.descale),
+                           max(3, args.steps // 2), max(1, args.warmup // 2), torch)
+            t5 = cfg5.flops / (ms5 * 1e-3) / 1e12
+            rec["fp8"] = {"workload": "2048x2048 edit: B=1, S=33280 (512 text + 2 x 128x128), "
+                                      "H=24, D=128, e4m3 in, bf16 out",
+                          "ms_per_call": round(ms5, 4), "tflops": round(t5, 2),
+                          "peak": PEAK_FP8, "frac": round(t5 / PEAK_FP8, 4),
+                          "traffic": stored_traffic("attn_fwd_fp8_2048px_edit",
+                                                    KERNEL_SOURCES_FP8)}
+            del q5, k5, v5, o5
+        except kl.KleinError as e:
+            rec["fp8"] = {"error": str(e)}
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,116 @@
+/*
+ * klein_attn.h -- C ABI of the MI355X (gfx950) RoPE-4D joint-attention library.
+ *
+ * What the library computes
+ * -------------------------
+ * The joint blocks of FLUX.3 Image Klein run self-attention over one sequence
+ * that concatenates text, noisy-image-latent and reference-image tokens, with
+ * every token attending to every other token, and encode position with a
+ * rotary embedding over four axes: time step t, height h, width w and sequence
+ * length l ("Flux.3 Image Klein arrives in Diffusers with a modular
+ * architecture", bytechap.com, section "How it works").  The prompt padding is
+ * attended and one prompt is handled per call ("FLUX.3 Image Klein open
+ * weights ...", kimiseek.app, section "Limitations and unconfirmed points"),
+ * so there is no mask; reference and output share (h, w) coordinates (same
+ * page, section "Adoption and evaluation proposals"), so positions are given
+ * per token.  For every batch entry b and head h:
+ *
+ *   q'_i = R(pos_i) q_i,   k'_j = R(pos_j) k_j
+ *   out_i = sum_j softmax_j(<q'_i, k'_j> / sqrt(D)) v_j      (i, j in [0, S))
+ *
+ * R is RoPE-4D: D is split into four blocks of D/4 channels in the order
+ * t, h, w, l; inside axis block a the interleaved channel pair (2j, 2j+1),
+ * j < D/8, is rotated by the angle pos_a * 10000^(-2j/(D/4)), a pair (x, y)
+ * becoming (x cos - y sin, x sin + y cos).  V is not rotated.  (The pages
+ * name the axes but print no formula; this is the plainest reading and the
+ * one the CPU oracle of this repository implements.)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers to tensors are DEVICE pointers, owned by the caller, 16-byte
+ *    aligned.  The library allocates nothing and keeps no per-call state.
+ *  - q, k, v, out are contiguous [B][S][H][D] (D fastest, then heads, then
+ *    tokens, then batch).  out is always bfloat16.
+ *  - pos_thwl is contiguous int32 [S][4] in the order (t, h, w, l) and is
+ *    shared by every batch entry.  Angles are formed in fp32; accuracy is
+ *    stated for |pos| < 4096 on every axis (larger values are accepted, with
+ *    angle error growing like |pos| * 2^-24 revolutions).
+ *  - D must be 64 or 128; B, S, H >= 1; B*H*ceil(S/256) < 2^31.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL means the null
+ *    stream).  The status reports argument and launch errors only, never
+ *    results of device work.  Argument checks run before any HIP call, so an
+ *    invalid call touches no device.  No C++ exception crosses this ABI.
+ *  - Calls are thread-safe; concurrent calls on different streams are fine.
+ */
+#ifndef KLEIN_ATTN_H
+#define KLEIN_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KLEIN_DTYPE_BF16 = 0,      /* q, k, v are bfloat16 */
+  KLEIN_DTYPE_FP8_E4M3 = 1   /* q, k, v are OCP FP8 E4M3FN codes, descale 1 */
+} klein_dtype_t;
+
+typedef enum {
+  KLEIN_OK = 0,
+  KLEIN_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, size < 1, bad dtype, bad descale */
+  KLEIN_ERR_UNSUPPORTED = 2,  /* D not in {64, 128}, or grid too large */
+  KLEIN_ERR_NO_DEVICE = 3,    /* the HIP runtime found no usable GPU */
+  KLEIN_ERR_LAUNCH = 4        /* the kernel launch itself failed */
+} klein_status_t;
+
+/* Opaque stream handle: a hipStream_t passed as a pointer. */
+typedef void* klein_stream_t;
+
+/*
+ * RoPE-4D joint self-attention forward (the definition above).
+ *   q, k, v : [B][S][H][D] bfloat16 (dtype BF16) or E4M3FN codes (FP8_E4M3,
+ *             all descales 1; use klein_rope4d_attn_fwd_fp8 for scales)
+ *   pos_thwl: [S][4] int32 (t, h, w, l)
+ *   out     : [B][S][H][D] bfloat16, written completely; must not alias inputs
+ * Softmax scale is fixed at 1/sqrt(D).  Accumulation is fp32.
+ */
+klein_status_t klein_rope4d_attn_fwd(const void* q, const void* k, const void* v,
+                                     const int32_t* pos_thwl, void* out,
+                                     int B, int S, int H, int D,
+                                     klein_dtype_t dtype, klein_stream_t stream);
+
+/*
+ * FP8 variant with per-tensor scales: the value of an element is
+ * decode_e4m3(code) * descale, for q, k and v separately (the FP8 attention
+ * the Blackwell write-up benchmarks -- "How FLUX 3 Image Klein was made 3-4x
+ * faster on NVIDIA Blackwell", section "Method 2", attention table -- read as
+ * per-tensor scaled E4M3).  Descales must be finite and > 0.  The rotated Q/K
+ * are re-quantised to E4M3 on chip and softmax stays fp32; out is bfloat16.
+ */
+klein_status_t klein_rope4d_attn_fwd_fp8(const void* q, const void* k, const void* v,
+                                         const int32_t* pos_thwl, void* out,
+                                         int B, int S, int H, int D,
+                                         float q_descale, float k_descale,
+                                         float v_descale, klein_stream_t stream);
+
+/*
+ * Test hook: y = R(pos) x for bfloat16 x, y [B][S][H][D] (same layout rules),
+ * computed with the very device routine the attention kernels use for Q and
+ * K, rounded to bfloat16.  x and y may be the same buffer.
+ */
+klein_status_t klein_rope4d_apply(const void* x, const int32_t* pos_thwl, void* y,
+                                  int B, int S, int H, int D,
+                                  klein_stream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* klein_status_string(klein_status_t status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int klein_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KLEIN_ATTN_H */

@@ -1,0 +1,128 @@
+"""RoPE-4D joint self-attention for MI355X (gfx950): Python binding.
+
+The functions here carry the names of the C ABI in include/klein_attn.h and
+only marshal arguments: torch tensors (already on the GPU) become device
+pointers and sizes, torch's current stream becomes the HIP stream, and a
+non-zero status becomes a KleinError.  Every step of the computation runs in
+the HIP kernels of libklein_attn.so; if that library is missing the calls
+raise instead of computing anything another way.
+"""
+
+import torch
+
+from . import _capi
+from ._capi import (KLEIN_DTYPE_BF16, KLEIN_DTYPE_FP8_E4M3, KLEIN_ERR_INVALID_ARG,
+                    KLEIN_ERR_LAUNCH, KLEIN_ERR_NO_DEVICE, KLEIN_ERR_UNSUPPORTED, KLEIN_OK)
+
+__all__ = [
+    "KleinError", "klein_rope4d_attn_fwd", "klein_rope4d_attn_fwd_fp8",
+    "klein_rope4d_apply", "klein_status_string", "klein_version", "library_path",
+    "KLEIN_DTYPE_BF16", "KLEIN_DTYPE_FP8_E4M3",
+]
+
+
+class KleinError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({klein_status_string(status)})")
+
+
+def library_path() -> str:
+    return _capi.LIB_PATH
+
+
+def klein_status_string(status: int) -> str:
+    return _capi.lib().klein_status_string(int(status)).decode()
+
+
+def klein_version() -> int:
+    return _capi.lib().klein_version()
+
+
+def _stream(stream, dev):
+    if stream is None:
+        return torch.cuda.current_stream(dev).cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(st, where):
+    if st != KLEIN_OK:
+        raise KleinError(st, where)
+
+
+def _bshd(t, name):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, S, H, D], got shape {tuple(t.shape)}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    return tuple(t.shape)
+
+
+def _pos(pos, S):
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (S, 4) or not pos.is_cuda \
+            or not pos.is_contiguous():
+        raise ValueError(f"pos_thwl must be a contiguous int32 GPU tensor [S, 4] = [{S}, 4]")
+
+
+_FP8_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def klein_rope4d_attn_fwd(q, k, v, pos_thwl, out, dtype=None, stream=None):
+    """out <- RoPE-4D joint attention of q, k, v ([B, S, H, D]) at pos_thwl [S, 4].
+
+    dtype: KLEIN_DTYPE_BF16 (q/k/v bfloat16) or KLEIN_DTYPE_FP8_E4M3 (E4M3 codes,
+    descale 1); inferred from q.dtype when None.  out: bfloat16 [B, S, H, D].
+    """
+    B, S, H, D = _bshd(q, "q")
+    for t, n in ((k, "k"), (v, "v"), (out, "out")):
+        if _bshd(t, n) != (B, S, H, D):
+            raise ValueError(f"{n} must have q's shape {(B, S, H, D)}")
+    _pos(pos_thwl, S)
+    if dtype is None:
+        dtype = KLEIN_DTYPE_FP8_E4M3 if q.dtype in _FP8_DTYPES else KLEIN_DTYPE_BF16
+    want = torch.bfloat16 if dtype == KLEIN_DTYPE_BF16 else None
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if (want is not None and t.dtype != want) or (want is None and t.dtype not in _FP8_DTYPES):
+            raise ValueError(f"{n} has dtype {t.dtype}, which does not match the dtype code {dtype}")
+    if out.dtype != torch.bfloat16:
+        raise ValueError("out must be bfloat16")
+    st = _capi.lib().klein_rope4d_attn_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), pos_thwl.data_ptr(), out.data_ptr(),
+        B, S, H, D, int(dtype), _stream(stream, q.device))
+    _check(st, "klein_rope4d_attn_fwd")
+    return out
+
+
+def klein_rope4d_attn_fwd_fp8(q, k, v, pos_thwl, out, q_descale, k_descale, v_descale,
+                              stream=None):
+    """FP8 E4M3 q, k, v (uint8 or float8_e4m3fn) with per-tensor descales; bf16 out."""
+    B, S, H, D = _bshd(q, "q")
+    for t, n in ((k, "k"), (v, "v"), (out, "out")):
+        if _bshd(t, n) != (B, S, H, D):
+            raise ValueError(f"{n} must have q's shape {(B, S, H, D)}")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype not in _FP8_DTYPES:
+            raise ValueError(f"{n} must hold E4M3 codes (uint8 or float8_e4m3fn)")
+    if out.dtype != torch.bfloat16:
+        raise ValueError("out must be bfloat16")
+    _pos(pos_thwl, S)
+    st = _capi.lib().klein_rope4d_attn_fwd_fp8(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), pos_thwl.data_ptr(), out.data_ptr(),
+        B, S, H, D, float(q_descale), float(k_descale), float(v_descale),
+        _stream(stream, q.device))
+    _check(st, "klein_rope4d_attn_fwd_fp8")
+    return out
+
+
+def klein_rope4d_apply(x, pos_thwl, y, stream=None):
+    """y <- RoPE-4D(x) for bfloat16 x, y [B, S, H, D] (the kernels' own routine)."""
+    B, S, H, D = _bshd(x, "x")
+    if _bshd(y, "y") != (B, S, H, D) or x.dtype != torch.bfloat16 or y.dtype != torch.bfloat16:
+        raise ValueError("x and y must be bfloat16 tensors of one shape")
+    _pos(pos_thwl, S)
+    st = _capi.lib().klein_rope4d_apply(x.data_ptr(), pos_thwl.data_ptr(), y.data_ptr(),
+                                        B, S, H, D, _stream(stream, x.device))
+    _check(st, "klein_rope4d_apply")
+    return y

@@ -1,0 +1,50 @@
+"""ctypes declarations of the C ABI in include/klein_attn.h.
+
+Loading fails loudly when the HIP library has not been built: there is no
+fallback path of any kind.
+"""
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libklein_attn.so")
+
+KLEIN_DTYPE_BF16 = 0
+KLEIN_DTYPE_FP8_E4M3 = 1
+
+KLEIN_OK = 0
+KLEIN_ERR_INVALID_ARG = 1
+KLEIN_ERR_UNSUPPORTED = 2
+KLEIN_ERR_NO_DEVICE = 3
+KLEIN_ERR_LAUNCH = 4
+
+_lib = None
+
+_vp, _i32p, _int, _f32 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+
+SIGNATURES = {
+    "klein_rope4d_attn_fwd": (_int, [_vp, _vp, _vp, _i32p, _vp, _int, _int, _int, _int, _int, _vp]),
+    "klein_rope4d_attn_fwd_fp8": (_int, [_vp, _vp, _vp, _i32p, _vp, _int, _int, _int, _int,
+                                         _f32, _f32, _f32, _vp]),
+    "klein_rope4d_apply": (_int, [_vp, _i32p, _vp, _int, _int, _int, _int, _vp]),
+    "klein_status_string": (ctypes.c_char_p, [_int]),
+    "klein_version": (_int, []),
+}
+
+
+def lib():
+    """The loaded library (ctypes.CDLL), loading it on first use."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build the HIP library first "
+                "(python -m joint_attention_rope_amd.build)")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib

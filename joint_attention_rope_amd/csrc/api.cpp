@@ -1,0 +1,131 @@
+// C ABI of the RoPE-4D joint-attention library: argument checks, RoPE
+// frequency tables, kernel dispatch, status mapping.  Declarations and the
+// contract of every entry point live in include/klein_attn.h.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/klein_attn.h"
+#include "klein_launch.hpp"
+
+namespace {
+
+using klein::LaunchArgs;
+
+constexpr double kTheta = 10000.0;
+constexpr double kPi = 3.14159265358979323846;
+
+// w_j = theta^(-2j/(D/4)) / (2 pi) revolutions per position unit, split into a
+// 12-significant-bit head and an fp32 tail (see RopeFreqs).
+klein::RopeFreqs make_freqs(int D) {
+  klein::RopeFreqs f{};
+  const int da = D / 4;
+  for (int j = 0; j < 16; ++j) {
+    if (j >= da / 2) { f.hi[j] = 0.f; f.lo[j] = 0.f; continue; }
+    const double w = std::pow(kTheta, -2.0 * j / da) / (2.0 * kPi);
+    int e = 0;
+    const double m = std::frexp(w, &e);                 // w = m * 2^e, m in [0.5, 1)
+    const double hi = std::ldexp(std::nearbyint(std::ldexp(m, 12)), e - 12);
+    f.hi[j] = (float)hi;                                 // exact: <= 12 bits
+    f.lo[j] = (float)(w - hi);
+  }
+  return f;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+klein_status_t check_common(const void* q, const void* k, const void* v, const int32_t* pos,
+                            const void* out, int B, int S, int H, int D) {
+  if (!q || !k || !v || !pos || !out) return KLEIN_ERR_INVALID_ARG;
+  if (B < 1 || S < 1 || H < 1) return KLEIN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return KLEIN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(pos))
+    return KLEIN_ERR_INVALID_ARG;
+  return KLEIN_OK;
+}
+
+klein_status_t map_hip(hipError_t e) {
+  if (e == hipSuccess) return KLEIN_OK;
+  if (e == hipErrorNoDevice || e == hipErrorInvalidDevice) return KLEIN_ERR_NO_DEVICE;
+  if (e == hipErrorNotSupported) return KLEIN_ERR_UNSUPPORTED;
+  return KLEIN_ERR_LAUNCH;
+}
+
+LaunchArgs make_args(const void* q, const void* k, const void* v, const int32_t* pos, void* out,
+                     int B, int S, int H, int D, klein_stream_t stream) {
+  LaunchArgs a{};
+  a.q = q; a.k = k; a.v = v; a.pos = pos; a.out = out;
+  a.B = B; a.S = S; a.H = H; a.D = D;
+  a.qscale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  a.descale[0] = a.descale[1] = a.descale[2] = 1.0f;
+  a.freqs = make_freqs(D);
+  a.stream = reinterpret_cast<hipStream_t>(stream);
+  return a;
+}
+
+constexpr long long kMaxGrid = 2147483647LL;
+
+}  // namespace
+
+extern "C" {
+
+klein_status_t klein_rope4d_attn_fwd(const void* q, const void* k, const void* v,
+                                     const int32_t* pos_thwl, void* out, int B, int S, int H,
+                                     int D, klein_dtype_t dtype, klein_stream_t stream) {
+  if (dtype == KLEIN_DTYPE_FP8_E4M3)
+    return klein_rope4d_attn_fwd_fp8(q, k, v, pos_thwl, out, B, S, H, D, 1.f, 1.f, 1.f, stream);
+  if (dtype != KLEIN_DTYPE_BF16) return KLEIN_ERR_INVALID_ARG;
+  klein_status_t st = check_common(q, k, v, pos_thwl, out, B, S, H, D);
+  if (st != KLEIN_OK) return st;
+  if (klein::attn_fwd_bf16_grid(B, S, H) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
+  try {
+    return map_hip(klein::launch_attn_fwd_bf16(make_args(q, k, v, pos_thwl, out, B, S, H, D, stream)));
+  } catch (...) {
+    return KLEIN_ERR_LAUNCH;
+  }
+}
+
+klein_status_t klein_rope4d_attn_fwd_fp8(const void* q, const void* k, const void* v,
+                                         const int32_t* pos_thwl, void* out, int B, int S, int H,
+                                         int D, float q_descale, float k_descale, float v_descale,
+                                         klein_stream_t stream) {
+  klein_status_t st = check_common(q, k, v, pos_thwl, out, B, S, H, D);
+  if (st != KLEIN_OK) return st;
+  for (float s : {q_descale, k_descale, v_descale})
+    if (!(std::isfinite(s) && s > 0.f)) return KLEIN_ERR_INVALID_ARG;
+  if (klein::attn_fwd_fp8_grid(B, S, H) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
+  try {
+    LaunchArgs a = make_args(q, k, v, pos_thwl, out, B, S, H, D, stream);
+    a.descale[0] = q_descale; a.descale[1] = k_descale; a.descale[2] = v_descale;
+    return map_hip(klein::launch_attn_fwd_fp8(a));
+  } catch (...) {
+    return KLEIN_ERR_LAUNCH;
+  }
+}
+
+klein_status_t klein_rope4d_apply(const void* x, const int32_t* pos_thwl, void* y, int B, int S,
+                                  int H, int D, klein_stream_t stream) {
+  if (!x || !pos_thwl || !y) return KLEIN_ERR_INVALID_ARG;
+  if (B < 1 || S < 1 || H < 1) return KLEIN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return KLEIN_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(pos_thwl)) return KLEIN_ERR_INVALID_ARG;
+  try {
+    return map_hip(klein::launch_rope4d_apply(make_args(x, x, x, pos_thwl, y, B, S, H, D, stream)));
+  } catch (...) {
+    return KLEIN_ERR_LAUNCH;
+  }
+}
+
+const char* klein_status_string(klein_status_t status) {
+  switch (status) {
+    case KLEIN_OK: return "ok";
+    case KLEIN_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, size < 1, bad dtype or descale)";
+    case KLEIN_ERR_UNSUPPORTED: return "unsupported (head dim must be 64 or 128; grid too large)";
+    case KLEIN_ERR_NO_DEVICE: return "no usable GPU";
+    case KLEIN_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int klein_version(void) { return 100; }
+
+}  // extern "C"

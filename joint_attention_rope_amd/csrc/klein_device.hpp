@@ -1,0 +1,81 @@
+// Device-side building blocks shared by the gfx950 kernels of this library:
+// vector types, bf16 packing, the RoPE-4D chunk rotation and the XCD-aware
+// workgroup order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace klein {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// RoPE-4D frequencies in revolutions per unit of position, w_j = omega_j/(2 pi),
+// omega_j = 10000^(-2j/(D/4)), j < D/8.  Each w_j is split as hi + lo with hi
+// holding at most 12 significant bits, so pos * hi is exact in fp32 for
+// |pos| < 4096 and its fractional part loses nothing; lo carries the rest.
+struct RopeFreqs {
+  float hi[16];
+  float lo[16];
+};
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// bf16 halves of a packed word (element 2j in the low half: little endian)
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// two floats -> packed bf16x2, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t r = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Rotate one 16-byte chunk: 8 consecutive channels = 4 interleaved pairs of a
+// single axis block, pairs j0 .. j0+3, at integer position p on that axis.
+// Each pair (x, y) -> (x cos - y sin, x sin + y cos), then * scale, -> bf16.
+// v_sin_f32 / v_cos_f32 take their argument in revolutions.
+__device__ __forceinline__ u32x4_t rope_chunk(u32x4_t x, int p, const float* whi,
+                                              const float* wlo, float scale) {
+  const float fp = (float)p;
+  u32x4_t y;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const float rev = __builtin_amdgcn_fractf(fp * whi[jj]) + fp * wlo[jj];
+    const float s = __builtin_amdgcn_sinf(rev);
+    const float c = __builtin_amdgcn_cosf(rev);
+    const float a = bf16_lo(x[jj]);
+    const float b = bf16_hi(x[jj]);
+    y[jj] = pack_bf16x2((a * c - b * s) * scale, (a * s + b * c) * scale);
+  }
+  return y;
+}
+
+// Workgroups are handed to the 8 XCDs round robin (block i -> XCD i % 8), and
+// each XCD has its own L2.  Remap so that XCD x runs a contiguous range of the
+// logical work list; consecutive logical items share a (batch, head) and so
+// stream the same K/V through that XCD's L2.  A bijection on [0, n).
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int per = n >> 3, extra = n & 7;
+  return xcd * per + (xcd < extra ? xcd : extra) + slot;
+}
+
+// Reduce a per-lane value with the lane 32 apart (lanes l and l^32 hold the
+// two halves of one query's keys in the 32x32 MFMA accumulator layout).
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+}  // namespace klein

@@ -1,0 +1,30 @@
+// Host-side launch descriptors shared by the C ABI and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "klein_device.hpp"
+
+namespace klein {
+
+struct LaunchArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* pos;
+  void* out;
+  int B, S, H, D;
+  float qscale_log2;   // log2(e) / sqrt(D), folded into Q after the rotation
+  float descale[3];    // fp8 per-tensor descales of q, k, v (1 for bf16)
+  RopeFreqs freqs;
+  hipStream_t stream;
+};
+
+hipError_t launch_attn_fwd_bf16(const LaunchArgs& a);
+long long attn_fwd_bf16_grid(int B, int S, int H);
+hipError_t launch_attn_fwd_fp8(const LaunchArgs& a);
+long long attn_fwd_fp8_grid(int B, int S, int H);
+hipError_t launch_rope4d_apply(const LaunchArgs& a);
+
+}  // namespace klein

@@ -1,0 +1,75 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects invalid arguments before touching any device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from joint_attention_rope_amd import _capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "klein_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(klein_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted([
+        "klein_rope4d_attn_fwd", "klein_rope4d_attn_fwd_fp8", "klein_rope4d_apply",
+        "klein_status_string", "klein_version"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _capi.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _capi.SIGNATURES, name
+
+
+def test_status_strings():
+    lib = _capi.lib()
+    for code in range(5):
+        assert lib.klein_status_string(code)
+    assert lib.klein_status_string(99) == b"unknown status"
+    assert lib.klein_version() >= 100
+
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced: checks fail first
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 128, 0), _capi.KLEIN_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, 0, FAKE, 1, 8, 1, 128, 0), _capi.KLEIN_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 1, 128, 0), _capi.KLEIN_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, 1, 128, 0), _capi.KLEIN_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 0, 128, 0), _capi.KLEIN_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 96, 0), _capi.KLEIN_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 256, 0), _capi.KLEIN_ERR_UNSUPPORTED),
+    ((FAKE + 2, FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 128, 0), _capi.KLEIN_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE + 8, 1, 8, 1, 64, 0), _capi.KLEIN_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 128, 7), _capi.KLEIN_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 2 ** 20, 2 ** 30, 2 ** 10, 128, 0), _capi.KLEIN_ERR_UNSUPPORTED),
+])
+def test_attn_argument_checks(args, status):
+    assert _capi.lib().klein_rope4d_attn_fwd(*args, None) == status
+
+
+@pytest.mark.parametrize("scales", [(0.0, 1.0, 1.0), (1.0, -1.0, 1.0), (1.0, 1.0, float("nan")),
+                                    (1.0, float("inf"), 1.0)])
+def test_fp8_descale_checks(scales):
+    st = _capi.lib().klein_rope4d_attn_fwd_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 128,
+                                               *scales, None)
+    assert st == _capi.KLEIN_ERR_INVALID_ARG
+
+
+def test_rope_apply_checks():
+    lib = _capi.lib()
+    assert lib.klein_rope4d_apply(0, FAKE, FAKE, 1, 8, 1, 128, None) == _capi.KLEIN_ERR_INVALID_ARG
+    assert lib.klein_rope4d_apply(FAKE, FAKE, FAKE, 1, 8, 1, 32, None) == _capi.KLEIN_ERR_UNSUPPORTED
+    assert lib.klein_rope4d_apply(FAKE, FAKE, FAKE + 4, 1, 8, 1, 64, None) == _capi.KLEIN_ERR_INVALID_ARG

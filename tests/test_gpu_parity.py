@@ -1,0 +1,61 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded bits.
+
+Small shapes are compared element by element over the whole output; the
+workload shapes are run at full size in the benchmark's launch configuration
+and checked on sampled query rows (every batch entry and head), which the
+oracle computes one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import (assert_bf16_close, bf16_tensor_to_f64, oracle_full, oracle_rows,
+                     random_inputs, run_attention, sample_rows)
+from workloads import get_config, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _print_case(*a):
+    print("[case]", *a, flush=True)
+
+
+def test_tiny_workload_full():
+    inp = make_inputs(get_config(1))
+    _print_case("workload 1", inp.q.shape)
+    out = bf16_tensor_to_f64(run_attention(inp))
+    assert_bf16_close(out, oracle_full(inp), "workload 1")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("S", [1, 2, 17, 63, 64, 65, 255, 256, 257, 300, 577])
+def test_ragged_full(S, D):
+    inp = random_inputs(2, S, 3, D, seed=1000 + S * 7 + D)
+    _print_case("ragged", S, D)
+    out = bf16_tensor_to_f64(run_attention(inp))
+    assert_bf16_close(out, oracle_full(inp), f"S={S} D={D}")
+
+
+def test_large_positions_full():
+    """Positions spread over +-4000 on every axis (the documented accuracy range)."""
+    inp = random_inputs(1, 200, 2, 128, seed=77, pos_lo=-4000, pos_hi=4000)
+    out = bf16_tensor_to_f64(run_attention(inp))
+    assert_bf16_close(out, oracle_full(inp), "large positions")
+
+
+@pytest.mark.parametrize("cid,overrides", [
+    (2, {}),
+    (3, {}),
+    (4, {}),
+    (2, {"text": 480}),     # prompt padded to a multiple of 80 tokens
+    (2, {"text": 560}),
+])
+def test_workload_sampled_rows(cid, overrides):
+    cfg = get_config(cid, **overrides)
+    inp = make_inputs(cfg)
+    _print_case("workload", cid, overrides, inp.q.shape)
+    out = run_attention(inp)
+    rows = sample_rows(cfg.S, cfg.text, n=24, seed=cid)
+    gpu = bf16_tensor_to_f64(out[:, torch.from_numpy(rows).to(out.device)])
+    assert_bf16_close(gpu, oracle_rows(inp, rows), f"workload {cid} {overrides}")
