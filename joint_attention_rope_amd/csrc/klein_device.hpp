@@ -27,6 +27,22 @@ struct RopeFreqs {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// Fourth word of a raw buffer descriptor on gfx9-family GPUs (32-bit data
+// format, no swizzle): loads past the descriptor's size return zero.
+constexpr int kBufferWord3 = 0x00020000;
+
+// Raw buffer descriptor over [base, base + bytes).  Every operand is forced
+// into scalar registers (all callers pass wave-uniform values), so loads
+// through it never need a per-lane descriptor loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const int n = __builtin_amdgcn_readfirstlane(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), 0, n, kBufferWord3);
+}
+
 // bf16 halves of a packed word (element 2j in the low half: little endian)
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
