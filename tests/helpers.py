@@ -89,3 +89,28 @@ def oracle_full(inp):
 def oracle_rows(inp, rows):
     import oracle
     return oracle.attention_inputs_rows(inp, rows)
+
+
+def random_fp8_inputs(B, S, H, D, seed, pos_lo=-50, pos_hi=600, unit_scale=False):
+    """Seeded fp8 inputs by the FP8 workload's recipe: N(0,1) rounded to bf16,
+    then E4M3 with a per-tensor amax/448 scale (or scale 1 if unit_scale)."""
+    from workloads import bf16_bits_from_f32, e4m3_encode, get_config
+    rng = np.random.default_rng(seed)
+    shape = (B, S, H, D)
+    codes, scales = [], []
+    for _ in range(3):
+        x = rng.standard_normal(shape).astype(np.float32)
+        xb = (bf16_bits_from_f32(x).astype(np.uint32) << np.uint32(16)).view(np.float32)
+        sc = 1.0 if unit_scale else float(np.float32(np.max(np.abs(xb)) / 448.0))
+        codes.append(e4m3_encode(xb.astype(np.float64) / sc))
+        scales.append(sc)
+    pos = rng.integers(pos_lo, pos_hi, size=(S, 4)).astype(np.int32)
+    return Inputs(get_config(5, B=B, H=H, D=D), codes[0], codes[1], codes[2], pos,
+                  descale=tuple(scales))
+
+
+def assert_fp8_close(gpu, ref, what=""):
+    max_abs, rel = errors(gpu, ref)
+    assert np.isfinite(gpu).all(), f"{what}: non-finite output"
+    assert rel <= FP8_REL_L2, f"{what}: rel_l2 {rel:.3e} (<= {FP8_REL_L2}), max_abs {max_abs:.3e}"
+    return max_abs, rel
