@@ -17,11 +17,19 @@
 // LDS: K is rotated by RoPE-4D on the way, V is transposed to V^T.  K and V^T
 // are double-buffered in LDS (tile t in buffer t & 1).
 //
-// MFMA orientation: S^T = K' Q'^T on v_mfma_f32_32x32x16_bf16 puts keys on
-// the MFMA rows and queries on its columns, so a lane holds 16 keys of one
-// query and the row max / row sum need one exchange with the lane 32 apart.
-// O^T += V^T P^T uses P straight from the S^T accumulators (as bf16) as the B
-// operand.  Keys of a tile sit in LDS in a permuted row order so that
+// Precision: the rotated Q' (times log2(e)/sqrt(D)) and K' are rounded to
+// fp16, not bf16, and S^T = K' Q'^T runs on v_mfma_f32_32x32x16_f16 (same
+// rate as bf16).  With bf16 the rounding of Q' and K' alone reaches a relative
+// L2 error of ~5e-3 on key channels with x8 outliers; fp16's three extra
+// mantissa bits cut it about 2x.  The price is range: elementwise |k| must
+// stay below ~46000 and |q| below ~360000 (fp16 max 65504 after the
+// rotation's sqrt 2 and the softmax scale).  P and V stay bf16 for O^T += V^T P^T.
+//
+// MFMA orientation: S^T = K' Q'^T puts keys on the MFMA rows and queries on
+// its columns, so a lane holds 16 keys of one query and the row max / row sum
+// need one exchange with the lane 32 apart.  O^T += V^T P^T
+// (v_mfma_f32_32x32x16_bf16) uses P straight from the S^T accumulators (as
+// bf16) as the B operand.  Keys of a tile sit in LDS in a permuted row order so that
 // accumulator register i of a lane in half g holds key 16g + i of its 32-key
 // block; P's registers 8j..8j+7 then pair with the 8 contiguous keys
 // 16g + 8j .. 16g + 8j + 7 of a V^T row, one 16-byte LDS read.
@@ -86,14 +94,14 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   // Rows past S load row S-1 (in bounds) and are never stored.
   const int qrow = qt * BM + wave * 32 + lr;
   const int qload = qrow < S ? qrow : S - 1;
-  bf16x8_t qreg[KS];
+  f16x8_t qreg[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int d0 = 16 * ks + 8 * g;
     const int a = d0 / DA, j0 = (d0 % DA) / 2;
     const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qb + (size_t)qload * rs + d0);
-    qreg[ks] = __builtin_bit_cast(bf16x8_t,
-                                  rope_chunk(x, pos[4 * qload + a], &fr.hi[j0], &fr.lo[j0], qscale));
+    qreg[ks] = __builtin_bit_cast(
+        f16x8_t, rope_chunk<true>(x, pos[4 * qload + a], &fr.hi[j0], &fr.lo[j0], qscale));
   }
 
   // ---- staging assignment (per group of 256 threads): chunk lc of a row
@@ -151,7 +159,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
       const int key = kk0 + it;                         // 0..31 within the half
       const int row = 32 * half + key_to_row(key);
       *reinterpret_cast<u32x4_t*>(&k_lds[buf][row * KROW + 8 * lc]) =
-          rope_chunk(kx[it], kp[it], whi, wlo, 1.0f);
+          rope_chunk<true>(kx[it], kp[it], whi, wlo, 1.0f);
     }
   };
   auto stage_v = [&](int buf) {
@@ -186,9 +194,9 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+        const f16x8_t a = *reinterpret_cast<const f16x8_t*>(
             &k_lds[buf][(32 * kbk + lr) * KROW + 16 * ks + 8 * g]);
-        sc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sc[kbk], 0, 0, 0);
+        sc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qreg[ks], sc[kbk], 0, 0, 0);
       }
   };
   // O^T += V^T(tile in buf) P^T

@@ -10,6 +10,8 @@ namespace klein {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -53,10 +55,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Rotate one 16-byte chunk: 8 consecutive channels = 4 interleaved pairs of a
-// single axis block, pairs j0 .. j0+3, at integer position p on that axis.
-// Each pair (x, y) -> (x cos - y sin, x sin + y cos), then * scale, -> bf16.
+// two floats -> packed f16x2, round to nearest even
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  f16x2_t r = __builtin_convertvector((f32x2_t){a, b}, f16x2_t);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Rotate one 16-byte chunk of bf16: 8 consecutive channels = 4 interleaved
+// pairs of a single axis block, pairs j0 .. j0+3, at integer position p on
+// that axis.  Each pair (x, y) -> (x cos - y sin, x sin + y cos), then
+// * scale, rounded to bf16 (F16 = false) or to fp16 (F16 = true).
 // v_sin_f32 / v_cos_f32 take their argument in revolutions.
+template <bool F16 = false>
 __device__ __forceinline__ u32x4_t rope_chunk(u32x4_t x, int p, const float* whi,
                                               const float* wlo, float scale) {
   const float fp = (float)p;
@@ -68,7 +78,8 @@ __device__ __forceinline__ u32x4_t rope_chunk(u32x4_t x, int p, const float* whi
     const float c = __builtin_amdgcn_cosf(rev);
     const float a = bf16_lo(x[jj]);
     const float b = bf16_hi(x[jj]);
-    y[jj] = pack_bf16x2((a * c - b * s) * scale, (a * s + b * c) * scale);
+    const float u = (a * c - b * s) * scale, w = (a * s + b * c) * scale;
+    y[jj] = F16 ? pack_f16x2(u, w) : pack_bf16x2(u, w);
   }
   return y;
 }

@@ -56,6 +56,19 @@ def test_workload_sampled_rows(cid, overrides):
     inp = make_inputs(cfg)
     _print_case("workload", cid, overrides, inp.q.shape)
     out = run_attention(inp)
-    rows = sample_rows(cfg.S, cfg.text, n=24, seed=cid)
+    rows = sample_rows(cfg.S, cfg.text, n=64, seed=cid)
     gpu = bf16_tensor_to_f64(out[:, torch.from_numpy(rows).to(out.device)])
     assert_bf16_close(gpu, oracle_rows(inp, rows), f"workload {cid} {overrides}")
+
+
+def test_large_magnitudes_within_documented_range():
+    """Scores run on fp16 operands: |k| up to ~4e4 and |q| up to ~3e5 must work."""
+    inp = random_inputs(1, 150, 2, 128, seed=91)
+    from workloads import bf16_bits_from_f32
+    import oracle
+    k = oracle.bf16_to_f64(inp.k) * 3.0e4 / 4.5          # max |k| ~ 3e4
+    inp.k = bf16_bits_from_f32(k.astype(np.float32))
+    q = oracle.bf16_to_f64(inp.q) * 1.0e-3
+    inp.q = bf16_bits_from_f32(q.astype(np.float32))
+    out = bf16_tensor_to_f64(run_attention(inp))
+    assert_bf16_close(out, oracle_full(inp), "large |k|")
