@@ -17,7 +17,6 @@ Prints ONE JSON line.  Fields beyond the common ones:
 """
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -29,28 +28,18 @@ sys.path.insert(0, ROOT)
 METRIC = "joint-attention TFLOP/s + % MFMA peak at 2048² (16,896 tok, 24 heads×128)"
 PEAK_BF16 = 2516.6      # dense bf16 MFMA, TFLOP/s (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_FP8 = 5033.2       # dense fp8 MFMA, TFLOP/s
-KERNEL_SOURCES = ["klein_device.hpp", "attn_fwd_bf16.hip"]
-KERNEL_SOURCES_FP8 = ["klein_device.hpp", "attn_fwd_fp8.hip"]
-
-
-def sources_hash(names):
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "joint_attention_rope_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
-def stored_traffic(kind, names):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kind}.json")
+def stored_traffic(name, kernel):
+    """Memory bytes per launch from a committed rocprofv3 counter summary
+    (profiles/traffic_<name>.json), if it was taken on the current kernel
+    sources; else None."""
+    from joint_attention_rope_amd.profiling import KERNEL_SOURCES, sources_hash
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("sources_hash") != sources_hash(names):
+    if rec.get("sources_hash") != sources_hash(KERNEL_SOURCES[kernel]):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -117,6 +106,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after timing, run an elementwise fp32 copy of MIB MiB three "
+                         "times (a kernel of known HBM traffic for scaling counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -136,7 +128,7 @@ def main():
     ms = time_gpu(lambda: kl.klein_rope4d_attn_fwd(q, k, v, pos, out), args.steps,
                   args.warmup, torch)
     tflops = cfg.flops / (ms * 1e-3) / 1e12
-    traffic = stored_traffic("attn_fwd_bf16_2048px_t2i_cfg", KERNEL_SOURCES)
+    traffic = stored_traffic("attn_fwd_bf16_2048px_t2i_cfg", "attn_fwd_bf16_kernel")
     rec = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -173,10 +165,19 @@ def main():
                           "ms_per_call": round(ms5, 4), "tflops": round(t5, 2),
                           "peak": PEAK_FP8, "frac": round(t5 / PEAK_FP8, 4),
                           "traffic": stored_traffic("attn_fwd_fp8_2048px_edit",
-                                                    KERNEL_SOURCES_FP8)}
+                                                    "attn_fwd_fp8_kernel")}
             del q5, k5, v5, o5
         except kl.KleinError as e:
             rec["fp8"] = {"error": str(e)}
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)        # reads 4n bytes, writes 4n bytes
+        torch.cuda.synchronize()
+        rec["copy_calibration_bytes"] = 4 * n
+        del src, dst
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

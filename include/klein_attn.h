@@ -36,6 +36,10 @@
  *    stated for |pos| < 4096 on every axis (larger values are accepted, with
  *    angle error growing like |pos| * 2^-24 revolutions).
  *  - D must be 64 or 128; B, S, H >= 1; B*H*ceil(S/256) < 2^31.
+ *  - bf16 path: the rotated Q (times log2(e)/sqrt(D)) and K are held on chip
+ *    as fp16 for the score products (three more mantissa bits than bf16), so
+ *    elementwise |k| must stay below ~46000 and |q| below ~360000; larger
+ *    magnitudes overflow fp16.  P and V are bf16; accumulation is fp32.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL means the null
  *    stream).  The status reports argument and launch errors only, never
  *    results of device work.  Argument checks run before any HIP call, so an
