@@ -2,20 +2,23 @@
 //
 // One workgroup owns one (batch, head, tile of BM = 256 queries) and streams
 // every key of the sequence (no mask: all tokens attend to all tokens) in tiles
-// of BN = 64 keys.  It runs 8 waves, 32 queries each, two waves per SIMD:
-// group A = waves 0-3 and group B = waves 4-7, so each SIMD holds one wave of
-// each group.  The groups ping-pong: while one group issues its MFMAs, the
-// other does its VALU work on the same SIMDs, and a workgroup barrier ends
-// each phase:
+// of BN = 64 keys.  Its 8 waves (two per SIMD) own 32 queries each and run the
+// same software pipeline; K' and V^T are double-buffered in LDS and one
+// workgroup barrier per tile separates producers from consumers:
 //
-//   phase X_t:  A: O^T += V(t-1)^T P(t-1)^T ; S(t) = K'(t) Q'^T      [MFMA]
-//               B: P(t-1) = softmax step of S(t-1); stage V(t), half of K(t+1)
-//   phase Y_t:  A: P(t) = softmax step of S(t); stage the other half of K(t+1)
-//               B: O^T += V(t-1)^T P(t-1)^T ; S(t) = K'(t) Q'^T      [MFMA]
+//   iteration t (S(t) already in registers):
+//     softmax max of S(t); rare rescale of O and l
+//     region A:  S(t+1) = K'(t+1) Q'^T  (16 MFMAs)       interleaved with
+//                P(t) = 2^(S(t) - m), row sums, bf16 pack   (VALU)
+//     region B:  O^T += V(t)^T P(t)^T  (16 MFMAs)        interleaved with
+//                staging K'(t+2) (RoPE-4D) and V(t+1)^T into LDS, and the
+//                buffer loads of K(t+3), V(t+2) from HBM
+//     barrier
 //
-// "Staging" moves a tile from registers (loaded from HBM a phase earlier) to
-// LDS: K is rotated by RoPE-4D on the way, V is transposed to V^T.  K and V^T
-// are double-buffered in LDS (tile t in buffer t & 1).
+// Each wave overlaps its own MFMAs with its own VALU work, and both waves of
+// a SIMD issue VALU: measured on this chip, one wave alone issues VALU at
+// about half the rate two waves reach together, and the softmax / RoPE VALU
+// work per tile is as large as the MFMA work.
 //
 // Precision: the rotated Q' (times log2(e)/sqrt(D)) and K' are rounded to
 // fp16, not bf16, and S^T = K' Q'^T runs on v_mfma_f32_32x32x16_f16 (same
@@ -29,19 +32,24 @@
 // its columns, so a lane holds 16 keys of one query and the row max / row sum
 // need one exchange with the lane 32 apart.  O^T += V^T P^T
 // (v_mfma_f32_32x32x16_bf16) uses P straight from the S^T accumulators (as
-// bf16) as the B operand.  Keys of a tile sit in LDS in a permuted row order so that
-// accumulator register i of a lane in half g holds key 16g + i of its 32-key
-// block; P's registers 8j..8j+7 then pair with the 8 contiguous keys
+// bf16) as the B operand.  Keys of a tile sit in LDS in a permuted row order
+// so that accumulator register i of a lane in half g holds key 16g + i of its
+// 32-key block; P's registers 8j..8j+7 then pair with the 8 contiguous keys
 // 16g + 8j .. 16g + 8j + 7 of a V^T row, one 16-byte LDS read.
 //
-// Softmax runs in the exp2 domain (Q carries log2(e)/sqrt(D)).  O and l are
-// rescaled only when a row's running max grows by more than TAU = 8, so
-// p = 2^(s - m) <= 2^8 in between; the final O / l is the same either way.
+// Softmax runs in the exp2 domain (Q carries log2(e)/sqrt(D)).  The score
+// MFMA chains start from -m (the running row max) rather than zero, so the
+// accumulators hold s - m directly.  O and l are rescaled only when a row's
+// max grows by more than TAU = 8, so p = 2^(s - m) <= 2^8 in between; the
+// final O / l is the same either way.
 //
 // LDS bank spreading: K rows are padded by 16 bytes (the 16 lanes of one
-// 16-byte read phase hit 16 consecutive rows); V^T rows (64 keys, 128 bytes)
-// are unpadded and their 8-key chunks are XOR-swizzled by (d ^ (d >> 3)) & 7,
-// which keeps both the MFMA operand reads and the transposing stores spread.
+// 16-byte read phase hit 16 consecutive rows).  V^T rows (64 keys, 128 bytes)
+// are unpadded; 8-key chunk c of row d sits at chunk c ^ s(d mod 32),
+// s(r) = (r >> 1) & 7.  The swizzle depends only on the row inside a 32-row
+// MFMA block, so each lane's four V^T operand addresses are fixed per lane
+// (plus a constant per block), and both the reads and the transposing
+// stores stay spread over the banks.
 #include "klein_device.hpp"
 #include "klein_launch.hpp"
 
@@ -61,24 +69,23 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     uint16_t* __restrict__ out, int S, int H, int nqt, RopeFreqs fr, float qscale) {
   constexpr int BM = 256;              // queries per workgroup (8 waves x 32)
   constexpr int BN = 64;               // keys per tile
+  constexpr int NT = 512;              // threads
   constexpr int CPR = D / 8;           // 16-byte chunks per token row
-  constexpr int KPV = BN * CPR / 256;  // keys per thread when a group stages V
-  constexpr int KPK = 32 * CPR / 256;  // keys per thread when a group stages half of K
+  constexpr int KPT = BN * CPR / NT;   // keys per thread when staging a tile
   constexpr int KS = D / 16;           // MFMA k-steps of Q K^T
   constexpr int MB = D / 32;           // 32-row blocks of O^T
-  constexpr int KROW = D + 8;          // LDS row stride of K (bf16), padded
+  constexpr int KROW = D + 8;          // LDS row stride of K' (16-bit), padded
   constexpr int VROW = BN;             // LDS row stride of V^T (bf16), swizzled
   constexpr int DA = D / 4;            // channels per RoPE axis
   constexpr float TAU = 8.0f;
-  static_assert(KPV >= 2 && KPV % 2 == 0 && KPK >= 1, "tile/thread split");
+  static_assert(KPT >= 1 && (BN * CPR) % NT == 0, "tile/thread split");
+  static_assert(KPT == 1 || KPT % 2 == 0, "V^T store packs key pairs");
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VROW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lr = lane & 31;
-  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);   // 0 = A, 1 = B (wave-uniform)
-  const int gt = tid & 255;            // thread index inside the group
 
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int qt = work % nqt;
@@ -90,7 +97,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   const uint16_t* kb = k + base;
   const uint16_t* vb = v + base;
 
-  // ---- this lane's query: rotate, scale by log2(e)/sqrt(D), keep in VGPRs.
+  // ---- this lane's query: rotate, scale by log2(e)/sqrt(D), fp16 in VGPRs.
   // Rows past S load row S-1 (in bounds) and are never stored.
   const int qrow = qt * BM + wave * 32 + lr;
   const int qload = qrow < S ? qrow : S - 1;
@@ -104,73 +111,71 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
         f16x8_t, rope_chunk<true>(x, pos[4 * qload + a], &fr.hi[j0], &fr.lo[j0], qscale));
   }
 
-  // ---- staging assignment (per group of 256 threads): chunk lc of a row
-  const int lc = gt % CPR;
-  const int vk0 = (gt / CPR) * KPV;    // V: keys vk0 .. vk0+KPV-1 of the tile
-  const int kk0 = (gt / CPR) * KPK;    // K: keys kk0 .. kk0+KPK-1 of a half tile
+  // ---- staging assignment.  K: chunk lc of keys lk .. lk+KPT-1 (16 lanes per
+  // key row, full 256-byte rows per load).  V: chunk vc of keys vk .. vk+KPT-1
+  // with consecutive lanes on consecutive key groups (spreads the V^T stores).
+  const int lc = tid % CPR;
+  const int lk = (tid / CPR) * KPT;
+  const int vk = (tid % (BN / KPT)) * KPT;
+  const int vc = tid / (BN / KPT);
   const int la = (8 * lc) / DA, lj0 = ((8 * lc) % DA) / 2;
   float whi[4], wlo[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) { whi[jj] = fr.hi[lj0 + jj]; wlo[jj] = fr.lo[lj0 + jj]; }
 
-  const int nkt = (S + BN - 1) / BN;
-  u32x4_t kx[KPK], vx[KPV];
-  int kp[KPK];
-
   // Global -> registers through buffer loads.  Each tile gets a descriptor
   // whose base is the tile's first row and whose size covers only the rows
   // that exist, so the hardware returns zeros for rows past S (no clamping and
-  // no per-load address arithmetic: the per-thread byte offsets below are
-  // fixed for the whole loop).
+  // no per-load address arithmetic: the per-thread byte offsets are fixed).
   const int rowb = (int)(rs * 2);                          // bytes per token row
-  int voff_k[KPK], voff_p[KPK], voff_v[KPV];
-#pragma unroll
-  for (int it = 0; it < KPK; ++it) {
-    voff_k[it] = (32 * grp + kk0 + it) * rowb + 16 * lc;
-    voff_p[it] = ((32 * grp + kk0 + it) * 4 + la) * 4;
-  }
-#pragma unroll
-  for (int it = 0; it < KPV; ++it) voff_v[it] = (vk0 + it) * rowb + 16 * lc;
+  // byte offsets of key lk / vk (key + it adds it * rowb, a scalar offset)
+  const int voff = lk * rowb + 16 * lc;
+  const int voff_v = vk * rowb + 16 * vc;
+  const int voff_p = (lk * 4 + la) * 4;
+  const int nkt = (S + BN - 1) / BN;
+  u32x4_t kx[KPT], vx[KPT];
+  int kp[KPT];
   auto tile_rows = [&](int kt) {
     const int n = S - kt * BN;
     return n < 0 ? 0 : (n > BN ? BN : n);
   };
-  auto load_k_half = [&](int kt, int half) {
+  auto load_k = [&](int kt) {
     const int n = tile_rows(kt);
     const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(kb + (size_t)kt * BN * rs, n * rowb);
     const __amdgpu_buffer_rsrc_t rp = uniform_rsrc(pos + (size_t)kt * BN * 4, n * 16);
-    (void)half;   // the offsets already select this group's half
 #pragma unroll
-    for (int it = 0; it < KPK; ++it) {
-      kx[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, voff_k[it], 0, 0));
-      kp[it] = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, voff_p[it], 0, 0);
+    for (int it = 0; it < KPT; ++it) {
+      kx[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, voff, it * rowb, 0));
+      kp[it] = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, voff_p, it * 16, 0);
     }
   };
   auto load_v = [&](int kt) {
     const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(vb + (size_t)kt * BN * rs, tile_rows(kt) * rowb);
 #pragma unroll
-    for (int it = 0; it < KPV; ++it)
-      vx[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v[it], 0, 0));
+    for (int it = 0; it < KPT; ++it)
+      vx[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v, it * rowb, 0));
   };
-  // Registers -> LDS: K rotated, at its permuted row; V transposed to V^T.
-  auto stage_k_half = [&](int buf, int half) {
+  // Registers -> LDS: K rotated (fp16), at its permuted row; V transposed.
+  auto stage_k = [&](int buf) {
 #pragma unroll
-    for (int it = 0; it < KPK; ++it) {
-      const int key = kk0 + it;                         // 0..31 within the half
-      const int row = 32 * half + key_to_row(key);
+    for (int it = 0; it < KPT; ++it) {
+      const int key = lk + it;
+      const int row = (key & ~31) + key_to_row(key & 31);
       *reinterpret_cast<u32x4_t*>(&k_lds[buf][row * KROW + 8 * lc]) =
           rope_chunk<true>(kx[it], kp[it], whi, wlo, 1.0f);
     }
   };
-  auto stage_v = [&](int buf) {
+  auto stage_v_word = [&](int buf, int e) {
+    const int d = 8 * vc + e;
+    uint16_t* vrow = &v_lds[buf][d * VROW];
+    const int sw = ((d & 31) >> 1) & 7;
+    if constexpr (KPT == 1) {
+      const uint32_t w = vx[0][e >> 1];
+      vrow[(((vk >> 3) ^ sw) << 3) + (vk & 7)] = (uint16_t)((e & 1) ? (w >> 16) : w);
+    } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * lc + e;
-      uint16_t* vrow = &v_lds[buf][d * VROW];
-      const int sw = (d ^ (d >> 3)) & 7;
-#pragma unroll
-      for (int it = 0; it < KPV; it += 2) {
-        const int key = vk0 + it;
+      for (int it = 0; it < KPT; it += 2) {
+        const int key = vk + it;
         const uint32_t w0 = vx[it][e >> 1], w1 = vx[it + 1][e >> 1];
         const uint32_t pk = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))
                                     : ((w0 & 0xffffu) | (w1 << 16));
@@ -178,47 +183,68 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
       }
     }
   };
+  auto stage_v = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) stage_v_word(buf, e);
+  };
+  // this lane's V^T operand offsets (elements) for (kbk, j) of block mb = 0;
+  // block mb adds 32 * mb * VROW
+  int voffr[2][2];
+  {
+    const int sw = (lr >> 1) & 7;
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        voffr[kbk][j] = lr * VROW + (((4 * kbk + 2 * g + j) ^ sw) << 3);
+  }
 
   f32x16_t o[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) o[mb] = (f32x16_t){};
-  f32x16_t sc[2];
-  uint32_t pw[2][8];
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = 0.f, l_run = 0.f;
 
-  // S^T = K'(tile in buf) Q'^T, two 32-key blocks
-  auto gemm1 = [&](int buf) {
+  // S^T = K'(tile in buf) Q'^T, two 32-key blocks, each a chain of KS MFMAs
+  // (used on its own only in the prologue)
+  auto qk = [&](int buf, f32x16_t* s) {
 #pragma unroll
-    for (int kbk = 0; kbk < 2; ++kbk) sc[kbk] = (f32x16_t){};
+    for (int kbk = 0; kbk < 2; ++kbk) {
+      s[kbk] = (f32x16_t){};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int kbk = 0; kbk < 2; ++kbk) {
+      for (int ks = 0; ks < KS; ++ks) {
         const f16x8_t a = *reinterpret_cast<const f16x8_t*>(
             &k_lds[buf][(32 * kbk + lr) * KROW + 16 * ks + 8 * g]);
-        sc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qreg[ks], sc[kbk], 0, 0, 0);
+        s[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qreg[ks], s[kbk], 0, 0, 0);
       }
+    }
   };
-  // O^T += V^T(tile in buf) P^T
-  auto gemm2 = [&](int buf) {
+  // Scores are kept relative to the running max: the S MFMA chains start
+  // from C = cinit = -m_run instead of zero, so S' = S - m needs no VALU
+  // subtraction.  Row max of the 32 values a lane holds, as a max3 tree.
+  auto rowmax32 = [&](const f32x16_t* sc) {
+    float m[12];
 #pragma unroll
-    for (int kbk = 0; kbk < 2; ++kbk)
+    for (int i = 0; i < 10; ++i) {
+      const int a = 3 * i, b = 3 * i + 1, c = 3 * i + 2;
+      m[i] = __builtin_fmaxf(sc[a >> 4][a & 15],
+                             __builtin_fmaxf(sc[b >> 4][b & 15], sc[c >> 4][c & 15]));
+    }
+    m[10] = sc[1][14];
+    m[11] = sc[1][15];
+    float n[4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const u32x4_t pv = {pw[kbk][4 * j], pw[kbk][4 * j + 1], pw[kbk][4 * j + 2], pw[kbk][4 * j + 3]};
-        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int d = 32 * mb + lr;
-          const int kc = 4 * kbk + 2 * g + j;
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-              &v_lds[buf][d * VROW + ((kc ^ ((d ^ (d >> 3)) & 7)) << 3)]);
-          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[mb], 0, 0, 0);
-        }
-      }
+    for (int i = 0; i < 4; ++i) n[i] = __builtin_fmaxf(m[3 * i], __builtin_fmaxf(m[3 * i + 1], m[3 * i + 2]));
+    return pair_max(__builtin_fmaxf(n[0], __builtin_fmaxf(n[1], __builtin_fmaxf(n[2], n[3]))));
   };
-  // P(t) from S(t): mask keys past S, lazy rescale, exp2, row sum, pack to bf16
-  auto softmax = [&](int t) {
+  f32x16_t cinit;
+  auto set_cinit = [&]() {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cinit[i] = -m_run;
+  };
+  // mask keys past S (last tile only), then the rare rescale: when some row's
+  // max rose more than TAU above m_run, m_run moves up by delta, O and l take
+  // 2^-delta, and the relative scores of this tile shift by -delta
+  auto softmax_max = [&](int t, f32x16_t* sc) {
     if (t * BN + BN > S) {
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk)
@@ -226,86 +252,150 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
         for (int i = 0; i < 16; ++i)
           if (t * BN + 32 * kbk + 16 * g + i >= S) sc[kbk][i] = kNegInf;
     }
-    // row max as a balanced tree (the VALU wave has no partner to hide
-    // the latency of a serial chain)
-    float m8[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      m8[i] = __builtin_fmaxf(__builtin_fmaxf(sc[0][i], sc[0][i + 8]),
-                              __builtin_fmaxf(sc[1][i], sc[1][i + 8]));
-#pragma unroll
-    for (int w = 4; w >= 1; w >>= 1)
-#pragma unroll
-      for (int i = 0; i < w; ++i) m8[i] = __builtin_fmaxf(m8[i], m8[i + w]);
-    const float mx = pair_max(m8[0]);
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU)) {
-      const float m_new = __builtin_fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+    const float mx = rowmax32(sc);
+    if (__builtin_amdgcn_ballot_w64(mx > TAU)) {
+      const float delta = __builtin_fmaxf(mx, 0.f);
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      m_run += delta;
       l_run *= alpha;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) o[mb] *= alpha;
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk) sc[kbk] -= delta;
+      set_cinit();
     }
-    // p = 2^(s - m); four independent partial row sums
+  };
+
+  // Region A: S(t+1) = K'(t+1) Q'^T (2 KS MFMAs, operands read two MFMAs
+  // ahead) with one slice of the softmax of S(t) after each MFMA; the
+  // sched_barrier fences keep the compiler from regrouping the slices.
+  constexpr int NA = 2 * KS;                 // MFMAs in region A
+  const bf16x2_t kOnesBf16x2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+  constexpr int SA = 16;                     // softmax slices (2 scores each)
+  auto region_a = [&](int kbuf, const f32x16_t* cur, f32x16_t* nxt, uint32_t (*pw)[8]) {
+    f16x8_t ka[NA];
+    auto read_k = [&](int i) {
+      const int kbk = i / KS, ks = i % KS;
+      ka[i] = *reinterpret_cast<const f16x8_t*>(
+          &k_lds[kbuf][(32 * kbk + lr) * KROW + 16 * ks + 8 * g]);
+    };
+    nxt[0] = cinit;
+    nxt[1] = cinit;
+    read_k(0);
+    read_k(1);
     float ls4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      if (i + 2 < NA) read_k(i + 2);
+      const int kbk = i / KS, ks = i % KS;
+      nxt[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[i], qreg[ks], nxt[kbk], 0, 0, 0);
+#pragma unroll
+      for (int sl = i * SA / NA; sl < (i + 1) * SA / NA; ++sl) {
+        const int kb2 = sl >> 3, w = sl & 7;
+        const float p0 = __builtin_amdgcn_exp2f(cur[kb2][2 * w]);
+        const float p1 = __builtin_amdgcn_exp2f(cur[kb2][2 * w + 1]);
+        const uint32_t pk = pack_bf16x2(p0, p1);
+        pw[kb2][w] = pk;
+        // row sum of the bf16 P that the MFMA consumes: one dot2 per pair
+        ls4[w & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk),
+                                                     kOnesBf16x2, ls4[w & 3], false);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
+  };
+
+  // Region B: O^T += V(t)^T P(t)^T (4 MB MFMAs) with the staging of K'(t+2)
+  // (RoPE-4D, one pair per slice) and V(t+1)^T (one transposed word per
+  // slice) spread over the MFMAs; then the loads of K(t+3), V(t+2).
+  constexpr int NB = 4 * MB;                 // MFMAs in region B
+  constexpr int NROT = 4 * KPT;              // RoPE pairs to stage
+  constexpr int NVW = 8;                     // V^T words (or halfwords) to stage
+  constexpr int NIT = NROT + NVW;
+  auto region_b = [&](int vbuf, int kdst, int vdst, const uint32_t (*pw)[8]) {
+    bf16x8_t va[NB];
+    auto read_v = [&](int i) {
+      const int mb = i / 4, kbk = (i >> 1) & 1, j = i & 1;
+      va[i] = *reinterpret_cast<const bf16x8_t*>(
+          &v_lds[vbuf][voffr[kbk][j] + 32 * mb * VROW]);
+    };
+    read_v(0);
+    read_v(1);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (i + 2 < NB) read_v(i + 2);
+      const int mb = i / 4, kbk = (i >> 1) & 1, j = i & 1;
+      const u32x4_t pvw = {pw[kbk][4 * j], pw[kbk][4 * j + 1], pw[kbk][4 * j + 2],
+                           pw[kbk][4 * j + 3]};
+      o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], __builtin_bit_cast(bf16x8_t, pvw),
+                                                      o[mb], 0, 0, 0);
+#pragma unroll
+      for (int item = i * NIT / NB; item < (i + 1) * NIT / NB; ++item) {
+        if (item < NROT) {
+          // one RoPE pair of K chunk c
+          const int c = item / 4, jj = item % 4;
+          const float fp = (float)kp[c];
+          const float rev = __builtin_amdgcn_fractf(fp * whi[jj]) + fp * wlo[jj];
+          const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+          const float xa = bf16_lo(kx[c][jj]), xb = bf16_hi(kx[c][jj]);
+          const int key = lk + c;
+          const int row = (key & ~31) + key_to_row(key & 31);
+          *reinterpret_cast<uint32_t*>(&k_lds[kdst][row * KROW + 8 * lc + 2 * jj]) =
+              pack_f16x2(xa * cs - xb * sn, xa * sn + xb * cs);
+        } else {
+          stage_v_word(vdst, item - NROT);     // one V^T word
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- prologue: K'(0), K'(1), V(0)^T in LDS; S(0) in registers; K(2), V(1)
+  // in flight
+  load_k(0);
+  load_v(0);
+  stage_k(0);
+  stage_v(0);
+  load_k(1);
+  stage_k(1);
+  load_k(2);
+  load_v(1);
+  __syncthreads();
+  f32x16_t sa[2], sb[2];
+  uint32_t pw[2][8];
+  qk(0, sa);
+  __syncthreads();        // K buffer 0 is refilled in iteration 0
+  // m_run starts at tile 0's exact row max (keys past S masked), so scores
+  // are relative from the first tile on and no row can underflow
+  if (BN > S) {
 #pragma unroll
     for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const float p0 = __builtin_amdgcn_exp2f(sc[kbk][2 * w] - m_run);
-        const float p1 = __builtin_amdgcn_exp2f(sc[kbk][2 * w + 1] - m_run);
-        ls4[(2 * w) & 3] += p0;
-        ls4[(2 * w + 1) & 3] += p1;
-        pw[kbk][w] = pack_bf16x2(p0, p1);
-      }
-    const float ls = (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
-    l_run += ls;
-  };
-
-  // ---- prologue: K(0) into LDS (half per group); each group pre-loads what
-  // its first VALU phase stages (A: K(1) half 0; B: V(0), K(1) half 1)
-  load_k_half(0, grp);
-  stage_k_half(0, grp);
-  load_k_half(1, grp);
-  if (grp == 1) load_v(0);
-  __syncthreads();
-
-  // Each group runs its own copy of the loop, so values one group keeps
-  // across phases never occupy registers in the other.  Both copies execute
-  // exactly two barriers per iteration, in step.  MFMA phases hold only LDS
-  // reads and MFMAs; a group issues the global loads for its next VALU phase
-  // at the end of its current one, so they fly during its MFMA phase.
-  if (grp == 0) {
-    for (int t = 0; t <= nkt; ++t) {
-      // X_t: MFMA phase
-      if (t >= 1) gemm2((t - 1) & 1);
-      if (t < nkt) gemm1(t & 1);
-      __syncthreads();
-      // Y_t: VALU phase
-      if (t < nkt) {
-        softmax(t);
-        stage_k_half((t + 1) & 1, 0);                // K(t+1) half 0
-        load_k_half(t + 2, 0);                       // staged in Y_{t+1}
-      }
-      __syncthreads();
-    }
-  } else {
-    for (int t = 0; t <= nkt; ++t) {
-      // X_t: VALU phase
-      if (t >= 1) softmax(t - 1);
-      if (t < nkt) {
-        stage_v(t & 1);                              // V(t)
-        stage_k_half((t + 1) & 1, 1);                // K(t+1) half 1
-        load_v(t + 1);                               // staged in X_{t+1}
-        load_k_half(t + 2, 1);
-      }
-      __syncthreads();
-      // Y_t: MFMA phase
-      if (t >= 1) gemm2((t - 1) & 1);
-      if (t < nkt) gemm1(t & 1);
-      __syncthreads();
-    }
+      for (int i = 0; i < 16; ++i)
+        if (32 * kbk + 16 * g + i >= S) sa[kbk][i] = kNegInf;
   }
+  m_run = rowmax32(sa);
+#pragma unroll
+  for (int kbk = 0; kbk < 2; ++kbk) sa[kbk] -= m_run;
+  set_cinit();
+
+  // one pipeline step; `cur` holds S(t), `nxt` receives S(t+1)
+  auto step = [&](int t, f32x16_t* cur, f32x16_t* nxt) {
+    softmax_max(t, cur);
+    region_a((t + 1) & 1, cur, nxt, pw);
+    // K(t+2) into buffer t&1 (it held K(t), consumed last step); V(t+1) into
+    // buffer (t+1)&1 (it held V(t-1), consumed last step)
+    region_b(t & 1, t & 1, (t + 1) & 1, pw);
+    load_k(t + 3);
+    load_v(t + 2);
+    __syncthreads();
+  };
+  int t = 0;
+  for (; t + 1 < nkt; t += 2) {
+    step(t, sa, sb);
+    step(t + 1, sb, sa);
+  }
+  if (t < nkt) step(t, sa, sb);
 
   // ---- epilogue: O / l, bf16, store (lane holds channels 32mb + 8(i/4) + 4g + i%4)
   const float inv = 1.0f / pair_sum(l_run);
