@@ -43,13 +43,17 @@
 // max grows by more than TAU = 8, so p = 2^(s - m) <= 2^8 in between; the
 // final O / l is the same either way.
 //
+// V stays row-major in LDS ([key][d], staged with plain 16-byte copies) and
+// the V^T operand of O^T += V^T P^T is read with ds_read_b64_tr_b16: inside a
+// 16-lane group, lane i receives element i % 4 of the 8-byte words addressed
+// by lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.  Pointing lane L at
+// V[key0 + L/4][d0 + 4 (L % 4) .. + 3] hands lane i keys key0 .. key0+3 of
+// channel d0 + i; two such reads give the 8 keys of one MFMA operand.
+//
 // LDS bank spreading: K rows are padded by 16 bytes (the 16 lanes of one
-// 16-byte read phase hit 16 consecutive rows).  V^T rows (64 keys, 128 bytes)
-// are unpadded; 8-key chunk c of row d sits at chunk c ^ s(d mod 32),
-// s(r) = (r >> 1) & 7.  The swizzle depends only on the row inside a 32-row
-// MFMA block, so each lane's four V^T operand addresses are fixed per lane
-// (plus a constant per block), and both the reads and the transposing
-// stores stay spread over the banks.
+// 16-byte read phase hit 16 consecutive rows); V rows by 64 bytes, so the 4
+// rows x 64 bytes a 32-lane transposing read phase touches fall on disjoint
+// banks.  Every operand address is a per-lane base plus a constant.
 #include "klein_device.hpp"
 #include "klein_launch.hpp"
 
@@ -75,14 +79,14 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   constexpr int KS = D / 16;           // MFMA k-steps of Q K^T
   constexpr int MB = D / 32;           // 32-row blocks of O^T
   constexpr int KROW = D + 8;          // LDS row stride of K' (16-bit), padded
-  constexpr int VROW = BN;             // LDS row stride of V^T (bf16), swizzled
+  constexpr int VROW = D + 32;         // LDS row stride of V (bf16), padded
   constexpr int DA = D / 4;            // channels per RoPE axis
   constexpr float TAU = 8.0f;
   static_assert(KPT >= 1 && (BN * CPR) % NT == 0, "tile/thread split");
   static_assert(KPT == 1 || KPT % 2 == 0, "V^T store packs key pairs");
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VROW];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BN * VROW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lr = lane & 31;
@@ -111,13 +115,10 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
         f16x8_t, rope_chunk<true>(x, pos[4 * qload + a], &fr.hi[j0], &fr.lo[j0], qscale));
   }
 
-  // ---- staging assignment.  K: chunk lc of keys lk .. lk+KPT-1 (16 lanes per
-  // key row, full 256-byte rows per load).  V: chunk vc of keys vk .. vk+KPT-1
-  // with consecutive lanes on consecutive key groups (spreads the V^T stores).
+  // ---- staging assignment: chunk lc of keys lk .. lk+KPT-1 of a K or V tile
+  // (CPR lanes per key row, whole rows per load)
   const int lc = tid % CPR;
   const int lk = (tid / CPR) * KPT;
-  const int vk = (tid % (BN / KPT)) * KPT;
-  const int vc = tid / (BN / KPT);
   const int la = (8 * lc) / DA, lj0 = ((8 * lc) % DA) / 2;
   float whi[4], wlo[4];
 #pragma unroll
@@ -128,9 +129,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   // that exist, so the hardware returns zeros for rows past S (no clamping and
   // no per-load address arithmetic: the per-thread byte offsets are fixed).
   const int rowb = (int)(rs * 2);                          // bytes per token row
-  // byte offsets of key lk / vk (key + it adds it * rowb, a scalar offset)
+  // byte offsets of key lk (key lk + it adds it * rowb, a scalar offset)
   const int voff = lk * rowb + 16 * lc;
-  const int voff_v = vk * rowb + 16 * vc;
   const int voff_p = (lk * 4 + la) * 4;
   const int nkt = (S + BN - 1) / BN;
   u32x4_t kx[KPT], vx[KPT];
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(vb + (size_t)kt * BN * rs, tile_rows(kt) * rowb);
 #pragma unroll
     for (int it = 0; it < KPT; ++it)
-      vx[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v, it * rowb, 0));
+      vx[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, it * rowb, 0));
   };
   // Registers -> LDS: K rotated (fp16), at its permuted row; V transposed.
   auto stage_k = [&](int buf) {
@@ -165,39 +165,18 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
           rope_chunk<true>(kx[it], kp[it], whi, wlo, 1.0f);
     }
   };
-  auto stage_v_word = [&](int buf, int e) {
-    const int d = 8 * vc + e;
-    uint16_t* vrow = &v_lds[buf][d * VROW];
-    const int sw = ((d & 31) >> 1) & 7;
-    if constexpr (KPT == 1) {
-      const uint32_t w = vx[0][e >> 1];
-      vrow[(((vk >> 3) ^ sw) << 3) + (vk & 7)] = (uint16_t)((e & 1) ? (w >> 16) : w);
-    } else {
-#pragma unroll
-      for (int it = 0; it < KPT; it += 2) {
-        const int key = vk + it;
-        const uint32_t w0 = vx[it][e >> 1], w1 = vx[it + 1][e >> 1];
-        const uint32_t pk = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))
-                                    : ((w0 & 0xffffu) | (w1 << 16));
-        *reinterpret_cast<uint32_t*>(&vrow[(((key >> 3) ^ sw) << 3) + (key & 7)]) = pk;
-      }
-    }
+  auto stage_v_chunk = [&](int buf, int it) {
+    *reinterpret_cast<u32x4_t*>(&v_lds[buf][(lk + it) * VROW + 8 * lc]) = vx[it];
   };
   auto stage_v = [&](int buf) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) stage_v_word(buf, e);
+    for (int it = 0; it < KPT; ++it) stage_v_chunk(buf, it);
   };
-  // this lane's V^T operand offsets (elements) for (kbk, j) of block mb = 0;
-  // block mb adds 32 * mb * VROW
-  int voffr[2][2];
-  {
-    const int sw = (lr >> 1) & 7;
-#pragma unroll
-    for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        voffr[kbk][j] = lr * VROW + (((4 * kbk + 2 * g + j) ^ sw) << 3);
-  }
+  // this lane's base element of the transposing V reads (see the header):
+  // lane L = lane % 16 of group G = lane / 16 reads row 16 (G / 2) + L / 4,
+  // channels 16 (G % 2) + 4 (L % 4) .. + 3, of the 4-key group addressed
+  const int vtr_base = (16 * (lane >> 5) + ((lane & 15) >> 2)) * VROW +
+                       16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   f32x16_t o[MB];
 #pragma unroll
@@ -306,18 +285,25 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   };
 
   // Region B: O^T += V(t)^T P(t)^T (4 MB MFMAs) with the staging of K'(t+2)
-  // (RoPE-4D, one pair per slice) and V(t+1)^T (one transposed word per
-  // slice) spread over the MFMAs; then the loads of K(t+3), V(t+2).
+  // (RoPE-4D, one pair per slice) and V(t+1) spread over the MFMAs; then the
+  // loads of K(t+3), V(t+2).
   constexpr int NB = 4 * MB;                 // MFMAs in region B
   constexpr int NROT = 4 * KPT;              // RoPE pairs to stage
-  constexpr int NVW = 8;                     // V^T words (or halfwords) to stage
+  constexpr int NVW = KPT;                   // V chunks to stage
   constexpr int NIT = NROT + NVW;
   auto region_b = [&](int vbuf, int kdst, int vdst, const uint32_t (*pw)[8]) {
     bf16x8_t va[NB];
     auto read_v = [&](int i) {
       const int mb = i / 4, kbk = (i >> 1) & 1, j = i & 1;
-      va[i] = *reinterpret_cast<const bf16x8_t*>(
-          &v_lds[vbuf][voffr[kbk][j] + 32 * mb * VROW]);
+      // keys 32 kbk + 16 g + 8 j + [0, 4) and + [4, 8), channel 32 mb + lr
+      const uint16_t* src = &v_lds[vbuf][vtr_base + (32 * kbk + 8 * j) * VROW + 32 * mb];
+      typedef short s16x4_t __attribute__((ext_vector_type(4)));
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t*)(src));
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t*)(src + 4 * VROW));
+      const s16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      va[i] = __builtin_bit_cast(bf16x8_t, both);
     };
     read_v(0);
     read_v(1);
@@ -343,7 +329,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
           *reinterpret_cast<uint32_t*>(&k_lds[kdst][row * KROW + 8 * lc + 2 * jj]) =
               pack_f16x2(xa * cs - xb * sn, xa * sn + xb * cs);
         } else {
-          stage_v_word(vdst, item - NROT);     // one V^T word
+          stage_v_chunk(vdst, item - NROT);    // one V chunk
         }
       }
       __builtin_amdgcn_sched_barrier(0);
