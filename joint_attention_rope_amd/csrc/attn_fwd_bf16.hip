@@ -307,6 +307,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     };
     read_v(0);
     read_v(1);
+    u32x4_t ky;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       if (i + 2 < NB) read_v(i + 2);
@@ -324,10 +325,12 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
           const float rev = __builtin_amdgcn_fractf(fp * whi[jj]) + fp * wlo[jj];
           const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
           const float xa = bf16_lo(kx[c][jj]), xb = bf16_hi(kx[c][jj]);
-          const int key = lk + c;
-          const int row = (key & ~31) + key_to_row(key & 31);
-          *reinterpret_cast<uint32_t*>(&k_lds[kdst][row * KROW + 8 * lc + 2 * jj]) =
-              pack_f16x2(xa * cs - xb * sn, xa * sn + xb * cs);
+          ky[jj] = pack_f16x2(xa * cs - xb * sn, xa * sn + xb * cs);
+          if (jj == 3) {        // chunk complete: one 16-byte store
+            const int key = lk + c;
+            const int row = (key & ~31) + key_to_row(key & 31);
+            *reinterpret_cast<u32x4_t*>(&k_lds[kdst][row * KROW + 8 * lc]) = ky;
+          }
         } else {
           stage_v_chunk(vdst, item - NROT);    // one V chunk
         }
