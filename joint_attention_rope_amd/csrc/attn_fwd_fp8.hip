@@ -1,32 +1,50 @@
 // RoPE-4D joint self-attention forward, FP8 E4M3 in / bf16 out, for gfx950.
 //
 // Inputs are OCP E4M3FN codes with per-tensor descales: value = code * dX.
-// One workgroup of 8 waves owns one (batch, head, tile of 256 queries); each
-// wave owns 32 queries and streams all keys in tiles of 64.  Every key is
-// rotated and re-quantised on its way to LDS, and scores are fp8 MFMAs:
+// One workgroup of 8 waves (two per SIMD) owns one (batch, head, tile of 256
+// queries); each wave owns 32 queries and streams all keys in tiles of 64.
+// Every key is rotated and re-quantised on its way to LDS, and both products
+// are fp8 MFMAs (v_mfma_scale_f32_32x32x64_f8f6f4, fp32 accumulation):
 //
-//   Q'' = e4m3(R(q_code) / sqrt 2)      (registers, once)
-//   K'' = e4m3(R(k_code) / sqrt 2)      (LDS, per tile)
-//   V   = v_code                        (LDS as V^T, per tile, bytes transposed)
+//   Q'' = e4m3(R(q_code) * c)            registers, once; c = G / 2^n
+//   K'' = e4m3(R(k_code) / sqrt 2)       LDS, per tile
+//   S^T = 2^n K'' Q''^T - m              the 2^n is the MFMA's E8M0 operand
+//                                        scale, -m the chain's initial value
+//   p   = 2^S,  P8 = e4m3(p)             m is the running row max, raised
+//                                        only when a row grows by more than
+//                                        TAU = 8.75, so p <= 2^8.75 < 448
+//   O^T += V^T P8^T                      V row-major in LDS, read transposed
+//   out = O * dv / l,                    l = sum of p (fp32)
 //
-// R is RoPE-4D on the decoded codes; a rotated pair component can grow by at
-// most sqrt 2, so |R(code)| / sqrt 2 <= 448 and re-quantisation never leaves
-// the E4M3 range.  The descales factor out: <q', k'> = 2 dq dk <Q'', K''>.
+// with G = dq dk log2(e) sqrt(2) / sqrt(D): the exp2-domain score of query i
+// and key j is dq dk log2(e)/sqrt(D) <R q_i, R k_j> = G <R q_i, K''_j>, and n
+// is picked so that c lies in (1/(2 sqrt 2), 1/sqrt 2].  A rotated pair
+// component grows by at most sqrt 2, so |R(code)| c <= 448 and neither
+// re-quantisation leaves the E4M3 range.  Softmax therefore needs no VALU
+// multiply at all: one v_exp_f32 and half a conversion per score.
 //
-//   S^T  = K'' Q''^T                    v_mfma_f32_32x32x64_f8f6f4, fp32 acc
-//   s    = S * 2 dq dk log2(e)/sqrt(D)  exp2 domain, fused into the exponent
-//   p    = 2^(s - m), m the running row max, rescaled only when it grows by
-//          more than TAU = 8, so p <= 2^8
-//   P8   = e4m3(p * 448 / 2^8)          within range by construction
-//   O^T += V^T P8^T                     fp8 MFMA, fp32 acc (64 keys per MFMA)
-//   out  = O * dv * 2^8 / 448 / l,      l = sum of p (fp32)
+// Schedule (per wave; K'' and V double-buffered in LDS, one barrier a tile):
+//   softmax max of S(t); rare rescale of O and l
+//   region A:  S(t+1) MFMAs      interleaved with  p = 2^S(t), P8, row sums
+//   region B:  O^T += V(t)^T P8  interleaved with  staging K''(t+2) and
+//                                                   V(t+1) into LDS
+//   buffer loads of K(t+3), V(t+2); barrier
 //
-// The score MFMA orientation, the permuted key order inside a 32-key block and
-// the lane-pair row reductions are those of the bf16 kernel.  Unlike the bf16
-// kernel this one is limited by VALU work (one fp8 MFMA covers 64 keys), so
-// all eight waves run the same sequence -- stage tile t+1, S(t), softmax(t),
-// O += P(t) V(t) -- with K'' and V^T double-buffered in LDS and one barrier
-// per tile; the two waves sharing a SIMD interleave freely.
+// Rotation of keys: cos and sin (times 1/sqrt 2) of every (position, pair)
+// with position in [0, 512) come from an LDS table built once per workgroup;
+// a wave that holds any other position computes them directly instead.
+//
+// MFMA operands: the score MFMA puts keys on rows and queries on columns, and
+// keys sit in LDS in a permuted row order so that accumulator register i of a
+// lane in half g holds key 16g + i of its 32-key block.  The P8 bytes of a
+// lane then cover keys 16g + [0,16) and 32 + 16g + [0,16); the V^T operand
+// holds the same keys of one channel, gathered by ds_read_b64_tr_b8 reads: in
+// a group of 16 lanes, lane i receives byte i % 8 of the 8-byte words that
+// lanes 2e + i/8 (e = 0..7) address, so pointing lane 2e + h at
+// V[key0 + e][c0 + 8h .. + 7] hands lane i channel c0 + i of keys key0 ..
+// key0 + 7.
+#include <cmath>
+
 #include "klein_device.hpp"
 #include "klein_launch.hpp"
 
@@ -35,51 +53,27 @@ namespace klein {
 namespace {
 
 constexpr float kInvSqrt2 = 0.70710678118654752f;
-constexpr float kP8Scale = 448.0f / 256.0f;      // p <= 2^TAU = 256 maps to <= 448
+constexpr int kTabN = 512;        // positions covered by the cos/sin table
 
 __device__ __forceinline__ int key_to_row8(int kk) {
   const int g = kk >> 4, i = kk & 15;
   return ((i >> 2) << 3) + (g << 2) + (i & 3);
 }
 
-// Decode 16 E4M3 codes, rotate the 8 interleaved pairs (pairs j0 .. j0+7 of
-// one axis block) at position p, scale by 1/sqrt 2 and re-encode (RNE).
-__device__ __forceinline__ u32x4_t rope_requant16(u32x4_t x, int p, const float* whi,
-                                                  const float* wlo) {
+// (cos, sin) * scale of the angle pos * w (w in revolutions, split hi + lo)
+__device__ __forceinline__ float2 rope_cs(int p, float whi, float wlo, float scale) {
   const float fp = (float)p;
-  u32x4_t y;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const auto v0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[w], false);   // bytes 0, 1
-    const auto v1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[w], true);    // bytes 2, 3
-    float c[2], s[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int jj = 2 * w + half;
-      const float rev = __builtin_amdgcn_fractf(fp * whi[jj]) + fp * wlo[jj];
-      s[half] = __builtin_amdgcn_sinf(rev) * kInvSqrt2;
-      c[half] = __builtin_amdgcn_cosf(rev) * kInvSqrt2;
-    }
-    int outw = __builtin_amdgcn_cvt_pk_fp8_f32(v0[0] * c[0] - v0[1] * s[0],
-                                               v0[0] * s[0] + v0[1] * c[0], 0, false);
-    outw = __builtin_amdgcn_cvt_pk_fp8_f32(v1[0] * c[1] - v1[1] * s[1],
-                                           v1[0] * s[1] + v1[1] * c[1], outw, true);
-    y[w] = (uint32_t)outw;
-  }
-  return y;
+  const float rev = __builtin_amdgcn_fractf(fp * whi) + fp * wlo;
+  return make_float2(__builtin_amdgcn_cosf(rev) * scale, __builtin_amdgcn_sinf(rev) * scale);
 }
 
-// 4 x 4 byte transpose: in[i] holds bytes (d0..d3) of key i; out[j] holds
-// byte j of keys 0..3.
-__device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[4]) {
-  const uint32_t a_lo = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);  // k0d0 k1d0 k0d1 k1d1
-  const uint32_t a_hi = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);  // k0d2 k1d2 k0d3 k1d3
-  const uint32_t b_lo = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);
-  const uint32_t b_hi = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
-  out[0] = __builtin_amdgcn_perm(b_lo, a_lo, 0x05040100u);
-  out[1] = __builtin_amdgcn_perm(b_lo, a_lo, 0x07060302u);
-  out[2] = __builtin_amdgcn_perm(b_hi, a_hi, 0x05040100u);
-  out[3] = __builtin_amdgcn_perm(b_hi, a_hi, 0x07060302u);
+// Rotate pair (x, y) held as E4M3 bytes 2h, 2h+1 of `word` by (c, s) and
+// write it, re-encoded (RNE), into half h of `acc`.
+template <bool HI>
+__device__ __forceinline__ int rope_pair_fp8(uint32_t word, float2 cs, int acc) {
+  const auto xy = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, HI);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(xy[0] * cs.x - xy[1] * cs.y, xy[0] * cs.y + xy[1] * cs.x,
+                                         acc, HI);
 }
 
 }  // namespace
@@ -88,22 +82,30 @@ template <int D>
 __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     const int32_t* __restrict__ pos, uint16_t* __restrict__ out, int S, int H, int nqt,
-    RopeFreqs fr, float s_scale, float o_scale) {
+    RopeFreqs fr, float q_mul, int sc_a, int sc_b, float o_scale) {
   constexpr int BM = 256;              // queries per workgroup (8 waves x 32)
   constexpr int BN = 64;               // keys per tile
-  constexpr int CPK = D / 16;          // 16-byte chunks per K row
-  constexpr int KS = D / 64;           // fp8 MFMA k-steps of Q K^T
+  constexpr int NT = 512;              // threads
+  constexpr int CPK = D / 16;          // 16-byte chunks per token row
+  constexpr int NCH = BN * CPK;        // chunks per K (or V) tile
+  constexpr int KS = D / 64;           // k-steps of the score MFMA
   constexpr int MB = D / 32;           // 32-row blocks of O^T
-  constexpr int KROW = D + 16;         // LDS row stride of K'' (bytes), padded
-  constexpr int VROW = BN + 16;        // LDS row stride of V^T (bytes), padded
+  constexpr int KROW = D + 16;         // LDS row stride of K'' (bytes)
+  constexpr int VROW = D + 32;         // LDS row stride of V (bytes)
   constexpr int DA = D / 4;            // channels per RoPE axis
-  constexpr float TAU = 8.0f;
-  constexpr int KTHREADS = BN * CPK;   // threads that stage K (one chunk each)
-  constexpr int VTHREADS = (BN / 4) * (D / 4);   // threads that stage V (4 keys x 4 d)
-  static_assert(KTHREADS <= 512 && VTHREADS <= 512, "staging split");
+  constexpr int NJ = D / 8;            // rotation pairs per axis
+  constexpr int TROW = NJ + 1;         // cos/sin table row stride (float2)
+  constexpr int TSLOT = 9;             // per-thread fallback slot stride
+  constexpr int TAB = kTabN * TROW;    // start of the fallback slots
+  constexpr float TAU = 8.75f;         // 2^TAU < 448
+  static_assert(NCH == NT || 2 * NCH == NT, "one K and one V chunk per thread (D 128) "
+                                            "or one of either (D 64)");
 
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][BN * KROW];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[2][D * VROW];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[2][BN * VROW];
+  // table rows for positions [0, kTabN), then 8 per-thread slots; the odd
+  // strides (in float2) spread neighbouring rows and slots over all banks
+  __shared__ __attribute__((aligned(16))) float2 cs_tab[TAB + TSLOT * NT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lr = lane & 31;
@@ -119,7 +121,14 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   const uint8_t* vbase = v + base;
   const int rowb = (int)rs;
 
-  // ---- Q'': this lane's query, dims 64 ks + 32 g + [0, 32) per k-step
+  // ---- cos/sin table: entry p * TROW + j = (cos, sin)(p w_j) / sqrt 2
+  for (int e = tid; e < kTabN * NJ; e += NT) {
+    const int j = e % NJ, p = e / NJ;
+    cs_tab[p * TROW + j] = rope_cs(p, fr.hi[j], fr.lo[j], kInvSqrt2);
+  }
+
+  // ---- Q'': this lane's query, dims 64 ks + 32 g + [0, 32) per k-step.
+  // Rows past S load row S-1 (in bounds) and are never stored.
   const int qrow = qt * BM + wave * 32 + lr;
   const int qload = qrow < S ? qrow : S - 1;
   i32x8_t qreg[KS];
@@ -129,104 +138,134 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
     for (int hc = 0; hc < 2; ++hc) {
       const int d0 = 64 * ks + 32 * g + 16 * hc;
       const int a = d0 / DA, j0 = (d0 % DA) / 2;
+      const int p = pos[4 * qload + a];
       const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qb + (size_t)qload * rs + d0);
-      const u32x4_t y = rope_requant16(x, pos[4 * qload + a], &fr.hi[j0], &fr.lo[j0]);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) qreg[ks][4 * hc + w] = (int)y[w];
+      for (int w = 0; w < 4; ++w) {
+        int word = rope_pair_fp8<false>(x[w], rope_cs(p, fr.hi[j0 + 2 * w], fr.lo[j0 + 2 * w], q_mul), 0);
+        word = rope_pair_fp8<true>(x[w], rope_cs(p, fr.hi[j0 + 2 * w + 1], fr.lo[j0 + 2 * w + 1], q_mul), word);
+        qreg[ks][4 * hc + w] = word;
+      }
     }
   }
 
-  // ---- staging assignment
-  const bool kst = tid < KTHREADS;
-  const int kkey = tid / CPK, kc = tid % CPK;           // K: key, 16-byte chunk
+  // ---- staging assignment.  D = 128: every thread stages chunk tid of the K
+  // tile and chunk tid of the V tile.  D = 64: threads [0, 256) stage K,
+  // threads [256, 512) stage V.
+  const bool kst = NCH == NT || tid < NCH;
+  const bool vst = NCH == NT || tid >= NCH;
+  const int vid = NCH == NT ? tid : tid - NCH;
+  const int kkey = tid / CPK, kc = tid % CPK;            // K: key, chunk
   const int ka = (16 * kc) / DA, kj0 = ((16 * kc) % DA) / 2;
-  float whi[8], wlo[8];
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    const int j = kj0 + jj < D / 8 ? kj0 + jj : D / 8 - 1;
-    whi[jj] = fr.hi[j];
-    wlo[jj] = fr.lo[j];
-  }
-  const bool vst = tid < VTHREADS;
-  const int vkq = tid % (BN / 4), vdq = tid / (BN / 4);  // V: keys 4 vkq.., d 4 vdq..
+  const int vkey = vid / CPK, vc = vid % CPK;            // V: key, chunk
   const int voff_k = kkey * rowb + 16 * kc;
   const int voff_p = (kkey * 4 + ka) * 4;
-  int voff_v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) voff_v[i] = (4 * vkq + i) * rowb + 4 * vdq;
+  const int voff_v = vkey * rowb + 16 * vc;
+  const int krow = (kkey & ~31) + key_to_row8(kkey & 31);
 
   const int nkt = (S + BN - 1) / BN;
-  u32x4_t kx = {0u, 0u, 0u, 0u};
-  int kp = 0;
-  uint32_t vx[4] = {0u, 0u, 0u, 0u};
+  u32x4_t kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+  // positions of this thread's K chunk, loaded one step ahead of the K data:
+  // slot kt & 1 holds tile kt's
+  int kpos0 = 0, kpos1 = 0;
 
   auto tile_rows = [&](int kt) {
     const int n = S - kt * BN;
     return n < 0 ? 0 : (n > BN ? BN : n);
   };
   // global -> registers (rows past S read as zero through the descriptors)
-  auto load_tile = [&](int kt) {
-    const int n = tile_rows(kt);
+  auto load_k = [&](int kt) {
     if (kst) {
+      const int n = tile_rows(kt);
       const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(kbase + (size_t)kt * BN * rs, n * rowb);
-      const __amdgpu_buffer_rsrc_t rp = uniform_rsrc(pos + (size_t)kt * BN * 4, n * 16);
       kx = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, voff_k, 0, 0));
-      kp = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, voff_p, 0, 0);
-    }
-    if (vst) {
-      const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(vbase + (size_t)kt * BN * rs, n * rowb);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vx[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff_v[i], 0, 0);
     }
   };
-  // registers -> LDS: K'' at its permuted row, V transposed to V^T
-  auto stage_tile = [&](int buf) {
+  auto load_pos = [&](int kt, int& slot) {
     if (kst) {
-      const int row = (kkey & ~31) + key_to_row8(kkey & 31);
-      *reinterpret_cast<u32x4_t*>(&k_lds[buf][row * KROW + 16 * kc]) =
-          rope_requant16(kx, kp, whi, wlo);
-    }
-    if (vst) {
-      uint32_t t4[4];
-      transpose4x4(vx, t4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint32_t*>(&v_lds[buf][(4 * vdq + j) * VROW + 4 * vkq]) = t4[j];
+      const __amdgpu_buffer_rsrc_t rp = uniform_rsrc(pos + (size_t)kt * BN * 4, tile_rows(kt) * 16);
+      slot = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, voff_p, 0, 0);
     }
   };
+  auto load_v = [&](int kt) {
+    if (vst) {
+      const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(vbase + (size_t)kt * BN * rs, tile_rows(kt) * rowb);
+      vx = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v, 0, 0));
+    }
+  };
+  auto stage_v = [&](int buf) {
+    if (vst) *reinterpret_cast<u32x4_t*>(&v_lds[buf][vkey * VROW + 16 * vc]) = vx;
+  };
+  // (cos, sin) / sqrt 2 of the 8 pairs of this thread's K chunk, as an index
+  // into cs_tab: the table row of its position, or (position outside the
+  // table) its own 8 slots past the table, filled here.  The branch is
+  // divergent and skipped by waves whose positions all lie in the table.
+  auto key_cs_index = [&](int kp) {
+    const bool oob = kst && (unsigned)kp >= (unsigned)kTabN;
+    if (oob) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        int j = kj0 + jj;
+        asm volatile("" : "+v"(j));      // keep the loads in this rare path
+        cs_tab[TAB + TSLOT * tid + jj] = rope_cs(kp, fr.hi[j], fr.lo[j], kInvSqrt2);
+      }
+    }
+    return oob ? TAB + TSLOT * tid : (kst ? kp : 0) * TROW + kj0;
+  };
+  // one rotated pair of the K chunk; the 16-byte LDS store after the last
+  u32x4_t ky;
+  auto rope_item = [&](int kdst, int jj, float2 cs) {
+    const int w = jj >> 1;
+    ky[w] = (uint32_t)((jj & 1) ? rope_pair_fp8<true>(kx[w], cs, (int)ky[w])
+                                : rope_pair_fp8<false>(kx[w], cs, (int)ky[w]));
+    if (jj == 7 && kst) *reinterpret_cast<u32x4_t*>(&k_lds[kdst][krow * KROW + 16 * kc]) = ky;
+  };
+  auto stage_k = [&](int buf, int kp) {
+    const int ci = key_cs_index(kp);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) rope_item(buf, jj, cs_tab[ci + jj]);
+  };
+  // lane base of the transposing V reads: lane L of group G = L / 16 reads
+  // row 16 (G / 2) + (L % 16) / 2, channels 16 (G % 2) + 8 (L % 2) .. + 7
+  const int vtr_base = (16 * (lane >> 5) + ((lane & 15) >> 1)) * VROW +
+                       16 * ((lane >> 4) & 1) + 8 * (lane & 1);
 
   f32x16_t o[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) o[mb] = (f32x16_t){};
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = 0.f, l_run = 0.f;
 
-  load_tile(0);
-  stage_tile(0);
-  load_tile(1);
-  __syncthreads();
-
-  for (int t = 0; t < nkt; ++t) {
-    const int buf = t & 1;
-    // ---- S^T = K'' Q''^T: two 32-key blocks, KS k-steps of 64 dims
-    f32x16_t sc[2];
+  auto read_k = [&](int kbuf, int kbk, int ks) {
+    const uint8_t* src = &k_lds[kbuf][(32 * kbk + lr) * KROW + 64 * ks + 32 * g];
+    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(src);
+    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(src + 16);
+    return (i32x8_t){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  auto score_mfma = [&](i32x8_t a, int ks, f32x16_t c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qreg[ks], c, 0, 0, 0, sc_a, 0, sc_b);
+  };
+  auto rowmax32 = [&](const f32x16_t* sc) {
+    float m[12];
 #pragma unroll
-    for (int kbk = 0; kbk < 2; ++kbk) {
-      sc[kbk] = (f32x16_t){};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint8_t* src = &k_lds[buf][(32 * kbk + lr) * KROW + 64 * ks + 32 * g];
-        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(src);
-        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(src + 16);
-        const i32x8_t a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        sc[kbk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qreg[ks], sc[kbk], 0, 0,
-                                                                  0, 0, 0, 0);
-      }
+    for (int i = 0; i < 10; ++i) {
+      const int a = 3 * i, b2 = 3 * i + 1, c = 3 * i + 2;
+      m[i] = __builtin_fmaxf(sc[a >> 4][a & 15],
+                             __builtin_fmaxf(sc[b2 >> 4][b2 & 15], sc[c >> 4][c & 15]));
     }
-    // ---- stage tile t+1 into the other buffer while the MFMAs run
-    stage_tile(buf ^ 1);
-
-    // ---- softmax step on raw scores (scaled into the exp2 domain)
+    m[10] = sc[1][14];
+    m[11] = sc[1][15];
+    float n[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) n[i] = __builtin_fmaxf(m[3 * i], __builtin_fmaxf(m[3 * i + 1], m[3 * i + 2]));
+    return pair_max(__builtin_fmaxf(n[0], __builtin_fmaxf(n[1], __builtin_fmaxf(n[2], n[3]))));
+  };
+  f32x16_t cinit;
+  auto set_cinit = [&]() {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cinit[i] = -m_run;
+  };
+  auto mask_tail = [&](int t, f32x16_t* sc) {
     if (t * BN + BN > S) {
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk)
@@ -234,58 +273,151 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
         for (int i = 0; i < 16; ++i)
           if (t * BN + 32 * kbk + 16 * g + i >= S) sc[kbk][i] = kNegInf;
     }
-    float m8[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      m8[i] = __builtin_fmaxf(__builtin_fmaxf(sc[0][i], sc[0][i + 8]),
-                              __builtin_fmaxf(sc[1][i], sc[1][i + 8]));
-#pragma unroll
-    for (int w = 4; w >= 1; w >>= 1)
-#pragma unroll
-      for (int i = 0; i < w; ++i) m8[i] = __builtin_fmaxf(m8[i], m8[i + w]);
-    const float mx = pair_max(m8[0]) * s_scale;
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU)) {
-      const float m_new = __builtin_fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+  };
+  auto softmax_max = [&](int t, f32x16_t* sc) {
+    mask_tail(t, sc);
+    const float mx = rowmax32(sc);
+    if (__builtin_amdgcn_ballot_w64(mx > TAU)) {
+      const float delta = __builtin_fmaxf(mx, 0.f);
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      m_run += delta;
       l_run *= alpha;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) o[mb] *= alpha;
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk) sc[kbk] -= delta;
+      set_cinit();
     }
-    // p = 2^(raw * s_scale - m); P8 packed in key order 16g + i, 32 + 16g + i
+  };
+
+  // Region A: S(t+1) (2 KS MFMAs, K'' operands read two ahead) with the
+  // softmax of S(t) in 8 slices of 4 scores (one P8 word each).
+  constexpr int NA = 2 * KS;
+  auto region_a = [&](int kbuf, const f32x16_t* cur, f32x16_t* nxt, i32x8_t& pb) {
+    i32x8_t kop[NA];
+    nxt[0] = cinit;
+    nxt[1] = cinit;
+    kop[0] = read_k(kbuf, 0 / KS, 0 % KS);
+    if (NA > 1) kop[1 % NA] = read_k(kbuf, 1 / KS, 1 % KS);
     float ls4[4] = {0.f, 0.f, 0.f, 0.f};
-    i32x8_t pb;
 #pragma unroll
-    for (int kbk = 0; kbk < 2; ++kbk)
+    for (int i = 0; i < NA; ++i) {
+      if (i + 2 < NA) kop[i + 2] = read_k(kbuf, (i + 2) / KS, (i + 2) % KS);
+      const int kbk = i / KS, ks = i % KS;
+      nxt[kbk] = score_mfma(kop[i], ks, nxt[kbk]);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float pv[4];
+      for (int sl = i * 8 / NA; sl < (i + 1) * 8 / NA; ++sl) {
+        const int kb2 = sl >> 2, w = sl & 3;
+        float p[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][4 * w + e], s_scale, -m_run));
-          ls4[e] += pv[e];
+          p[e] = __builtin_amdgcn_exp2f(cur[kb2][4 * w + e]);
+          ls4[e] += p[e];
         }
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0] * kP8Scale, pv[1] * kP8Scale, 0, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2] * kP8Scale, pv[3] * kP8Scale, word, true);
-        pb[4 * kbk + w] = word;
+        // both halves of the word are rewritten: the old word only fills
+        // the operand that the conversion keeps
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pb[4 * kb2 + w], false);
+        pb[4 * kb2 + w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
       }
-    l_run += (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
-
-    // ---- O^T += V^T P8^T: one 64-key MFMA per 32-row block of D
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const uint8_t* src = &v_lds[buf][(32 * mb + lr) * VROW + 16 * g];
-      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(src);
-      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(src + 32);
-      const i32x8_t a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      o[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, o[mb], 0, 0, 0, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    load_tile(t + 2);
-    __syncthreads();
-  }
+    l_run += (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
+    // Pin the score MFMAs here: their results are only read in the next
+    // step, and without a use here they would be sunk to it, away from the
+    // softmax work they are meant to overlap.
+    asm volatile("" : "+v"(nxt[0]), "+v"(nxt[1]));
+  };
 
-  // ---- epilogue: O * dv * 2^8/448 / l -> bf16
+  // Region B: O^T += V(t)^T P8^T (MB MFMAs, V^T operands read two ahead) with
+  // the staging of K''(t+2) (8 rotated pairs) and V(t+1) spread over them.
+  auto read_v = [&](int vbuf, int mb) {
+    typedef int i32x2v_t __attribute__((ext_vector_type(2)));
+    i32x2v_t r[4];
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr)
+        r[2 * qq + rr] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2v_t*)(&v_lds[vbuf][vtr_base + (32 * qq + 8 * rr) * VROW + 32 * mb]));
+    return (i32x8_t){r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+  };
+  constexpr int NIT = 9;               // 8 rotated pairs, then the V chunk
+  auto region_b = [&](int vbuf, int kdst, int vdst, const i32x8_t& pb, int ci) {
+    i32x8_t vop[MB];
+    float2 kcs[8];
+    vop[0] = read_v(vbuf, 0);
+    vop[1] = read_v(vbuf, 1);
+    kcs[0] = cs_tab[ci];
+    kcs[1] = cs_tab[ci + 1];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      if (i + 2 < MB) vop[i + 2] = read_v(vbuf, i + 2);
+      o[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[i], pb, o[i], 0, 0, 0, 0, 0, 0);
+#pragma unroll
+      for (int item = i * NIT / MB; item < (i + 1) * NIT / MB; ++item) {
+        if (item + 2 < 8) kcs[item + 2] = cs_tab[ci + item + 2];
+        if (item < 8) rope_item(kdst, item, kcs[item]);
+        else stage_v(vdst);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- prologue: table, K''(0), K''(1), V(0) in LDS; S(0) in registers;
+  // K(2), V(1) in flight
+  load_k(0);
+  load_pos(0, kpos0);
+  load_v(0);
+  __syncthreads();                     // table complete
+  stage_k(0, kpos0);
+  stage_v(0);
+  load_k(1);
+  load_pos(1, kpos1);
+  stage_k(1, kpos1);
+  load_k(2);
+  load_pos(2, kpos0);
+  load_pos(3, kpos1);
+  load_v(1);
+  __syncthreads();
+  f32x16_t sa[2], sb[2];
+#pragma unroll
+  for (int kbk = 0; kbk < 2; ++kbk) {
+    sa[kbk] = (f32x16_t){};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) sa[kbk] = score_mfma(read_k(0, kbk, ks), ks, sa[kbk]);
+  }
+  __syncthreads();                     // K'' buffer 0 is refilled in iteration 0
+  // m starts at tile 0's exact row max, so scores are relative from the start
+  mask_tail(0, sa);
+  m_run = rowmax32(sa);
+#pragma unroll
+  for (int kbk = 0; kbk < 2; ++kbk) sa[kbk] -= m_run;
+  set_cinit();
+
+  i32x8_t pb = {};
+  // one pipeline step; `cur` holds S(t), `nxt` receives S(t+1), `kps` holds
+  // the positions of K(t+2) and receives those of K(t+4).  The only branches
+  // (rare rescale, rare rotation fallback) come first, so that regions A and
+  // B form one block whose interleaving the compiler keeps.
+  auto step = [&](int t, f32x16_t* cur, f32x16_t* nxt, int& kps) {
+    const int ci = key_cs_index(kps);
+    softmax_max(t, cur);
+    region_a((t + 1) & 1, cur, nxt, pb);
+    // K''(t+2) into buffer t&1 (it held K''(t)); V(t+1) into buffer (t+1)&1
+    region_b(t & 1, t & 1, (t + 1) & 1, pb, ci);
+    load_k(t + 3);
+    load_pos(t + 4, kps);
+    load_v(t + 2);
+    __syncthreads();
+  };
+  int t = 0;
+  for (; t + 1 < nkt; t += 2) {
+    step(t, sa, sb, kpos0);
+    step(t + 1, sb, sa, kpos1);
+  }
+  if (t < nkt) step(t, sa, sb, kpos0);
+
+  // ---- epilogue: O * dv / l -> bf16
   const float inv = o_scale / pair_sum(l_run);
   if (qrow < S) {
     uint16_t* orow = out + (size_t)b * S * rs + (size_t)h * D + (size_t)qrow * rs;
@@ -302,16 +434,33 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   }
 }
 
+// Score scale split: G = dq dk log2(e) sqrt(2) / sqrt(D) = c * 2^n with c in
+// (1/(2 sqrt 2), 1/sqrt 2]; 2^n goes to the MFMA as two E8M0 operand scales
+// (each in [2^-127, 2^127]).  |n| > 254 is clamped (descale products that far
+// out underflow or overflow fp32 scores anyway).
+struct Fp8Scales {
+  float q_mul;
+  int sc_a, sc_b;
+};
+static Fp8Scales fp8_scales(const LaunchArgs& a) {
+  const double G = (double)a.descale[0] * (double)a.descale[1] *
+                   1.4426950408889634 * 1.4142135623730951 / std::sqrt((double)a.D);
+  int n = (int)std::ceil(std::log2(G * 1.4142135623730951));
+  if (n > 254) n = 254;
+  if (n < -254) n = -254;
+  const int na = n / 2, nb = n - na;
+  return {(float)std::ldexp(G, -n), 127 + na, 127 + nb};
+}
+
 template <int D>
 static hipError_t launch_fp8(const LaunchArgs& a) {
   const int nqt = (a.S + 255) / 256;
   const long long n = (long long)a.B * a.H * nqt;
-  // scores: <q', k'> = 2 dq dk <Q'', K''>, times log2(e)/sqrt(D)
-  const float s_scale = 2.0f * a.descale[0] * a.descale[1] * a.qscale_log2;
-  const float o_scale = a.descale[2] / (448.0f / 256.0f);
+  const Fp8Scales s = fp8_scales(a);
   hipLaunchKernelGGL((attn_fwd_fp8_kernel<D>), dim3((unsigned)n), dim3(512), 0, a.stream,
                      (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, a.pos,
-                     (uint16_t*)a.out, a.S, a.H, nqt, a.freqs, s_scale, o_scale);
+                     (uint16_t*)a.out, a.S, a.H, nqt, a.freqs, s.q_mul, s.sc_a, s.sc_b,
+                     a.descale[2]);
   return hipGetLastError();
 }
 
