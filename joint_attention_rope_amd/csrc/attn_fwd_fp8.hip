@@ -53,7 +53,10 @@ namespace klein {
 namespace {
 
 constexpr float kInvSqrt2 = 0.70710678118654752f;
-constexpr int kTabN = 512;        // positions covered by the cos/sin table
+constexpr int kTabN = 1024;       // positions covered by the cos/sin table
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef short s2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int key_to_row8(int kk) {
   const int g = kk >> 4, i = kk & 15;
@@ -76,6 +79,20 @@ __device__ __forceinline__ int rope_pair_fp8(uint32_t word, float2 cs, int acc) 
                                          acc, HI);
 }
 
+// The same in packed fp16 (decode, two packed FMA-type ops, encode): E4M3
+// values are exact in fp16, and (c, s) carry fp16's 11-bit mantissa, far
+// finer than the 4 significant bits the result is rounded to.
+template <bool HI>
+__device__ __forceinline__ int rope_pair_fp8_h(uint32_t word, h2_t cs, int acc) {
+  const h2_t xy = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)word, 1.0f, HI);
+  const h2_t xx = {xy[0], xy[0]}, yy = {xy[1], xy[1]};
+  const h2_t t = yy * (h2_t){cs[1], cs[0]};                    // (y s, y c)
+  const h2_t r = __builtin_elementwise_fma(xx, cs, (h2_t){-t[0], t[1]});
+  const s2_t out = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(__builtin_bit_cast(s2_t, acc), r,
+                                                            1.0f, HI);
+  return __builtin_bit_cast(int, out);
+}
+
 }  // namespace
 
 template <int D>
@@ -94,8 +111,8 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   constexpr int VROW = D + 32;         // LDS row stride of V (bytes)
   constexpr int DA = D / 4;            // channels per RoPE axis
   constexpr int NJ = D / 8;            // rotation pairs per axis
-  constexpr int TROW = NJ + 1;         // cos/sin table row stride (float2)
-  constexpr int TSLOT = 9;             // per-thread fallback slot stride
+  constexpr int TROW = NJ + 2;         // cos/sin table row stride (half2)
+  constexpr int TSLOT = 10;            // per-thread fallback slot stride
   constexpr int TAB = kTabN * TROW;    // start of the fallback slots
   constexpr float TAU = 8.75f;         // 2^TAU < 448
   static_assert(NCH == NT || 2 * NCH == NT, "one K and one V chunk per thread (D 128) "
@@ -103,9 +120,10 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
 
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][BN * KROW];
   __shared__ __attribute__((aligned(16))) uint8_t v_lds[2][BN * VROW];
-  // table rows for positions [0, kTabN), then 8 per-thread slots; the odd
-  // strides (in float2) spread neighbouring rows and slots over all banks
-  __shared__ __attribute__((aligned(16))) float2 cs_tab[TAB + TSLOT * NT];
+  // fp16 (cos, sin) / sqrt 2: table rows for positions [0, kTabN), then 8
+  // per-thread slots.  Row and slot strides of 2 (mod 4) dwords spread 32
+  // rows over all banks and keep pairs of entries 8-byte aligned.
+  __shared__ __attribute__((aligned(16))) h2_t cs_tab[TAB + TSLOT * NT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lr = lane & 31;
@@ -124,7 +142,8 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   // ---- cos/sin table: entry p * TROW + j = (cos, sin)(p w_j) / sqrt 2
   for (int e = tid; e < kTabN * NJ; e += NT) {
     const int j = e % NJ, p = e / NJ;
-    cs_tab[p * TROW + j] = rope_cs(p, fr.hi[j], fr.lo[j], kInvSqrt2);
+    const float2 c = rope_cs(p, fr.hi[j], fr.lo[j], kInvSqrt2);
+    cs_tab[p * TROW + j] = (h2_t){(_Float16)c.x, (_Float16)c.y};
   }
 
   // ---- Q'': this lane's query, dims 64 ks + 32 g + [0, 32) per k-step.
@@ -207,17 +226,18 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
       for (int jj = 0; jj < 8; ++jj) {
         int j = kj0 + jj;
         asm volatile("" : "+v"(j));      // keep the loads in this rare path
-        cs_tab[TAB + TSLOT * tid + jj] = rope_cs(kp, fr.hi[j], fr.lo[j], kInvSqrt2);
+        const float2 c = rope_cs(kp, fr.hi[j], fr.lo[j], kInvSqrt2);
+        cs_tab[TAB + TSLOT * tid + jj] = (h2_t){(_Float16)c.x, (_Float16)c.y};
       }
     }
     return oob ? TAB + TSLOT * tid : (kst ? kp : 0) * TROW + kj0;
   };
   // one rotated pair of the K chunk; the 16-byte LDS store after the last
   u32x4_t ky;
-  auto rope_item = [&](int kdst, int jj, float2 cs) {
+  auto rope_item = [&](int kdst, int jj, h2_t cs) {
     const int w = jj >> 1;
-    ky[w] = (uint32_t)((jj & 1) ? rope_pair_fp8<true>(kx[w], cs, (int)ky[w])
-                                : rope_pair_fp8<false>(kx[w], cs, (int)ky[w]));
+    ky[w] = (uint32_t)((jj & 1) ? rope_pair_fp8_h<true>(kx[w], cs, (int)ky[w])
+                                : rope_pair_fp8_h<false>(kx[w], cs, (int)ky[w]));
     if (jj == 7 && kst) *reinterpret_cast<u32x4_t*>(&k_lds[kdst][krow * KROW + 16 * kc]) = ky;
   };
   auto stage_k = [&](int buf, int kp) {
@@ -344,7 +364,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   constexpr int NIT = 9;               // 8 rotated pairs, then the V chunk
   auto region_b = [&](int vbuf, int kdst, int vdst, const i32x8_t& pb, int ci) {
     i32x8_t vop[MB];
-    float2 kcs[8];
+    h2_t kcs[8];
     vop[0] = read_v(vbuf, 0);
     vop[1] = read_v(vbuf, 1);
     kcs[0] = cs_tab[ci];
