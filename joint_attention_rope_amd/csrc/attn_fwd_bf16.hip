@@ -59,6 +59,8 @@
 
 namespace klein {
 
+constexpr int kTabN = 256;        // positions covered by the cos/sin table
+
 // LDS row of key kk (0..31) of a 32-key block: the MFMA output row r holds
 // key 16*((r/4)&1) + 4*(r/8) + (r%4); this is the inverse map.
 __device__ __forceinline__ int key_to_row(int kk) {
@@ -82,11 +84,18 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   constexpr int VROW = D + 32;         // LDS row stride of V (bf16), padded
   constexpr int DA = D / 4;            // channels per RoPE axis
   constexpr float TAU = 8.0f;
+  constexpr int NJ = D / 8;            // rotation pairs per axis
+  constexpr int TROW = NJ + 1;         // cos/sin table row stride (float2)
+  constexpr int TSLOT = 4 * KPT + 1;   // per-thread fallback slot stride
+  constexpr int TAB = kTabN * TROW;    // start of the fallback slots
   static_assert(KPT >= 1 && (BN * CPR) % NT == 0, "tile/thread split");
   static_assert(KPT == 1 || KPT % 2 == 0, "V^T store packs key pairs");
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BN * VROW];
+  // (cos, sin) of every pair at positions [0, kTabN), then per-thread slots
+  // for keys at other positions; odd strides spread rows over the banks
+  __shared__ __attribute__((aligned(16))) float2 cs_tab[TAB + TSLOT * NT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lr = lane & 31;
@@ -100,6 +109,13 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   const uint16_t* qb = q + base;
   const uint16_t* kb = k + base;
   const uint16_t* vb = v + base;
+
+  // ---- cos/sin table (the very values rope_chunk computes)
+  for (int e = tid; e < kTabN * NJ; e += NT) {
+    const int j = e % NJ, p = e / NJ;
+    const float rev = __builtin_amdgcn_fractf((float)p * fr.hi[j]) + (float)p * fr.lo[j];
+    cs_tab[p * TROW + j] = make_float2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+  }
 
   // ---- this lane's query: rotate, scale by log2(e)/sqrt(D), fp16 in VGPRs.
   // Rows past S load row S-1 (in bounds) and are never stored.
@@ -120,9 +136,6 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   const int lc = tid % CPR;
   const int lk = (tid / CPR) * KPT;
   const int la = (8 * lc) / DA, lj0 = ((8 * lc) % DA) / 2;
-  float whi[4], wlo[4];
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) { whi[jj] = fr.hi[lj0 + jj]; wlo[jj] = fr.lo[lj0 + jj]; }
 
   // Global -> registers through buffer loads.  Each tile gets a descriptor
   // whose base is the tile's first row and whose size covers only the rows
@@ -134,20 +147,47 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   const int voff_p = (lk * 4 + la) * 4;
   const int nkt = (S + BN - 1) / BN;
   u32x4_t kx[KPT], vx[KPT];
-  int kp[KPT];
+  // positions of this thread's K keys, loaded one step ahead of the K data:
+  // ring slot kt & 1 holds tile kt's
+  int kpos0[KPT], kpos1[KPT];
   auto tile_rows = [&](int kt) {
     const int n = S - kt * BN;
     return n < 0 ? 0 : (n > BN ? BN : n);
   };
   auto load_k = [&](int kt) {
-    const int n = tile_rows(kt);
-    const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(kb + (size_t)kt * BN * rs, n * rowb);
-    const __amdgpu_buffer_rsrc_t rp = uniform_rsrc(pos + (size_t)kt * BN * 4, n * 16);
+    const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(kb + (size_t)kt * BN * rs, tile_rows(kt) * rowb);
 #pragma unroll
-    for (int it = 0; it < KPT; ++it) {
+    for (int it = 0; it < KPT; ++it)
       kx[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, voff, it * rowb, 0));
-      kp[it] = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, voff_p, it * 16, 0);
+  };
+  auto load_pos = [&](int kt, int* slot) {
+    const __amdgpu_buffer_rsrc_t rp = uniform_rsrc(pos + (size_t)kt * BN * 4, tile_rows(kt) * 16);
+#pragma unroll
+    for (int it = 0; it < KPT; ++it)
+      slot[it] = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, voff_p, it * 16, 0);
+  };
+  // (cos, sin) of the 4 pairs of K chunk `it`, as an index into cs_tab: the
+  // table row of its position, or (position outside the table) the thread's
+  // own slots, filled here in a divergent branch that waves whose positions
+  // all lie in the table skip.
+  auto key_cs_index = [&](const int* kp, int it) {
+    const bool oob = (unsigned)kp[it] >= (unsigned)kTabN;
+    if (oob) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        int j = lj0 + jj;
+        asm volatile("" : "+v"(j));      // keep the loads in this rare path
+        const float rev = __builtin_amdgcn_fractf((float)kp[it] * fr.hi[j]) + (float)kp[it] * fr.lo[j];
+        cs_tab[TAB + TSLOT * tid + 4 * it + jj] =
+            make_float2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+      }
     }
+    return oob ? TAB + TSLOT * tid + 4 * it : kp[it] * TROW + lj0;
+  };
+  // one rotated pair (x, y) -> (x c - y s, x s + y c), fp16
+  auto rot_pair = [&](uint32_t xw, float2 cs) {
+    const float xa = bf16_lo(xw), xb = bf16_hi(xw);
+    return pack_f16x2(xa * cs.x - xb * cs.y, xa * cs.y + xb * cs.x);
   };
   auto load_v = [&](int kt) {
     const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(vb + (size_t)kt * BN * rs, tile_rows(kt) * rowb);
@@ -156,13 +196,16 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
       vx[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, it * rowb, 0));
   };
   // Registers -> LDS: K rotated (fp16), at its permuted row; V transposed.
-  auto stage_k = [&](int buf) {
+  auto stage_k = [&](int buf, const int* kp) {
 #pragma unroll
     for (int it = 0; it < KPT; ++it) {
+      const int ci = key_cs_index(kp, it);
       const int key = lk + it;
       const int row = (key & ~31) + key_to_row(key & 31);
-      *reinterpret_cast<u32x4_t*>(&k_lds[buf][row * KROW + 8 * lc]) =
-          rope_chunk<true>(kx[it], kp[it], whi, wlo, 1.0f);
+      u32x4_t y;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) y[jj] = rot_pair(kx[it][jj], cs_tab[ci + jj]);
+      *reinterpret_cast<u32x4_t*>(&k_lds[buf][row * KROW + 8 * lc]) = y;
     }
   };
   auto stage_v_chunk = [&](int buf, int it) {
@@ -291,7 +334,13 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   constexpr int NROT = 4 * KPT;              // RoPE pairs to stage
   constexpr int NVW = KPT;                   // V chunks to stage
   constexpr int NIT = NROT + NVW;
-  auto region_b = [&](int vbuf, int kdst, int vdst, const uint32_t (*pw)[8]) {
+  auto region_b = [&](int vbuf, int kdst, int vdst, const uint32_t (*pw)[8], const int* ci) {
+    float2 kcs[NROT];
+    auto read_cs = [&](int item) {
+      if (item < NROT) kcs[item] = cs_tab[ci[item / 4] + item % 4];
+    };
+    read_cs(0);
+    read_cs(1);
     bf16x8_t va[NB];
     auto read_v = [&](int i) {
       const int mb = i / 4, kbk = (i >> 1) & 1, j = i & 1;
@@ -318,14 +367,11 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
                                                       o[mb], 0, 0, 0);
 #pragma unroll
       for (int item = i * NIT / NB; item < (i + 1) * NIT / NB; ++item) {
+        read_cs(item + 2);
         if (item < NROT) {
           // one RoPE pair of K chunk c
           const int c = item / 4, jj = item % 4;
-          const float fp = (float)kp[c];
-          const float rev = __builtin_amdgcn_fractf(fp * whi[jj]) + fp * wlo[jj];
-          const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
-          const float xa = bf16_lo(kx[c][jj]), xb = bf16_hi(kx[c][jj]);
-          ky[jj] = pack_f16x2(xa * cs - xb * sn, xa * sn + xb * cs);
+          ky[jj] = rot_pair(kx[c][jj], kcs[item]);
           if (jj == 3) {        // chunk complete: one 16-byte store
             const int key = lk + c;
             const int row = (key & ~31) + key_to_row(key & 31);
@@ -342,12 +388,17 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   // ---- prologue: K'(0), K'(1), V(0)^T in LDS; S(0) in registers; K(2), V(1)
   // in flight
   load_k(0);
+  load_pos(0, kpos0);
   load_v(0);
-  stage_k(0);
+  __syncthreads();                     // table complete
+  stage_k(0, kpos0);
   stage_v(0);
   load_k(1);
-  stage_k(1);
+  load_pos(1, kpos1);
+  stage_k(1, kpos1);
   load_k(2);
+  load_pos(2, kpos0);
+  load_pos(3, kpos1);
   load_v(1);
   __syncthreads();
   f32x16_t sa[2], sb[2];
@@ -369,22 +420,29 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   set_cinit();
 
   // one pipeline step; `cur` holds S(t), `nxt` receives S(t+1)
-  auto step = [&](int t, f32x16_t* cur, f32x16_t* nxt) {
+  // `kps` holds the positions of K(t+2) and receives those of K(t+4).  The
+  // rare branches (rotation fallback, rescale) come first, so that regions
+  // A and B form one block whose interleaving the compiler keeps.
+  auto step = [&](int t, f32x16_t* cur, f32x16_t* nxt, int* kps) {
+    int ci[KPT];
+#pragma unroll
+    for (int it = 0; it < KPT; ++it) ci[it] = key_cs_index(kps, it);
     softmax_max(t, cur);
     region_a((t + 1) & 1, cur, nxt, pw);
     // K(t+2) into buffer t&1 (it held K(t), consumed last step); V(t+1) into
     // buffer (t+1)&1 (it held V(t-1), consumed last step)
-    region_b(t & 1, t & 1, (t + 1) & 1, pw);
+    region_b(t & 1, t & 1, (t + 1) & 1, pw, ci);
     load_k(t + 3);
+    load_pos(t + 4, kps);
     load_v(t + 2);
     __syncthreads();
   };
   int t = 0;
   for (; t + 1 < nkt; t += 2) {
-    step(t, sa, sb);
-    step(t + 1, sb, sa);
+    step(t, sa, sb, kpos0);
+    step(t + 1, sb, sa, kpos1);
   }
-  if (t < nkt) step(t, sa, sb);
+  if (t < nkt) step(t, sa, sb, kpos0);
 
   // ---- epilogue: O / l, bf16, store (lane holds channels 32mb + 8(i/4) + 4g + i%4)
   const float inv = 1.0f / pair_sum(l_run);
