@@ -1,7 +1,7 @@
 """Turn rocprofv3 CSV output into the committed profile summaries.
 
-Three rocprofv3 runs of bench.py feed it (each with --copy-calibration, which
-adds an elementwise fp32 copy of known size):
+Three rocprofv3 runs of bench.py feed the trace/traffic summary (each with
+--copy-calibration, which adds an elementwise fp32 copy of known size):
 
   rocprofv3 --kernel-trace --stats --output-format csv -d STATS -o run -- python3 bench.py ...
   rocprofv3 --pmc FETCH_SIZE      --output-format csv -d FETCH -o run -- python3 bench.py ...
@@ -14,6 +14,9 @@ attention kernel next to its algorithmic bytes.
   python -m joint_attention_rope_amd.profiling --kernel attn_fwd_bf16_kernel \
       --name attn_fwd_bf16_2048px_t2i_cfg --workload 4 --stats STATS --fetch FETCH \
       --write WRITE --steps 5 --copy-mib 1024 --command "..."
+
+Two more --pmc runs with the SQ counter sets below feed the instruction and
+utilisation summary (--counters PASS1 PASS2 instead of --stats/--fetch/--write).
 """
 
 import argparse
@@ -66,6 +69,67 @@ def counter_per_dispatch(pmc_dir, kernel, counter):
             if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter]
 
 
+# Counter passes (8 SQ counters and one GRBM counter per pass at most).
+COUNTER_PASSES = [
+    "GRBM_GUI_ACTIVE SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU "
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_TRANS_F32 SQ_WAIT_INST_LDS SQ_ACTIVE_INST_LDS",
+    "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_SALU "
+    "SQ_INSTS_VMEM SQ_WAVES SQ_ACTIVE_INST_ANY",
+]
+SIMDS = 256 * 4
+
+
+def counter_means(dirs, kernel):
+    """Mean per dispatch of every counter collected for `kernel` in `dirs`
+    (values of one dispatch summed over the units that report them)."""
+    out = {}
+    for d in dirs:
+        per = {}
+        for r in _rows(_find(d, "counter_collection.csv")):
+            if kernel in r["Kernel_Name"]:
+                key = (r["Dispatch_Id"], r["Counter_Name"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        by = {}
+        for (_, c), v in per.items():
+            by.setdefault(c, []).append(v)
+        for c, vs in by.items():
+            out[c] = sum(vs) / len(vs)
+    return out
+
+
+def counters_markdown(kernel, cfg, dirs, command):
+    """Instruction mix per wave-tile (one wave's 32 queries against one
+    64-key tile) and MFMA utilisation from the SQ counter passes."""
+    c = counter_means(dirs, kernel)
+    nqt = (cfg.S + 255) // 256
+    nkt = (cfg.S + 63) // 64
+    tiles = cfg.B * cfg.H * nqt * 8 * nkt
+    rows = [("SQ_INSTS_MFMA", "MFMA instructions"), ("SQ_INSTS_VALU", "VALU instructions (incl. MFMA)"),
+            ("SQ_INSTS_VALU_TRANS_F32", "transcendental VALU (exp, sin, cos)"),
+            ("SQ_INSTS_LDS", "LDS instructions"), ("SQ_LDS_BANK_CONFLICT", "LDS bank-conflict cycles"),
+            ("SQ_INSTS_SALU", "SALU instructions"), ("SQ_INSTS_VMEM", "vector memory instructions"),
+            ("SQ_VALU_MFMA_BUSY_CYCLES", "MFMA busy cycles"),
+            ("SQ_WAIT_INST_LDS", "cycles waiting for LDS data (x4)"),
+            ("SQ_WAIT_INST_ANY", "cycles waiting for any dependency (x4)"),
+            ("SQ_WAVE_CYCLES", "wave cycles (x4)")]
+    lines = ["| counter | meaning | per dispatch | per wave-tile |", "|---|---|---|---|"]
+    for k, m in rows:
+        if k in c:
+            lines.append(f"| {k} | {m} | {c[k]:.4e} | {c[k] / tiles:.2f} |")
+    util = ""
+    if "GRBM_GUI_ACTIVE" in c and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+        # GRBM_GUI_ACTIVE is reported once per XCD: the busy cycles of one
+        # dispatch are its mean over the 8 XCDs
+        busy = c["GRBM_GUI_ACTIVE"] / 8
+        util = (f"\nMFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x {SIMDS} SIMDs) "
+                f"= {c['SQ_VALU_MFMA_BUSY_CYCLES']:.4e} / ({busy:.4e} x {SIMDS}) = "
+                f"**{100 * c['SQ_VALU_MFMA_BUSY_CYCLES'] / (busy * SIMDS):.1f} %** of the cycles the "
+                f"GPU was busy with the dispatch.\n")
+    return (f"## Counters (rocprofv3 --pmc, two passes)\n\nWave-tiles per dispatch: {tiles} "
+            f"(B x H x {nqt} query tiles x 8 waves x {nkt} key tiles).\n\n```\n{command}\n```\n\n"
+            + "\n".join(lines) + "\n" + util)
+
+
 def algorithmic_bytes(workload):
     from workloads import get_config
     cfg = get_config(workload)
@@ -79,18 +143,29 @@ def main():
     ap.add_argument("--kernel", required=True)
     ap.add_argument("--name", required=True)
     ap.add_argument("--workload", type=int, required=True)
-    ap.add_argument("--stats", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
-    ap.add_argument("--steps", type=int, required=True, help="timed calls (last N dispatches)")
-    ap.add_argument("--copy-mib", type=int, required=True)
+    ap.add_argument("--stats")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--steps", type=int, help="timed calls (last N dispatches)")
+    ap.add_argument("--copy-mib", type=int)
     ap.add_argument("--command", required=True)
     ap.add_argument("--bench-ms", type=float, default=None,
                     help="ms per call that bench.py printed in the stats run")
+    ap.add_argument("--counters", nargs=2, metavar=("PASS1", "PASS2"),
+                    help="write profiles/<name>_counters.md from two --pmc runs instead")
     args = ap.parse_args()
 
     import sys
     sys.path.insert(0, ROOT)
+    if args.counters:
+        from workloads import get_config
+        md = f"# {args.name} counters\n\nKernel `{args.kernel}`; sources hash " \
+             f"{sources_hash(KERNEL_SOURCES[args.kernel])}.\n\n" + \
+             counters_markdown(args.kernel, get_config(args.workload), args.counters, args.command)
+        with open(os.path.join(ROOT, "profiles", f"{args.name}_counters.md"), "w") as f:
+            f.write(md)
+        print(md)
+        return
     cfg, algo_read, algo_write = algorithmic_bytes(args.workload)
     durs = kernel_durations_ns(args.stats, args.kernel)
     timed = durs[-args.steps:]
