@@ -7,21 +7,27 @@
 // are fp8 MFMAs (v_mfma_scale_f32_32x32x64_f8f6f4, fp32 accumulation):
 //
 //   Q'' = e4m3(R(q_code) * c)            registers, once; c = G / 2^n
-//   K'' = e4m3(R(k_code) / sqrt 2)       LDS, per tile
-//   S^T = 2^n K'' Q''^T - m              the 2^n is the MFMA's E8M0 operand
-//                                        scale, -m the chain's initial value
-//   p   = 2^S,  P8 = e4m3(p)             m is the running row max, raised
-//                                        only when a row grows by more than
-//                                        TAU = 8.75, so p <= 2^8.75 < 448
+//   K'' = e4m3(R(k_code) / 2)            LDS, per tile
+//   S^T = 2^n K'' Q''^T + c0 - m         the 2^n is the MFMA's E8M0 operand
+//                                        scale, c0 - m the chain's initial
+//                                        value, c0 = log2(1.75)
+//   p   = 2^S = 1.75 * 2^(s - m)         m is the running row max, raised only
+//   P8  = e4m3(p)                        when a row grows by more than TAU = 8,
+//                                        so p <= 1.75 * 2^8 = 448
 //   O^T += V^T P8^T                      V row-major in LDS, read transposed
-//   out = O * dv / l,                    l = sum of p (fp32)
+//   out = O * dv / l,                    l = sum of p (fp32; the 1.75 cancels)
 //
-// with G = dq dk log2(e) sqrt(2) / sqrt(D): the exp2-domain score of query i
-// and key j is dq dk log2(e)/sqrt(D) <R q_i, R k_j> = G <R q_i, K''_j>, and n
-// is picked so that c lies in (1/(2 sqrt 2), 1/sqrt 2].  A rotated pair
-// component grows by at most sqrt 2, so |R(code)| c <= 448 and neither
-// re-quantisation leaves the E4M3 range.  Softmax therefore needs no VALU
-// multiply at all: one v_exp_f32 and half a conversion per score.
+// with G = 2 dq dk log2(e) / sqrt(D): the exp2-domain score of query i and
+// key j is dq dk log2(e)/sqrt(D) <R q_i, R k_j> = G <R q_i, K''_j>, and n is
+// picked so that c lies in (1/(2 sqrt 2), 1/sqrt 2].  A rotated pair
+// component grows by at most sqrt 2, so |R(code)| c <= 448, |R(code)| / 2 <=
+// 317, and neither re-quantisation leaves the E4M3 range.  Halving K (a power
+// of two) keeps the channels the rotation leaves alone -- the t and l axis
+// blocks of image tokens, at position 0 -- exact codes, which is worth a
+// fifth of the fp8 path's error against the oracle.  Softmax therefore needs no VALU
+// multiply at all: one v_exp_f32 and half a conversion per score.  The 1.75
+// (folded into the chain's start) lifts p so that the full E4M3 range is used
+// and fewer small probabilities fall to its subnormals.
 //
 // Schedule (per wave; K'' and V double-buffered in LDS, one barrier a tile):
 //   softmax max of S(t); rare rescale of O and l
@@ -30,7 +36,7 @@
 //                                                   V(t+1) into LDS
 //   buffer loads of K(t+3), V(t+2); barrier
 //
-// Rotation of keys: cos and sin (times 1/sqrt 2) of every (position, pair)
+// Rotation of keys: cos and sin (times 1/2) of every (position, pair)
 // with position in [0, 512) come from an LDS table built once per workgroup;
 // a wave that holds any other position computes them directly instead.
 //
@@ -52,7 +58,7 @@ namespace klein {
 
 namespace {
 
-constexpr float kInvSqrt2 = 0.70710678118654752f;
+constexpr float kHalf = 0.5f;
 constexpr int kTabN = 1024;       // positions covered by the cos/sin table
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
@@ -114,13 +120,14 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   constexpr int TROW = NJ + 2;         // cos/sin table row stride (half2)
   constexpr int TSLOT = 10;            // per-thread fallback slot stride
   constexpr int TAB = kTabN * TROW;    // start of the fallback slots
-  constexpr float TAU = 8.75f;         // 2^TAU < 448
+  constexpr float TAU = 8.0f;          // 1.75 * 2^TAU = 448
+  constexpr float C0 = 0.80735492205760410f;   // log2(1.75)
   static_assert(NCH == NT || 2 * NCH == NT, "one K and one V chunk per thread (D 128) "
                                             "or one of either (D 64)");
 
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][BN * KROW];
   __shared__ __attribute__((aligned(16))) uint8_t v_lds[2][BN * VROW];
-  // fp16 (cos, sin) / sqrt 2: table rows for positions [0, kTabN), then 8
+  // fp16 (cos, sin) / 2: table rows for positions [0, kTabN), then 8
   // per-thread slots.  Row and slot strides of 2 (mod 4) dwords spread 32
   // rows over all banks and keep pairs of entries 8-byte aligned.
   __shared__ __attribute__((aligned(16))) h2_t cs_tab[TAB + TSLOT * NT];
@@ -139,10 +146,10 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   const uint8_t* vbase = v + base;
   const int rowb = (int)rs;
 
-  // ---- cos/sin table: entry p * TROW + j = (cos, sin)(p w_j) / sqrt 2
+  // ---- cos/sin table: entry p * TROW + j = (cos, sin)(p w_j) / 2
   for (int e = tid; e < kTabN * NJ; e += NT) {
     const int j = e % NJ, p = e / NJ;
-    const float2 c = rope_cs(p, fr.hi[j], fr.lo[j], kInvSqrt2);
+    const float2 c = rope_cs(p, fr.hi[j], fr.lo[j], kHalf);
     cs_tab[p * TROW + j] = (h2_t){(_Float16)c.x, (_Float16)c.y};
   }
 
@@ -215,7 +222,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   auto stage_v = [&](int buf) {
     if (vst) *reinterpret_cast<u32x4_t*>(&v_lds[buf][vkey * VROW + 16 * vc]) = vx;
   };
-  // (cos, sin) / sqrt 2 of the 8 pairs of this thread's K chunk, as an index
+  // (cos, sin) / 2 of the 8 pairs of this thread's K chunk, as an index
   // into cs_tab: the table row of its position, or (position outside the
   // table) its own 8 slots past the table, filled here.  The branch is
   // divergent and skipped by waves whose positions all lie in the table.
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
       for (int jj = 0; jj < 8; ++jj) {
         int j = kj0 + jj;
         asm volatile("" : "+v"(j));      // keep the loads in this rare path
-        const float2 c = rope_cs(kp, fr.hi[j], fr.lo[j], kInvSqrt2);
+        const float2 c = rope_cs(kp, fr.hi[j], fr.lo[j], kHalf);
         cs_tab[TAB + TSLOT * tid + jj] = (h2_t){(_Float16)c.x, (_Float16)c.y};
       }
     }
@@ -283,7 +290,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   f32x16_t cinit;
   auto set_cinit = [&]() {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) cinit[i] = -m_run;
+    for (int i = 0; i < 16; ++i) cinit[i] = C0 - m_run;
   };
   auto mask_tail = [&](int t, f32x16_t* sc) {
     if (t * BN + BN > S) {
@@ -296,9 +303,9 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   };
   auto softmax_max = [&](int t, f32x16_t* sc) {
     mask_tail(t, sc);
-    const float mx = rowmax32(sc);
-    if (__builtin_amdgcn_ballot_w64(mx > TAU)) {
-      const float delta = __builtin_fmaxf(mx, 0.f);
+    const float mx = rowmax32(sc);              // (row max relative to m) + C0
+    if (__builtin_amdgcn_ballot_w64(mx > TAU + C0)) {
+      const float delta = __builtin_fmaxf(mx - C0, 0.f);
       const float alpha = __builtin_amdgcn_exp2f(-delta);
       m_run += delta;
       l_run *= alpha;
@@ -411,7 +418,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   mask_tail(0, sa);
   m_run = rowmax32(sa);
 #pragma unroll
-  for (int kbk = 0; kbk < 2; ++kbk) sa[kbk] -= m_run;
+  for (int kbk = 0; kbk < 2; ++kbk) sa[kbk] -= m_run - C0;
   set_cinit();
 
   i32x8_t pb = {};
@@ -454,7 +461,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   }
 }
 
-// Score scale split: G = dq dk log2(e) sqrt(2) / sqrt(D) = c * 2^n with c in
+// Score scale split: G = 2 dq dk log2(e) / sqrt(D) = c * 2^n with c in
 // (1/(2 sqrt 2), 1/sqrt 2]; 2^n goes to the MFMA as two E8M0 operand scales
 // (each in [2^-127, 2^127]).  |n| > 254 is clamped (descale products that far
 // out underflow or overflow fp32 scores anyway).
@@ -464,7 +471,7 @@ struct Fp8Scales {
 };
 static Fp8Scales fp8_scales(const LaunchArgs& a) {
   const double G = (double)a.descale[0] * (double)a.descale[1] *
-                   1.4426950408889634 * 1.4142135623730951 / std::sqrt((double)a.D);
+                   1.4426950408889634 * 2.0 / std::sqrt((double)a.D);
   int n = (int)std::ceil(std::log2(G * 1.4142135623730951));
   if (n > 254) n = 254;
   if (n < -254) n = -254;
