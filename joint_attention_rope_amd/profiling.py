@@ -130,6 +130,41 @@ def counters_markdown(kernel, cfg, dirs, command):
             + "\n".join(lines) + "\n" + util)
 
 
+def gemm_ceiling(sizes=(8192, 16384)):
+    """Vendor GEMM throughput on this GPU (hipBLASLt through torch): the
+    practical MFMA ceiling that a dense contraction reaches here, on random
+    and on all-zero operands (the difference is data-dependent power)."""
+    import torch
+    dev = "cuda"
+
+    def rate(fn, flops, n=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return flops / (e0.elapsed_time(e1) / n * 1e-3) / 1e12
+
+    rows = []
+    for m in sizes:
+        a = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+        b = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+        z = torch.zeros_like(a)
+        one = torch.tensor(1.0, device=dev)
+        a8 = a.to(torch.float8_e4m3fn)
+        b8 = b.to(torch.float8_e4m3fn).t().contiguous().t()
+        rows.append((m, rate(lambda: a @ b, 2 * m ** 3), rate(lambda: z @ z, 2 * m ** 3),
+                     rate(lambda: torch._scaled_mm(a8, b8, one, one, out_dtype=torch.bfloat16),
+                          2 * m ** 3)))
+        del a, b, z, a8, b8
+    return rows
+
+
 def algorithmic_bytes(workload):
     from workloads import get_config
     cfg = get_config(workload)
@@ -140,20 +175,28 @@ def algorithmic_bytes(workload):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--kernel", required=True)
-    ap.add_argument("--name", required=True)
-    ap.add_argument("--workload", type=int, required=True)
+    ap.add_argument("--kernel")
+    ap.add_argument("--name")
+    ap.add_argument("--workload", type=int)
     ap.add_argument("--stats")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--steps", type=int, help="timed calls (last N dispatches)")
     ap.add_argument("--copy-mib", type=int)
-    ap.add_argument("--command", required=True)
+    ap.add_argument("--command")
     ap.add_argument("--bench-ms", type=float, default=None,
                     help="ms per call that bench.py printed in the stats run")
     ap.add_argument("--counters", nargs=2, metavar=("PASS1", "PASS2"),
                     help="write profiles/<name>_counters.md from two --pmc runs instead")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="measure vendor GEMM throughput on the GPU and print a markdown table")
     args = ap.parse_args()
+    if args.gemm_ceiling:
+        print("| M = N = K | bf16, random | bf16, zeros | fp8 e4m3 (scaled_mm), random |")
+        print("|---|---|---|---|")
+        for m, r, z, f in gemm_ceiling():
+            print(f"| {m} | {r:.0f} TFLOP/s | {z:.0f} TFLOP/s | {f:.0f} TFLOP/s |", flush=True)
+        return
 
     import sys
     sys.path.insert(0, ROOT)
