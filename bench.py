@@ -115,6 +115,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--extra", action="store_true",
+                    help="also time multi-reference 2048x2048 edits (bf16, 2 references; "
+                         "fp8, 3 references) and report them under 'extra'")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, run an elementwise fp32 copy of MIB MiB three "
                          "times (a kernel of known HBM traffic for scaling counters)")
@@ -178,6 +181,27 @@ def main():
             del q5, k5, v5, o5
         except kl.KleinError as e:
             rec["fp8"] = {"error": str(e)}
+    if args.extra:
+        rec["extra"] = []
+        for cid, refs, peak in ((3, 2, PEAK_BF16), (5, 3, PEAK_FP8)):
+            c = get_config(cid, grid=128, refs=refs)
+            print(f"[extra] generating {c.dtype} S={c.S} inputs", file=sys.stderr, flush=True)
+            xi = make_inputs(c)
+            print(f"[extra] timing {c.dtype} S={c.S}", file=sys.stderr, flush=True)
+            xq, xk, xv, xp = to_device(xi, dev)
+            xo = torch.empty(xq.shape, dtype=torch.bfloat16, device=dev)
+            if xi.descale is None:
+                call = lambda: kl.klein_rope4d_attn_fwd(xq, xk, xv, xp, xo)
+            else:
+                call = lambda: kl.klein_rope4d_attn_fwd_fp8(xq, xk, xv, xp, xo, *xi.descale)
+            xms = time_gpu(call, 5, 2, torch)
+            xt = c.flops / (xms * 1e-3) / 1e12
+            rec["extra"].append({
+                "workload": f"2048x2048 edit with {refs} references: B={c.B}, S={c.S} "
+                            f"({c.text} text + {refs + 1} x 128x128), H={c.H}, D={c.D}, {c.dtype}",
+                "ms_per_call": round(xms, 4), "tflops": round(xt, 2), "peak": peak,
+                "frac": round(xt / peak, 4)})
+            del xq, xk, xv, xo
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)

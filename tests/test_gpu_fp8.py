@@ -52,6 +52,17 @@ def test_fp8_edit_workload_sampled_rows():
     assert_fp8_close(gpu, oracle_rows(inp, rows), "fp8 workload 5")
 
 
+def test_fp8_multi_reference_sampled_rows():
+    # 1024^2 edit with two references (t = 1, 2) and a prompt padded to 560
+    cfg = get_config(5, grid=64, refs=2, text=560)
+    inp = make_inputs(cfg)
+    print("[case] fp8 multi-reference", inp.q.shape, flush=True)
+    out = run_attention(inp)
+    rows = sample_rows(cfg.S, cfg.text, n=24, seed=55)
+    gpu = bf16_tensor_to_f64(out[:, torch.from_numpy(rows).to(out.device)])
+    assert_fp8_close(gpu, oracle_rows(inp, rows), "fp8 multi-reference")
+
+
 def test_fp8_deterministic():
     inp = random_fp8_inputs(1, 700, 4, 128, seed=3)
     a = run_attention(inp)

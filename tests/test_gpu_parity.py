@@ -50,6 +50,8 @@ def test_large_positions_full():
     (4, {}),
     (2, {"text": 480}),     # prompt padded to a multiple of 80 tokens
     (2, {"text": 560}),
+    (3, {"refs": 2, "text": 560}),   # two references at t = 1, 2: S = 560 + 3 x 64^2
+    (3, {"refs": 3, "text": 480}),   # three references: S = 480 + 4 x 64^2
 ])
 def test_workload_sampled_rows(cid, overrides):
     cfg = get_config(cid, **overrides)
