@@ -36,6 +36,10 @@ Modules:
   brute      -- pure-Python scalar loops for tiny shapes (the brute-force pin)
   fp8        -- OCP E4M3FN decoding (pinned: all 256 codes against the
                 format's definition and torch.float8_e4m3fn)
+  blocksparse -- the same attention restricted to kept (query block, key
+                block) pairs, the reading of the pages' sparsified attention
+                (pinned: brute force, every block kept = dense, one kept block
+                = dense on that block's keys)
 """
 
 from .joint_attention import (
@@ -46,11 +50,19 @@ from .joint_attention import (
     decode_inputs,
     rel_l2,
 )
+from .blocksparse import (
+    attention_blocksparse,
+    attention_blocksparse_inputs_rows,
+    attention_blocksparse_rows,
+)
 from .fp8 import e4m3_decode
 from .rope4d import rope4d, rope_frequencies
 
 __all__ = [
     "attention",
+    "attention_blocksparse",
+    "attention_blocksparse_inputs_rows",
+    "attention_blocksparse_rows",
     "attention_inputs_rows",
     "attention_rows",
     "bf16_to_f64",

@@ -44,3 +44,25 @@ def attention_scalar(q, k, v, pos, theta=10000.0):
                 for d in range(D):
                     out[b][i][h][d] = sum(e[j] * v[b][j][h][d] for j in range(S)) / z
     return out
+
+
+def attention_blocksparse_scalar(q, k, v, pos, mask, qblock, kblock, theta=10000.0):
+    """Block-sparse variant: query i attends to key j only when
+    mask[b][h][i // qblock][j // kblock] is nonzero; no kept key gives 0."""
+    B, S, H, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    out = [[[[0.0] * D for _ in range(H)] for _ in range(S)] for _ in range(B)]
+    for b in range(B):
+        for h in range(H):
+            qr = [rope_scalar(q[b][i][h], pos[i], theta) for i in range(S)]
+            kr = [rope_scalar(k[b][j][h], pos[j], theta) for j in range(S)]
+            for i in range(S):
+                kept = [j for j in range(S) if mask[b][h][i // qblock][j // kblock]]
+                if not kept:
+                    continue
+                s = {j: sum(qr[i][d] * kr[j][d] for d in range(D)) / math.sqrt(D) for j in kept}
+                m = max(s.values())
+                e = {j: math.exp(s[j] - m) for j in kept}
+                z = sum(e.values())
+                for d in range(D):
+                    out[b][i][h][d] = sum(e[j] * v[b][j][h][d] for j in kept) / z
+    return out
