@@ -99,6 +99,37 @@ klein_status_t klein_rope4d_attn_fwd_fp8(const void* q, const void* k, const voi
                                          float v_descale, klein_stream_t stream);
 
 /*
+ * Block-sparse variant: the same attention with each query attending only to
+ * the keys of the kept blocks of its query block.  This is how this library
+ * reads the sparsified attention of the Blackwell write-up ("How FLUX 3 Image
+ * Klein was made 3-4x faster on NVIDIA Blackwell", section "Method 2": weakly
+ * related query/key combinations are left out, the early denoising steps
+ * stay dense).  The page gives no rule for choosing the combinations, so the
+ * caller passes them:
+ *   block_mask: DEVICE pointer, uint8 [B][H][ceil(S/KLEIN_SPARSE_QBLOCK)]
+ *               [ceil(S/KLEIN_SPARSE_KBLOCK)], contiguous; nonzero = compute
+ *               the block of queries [i*QBLOCK, (i+1)*QBLOCK) against keys
+ *               [j*KBLOCK, (j+1)*KBLOCK).
+ * For query i in query block I: out_i = sum over keys j in kept blocks (I, J)
+ * of softmax_j(<q'_i, k'_j> / sqrt(D)) v_j, the softmax taken over those keys
+ * only; a query block with no kept block gets out = 0.  Work and time scale
+ * with the kept blocks; with every block kept the result is bit-identical to
+ * the dense entry points.  dtype BF16 ignores the descales; FP8_E4M3 uses
+ * them as klein_rope4d_attn_fwd_fp8 does (finite, > 0).
+ * ceil(S/KLEIN_SPARSE_KBLOCK) must not exceed 4096 (else UNSUPPORTED);
+ * a null mask is INVALID_ARG.
+ */
+#define KLEIN_SPARSE_QBLOCK 256
+#define KLEIN_SPARSE_KBLOCK 64
+klein_status_t klein_rope4d_attn_fwd_blocksparse(const void* q, const void* k, const void* v,
+                                                 const int32_t* pos_thwl, void* out,
+                                                 int B, int S, int H, int D,
+                                                 klein_dtype_t dtype, float q_descale,
+                                                 float k_descale, float v_descale,
+                                                 const uint8_t* block_mask,
+                                                 klein_stream_t stream);
+
+/*
  * Test hook: y = R(pos) x for bfloat16 x, y [B][S][H][D] (same layout rules),
  * computed with the very device routine the attention kernels use for Q and
  * K, rounded to bfloat16.  x and y may be the same buffer.

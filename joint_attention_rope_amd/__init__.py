@@ -12,12 +12,14 @@ import torch
 
 from . import _capi
 from ._capi import (KLEIN_DTYPE_BF16, KLEIN_DTYPE_FP8_E4M3, KLEIN_ERR_INVALID_ARG,
-                    KLEIN_ERR_LAUNCH, KLEIN_ERR_NO_DEVICE, KLEIN_ERR_UNSUPPORTED, KLEIN_OK)
+                    KLEIN_ERR_LAUNCH, KLEIN_ERR_NO_DEVICE, KLEIN_ERR_UNSUPPORTED, KLEIN_OK,
+                    KLEIN_SPARSE_KBLOCK, KLEIN_SPARSE_QBLOCK)
 
 __all__ = [
     "KleinError", "klein_rope4d_attn_fwd", "klein_rope4d_attn_fwd_fp8",
-    "klein_rope4d_apply", "klein_status_string", "klein_version", "library_path",
-    "KLEIN_DTYPE_BF16", "KLEIN_DTYPE_FP8_E4M3",
+    "klein_rope4d_attn_fwd_blocksparse", "klein_rope4d_apply", "klein_status_string",
+    "klein_version", "library_path", "KLEIN_DTYPE_BF16", "KLEIN_DTYPE_FP8_E4M3",
+    "KLEIN_SPARSE_QBLOCK", "KLEIN_SPARSE_KBLOCK", "blocksparse_mask_shape",
 ]
 
 
@@ -113,6 +115,46 @@ def klein_rope4d_attn_fwd_fp8(q, k, v, pos_thwl, out, q_descale, k_descale, v_de
         B, S, H, D, float(q_descale), float(k_descale), float(v_descale),
         _stream(stream, q.device))
     _check(st, "klein_rope4d_attn_fwd_fp8")
+    return out
+
+
+def blocksparse_mask_shape(B, S, H):
+    """Shape of the block mask of klein_rope4d_attn_fwd_blocksparse."""
+    return (B, H, -(-S // KLEIN_SPARSE_QBLOCK), -(-S // KLEIN_SPARSE_KBLOCK))
+
+
+def klein_rope4d_attn_fwd_blocksparse(q, k, v, pos_thwl, out, block_mask, dtype=None,
+                                      descales=(1.0, 1.0, 1.0), stream=None):
+    """Block-sparse RoPE-4D joint attention: queries of query block I attend to
+    the keys of the blocks J with block_mask[b, h, I, J] != 0 only.
+
+    block_mask: uint8 (or bool) GPU tensor of blocksparse_mask_shape(B, S, H).
+    dtype: KLEIN_DTYPE_BF16 or KLEIN_DTYPE_FP8_E4M3 (inferred from q.dtype when
+    None); descales (q, k, v) apply to fp8 only.  out: bfloat16 [B, S, H, D].
+    """
+    B, S, H, D = _bshd(q, "q")
+    for t, n in ((k, "k"), (v, "v"), (out, "out")):
+        if _bshd(t, n) != (B, S, H, D):
+            raise ValueError(f"{n} must have q's shape {(B, S, H, D)}")
+    _pos(pos_thwl, S)
+    if dtype is None:
+        dtype = KLEIN_DTYPE_FP8_E4M3 if q.dtype in _FP8_DTYPES else KLEIN_DTYPE_BF16
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        ok = t.dtype == torch.bfloat16 if dtype == KLEIN_DTYPE_BF16 else t.dtype in _FP8_DTYPES
+        if not ok:
+            raise ValueError(f"{n} has dtype {t.dtype}, which does not match the dtype code {dtype}")
+    if out.dtype != torch.bfloat16:
+        raise ValueError("out must be bfloat16")
+    if block_mask.dtype not in (torch.uint8, torch.bool) or not block_mask.is_cuda \
+            or not block_mask.is_contiguous() \
+            or tuple(block_mask.shape) != blocksparse_mask_shape(B, S, H):
+        raise ValueError("block_mask must be a contiguous uint8/bool GPU tensor of shape "
+                         f"{blocksparse_mask_shape(B, S, H)}")
+    dq, dk, dv = (float(x) for x in descales)
+    st = _capi.lib().klein_rope4d_attn_fwd_blocksparse(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), pos_thwl.data_ptr(), out.data_ptr(),
+        B, S, H, D, int(dtype), dq, dk, dv, block_mask.data_ptr(), _stream(stream, q.device))
+    _check(st, "klein_rope4d_attn_fwd_blocksparse")
     return out
 
 

@@ -18,6 +18,8 @@ KLEIN_ERR_INVALID_ARG = 1
 KLEIN_ERR_UNSUPPORTED = 2
 KLEIN_ERR_NO_DEVICE = 3
 KLEIN_ERR_LAUNCH = 4
+KLEIN_SPARSE_QBLOCK = 256
+KLEIN_SPARSE_KBLOCK = 64
 
 _lib = None
 
@@ -27,6 +29,8 @@ SIGNATURES = {
     "klein_rope4d_attn_fwd": (_int, [_vp, _vp, _vp, _i32p, _vp, _int, _int, _int, _int, _int, _vp]),
     "klein_rope4d_attn_fwd_fp8": (_int, [_vp, _vp, _vp, _i32p, _vp, _int, _int, _int, _int,
                                          _f32, _f32, _f32, _vp]),
+    "klein_rope4d_attn_fwd_blocksparse": (_int, [_vp, _vp, _vp, _i32p, _vp, _int, _int, _int,
+                                                 _int, _int, _f32, _f32, _f32, _vp, _vp]),
     "klein_rope4d_apply": (_int, [_vp, _i32p, _vp, _int, _int, _int, _int, _vp]),
     "klein_status_string": (ctypes.c_char_p, [_int]),
     "klein_version": (_int, []),

@@ -102,6 +102,35 @@ klein_status_t klein_rope4d_attn_fwd_fp8(const void* q, const void* k, const voi
   }
 }
 
+klein_status_t klein_rope4d_attn_fwd_blocksparse(const void* q, const void* k, const void* v,
+                                                 const int32_t* pos_thwl, void* out, int B,
+                                                 int S, int H, int D, klein_dtype_t dtype,
+                                                 float q_descale, float k_descale,
+                                                 float v_descale, const uint8_t* block_mask,
+                                                 klein_stream_t stream) {
+  if (dtype != KLEIN_DTYPE_BF16 && dtype != KLEIN_DTYPE_FP8_E4M3) return KLEIN_ERR_INVALID_ARG;
+  klein_status_t st = check_common(q, k, v, pos_thwl, out, B, S, H, D);
+  if (st != KLEIN_OK) return st;
+  if (!block_mask) return KLEIN_ERR_INVALID_ARG;
+  if ((S + KLEIN_SPARSE_KBLOCK - 1) / KLEIN_SPARSE_KBLOCK > klein::kSparseMaxTiles)
+    return KLEIN_ERR_UNSUPPORTED;
+  const bool fp8 = dtype == KLEIN_DTYPE_FP8_E4M3;
+  if (fp8)
+    for (float s : {q_descale, k_descale, v_descale})
+      if (!(std::isfinite(s) && s > 0.f)) return KLEIN_ERR_INVALID_ARG;
+  if ((fp8 ? klein::attn_fwd_fp8_grid(B, S, H) : klein::attn_fwd_bf16_grid(B, S, H)) > kMaxGrid)
+    return KLEIN_ERR_UNSUPPORTED;
+  try {
+    LaunchArgs a = make_args(q, k, v, pos_thwl, out, B, S, H, D, stream);
+    a.bmask = block_mask;
+    if (!fp8) return map_hip(klein::launch_attn_fwd_bf16(a));
+    a.descale[0] = q_descale; a.descale[1] = k_descale; a.descale[2] = v_descale;
+    return map_hip(klein::launch_attn_fwd_fp8(a));
+  } catch (...) {
+    return KLEIN_ERR_LAUNCH;
+  }
+}
+
 klein_status_t klein_rope4d_apply(const void* x, const int32_t* pos_thwl, void* y, int B, int S,
                                   int H, int D, klein_stream_t stream) {
   if (!x || !pos_thwl || !y) return KLEIN_ERR_INVALID_ARG;
@@ -119,13 +148,13 @@ const char* klein_status_string(klein_status_t status) {
   switch (status) {
     case KLEIN_OK: return "ok";
     case KLEIN_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, size < 1, bad dtype or descale)";
-    case KLEIN_ERR_UNSUPPORTED: return "unsupported (head dim must be 64 or 128; grid too large)";
+    case KLEIN_ERR_UNSUPPORTED: return "unsupported (head dim must be 64 or 128; grid or block mask too large)";
     case KLEIN_ERR_NO_DEVICE: return "no usable GPU";
     case KLEIN_ERR_LAUNCH: return "kernel launch failed";
   }
   return "unknown status";
 }
 
-int klein_version(void) { return 100; }
+int klein_version(void) { return 110; }
 
 }  // extern "C"

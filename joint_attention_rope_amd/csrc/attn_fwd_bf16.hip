@@ -68,11 +68,16 @@ __device__ __forceinline__ int key_to_row(int kk) {
   return ((i >> 2) << 3) + (g << 2) + (i & 3);
 }
 
-template <int D>
+// SPARSE: block-sparse variant; bmask holds one byte per (batch, head, query
+// tile of 256, key tile of 64), nonzero = compute, and only the kept key
+// tiles of a query tile stream through the pipeline (in ascending order, so
+// with every tile kept the result is bit-identical to the dense kernel).
+template <int D, bool SPARSE>
 __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ pos,
-    uint16_t* __restrict__ out, int S, int H, int nqt, RopeFreqs fr, float qscale) {
+    uint16_t* __restrict__ out, int S, int H, int nqt, RopeFreqs fr, float qscale,
+    const uint8_t* __restrict__ bmask) {
   constexpr int BM = 256;              // queries per workgroup (8 waves x 32)
   constexpr int BN = 64;               // keys per tile
   constexpr int NT = 512;              // threads
@@ -96,6 +101,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   // (cos, sin) of every pair at positions [0, kTabN), then per-thread slots
   // for keys at other positions; odd strides spread rows over the banks
   __shared__ __attribute__((aligned(16))) float2 cs_tab[TAB + TSLOT * NT];
+  __shared__ uint16_t klist[SPARSE ? kSparseMaxTiles + kSparsePad : 1];
+  __shared__ int klist_n;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lr = lane & 31;
@@ -146,6 +153,11 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   const int voff = lk * rowb + 16 * lc;
   const int voff_p = (lk * 4 + la) * 4;
   const int nkt = (S + BN - 1) / BN;
+  // tile index of pipeline position t (the kept list when SPARSE)
+  auto tl = [&](int t) -> int {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)klist[t]);
+    else return t;
+  };
   u32x4_t kx[KPT], vx[KPT];
   // positions of this thread's K keys, loaded one step ahead of the K data:
   // ring slot kt & 1 holds tile kt's
@@ -385,21 +397,42 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     }
   };
 
+  int nsteps = nkt;
+  if constexpr (SPARSE) {
+    if (wave == 0) {
+      const int n = build_kept_list(bmask + ((size_t)bh * nqt + qt) * nkt, nkt, klist, lane);
+      if (lane == 0) klist_n = n;
+    }
+    __syncthreads();
+    nsteps = __builtin_amdgcn_readfirstlane(klist_n);
+    if (nsteps == 0) {                 // nothing kept: the rows are zero
+      if (qrow < S) {
+        uint16_t* orow = out + base + (size_t)qrow * rs;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4)
+            *reinterpret_cast<uint2*>(orow + 32 * mb + 8 * i4 + 4 * g) = make_uint2(0u, 0u);
+      }
+      return;
+    }
+  }
+
   // ---- prologue: K'(0), K'(1), V(0)^T in LDS; S(0) in registers; K(2), V(1)
-  // in flight
-  load_k(0);
-  load_pos(0, kpos0);
-  load_v(0);
+  // in flight (pipeline positions; tl() maps them to tiles)
+  load_k(tl(0));
+  load_pos(tl(0), kpos0);
+  load_v(tl(0));
   __syncthreads();                     // table complete
   stage_k(0, kpos0);
   stage_v(0);
-  load_k(1);
-  load_pos(1, kpos1);
+  load_k(tl(1));
+  load_pos(tl(1), kpos1);
   stage_k(1, kpos1);
-  load_k(2);
-  load_pos(2, kpos0);
-  load_pos(3, kpos1);
-  load_v(1);
+  load_k(tl(2));
+  load_pos(tl(2), kpos0);
+  load_pos(tl(3), kpos1);
+  load_v(tl(1));
   __syncthreads();
   f32x16_t sa[2], sb[2];
   uint32_t pw[2][8];
@@ -407,12 +440,13 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   __syncthreads();        // K buffer 0 is refilled in iteration 0
   // m_run starts at tile 0's exact row max (keys past S masked), so scores
   // are relative from the first tile on and no row can underflow
-  if (BN > S) {
+  const int kt0 = tl(0);
+  if (kt0 * BN + BN > S) {
 #pragma unroll
     for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (32 * kbk + 16 * g + i >= S) sa[kbk][i] = kNegInf;
+        if (kt0 * BN + 32 * kbk + 16 * g + i >= S) sa[kbk][i] = kNegInf;
   }
   m_run = rowmax32(sa);
 #pragma unroll
@@ -427,22 +461,22 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     int ci[KPT];
 #pragma unroll
     for (int it = 0; it < KPT; ++it) ci[it] = key_cs_index(kps, it);
-    softmax_max(t, cur);
+    softmax_max(tl(t), cur);
     region_a((t + 1) & 1, cur, nxt, pw);
     // K(t+2) into buffer t&1 (it held K(t), consumed last step); V(t+1) into
     // buffer (t+1)&1 (it held V(t-1), consumed last step)
     region_b(t & 1, t & 1, (t + 1) & 1, pw, ci);
-    load_k(t + 3);
-    load_pos(t + 4, kps);
-    load_v(t + 2);
+    load_k(tl(t + 3));
+    load_pos(tl(t + 4), kps);
+    load_v(tl(t + 2));
     __syncthreads();
   };
   int t = 0;
-  for (; t + 1 < nkt; t += 2) {
+  for (; t + 1 < nsteps; t += 2) {
     step(t, sa, sb, kpos0);
     step(t + 1, sb, sa, kpos1);
   }
-  if (t < nkt) step(t, sa, sb, kpos0);
+  if (t < nsteps) step(t, sa, sb, kpos0);
 
   // ---- epilogue: O / l, bf16, store (lane holds channels 32mb + 8(i/4) + 4g + i%4)
   const float inv = 1.0f / pair_sum(l_run);
@@ -461,20 +495,20 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   }
 }
 
-template <int D>
+template <int D, bool SPARSE>
 static hipError_t launch_bf16(const LaunchArgs& a) {
   constexpr int BM = 256;
   const int nqt = (a.S + BM - 1) / BM;
   const long long n = (long long)a.B * a.H * nqt;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3((unsigned)n), dim3(512), 0,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, SPARSE>), dim3((unsigned)n), dim3(512), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     a.pos, (uint16_t*)a.out, a.S, a.H, nqt, a.freqs, a.qscale_log2);
+                     a.pos, (uint16_t*)a.out, a.S, a.H, nqt, a.freqs, a.qscale_log2, a.bmask);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd_bf16(const LaunchArgs& a) {
-  if (a.D == 128) return launch_bf16<128>(a);
-  return launch_bf16<64>(a);
+  if (a.bmask) return a.D == 128 ? launch_bf16<128, true>(a) : launch_bf16<64, true>(a);
+  return a.D == 128 ? launch_bf16<128, false>(a) : launch_bf16<64, false>(a);
 }
 
 long long attn_fwd_bf16_grid(int B, int S, int H) {

@@ -101,11 +101,15 @@ __device__ __forceinline__ int rope_pair_fp8_h(uint32_t word, h2_t cs, int acc) 
 
 }  // namespace
 
-template <int D>
+// SPARSE: block-sparse variant (one mask byte per batch, head, query tile of
+// 256 and key tile of 64; only kept key tiles stream through the pipeline, in
+// ascending order, so with every tile kept the result equals the dense one).
+template <int D, bool SPARSE>
 __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     const int32_t* __restrict__ pos, uint16_t* __restrict__ out, int S, int H, int nqt,
-    RopeFreqs fr, float q_mul, int sc_a, int sc_b, float o_scale) {
+    RopeFreqs fr, float q_mul, int sc_a, int sc_b, float o_scale,
+    const uint8_t* __restrict__ bmask) {
   constexpr int BM = 256;              // queries per workgroup (8 waves x 32)
   constexpr int BN = 64;               // keys per tile
   constexpr int NT = 512;              // threads
@@ -131,6 +135,8 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   // per-thread slots.  Row and slot strides of 2 (mod 4) dwords spread 32
   // rows over all banks and keep pairs of entries 8-byte aligned.
   __shared__ __attribute__((aligned(16))) h2_t cs_tab[TAB + TSLOT * NT];
+  __shared__ uint16_t klist[SPARSE ? kSparseMaxTiles + kSparsePad : 1];
+  __shared__ int klist_n;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lr = lane & 31;
@@ -190,6 +196,11 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   const int krow = (kkey & ~31) + key_to_row8(kkey & 31);
 
   const int nkt = (S + BN - 1) / BN;
+  // tile index of pipeline position t (the kept list when SPARSE)
+  auto tl = [&](int t) -> int {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)klist[t]);
+    else return t;
+  };
   u32x4_t kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
   // positions of this thread's K chunk, loaded one step ahead of the K data:
   // slot kt & 1 holds tile kt's
@@ -390,21 +401,42 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
     }
   };
 
+  int nsteps = nkt;
+  if constexpr (SPARSE) {
+    if (wave == 0) {
+      const int n = build_kept_list(bmask + ((size_t)bh * nqt + qt) * nkt, nkt, klist, lane);
+      if (lane == 0) klist_n = n;
+    }
+    __syncthreads();
+    nsteps = __builtin_amdgcn_readfirstlane(klist_n);
+    if (nsteps == 0) {                 // nothing kept: the rows are zero
+      if (qrow < S) {
+        uint16_t* orow = out + (size_t)b * S * rs + (size_t)h * D + (size_t)qrow * rs;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4)
+            *reinterpret_cast<uint2*>(orow + 32 * mb + 8 * i4 + 4 * g) = make_uint2(0u, 0u);
+      }
+      return;
+    }
+  }
+
   // ---- prologue: table, K''(0), K''(1), V(0) in LDS; S(0) in registers;
-  // K(2), V(1) in flight
-  load_k(0);
-  load_pos(0, kpos0);
-  load_v(0);
+  // K(2), V(1) in flight (pipeline positions; tl() maps them to tiles)
+  load_k(tl(0));
+  load_pos(tl(0), kpos0);
+  load_v(tl(0));
   __syncthreads();                     // table complete
   stage_k(0, kpos0);
   stage_v(0);
-  load_k(1);
-  load_pos(1, kpos1);
+  load_k(tl(1));
+  load_pos(tl(1), kpos1);
   stage_k(1, kpos1);
-  load_k(2);
-  load_pos(2, kpos0);
-  load_pos(3, kpos1);
-  load_v(1);
+  load_k(tl(2));
+  load_pos(tl(2), kpos0);
+  load_pos(tl(3), kpos1);
+  load_v(tl(1));
   __syncthreads();
   f32x16_t sa[2], sb[2];
 #pragma unroll
@@ -415,7 +447,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   }
   __syncthreads();                     // K'' buffer 0 is refilled in iteration 0
   // m starts at tile 0's exact row max, so scores are relative from the start
-  mask_tail(0, sa);
+  mask_tail(tl(0), sa);
   m_run = rowmax32(sa);
 #pragma unroll
   for (int kbk = 0; kbk < 2; ++kbk) sa[kbk] -= m_run - C0;
@@ -428,21 +460,21 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   // B form one block whose interleaving the compiler keeps.
   auto step = [&](int t, f32x16_t* cur, f32x16_t* nxt, int& kps) {
     const int ci = key_cs_index(kps);
-    softmax_max(t, cur);
+    softmax_max(tl(t), cur);
     region_a((t + 1) & 1, cur, nxt, pb);
     // K''(t+2) into buffer t&1 (it held K''(t)); V(t+1) into buffer (t+1)&1
     region_b(t & 1, t & 1, (t + 1) & 1, pb, ci);
-    load_k(t + 3);
-    load_pos(t + 4, kps);
-    load_v(t + 2);
+    load_k(tl(t + 3));
+    load_pos(tl(t + 4), kps);
+    load_v(tl(t + 2));
     __syncthreads();
   };
   int t = 0;
-  for (; t + 1 < nkt; t += 2) {
+  for (; t + 1 < nsteps; t += 2) {
     step(t, sa, sb, kpos0);
     step(t + 1, sb, sa, kpos1);
   }
-  if (t < nkt) step(t, sa, sb, kpos0);
+  if (t < nsteps) step(t, sa, sb, kpos0);
 
   // ---- epilogue: O * dv / l -> bf16
   const float inv = o_scale / pair_sum(l_run);
@@ -479,21 +511,21 @@ static Fp8Scales fp8_scales(const LaunchArgs& a) {
   return {(float)std::ldexp(G, -n), 127 + na, 127 + nb};
 }
 
-template <int D>
+template <int D, bool SPARSE>
 static hipError_t launch_fp8(const LaunchArgs& a) {
   const int nqt = (a.S + 255) / 256;
   const long long n = (long long)a.B * a.H * nqt;
   const Fp8Scales s = fp8_scales(a);
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D>), dim3((unsigned)n), dim3(512), 0, a.stream,
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, SPARSE>), dim3((unsigned)n), dim3(512), 0, a.stream,
                      (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, a.pos,
                      (uint16_t*)a.out, a.S, a.H, nqt, a.freqs, s.q_mul, s.sc_a, s.sc_b,
-                     a.descale[2]);
+                     a.descale[2], a.bmask);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd_fp8(const LaunchArgs& a) {
-  if (a.D == 128) return launch_fp8<128>(a);
-  return launch_fp8<64>(a);
+  if (a.bmask) return a.D == 128 ? launch_fp8<128, true>(a) : launch_fp8<64, true>(a);
+  return a.D == 128 ? launch_fp8<128, false>(a) : launch_fp8<64, false>(a);
 }
 
 long long attn_fwd_fp8_grid(int B, int S, int H) {

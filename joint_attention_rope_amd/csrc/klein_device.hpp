@@ -95,6 +95,32 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return xcd * per + (xcd < extra ? xcd : extra) + slot;
 }
 
+// Block-sparse attention: the kept key tiles of one query tile, listed in
+// ascending order by one wave (ballot + mbcnt compaction, so the order and
+// the result are deterministic).  kSparsePad sentinel entries (tile index
+// nkt, whose rows lie past S and read as zeros) follow the list, so a
+// pipeline that prefetches a few tiles ahead needs no bounds checks.
+constexpr int kSparseMaxTiles = 4096;
+constexpr int kSparsePad = 8;
+
+__device__ __forceinline__ int build_kept_list(const uint8_t* mrow, int nkt, uint16_t* list,
+                                               int lane) {
+  int n = 0;
+  for (int c = 0; c < nkt; c += 64) {
+    const int kt = c + lane;
+    const bool keep = kt < nkt && mrow[kt] != 0;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+    if (keep) {
+      const int r = (int)__builtin_amdgcn_mbcnt_hi(
+          (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      list[n + r] = (uint16_t)kt;
+    }
+    n += __builtin_popcountll(bal);
+  }
+  if (lane < kSparsePad) list[n + lane] = (uint16_t)nkt;
+  return n;
+}
+
 // Reduce a per-lane value with the lane 32 apart (lanes l and l^32 hold the
 // two halves of one query's keys in the 32x32 MFMA accumulator layout).
 __device__ __forceinline__ float pair_max(float x) {

@@ -19,6 +19,9 @@ struct LaunchArgs {
   float descale[3];    // fp8 per-tensor descales of q, k, v (1 for bf16)
   RopeFreqs freqs;
   hipStream_t stream;
+  // block-sparse mask [B][H][ceil(S/256)][ceil(S/64)] (nonzero = compute), or
+  // null for dense attention
+  const uint8_t* bmask = nullptr;
 };
 
 hipError_t launch_attn_fwd_bf16(const LaunchArgs& a);

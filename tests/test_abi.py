@@ -21,8 +21,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "klein_rope4d_attn_fwd", "klein_rope4d_attn_fwd_fp8", "klein_rope4d_apply",
-        "klein_status_string", "klein_version"])
+        "klein_rope4d_attn_fwd", "klein_rope4d_attn_fwd_fp8", "klein_rope4d_attn_fwd_blocksparse",
+        "klein_rope4d_apply", "klein_status_string", "klein_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -73,3 +73,18 @@ def test_rope_apply_checks():
     assert lib.klein_rope4d_apply(0, FAKE, FAKE, 1, 8, 1, 128, None) == _capi.KLEIN_ERR_INVALID_ARG
     assert lib.klein_rope4d_apply(FAKE, FAKE, FAKE, 1, 8, 1, 32, None) == _capi.KLEIN_ERR_UNSUPPORTED
     assert lib.klein_rope4d_apply(FAKE, FAKE, FAKE + 4, 1, 8, 1, 64, None) == _capi.KLEIN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 128, 0, 1.0, 1.0, 1.0, 0), _capi.KLEIN_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 128, 5, 1.0, 1.0, 1.0, FAKE), _capi.KLEIN_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 128, 1, 0.0, 1.0, 1.0, FAKE), _capi.KLEIN_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 96, 0, 1.0, 1.0, 1.0, FAKE), _capi.KLEIN_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64 * 4096 + 1, 1, 64, 0, 1.0, 1.0, 1.0, FAKE),
+     _capi.KLEIN_ERR_UNSUPPORTED),
+    ((0, FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 128, 0, 1.0, 1.0, 1.0, FAKE), _capi.KLEIN_ERR_INVALID_ARG),
+])
+def test_blocksparse_argument_checks(args, status):
+    """Null mask, bad dtype, bad fp8 descale, unsupported D, too many key
+    blocks (> 4096) and null tensors are rejected before any HIP call."""
+    assert _capi.lib().klein_rope4d_attn_fwd_blocksparse(*args, None) == status
