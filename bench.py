@@ -128,6 +128,7 @@ def main():
               "see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
     import joint_attention_rope_amd as kl
     from workloads import get_config, make_inputs
@@ -202,6 +203,36 @@ def main():
                 "ms_per_call": round(xms, 4), "tflops": round(xt, 2), "peak": peak,
                 "frac": round(xt / peak, 4)})
             del xq, xk, xv, xo
+        # block-sparse: the bench workloads with a seeded structured mask
+        # (text blocks, a band around each query block, 30 % of the rest)
+        from workloads import make_block_mask
+        for cid, peak in ((4, PEAK_BF16), (5, PEAK_FP8)):
+            c = get_config(cid)
+            print(f"[extra] block-sparse {c.dtype} S={c.S}", file=sys.stderr, flush=True)
+            xi = inp if cid == 4 else make_inputs(c)
+            xq, xk, xv, xp = to_device(xi, dev)
+            xo = torch.empty(xq.shape, dtype=torch.bfloat16, device=dev)
+            mask = make_block_mask(c.B, c.H, c.S, c.text, 0.3, seed=cid)
+            xm = torch.from_numpy(mask).to(dev)
+            desc = xi.descale or (1.0, 1.0, 1.0)
+            sms = time_gpu(lambda: kl.klein_rope4d_attn_fwd_blocksparse(
+                xq, xk, xv, xp, xo, xm, descales=desc), 5, 2, torch)
+            if xi.descale is None:
+                dense = lambda: kl.klein_rope4d_attn_fwd(xq, xk, xv, xp, xo)
+            else:
+                dense = lambda: kl.klein_rope4d_attn_fwd_fp8(xq, xk, xv, xp, xo, *xi.descale)
+            dms = time_gpu(dense, 5, 2, torch)
+            qn = np.minimum(256, c.S - 256 * np.arange(mask.shape[2]))
+            kn = np.minimum(64, c.S - 64 * np.arange(mask.shape[3]))
+            pairs = float(np.einsum("bhij,i,j->", mask.astype(np.float64), qn, kn))
+            eff = 4.0 * c.D * pairs / (sms * 1e-3) / 1e12
+            rec["extra"].append({
+                "workload": f"block-sparse {c.name}: B={c.B}, S={c.S}, H={c.H}, D={c.D}, "
+                            f"{c.dtype}; mask keeps {100 * mask.mean():.1f} % of 256x64 blocks",
+                "ms_per_call": round(sms, 4), "dense_ms_per_call": round(dms, 4),
+                "speedup_vs_dense": round(dms / sms, 3),
+                "effective_tflops": round(eff, 2), "peak": peak, "frac": round(eff / peak, 4)})
+            del xq, xk, xv, xo, xm
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)

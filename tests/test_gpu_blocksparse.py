@@ -12,7 +12,7 @@ import torch
 import joint_attention_rope_amd as kl
 from helpers import (assert_bf16_close, assert_fp8_close, bf16_tensor_to_f64, random_fp8_inputs,
                      random_inputs, run_attention, sample_rows, to_device)
-from workloads import get_config, make_inputs
+from workloads import get_config, make_block_mask, make_inputs
 
 pytestmark = pytest.mark.gpu
 QB, KB = kl.KLEIN_SPARSE_QBLOCK, kl.KLEIN_SPARSE_KBLOCK
@@ -95,23 +95,10 @@ def test_single_tile_lists_and_deterministic():
     assert_bf16_close(bf16_tensor_to_f64(a), oracle_sparse(inp, mask), "one tile per block")
 
 
-def structured_mask(B, H, S, text, keep_frac, seed):
-    """Every query block keeps the text key blocks, its own neighbourhood of
-    key blocks, and a seeded random share of the rest."""
-    shape = kl.blocksparse_mask_shape(B, S, H)
-    rng = np.random.default_rng(seed)
-    mask = (rng.random(shape) < keep_frac).astype(np.uint8)
-    mask[..., : -(-text // KB)] = 1
-    for i in range(shape[2]):
-        c = (i * QB) // KB
-        mask[:, :, i, max(0, c - 4):c + 8] = 1
-    return mask
-
-
 def test_workload_4_structured_mask_sampled_rows():
     cfg = get_config(4)
     inp = make_inputs(cfg)
-    mask = structured_mask(cfg.B, cfg.H, cfg.S, cfg.text, 0.3, seed=66)
+    mask = make_block_mask(cfg.B, cfg.H, cfg.S, cfg.text, 0.3, seed=66)
     out = run_sparse(inp, mask)
     rows = sample_rows(cfg.S, cfg.text, n=32, seed=66)
     gpu = bf16_tensor_to_f64(out[:, torch.from_numpy(rows).to(out.device)])

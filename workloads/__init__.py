@@ -16,6 +16,7 @@ image on the same (h, w) grid, told apart from the output by the t axis.
 
 from .configs import CONFIGS, Config, get_config
 from .generate import (
+    make_block_mask,
     Inputs,
     bf16_bits_from_f32,
     e4m3_encode,
@@ -24,6 +25,7 @@ from .generate import (
 )
 
 __all__ = [
+    "make_block_mask",
     "CONFIGS",
     "Config",
     "Inputs",

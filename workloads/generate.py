@@ -156,3 +156,24 @@ def make_inputs(cfg: Config, B: Optional[int] = None) -> Inputs:
         scales.append(np.float32(scale))
     return Inputs(cfg, codes[0], codes[1], codes[2], pos,
                   descale=tuple(float(s) for s in scales))
+
+
+def make_block_mask(B: int, H: int, S: int, text: int, keep_frac: float, seed: int,
+                    qblock: int = 256, kblock: int = 64, band: tuple = (4, 8)) -> np.ndarray:
+    """Seeded synthetic block mask for the block-sparse entry point, uint8
+    [B, H, ceil(S/qblock), ceil(S/kblock)] (1 = compute the block).
+
+    The pages give no rule for which query/key combinations a sparsified
+    attention keeps, so this stands in for one with a plausible structure:
+    every query block keeps all key blocks holding text tokens, a band of key
+    blocks around its own position in the token order (band[0] before,
+    band[1] after), and a seeded random share ``keep_frac`` of the rest.
+    """
+    nq, nk = -(-S // qblock), -(-S // kblock)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    mask = (rng.random((B, H, nq, nk)) < keep_frac).astype(np.uint8)
+    mask[..., : -(-text // kblock)] = 1
+    for i in range(nq):
+        c = (i * qblock) // kblock
+        mask[:, :, i, max(0, c - band[0]):c + band[1]] = 1
+    return mask
