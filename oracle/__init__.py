@@ -36,6 +36,9 @@ Modules:
   brute      -- pure-Python scalar loops for tiny shapes (the brute-force pin)
   fp8        -- OCP E4M3FN decoding (pinned: all 256 codes against the
                 format's definition and torch.float8_e4m3fn)
+  qkv_proj   -- the QKV projection feeding the attention, with RoPE-4D on its
+                q and k outputs (pinned: brute force, torch's linear at p = 0,
+                composition with the attention)
   blocksparse -- the same attention restricted to kept (query block, key
                 block) pairs, the reading of the pages' sparsified attention
                 (pinned: brute force, every block kept = dense, one kept block
@@ -56,6 +59,7 @@ from .blocksparse import (
     attention_blocksparse_rows,
 )
 from .fp8 import e4m3_decode
+from .qkv_proj import qkv_rope4d_proj
 from .rope4d import rope4d, rope_frequencies
 
 __all__ = [
@@ -68,6 +72,7 @@ __all__ = [
     "bf16_to_f64",
     "decode_inputs",
     "e4m3_decode",
+    "qkv_rope4d_proj",
     "rel_l2",
     "rope4d",
     "rope_frequencies",

@@ -66,3 +66,23 @@ def attention_blocksparse_scalar(q, k, v, pos, mask, qblock, kblock, theta=10000
                 for d in range(D):
                     out[b][i][h][d] = sum(e[j] * v[b][j][h][d] for j in kept) / z
     return out
+
+
+def qkv_proj_scalar(x, w, bias, pos, H, D, theta=10000.0):
+    """QKV projection then RoPE-4D on q and k, one scalar at a time.
+    x: [B][S][C]; w: [3HD][C]; bias: [3HD] or None.  Returns q', k', v as
+    nested lists [B][S][H][D]."""
+    B, S, C = len(x), len(x[0]), len(x[0][0])
+    outs = ([], [], [])
+    for b in range(B):
+        qb, kb, vb = [], [], []
+        for s in range(S):
+            y = [sum(x[b][s][c] * w[n][c] for c in range(C)) + (bias[n] if bias else 0.0)
+                 for n in range(3 * H * D)]
+            heads = [[y[t * H * D + h * D:t * H * D + (h + 1) * D] for h in range(H)]
+                     for t in range(3)]
+            qb.append([rope_scalar(heads[0][h], pos[s], theta) for h in range(H)])
+            kb.append([rope_scalar(heads[1][h], pos[s], theta) for h in range(H)])
+            vb.append([list(heads[2][h]) for h in range(H)])
+        outs[0].append(qb); outs[1].append(kb); outs[2].append(vb)
+    return outs
