@@ -130,6 +130,40 @@ klein_status_t klein_rope4d_attn_fwd_blocksparse(const void* q, const void* k, c
                                                  klein_stream_t stream);
 
 /*
+ * QKV projection with the RoPE-4D rotation fused into its epilogue -- the
+ * step that feeds the attention in each joint block ("Flux.3 Image Klein
+ * arrives in Diffusers with a modular architecture", section "How it works";
+ * the fused QKV GEMMs of "How FLUX 3 Image Klein was made 3-4x faster on
+ * NVIDIA Blackwell", section "Method 2"):
+ *   y = x W^T (+ bias);  q = y[:, 0:HD], k = y[:, HD:2HD], v = y[:, 2HD:3HD]
+ *   q_out = R(pos) q, k_out = R(pos) k  (fp16),  v_out = v  (bfloat16)
+ *   x       : [B][S][C] bfloat16 (C % 64 == 0, C <= 65536, else UNSUPPORTED)
+ *   w       : [3*H*D][C] bfloat16 (a linear layer's [out, in] layout)
+ *   bias    : [3*H*D] bfloat16, 8-byte aligned, or NULL
+ *   pos_thwl: [S][4] int32, shared by all batch entries
+ *   q_out, k_out: [B][S][H][D] fp16 (IEEE binary16), rotated; v_out: [B][S][H][D]
+ *   bfloat16.  Accumulation is fp32; the outputs are rounded once.  The fp16
+ *   q/k outputs hold |value| < 65504; klein_attn_fwd_prerotated takes them.
+ * Device pointers, 16-byte aligned (bias 8), caller-owned; nothing allocated.
+ */
+klein_status_t klein_qkv_rope4d_proj(const void* x, const void* w, const void* bias,
+                                     const int32_t* pos_thwl, void* q_out, void* k_out,
+                                     void* v_out, int B, int S, int C, int H, int D,
+                                     klein_stream_t stream);
+
+/*
+ * Joint attention of queries and keys that are already rotated (as
+ * klein_qkv_rope4d_proj emits them): out_i = sum_j softmax_j(<q_i, k_j> /
+ * sqrt(D)) v_j over all j, no mask -- the definition above with the rotation
+ * done upstream, so no positions are needed and the kernel's K tiles are
+ * plain copies.
+ *   q, k: [B][S][H][D] fp16 (|k| < ~46000, |q| < ~360000 as for the bf16 path)
+ *   v, out: [B][S][H][D] bfloat16.  D in {64, 128}.
+ */
+klein_status_t klein_attn_fwd_prerotated(const void* q, const void* k, const void* v, void* out,
+                                        int B, int S, int H, int D, klein_stream_t stream);
+
+/*
  * Test hook: y = R(pos) x for bfloat16 x, y [B][S][H][D] (same layout rules),
  * computed with the very device routine the attention kernels use for Q and
  * K, rounded to bfloat16.  x and y may be the same buffer.

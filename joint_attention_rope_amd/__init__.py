@@ -20,6 +20,7 @@ __all__ = [
     "klein_rope4d_attn_fwd_blocksparse", "klein_rope4d_apply", "klein_status_string",
     "klein_version", "library_path", "KLEIN_DTYPE_BF16", "KLEIN_DTYPE_FP8_E4M3",
     "KLEIN_SPARSE_QBLOCK", "KLEIN_SPARSE_KBLOCK", "blocksparse_mask_shape",
+    "klein_qkv_rope4d_proj", "klein_attn_fwd_prerotated",
 ]
 
 
@@ -155,6 +156,52 @@ def klein_rope4d_attn_fwd_blocksparse(q, k, v, pos_thwl, out, block_mask, dtype=
         q.data_ptr(), k.data_ptr(), v.data_ptr(), pos_thwl.data_ptr(), out.data_ptr(),
         B, S, H, D, int(dtype), dq, dk, dv, block_mask.data_ptr(), _stream(stream, q.device))
     _check(st, "klein_rope4d_attn_fwd_blocksparse")
+    return out
+
+
+def klein_qkv_rope4d_proj(x, w, bias, pos_thwl, q_out, k_out, v_out, stream=None):
+    """q_out, k_out (fp16, rotated), v_out (bf16) [B, S, H, D] <- x W^T + bias.
+
+    x: bf16 [B, S, C]; w: bf16 [3 H D, C]; bias: bf16 [3 H D] or None.
+    """
+    if x.dim() != 3 or x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bfloat16 GPU tensor [B, S, C]")
+    B, S, C = x.shape
+    Bq, Sq, H, D = _bshd(q_out, "q_out")
+    if (Bq, Sq) != (B, S) or _bshd(k_out, "k_out") != (B, S, H, D) \
+            or _bshd(v_out, "v_out") != (B, S, H, D):
+        raise ValueError("q_out, k_out, v_out must be [B, S, H, D] for x's B, S")
+    if q_out.dtype != torch.float16 or k_out.dtype != torch.float16 or v_out.dtype != torch.bfloat16:
+        raise ValueError("q_out and k_out must be float16, v_out bfloat16")
+    if w.dtype != torch.bfloat16 or tuple(w.shape) != (3 * H * D, C) or not w.is_cuda \
+            or not w.is_contiguous():
+        raise ValueError(f"w must be a contiguous bfloat16 GPU tensor [{3 * H * D}, {C}]")
+    if bias is not None and (bias.dtype != torch.bfloat16 or tuple(bias.shape) != (3 * H * D,)
+                             or not bias.is_cuda or not bias.is_contiguous()):
+        raise ValueError(f"bias must be None or a bfloat16 GPU tensor [{3 * H * D}]")
+    _pos(pos_thwl, S)
+    st = _capi.lib().klein_qkv_rope4d_proj(
+        x.data_ptr(), w.data_ptr(), 0 if bias is None else bias.data_ptr(), pos_thwl.data_ptr(),
+        q_out.data_ptr(), k_out.data_ptr(), v_out.data_ptr(), B, S, C, H, D,
+        _stream(stream, x.device))
+    _check(st, "klein_qkv_rope4d_proj")
+    return q_out, k_out, v_out
+
+
+def klein_attn_fwd_prerotated(q, k, v, out, stream=None):
+    """out <- joint attention of already rotated fp16 q, k and bf16 v [B, S, H, D]."""
+    B, S, H, D = _bshd(q, "q")
+    for t, n in ((k, "k"), (v, "v"), (out, "out")):
+        if _bshd(t, n) != (B, S, H, D):
+            raise ValueError(f"{n} must have q's shape {(B, S, H, D)}")
+    if q.dtype != torch.float16 or k.dtype != torch.float16:
+        raise ValueError("q and k must be float16 (rotated)")
+    if v.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise ValueError("v and out must be bfloat16")
+    st = _capi.lib().klein_attn_fwd_prerotated(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                               out.data_ptr(), B, S, H, D,
+                                               _stream(stream, q.device))
+    _check(st, "klein_attn_fwd_prerotated")
     return out
 
 

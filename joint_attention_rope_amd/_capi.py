@@ -31,6 +31,9 @@ SIGNATURES = {
                                          _f32, _f32, _f32, _vp]),
     "klein_rope4d_attn_fwd_blocksparse": (_int, [_vp, _vp, _vp, _i32p, _vp, _int, _int, _int,
                                                  _int, _int, _f32, _f32, _f32, _vp, _vp]),
+    "klein_qkv_rope4d_proj": (_int, [_vp, _vp, _vp, _i32p, _vp, _vp, _vp, _int, _int, _int,
+                                     _int, _int, _vp]),
+    "klein_attn_fwd_prerotated": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp]),
     "klein_rope4d_apply": (_int, [_vp, _i32p, _vp, _int, _int, _int, _int, _vp]),
     "klein_status_string": (ctypes.c_char_p, [_int]),
     "klein_version": (_int, []),

@@ -131,6 +131,50 @@ klein_status_t klein_rope4d_attn_fwd_blocksparse(const void* q, const void* k, c
   }
 }
 
+klein_status_t klein_attn_fwd_prerotated(const void* q, const void* k, const void* v, void* out,
+                                        int B, int S, int H, int D, klein_stream_t stream) {
+  if (!q || !k || !v || !out) return KLEIN_ERR_INVALID_ARG;
+  if (B < 1 || S < 1 || H < 1) return KLEIN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return KLEIN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return KLEIN_ERR_INVALID_ARG;
+  if (klein::attn_fwd_bf16_grid(B, S, H) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
+  try {
+    return map_hip(klein::launch_attn_fwd_prerotated(
+        make_args(q, k, v, nullptr, out, B, S, H, D, stream)));
+  } catch (...) {
+    return KLEIN_ERR_LAUNCH;
+  }
+}
+
+klein_status_t klein_qkv_rope4d_proj(const void* x, const void* w, const void* bias,
+                                     const int32_t* pos_thwl, void* q_out, void* k_out,
+                                     void* v_out, int B, int S, int C, int H, int D,
+                                     klein_stream_t stream) {
+  if (!x || !w || !pos_thwl || !q_out || !k_out || !v_out) return KLEIN_ERR_INVALID_ARG;
+  if (B < 1 || S < 1 || C < 1 || H < 1) return KLEIN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return KLEIN_ERR_UNSUPPORTED;
+  if (C % 64 != 0 || C > 65536) return KLEIN_ERR_UNSUPPORTED;
+  for (const void* p : {x, w, (const void*)q_out, (const void*)k_out, (const void*)v_out,
+                        (const void*)pos_thwl})
+    if (!aligned16(p)) return KLEIN_ERR_INVALID_ARG;
+  if (bias && (reinterpret_cast<uintptr_t>(bias) & 7u)) return KLEIN_ERR_INVALID_ARG;
+  if (klein::qkv_rope_proj_grid(B, S, H, D) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
+  if ((long long)B * S * H * D * 3 >= (1LL << 40)) return KLEIN_ERR_UNSUPPORTED;
+  try {
+    klein::QkvArgs a{};
+    a.x = (const uint16_t*)x; a.w = (const uint16_t*)w; a.bias = (const uint16_t*)bias;
+    a.pos = pos_thwl;
+    a.q = (uint16_t*)q_out; a.k = (uint16_t*)k_out; a.v = (uint16_t*)v_out;
+    a.B = B; a.S = S; a.C = C; a.H = H; a.D = D;
+    a.freqs = make_freqs(D);
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    return map_hip(klein::launch_qkv_rope_proj(a));
+  } catch (...) {
+    return KLEIN_ERR_LAUNCH;
+  }
+}
+
 klein_status_t klein_rope4d_apply(const void* x, const int32_t* pos_thwl, void* y, int B, int S,
                                   int H, int D, klein_stream_t stream) {
   if (!x || !pos_thwl || !y) return KLEIN_ERR_INVALID_ARG;

@@ -72,7 +72,10 @@ __device__ __forceinline__ int key_to_row(int kk) {
 // tile of 256, key tile of 64), nonzero = compute, and only the kept key
 // tiles of a query tile stream through the pipeline (in ascending order, so
 // with every tile kept the result is bit-identical to the dense kernel).
-template <int D, bool SPARSE>
+// PREROT: q and k arrive rotated, as fp16 (the projection's RoPE epilogue
+// emits them so); Q is only scaled and K tiles are copied to LDS as they
+// are, with no table, positions or rotation.
+template <int D, bool SPARSE, bool PREROT>
 __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ pos,
@@ -118,10 +121,12 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   const uint16_t* vb = v + base;
 
   // ---- cos/sin table (the very values rope_chunk computes)
-  for (int e = tid; e < kTabN * NJ; e += NT) {
-    const int j = e % NJ, p = e / NJ;
-    const float rev = __builtin_amdgcn_fractf((float)p * fr.hi[j]) + (float)p * fr.lo[j];
-    cs_tab[p * TROW + j] = make_float2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+  if constexpr (!PREROT) {
+    for (int e = tid; e < kTabN * NJ; e += NT) {
+      const int j = e % NJ, p = e / NJ;
+      const float rev = __builtin_amdgcn_fractf((float)p * fr.hi[j]) + (float)p * fr.lo[j];
+      cs_tab[p * TROW + j] = make_float2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+    }
   }
 
   // ---- this lane's query: rotate, scale by log2(e)/sqrt(D), fp16 in VGPRs.
@@ -134,8 +139,14 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     const int d0 = 16 * ks + 8 * g;
     const int a = d0 / DA, j0 = (d0 % DA) / 2;
     const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qb + (size_t)qload * rs + d0);
-    qreg[ks] = __builtin_bit_cast(
-        f16x8_t, rope_chunk<true>(x, pos[4 * qload + a], &fr.hi[j0], &fr.lo[j0], qscale));
+    if constexpr (PREROT) {
+      typedef float f32x8v_t __attribute__((ext_vector_type(8)));
+      const f32x8v_t xf = __builtin_convertvector(__builtin_bit_cast(f16x8_t, x), f32x8v_t);
+      qreg[ks] = __builtin_convertvector(xf * qscale, f16x8_t);
+    } else {
+      qreg[ks] = __builtin_bit_cast(
+          f16x8_t, rope_chunk<true>(x, pos[4 * qload + a], &fr.hi[j0], &fr.lo[j0], qscale));
+    }
   }
 
   // ---- staging assignment: chunk lc of keys lk .. lk+KPT-1 of a K or V tile
@@ -173,6 +184,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
       kx[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, voff, it * rowb, 0));
   };
   auto load_pos = [&](int kt, int* slot) {
+    if constexpr (PREROT) return;
     const __amdgpu_buffer_rsrc_t rp = uniform_rsrc(pos + (size_t)kt * BN * 4, tile_rows(kt) * 16);
 #pragma unroll
     for (int it = 0; it < KPT; ++it)
@@ -183,6 +195,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   // own slots, filled here in a divergent branch that waves whose positions
   // all lie in the table skip.
   auto key_cs_index = [&](const int* kp, int it) {
+    if constexpr (PREROT) return 0;
     const bool oob = (unsigned)kp[it] >= (unsigned)kTabN;
     if (oob) {
 #pragma unroll
@@ -211,12 +224,16 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   auto stage_k = [&](int buf, const int* kp) {
 #pragma unroll
     for (int it = 0; it < KPT; ++it) {
-      const int ci = key_cs_index(kp, it);
       const int key = lk + it;
       const int row = (key & ~31) + key_to_row(key & 31);
       u32x4_t y;
+      if constexpr (PREROT) {
+        y = kx[it];
+      } else {
+        const int ci = key_cs_index(kp, it);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) y[jj] = rot_pair(kx[it][jj], cs_tab[ci + jj]);
+        for (int jj = 0; jj < 4; ++jj) y[jj] = rot_pair(kx[it][jj], cs_tab[ci + jj]);
+      }
       *reinterpret_cast<u32x4_t*>(&k_lds[buf][row * KROW + 8 * lc]) = y;
     }
   };
@@ -343,13 +360,14 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   // (RoPE-4D, one pair per slice) and V(t+1) spread over the MFMAs; then the
   // loads of K(t+3), V(t+2).
   constexpr int NB = 4 * MB;                 // MFMAs in region B
-  constexpr int NROT = 4 * KPT;              // RoPE pairs to stage
+  constexpr int NROT = PREROT ? KPT : 4 * KPT;   // RoPE pairs (or K chunks) to stage
   constexpr int NVW = KPT;                   // V chunks to stage
   constexpr int NIT = NROT + NVW;
   auto region_b = [&](int vbuf, int kdst, int vdst, const uint32_t (*pw)[8], const int* ci) {
     float2 kcs[NROT];
     auto read_cs = [&](int item) {
-      if (item < NROT) kcs[item] = cs_tab[ci[item / 4] + item % 4];
+      if constexpr (!PREROT)
+        if (item < NROT) kcs[item] = cs_tab[ci[item / 4] + item % 4];
     };
     read_cs(0);
     read_cs(1);
@@ -380,7 +398,12 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
 #pragma unroll
       for (int item = i * NIT / NB; item < (i + 1) * NIT / NB; ++item) {
         read_cs(item + 2);
-        if (item < NROT) {
+        if (PREROT && item < NROT) {
+          // one pre-rotated K chunk, copied
+          const int key = lk + item;
+          const int row = (key & ~31) + key_to_row(key & 31);
+          *reinterpret_cast<u32x4_t*>(&k_lds[kdst][row * KROW + 8 * lc]) = kx[item];
+        } else if (item < NROT) {
           // one RoPE pair of K chunk c
           const int c = item / 4, jj = item % 4;
           ky[jj] = rot_pair(kx[c][jj], kcs[item]);
@@ -495,12 +518,12 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   }
 }
 
-template <int D, bool SPARSE>
+template <int D, bool SPARSE, bool PREROT = false>
 static hipError_t launch_bf16(const LaunchArgs& a) {
   constexpr int BM = 256;
   const int nqt = (a.S + BM - 1) / BM;
   const long long n = (long long)a.B * a.H * nqt;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, SPARSE>), dim3((unsigned)n), dim3(512), 0,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, SPARSE, PREROT>), dim3((unsigned)n), dim3(512), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      a.pos, (uint16_t*)a.out, a.S, a.H, nqt, a.freqs, a.qscale_log2, a.bmask);
   return hipGetLastError();
@@ -509,6 +532,10 @@ static hipError_t launch_bf16(const LaunchArgs& a) {
 hipError_t launch_attn_fwd_bf16(const LaunchArgs& a) {
   if (a.bmask) return a.D == 128 ? launch_bf16<128, true>(a) : launch_bf16<64, true>(a);
   return a.D == 128 ? launch_bf16<128, false>(a) : launch_bf16<64, false>(a);
+}
+
+hipError_t launch_attn_fwd_prerotated(const LaunchArgs& a) {
+  return a.D == 128 ? launch_bf16<128, false, true>(a) : launch_bf16<64, false, true>(a);
 }
 
 long long attn_fwd_bf16_grid(int B, int S, int H) {

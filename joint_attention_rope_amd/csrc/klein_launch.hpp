@@ -25,9 +25,27 @@ struct LaunchArgs {
 };
 
 hipError_t launch_attn_fwd_bf16(const LaunchArgs& a);
+hipError_t launch_attn_fwd_prerotated(const LaunchArgs& a);
 long long attn_fwd_bf16_grid(int B, int S, int H);
 hipError_t launch_attn_fwd_fp8(const LaunchArgs& a);
 long long attn_fwd_fp8_grid(int B, int S, int H);
 hipError_t launch_rope4d_apply(const LaunchArgs& a);
+
+// QKV projection with the RoPE-4D epilogue: x [B S][C] bf16, w [3 H D][C]
+// bf16, bias [3 H D] bf16 or null -> q', k' fp16 and v bf16, [B][S][H][D].
+struct QkvArgs {
+  const uint16_t* x;
+  const uint16_t* w;
+  const uint16_t* bias;
+  const int32_t* pos;
+  uint16_t* q;
+  uint16_t* k;
+  uint16_t* v;
+  int B, S, C, H, D;
+  RopeFreqs freqs;
+  hipStream_t stream;
+};
+hipError_t launch_qkv_rope_proj(const QkvArgs& a);
+long long qkv_rope_proj_grid(int B, int S, int H, int D);
 
 }  // namespace klein

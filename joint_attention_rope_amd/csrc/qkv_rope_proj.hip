@@ -1,0 +1,176 @@
+// QKV projection with the RoPE-4D rotation in its epilogue, for gfx950.
+//
+//   y = x W^T (+ bias)          x [M = B S][C] bf16, W [N = 3 H D][C] bf16
+//   q' = R(y[:, 0:HD]) -> fp16, k' = R(y[:, HD:2HD]) -> fp16, v = y[:, 2HD:] -> bf16
+//
+// computed as C^T = W x^T so that output features run down the MFMA rows:
+// accumulator registers 4c .. 4c+3 of a lane then hold four consecutive
+// channels d of one token (its MFMA column), and the interleaved RoPE pairs
+// (d, d+1) are register pairs of one lane.  The rotation, the bias and the
+// conversions happen in registers before the only store; the angle of each
+// pair is formed once per output element, like the attention kernels' Q.
+//
+// One workgroup of 8 waves computes 256 features x 256 tokens, K in steps of
+// 64; each wave owns 128 features x 64 tokens (4 x 2 tiles of
+// v_mfma_f32_32x32x16_bf16, 0.75 LDS operand reads per MFMA).  W and x tiles
+// are double-buffered in LDS (rows padded to 144 bytes, so the 16 rows one
+// 16-lane read phase touches fall on distinct banks) and staged through
+// registers one K step ahead; one barrier per K step.  Rows past N or M read
+// as zeros through the buffer descriptors and are not stored.
+#include "klein_device.hpp"
+#include "klein_launch.hpp"
+
+namespace klein {
+
+template <int D>
+__global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    const uint16_t* __restrict__ bias, const int32_t* __restrict__ pos,
+    uint16_t* __restrict__ qo, uint16_t* __restrict__ ko, uint16_t* __restrict__ vo,
+    int M, int N, int C, int S, int H, int ntile_n, RopeFreqs fr) {
+  constexpr int TN = 256, TM = 256, TK = 64;
+  constexpr int ROW = TK + 8;                  // LDS row stride (bf16 elements)
+  constexpr int DA = D / 4;
+  constexpr int CPR = TK / 8;                  // 16-byte chunks per tile row
+  constexpr int NLD = (TN + TM) * CPR / 512;   // chunks per thread per K step
+  static_assert(NLD == 8, "staging split");
+
+  __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][TN * ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t b_lds[2][TM * ROW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, lr = lane & 31;
+  const int wn = wave & 1, wm = wave >> 1;     // 2 x 4 waves: 128 features x 64 tokens
+  const int tn = blockIdx.x % ntile_n, tmi = blockIdx.x / ntile_n;
+  const int n0 = tn * TN, m0 = tmi * TM;
+  const int HD = H * D;
+
+  // ---- staging: chunk c = tid + 512 i; the first TN*CPR chunks are W rows,
+  // the rest x rows
+  const int rowb = C * 2;
+  const int nrows_a = min(TN, N - n0), nrows_b = min(TM, M - m0);
+  const __amdgpu_buffer_rsrc_t ra = uniform_rsrc(w + (size_t)n0 * C, nrows_a * rowb);
+  const __amdgpu_buffer_rsrc_t rb = uniform_rsrc(x + (size_t)m0 * C, nrows_b * rowb);
+  u32x4_t stg[NLD];
+  auto load = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int c = tid + 512 * i;
+      const bool isa = c < TN * CPR;
+      const int cc = isa ? c : c - TN * CPR;
+      const int row = cc / CPR, ch = cc % CPR;
+      const int off = row * rowb + (kt * TK + 8 * ch) * 2;
+      stg[i] = __builtin_bit_cast(u32x4_t, isa ? __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0)
+                                               : __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int c = tid + 512 * i;
+      const bool isa = c < TN * CPR;
+      const int cc = isa ? c : c - TN * CPR;
+      const int row = cc / CPR, ch = cc % CPR;
+      uint16_t* dst = isa ? &a_lds[buf][row * ROW + 8 * ch] : &b_lds[buf][row * ROW + 8 * ch];
+      *reinterpret_cast<u32x4_t*>(dst) = stg[i];
+    }
+  };
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = (f32x16_t){};
+
+  const int nk = C / TK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < TK / 16; ++ks) {
+      bf16x8_t av[4], bv[2];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        av[nb] = *reinterpret_cast<const bf16x8_t*>(
+            &a_lds[buf][(128 * wn + 32 * nb + lr) * ROW + 16 * ks + 8 * g]);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        bv[mb] = *reinterpret_cast<const bf16x8_t*>(
+            &b_lds[buf][(64 * wm + 32 * mb + lr) * ROW + 16 * ks + 8 * g]);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[nb], bv[mb], acc[nb][mb], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane column = token m, registers 4c..4c+3 = features
+  // n0 + 128 wn + 32 nb + 8 c + 4 g + 0..3
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int m = m0 + 64 * wm + 32 * mb + lr;
+    if (m >= M) continue;
+    const int s = m % S;
+    const int32_t* pm = pos + 4 * s;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int n = n0 + 128 * wn + 32 * nb + 8 * c4 + 4 * g;    // multiple of 4
+        if (n >= N) continue;
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          y[e] = acc[nb][mb][4 * c4 + e] + (bias ? bf16_lo((uint32_t)bias[n + e]) : 0.f);
+        const int which = n / HD, hd = n % HD, d = hd % D;
+        uint2 outw;
+        if (which < 2) {
+          const int a = d / DA, j0 = (d % DA) / 2;
+          const float fp = (float)pm[a];
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const int j = j0 + pr;
+            const float rev = __builtin_amdgcn_fractf(fp * fr.hi[j]) + fp * fr.lo[j];
+            const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+            const float xa = y[2 * pr], xb = y[2 * pr + 1];
+            y[2 * pr] = xa * cs - xb * sn;
+            y[2 * pr + 1] = xa * sn + xb * cs;
+          }
+          outw.x = pack_f16x2(y[0], y[1]);
+          outw.y = pack_f16x2(y[2], y[3]);
+          uint16_t* dst = (which == 0 ? qo : ko) + (size_t)m * HD + hd;
+          *reinterpret_cast<uint2*>(dst) = outw;
+        } else {
+          outw.x = pack_bf16x2(y[0], y[1]);
+          outw.y = pack_bf16x2(y[2], y[3]);
+          *reinterpret_cast<uint2*>(vo + (size_t)m * HD + hd) = outw;
+        }
+      }
+  }
+}
+
+hipError_t launch_qkv_rope_proj(const QkvArgs& a) {
+  const int M = a.B * a.S, N = 3 * a.H * a.D;
+  const int ntn = (N + 255) / 256, ntm = (M + 255) / 256;
+  const dim3 grid((unsigned)(ntn * ntm));
+  if (a.D == 128)
+    hipLaunchKernelGGL(qkv_rope_proj_kernel<128>, grid, dim3(512), 0, a.stream, a.x, a.w, a.bias,
+                       a.pos, a.q, a.k, a.v, M, N, a.C, a.S, a.H, ntn, a.freqs);
+  else
+    hipLaunchKernelGGL(qkv_rope_proj_kernel<64>, grid, dim3(512), 0, a.stream, a.x, a.w, a.bias,
+                       a.pos, a.q, a.k, a.v, M, N, a.C, a.S, a.H, ntn, a.freqs);
+  return hipGetLastError();
+}
+
+long long qkv_rope_proj_grid(int B, int S, int H, int D) {
+  const long long M = (long long)B * S, N = 3LL * H * D;
+  return ((N + 255) / 256) * ((M + 255) / 256);
+}
+
+}  // namespace klein

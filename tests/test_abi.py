@@ -22,6 +22,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "klein_rope4d_attn_fwd", "klein_rope4d_attn_fwd_fp8", "klein_rope4d_attn_fwd_blocksparse",
+        "klein_qkv_rope4d_proj", "klein_attn_fwd_prerotated",
         "klein_rope4d_apply", "klein_status_string", "klein_version"])
 
 
@@ -88,3 +89,17 @@ def test_blocksparse_argument_checks(args, status):
     """Null mask, bad dtype, bad fp8 descale, unsupported D, too many key
     blocks (> 4096) and null tensors are rejected before any HIP call."""
     assert _capi.lib().klein_rope4d_attn_fwd_blocksparse(*args, None) == status
+
+
+def test_qkv_proj_and_prerotated_argument_checks():
+    lib = _capi.lib()
+    U, I = _capi.KLEIN_ERR_UNSUPPORTED, _capi.KLEIN_ERR_INVALID_ARG
+    # x, w, bias, pos, q, k, v, B, S, C, H, D
+    ok = (FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, 1, 8, 128, 2, 64)
+    bad = [((0,) + ok[1:], I), (ok[:4] + (0,) + ok[5:], I), (ok[:9] + (96,) + ok[10:], U),
+           (ok[:11] + (32,), U), (ok[:7] + (0,) + ok[8:], I), (ok[:2] + (FAKE + 4,) + ok[3:], I)]
+    for args, st in bad:
+        assert lib.klein_qkv_rope4d_proj(*args, None) == st, args
+    assert lib.klein_attn_fwd_prerotated(0, FAKE, FAKE, FAKE, 1, 8, 1, 64, None) == I
+    assert lib.klein_attn_fwd_prerotated(FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 80, None) == U
+    assert lib.klein_attn_fwd_prerotated(FAKE, FAKE, FAKE + 8, FAKE, 1, 8, 1, 64, None) == I

@@ -1,0 +1,97 @@
+"""GPU parity of the QKV projection with its RoPE-4D epilogue and of the
+attention on pre-rotated queries and keys, each against the oracle.
+
+Tolerances of the projection: its outputs are fp32 sums rounded once, to
+fp16 (q', k': relative rounding error <= 2^-11) or bf16 (v: <= 2^-8), so the
+relative L2 error over a tensor is bounded by those with margin: 1e-3 for
+q', k' and 5e-3 for v.  The attention keeps the bf16 bounds of the hot path.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import joint_attention_rope_amd as kl
+from helpers import BF16_MAX_ABS, BF16_REL_L2, bf16_tensor_to_f64, errors
+from workloads import bf16_bits_from_f32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def bf16_dev(a):
+    bits = bf16_bits_from_f32(np.asarray(a, dtype=np.float32))
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV), \
+        (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f16_to_f64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def proj_case(B, S, C, H, D, bias, seed):
+    rng = np.random.default_rng(seed)
+    x_t, x = bf16_dev(rng.standard_normal((B, S, C)))
+    w_t, w = bf16_dev(rng.standard_normal((3 * H * D, C)) / np.sqrt(C))
+    b_t, b = bf16_dev(rng.standard_normal(3 * H * D) * 0.1) if bias else (None, None)
+    pos = rng.integers(-50, 600, size=(S, 4)).astype(np.int32)
+    return (x_t, w_t, b_t, torch.from_numpy(pos).to(DEV)), (x, w, b, pos)
+
+
+def run_proj(dev_args, B, S, H, D):
+    q = torch.empty(B, S, H, D, dtype=torch.float16, device=DEV)
+    k = torch.empty_like(q)
+    v = torch.empty(B, S, H, D, dtype=torch.bfloat16, device=DEV)
+    kl.klein_qkv_rope4d_proj(*dev_args, q, k, v)
+    torch.cuda.synchronize()
+    return q, k, v
+
+
+@pytest.mark.parametrize("B,S,C,H,D,bias", [
+    (2, 300, 128, 2, 64, True),      # partial feature and token tiles
+    (1, 513, 256, 4, 128, False),
+    (1, 1000, 3072, 2, 128, True),   # the hidden size of the bench shape
+    (3, 77, 192, 3, 64, True),
+])
+def test_projection_matches_oracle(B, S, C, H, D, bias):
+    import oracle
+    dev_args, host = proj_case(B, S, C, H, D, bias, seed=S + C)
+    q, k, v = run_proj(dev_args, B, S, H, D)
+    rq, rk, rv = oracle.qkv_rope4d_proj(*host, H, D)
+    for got, ref, bound, name in ((f16_to_f64(q), rq, 1e-3, "q'"), (f16_to_f64(k), rk, 1e-3, "k'"),
+                                  (bf16_tensor_to_f64(v), rv, 5e-3, "v")):
+        _, rel = errors(got, ref)
+        assert np.isfinite(got).all() and rel <= bound, f"{name}: rel_l2 {rel:.3e} > {bound}"
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("S", [1, 65, 577])
+def test_prerotated_attention_matches_oracle(S, D):
+    import oracle
+    rng = np.random.default_rng(S * 3 + D)
+    shape = (2, S, 3, D)
+    q = torch.from_numpy(rng.standard_normal(shape).astype(np.float16)).to(DEV)
+    k = torch.from_numpy(rng.standard_normal(shape).astype(np.float16)).to(DEV)
+    v_t, v = bf16_dev(rng.standard_normal(shape))
+    out = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+    kl.klein_attn_fwd_prerotated(q, k, v_t, out)
+    torch.cuda.synchronize()
+    ref = oracle.attention(f16_to_f64(q), f16_to_f64(k), v, np.zeros((S, 4), dtype=np.int32))
+    max_abs, rel = errors(bf16_tensor_to_f64(out), ref)
+    assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2, (max_abs, rel)
+
+
+def test_pipeline_matches_fused_definition():
+    # projection -> pre-rotated attention, against the fused attention
+    # definition of the unrotated projection at the true positions
+    import oracle
+    B, S, C, H, D = 1, 700, 256, 2, 128
+    dev_args, (x, w, b, pos) = proj_case(B, S, C, H, D, True, seed=71)
+    q, k, v = run_proj(dev_args, B, S, H, D)
+    out = torch.empty(B, S, H, D, dtype=torch.bfloat16, device=DEV)
+    kl.klein_attn_fwd_prerotated(q, k, v, out)
+    torch.cuda.synchronize()
+    y = (x @ w.T + b).reshape(B, S, 3, H, D)
+    ref = oracle.attention(y[:, :, 0], y[:, :, 1], y[:, :, 2], pos)
+    max_abs, rel = errors(bf16_tensor_to_f64(out), ref)
+    assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2, (max_abs, rel)
