@@ -15,7 +15,8 @@
 // v_mfma_f32_32x32x16_bf16, 0.75 LDS operand reads per MFMA).  W and x tiles
 // are double-buffered in LDS (rows padded to 144 bytes, so the 16 rows one
 // 16-lane read phase touches fall on distinct banks) and staged through
-// registers one K step ahead; one barrier per K step.  Rows past N or M read
+// registers one K step ahead, the stores interleaved with the MFMAs; one
+// barrier per K step.  Rows past N or M read
 // as zeros through the buffer descriptors and are not stored.
 #include "klein_device.hpp"
 #include "klein_launch.hpp"
@@ -86,27 +87,49 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
   load(0);
   store(0);
   __syncthreads();
+  // K step kt: the loads of step kt+1 go out first (past the last step they
+  // read in-range rows or the descriptors' zeros, and are never used); the
+  // operands of sub-step ks+1 are read during the MFMAs of ks; the stores of
+  // step kt+1 into the other buffer ride along the last two sub-steps (that
+  // buffer was last read before the previous barrier).
+  bf16x8_t av[2][4], bv[2][2];
+  auto read_ops = [&](int buf, int ks, int slot) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      av[slot][nb] = *reinterpret_cast<const bf16x8_t*>(
+          &a_lds[buf][(128 * wn + 32 * nb + lr) * ROW + 16 * ks + 8 * g]);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+      bv[slot][mb] = *reinterpret_cast<const bf16x8_t*>(
+          &b_lds[buf][(64 * wm + 32 * mb + lr) * ROW + 16 * ks + 8 * g]);
+  };
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) load(kt + 1);
+    load(kt + 1);
+    read_ops(buf, 0, 0);
 #pragma unroll
     for (int ks = 0; ks < TK / 16; ++ks) {
-      bf16x8_t av[4], bv[2];
+      if (ks + 1 < TK / 16) read_ops(buf, ks + 1, (ks + 1) & 1);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        av[nb] = *reinterpret_cast<const bf16x8_t*>(
-            &a_lds[buf][(128 * wn + 32 * nb + lr) * ROW + 16 * ks + 8 * g]);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        bv[mb] = *reinterpret_cast<const bf16x8_t*>(
-            &b_lds[buf][(64 * wm + 32 * mb + lr) * ROW + 16 * ks + 8 * g]);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[nb], bv[mb], acc[nb][mb], 0, 0, 0);
+      for (int i = 0; i < 8; ++i) {
+        const int nb = i >> 1, mb = i & 1;
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks & 1][nb], bv[ks & 1][mb],
+                                                             acc[nb][mb], 0, 0, 0);
+        if (ks >= 2) {       // (on the last step this fills a buffer no one reads)
+          const int j = 4 * (ks - 2) + (i >> 1);
+          if ((i & 1) == 0) {
+            const int c = tid + 512 * j;
+            const bool isa = c < TN * CPR;
+            const int cc = isa ? c : c - TN * CPR;
+            const int row = cc / CPR, ch = cc % CPR;
+            uint16_t* dst = isa ? &a_lds[buf ^ 1][row * ROW + 8 * ch]
+                                : &b_lds[buf ^ 1][row * ROW + 8 * ch];
+            *reinterpret_cast<u32x4_t*>(dst) = stg[j];
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < nk) store(buf ^ 1);
     __syncthreads();
   }
 
