@@ -233,6 +233,43 @@ def main():
                 "speedup_vs_dense": round(dms / sms, 3),
                 "effective_tflops": round(eff, 2), "peak": peak, "frac": round(eff / peak, 4)})
             del xq, xk, xv, xo, xm
+    if args.extra:
+        # QKV projection with the RoPE-4D epilogue at the bench shape (hidden
+        # C = H D = 3072, an assumption: the pages give no width), against
+        # torch's GEMM (hipBLASLt) on the same operands, and the attention on
+        # its pre-rotated output against the fused-rotation attention
+        c = get_config(4)
+        C = c.H * c.D
+        print(f"[extra] qkv projection M={c.B * c.S} N={3 * C} K={C}", file=sys.stderr, flush=True)
+        g = torch.Generator(device=dev).manual_seed(404)
+        xx = torch.randn(c.B, c.S, C, device=dev, generator=g).to(torch.bfloat16)
+        ww = (torch.randn(3 * C, C, device=dev, generator=g) / C ** 0.5).to(torch.bfloat16)
+        bb = (torch.randn(3 * C, device=dev, generator=g) * 0.1).to(torch.bfloat16)
+        pp = torch.from_numpy(inp.pos).to(dev)
+        qo = torch.empty(c.B, c.S, c.H, c.D, dtype=torch.float16, device=dev)
+        ko = torch.empty_like(qo)
+        vo = torch.empty(c.B, c.S, c.H, c.D, dtype=torch.bfloat16, device=dev)
+        oo = torch.empty_like(vo)
+        pms = time_gpu(lambda: kl.klein_qkv_rope4d_proj(xx, ww, bb, pp, qo, ko, vo), 10, 3, torch)
+        yy = torch.empty(c.B, c.S, 3 * C, dtype=torch.bfloat16, device=dev)
+        xm = xx.view(-1, C)
+        tms = time_gpu(lambda: torch.addmm(bb, xm, ww.t(), out=yy.view(-1, 3 * C)), 10, 3, torch)
+        ams = time_gpu(lambda: kl.klein_attn_fwd_prerotated(qo, ko, vo, oo), 10, 3, torch)
+        gf = 2.0 * c.B * c.S * 3 * C * C
+        rec["extra"].append({
+            "workload": f"QKV projection + RoPE-4D epilogue: x [{c.B}, {c.S}, {C}] bf16, "
+                        f"W [{3 * C}, {C}] bf16, bias; q', k' fp16, v bf16",
+            "ms_per_call": round(pms, 4), "tflops": round(gf / (pms * 1e-3) / 1e12, 2),
+            "peak": PEAK_BF16, "frac": round(gf / (pms * 1e-3) / 1e12 / PEAK_BF16, 4),
+            "torch_addmm_ms": round(tms, 4),
+            "torch_addmm_tflops": round(gf / (tms * 1e-3) / 1e12, 2)})
+        rec["extra"].append({
+            "workload": f"attention on pre-rotated fp16 q', k' (bf16 v): {c.name}, B={c.B}, "
+                        f"S={c.S}, H={c.H}, D={c.D}",
+            "ms_per_call": round(ams, 4), "tflops": round(c.flops / (ams * 1e-3) / 1e12, 2),
+            "peak": PEAK_BF16, "frac": round(c.flops / (ams * 1e-3) / 1e12 / PEAK_BF16, 4),
+            "fused_rotation_ms": round(ms, 4)})
+        del xx, ww, bb, qo, ko, vo, oo, yy
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
