@@ -134,7 +134,7 @@ klein_status_t klein_rope4d_attn_fwd_blocksparse(const void* q, const void* k, c
  * step that feeds the attention in each joint block ("Flux.3 Image Klein
  * arrives in Diffusers with a modular architecture", section "How it works";
  * the fused QKV GEMMs of "How FLUX 3 Image Klein was made 3-4x faster on
- * NVIDIA Blackwell", section "Method 2"):
+ * NVIDIA Blackwell", section "Method 1"):
  *   y = x W^T (+ bias);  q = y[:, 0:HD], k = y[:, HD:2HD], v = y[:, 2HD:3HD]
  *   q_out = R(pos) q, k_out = R(pos) k  (fp16),  v_out = v  (bfloat16)
  *   x       : [B][S][C] bfloat16 (C % 64 == 0, C <= 65536, else UNSUPPORTED)

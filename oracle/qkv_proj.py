@@ -5,7 +5,7 @@ This is the step that feeds the attention ("Flux.3 Image Klein arrives in
 Diffusers with a modular architecture", section "How it works": each joint
 block projects the concatenated token sequence to queries, keys and values
 and rotates queries and keys with the four-axis rotary embedding; "How FLUX 3
-Image Klein was made 3-4x faster on NVIDIA Blackwell", section "Method 2":
+Image Klein was made 3-4x faster on NVIDIA Blackwell", section "Method 1":
 the QKV projections are fused GEMMs).  With x [B, S, C], a weight W
 [3 H D, C] (a linear layer's [out, in] layout) and an optional bias [3 H D]:
 
