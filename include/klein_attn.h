@@ -49,6 +49,7 @@
 #ifndef KLEIN_ATTN_H
 #define KLEIN_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -97,6 +98,49 @@ klein_status_t klein_rope4d_attn_fwd_fp8(const void* q, const void* k, const voi
                                          int B, int S, int H, int D,
                                          float q_descale, float k_descale,
                                          float v_descale, klein_stream_t stream);
+
+/*
+ * The same attention (bf16, or FP8 E4M3 with per-tensor descales as in
+ * klein_rope4d_attn_fwd_fp8; dtype BF16 ignores the descales), scheduled so
+ * that every compute unit of the GPU stays busy to the end of the call.  The
+ * dense entry points give each workgroup one tile of 256 queries against all
+ * keys; when the B*H*ceil(S/256) tiles do not fill whole rounds of the GPU,
+ * the last round leaves compute units idle.  Here the whole rounds run the
+ * same way and each remaining tile's keys are cut into chunks at the same
+ * boundaries for every tile, one workgroup per chunk, so that all compute
+ * units share the tail; the chunks' partial results (unnormalised output,
+ * running max, row sum) go to `workspace`, and a second kernel on the same
+ * stream merges them in key order into the output rows.  Rows of tiles that
+ * run whole are bit-identical to the dense entry points'; rows of split tiles
+ * differ by the rounding of the probabilities against each chunk's own
+ * running max and the fp32 merge, within the same error bounds.  The result
+ * is deterministic (fixed merge order).
+ *   workspace      : DEVICE pointer, 256-byte aligned, caller-owned, at least
+ *                    the size klein_attn_workspace_size reports for the same
+ *                    shape on the current device (may be NULL when that is 0).
+ *                    Its contents on entry do not matter.  Two calls that
+ *                    use one workspace at the same time on different streams
+ *                    race.
+ *   workspace_bytes: its size; smaller than required is INVALID_ARG.
+ */
+klein_status_t klein_rope4d_attn_fwd_ws(const void* q, const void* k, const void* v,
+                                        const int32_t* pos_thwl, void* out,
+                                        int B, int S, int H, int D, klein_dtype_t dtype,
+                                        float q_descale, float k_descale, float v_descale,
+                                        void* workspace, size_t workspace_bytes,
+                                        klein_stream_t stream);
+
+/*
+ * Workspace bytes klein_rope4d_attn_fwd_ws needs for this shape on the
+ * current HIP device (0 when the tiles fill whole rounds, or the sequence is
+ * shorter than 2048 keys, and nothing is split).  At most
+ * 4 * (number of compute units) * (256 * D + 1024) * 4 bytes: 138 MB for
+ * D = 128 on 256 compute units.  Writes *bytes; INVALID_ARG for a
+ * null `bytes`, sizes < 1 or a bad dtype, UNSUPPORTED for D not in {64, 128},
+ * NO_DEVICE without a usable GPU.
+ */
+klein_status_t klein_attn_workspace_size(int B, int S, int H, int D, klein_dtype_t dtype,
+                                         size_t* bytes);
 
 /*
  * Block-sparse variant: the same attention with each query attending only to

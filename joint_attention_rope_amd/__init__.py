@@ -20,7 +20,8 @@ __all__ = [
     "klein_rope4d_attn_fwd_blocksparse", "klein_rope4d_apply", "klein_status_string",
     "klein_version", "library_path", "KLEIN_DTYPE_BF16", "KLEIN_DTYPE_FP8_E4M3",
     "KLEIN_SPARSE_QBLOCK", "KLEIN_SPARSE_KBLOCK", "blocksparse_mask_shape",
-    "klein_qkv_rope4d_proj", "klein_attn_fwd_prerotated",
+    "klein_qkv_rope4d_proj", "klein_attn_fwd_prerotated", "klein_rope4d_attn_fwd_ws",
+    "klein_attn_workspace_size",
 ]
 
 
@@ -116,6 +117,53 @@ def klein_rope4d_attn_fwd_fp8(q, k, v, pos_thwl, out, q_descale, k_descale, v_de
         B, S, H, D, float(q_descale), float(k_descale), float(v_descale),
         _stream(stream, q.device))
     _check(st, "klein_rope4d_attn_fwd_fp8")
+    return out
+
+
+def klein_attn_workspace_size(B, S, H, D, dtype=KLEIN_DTYPE_BF16):
+    """Bytes of workspace klein_rope4d_attn_fwd_ws needs for this shape on the
+    current device (0: nothing is split)."""
+    import ctypes
+    n = ctypes.c_size_t(0)
+    st = _capi.lib().klein_attn_workspace_size(int(B), int(S), int(H), int(D), int(dtype),
+                                               ctypes.byref(n))
+    _check(st, "klein_attn_workspace_size")
+    return n.value
+
+
+def klein_rope4d_attn_fwd_ws(q, k, v, pos_thwl, out, workspace, dtype=None,
+                             descales=(1.0, 1.0, 1.0), stream=None):
+    """The dense attention on the split-KV schedule (whole rounds of query
+    tiles, then the remaining tiles cut into key chunks over every compute unit).
+
+    workspace: a contiguous GPU tensor (any dtype) of at least
+    klein_attn_workspace_size(B, S, H, D, dtype) bytes, or None when that is 0.
+    dtype: inferred from q.dtype when None; descales (q, k, v) apply to fp8 only.
+    """
+    B, S, H, D = _bshd(q, "q")
+    for t, n in ((k, "k"), (v, "v"), (out, "out")):
+        if _bshd(t, n) != (B, S, H, D):
+            raise ValueError(f"{n} must have q's shape {(B, S, H, D)}")
+    _pos(pos_thwl, S)
+    if dtype is None:
+        dtype = KLEIN_DTYPE_FP8_E4M3 if q.dtype in _FP8_DTYPES else KLEIN_DTYPE_BF16
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        ok = t.dtype == torch.bfloat16 if dtype == KLEIN_DTYPE_BF16 else t.dtype in _FP8_DTYPES
+        if not ok:
+            raise ValueError(f"{n} has dtype {t.dtype}, which does not match the dtype code {dtype}")
+    if out.dtype != torch.bfloat16:
+        raise ValueError("out must be bfloat16")
+    if workspace is None:
+        wp, wb = 0, 0
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        wp, wb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    dq, dk, dv = (float(x) for x in descales)
+    st = _capi.lib().klein_rope4d_attn_fwd_ws(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), pos_thwl.data_ptr(), out.data_ptr(),
+        B, S, H, D, int(dtype), dq, dk, dv, wp, wb, _stream(stream, q.device))
+    _check(st, "klein_rope4d_attn_fwd_ws")
     return out
 
 

@@ -1,6 +1,7 @@
 // C ABI of the RoPE-4D joint-attention library: argument checks, RoPE
 // frequency tables, kernel dispatch, status mapping.  Declarations and the
 // contract of every entry point live in include/klein_attn.h.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -64,6 +65,24 @@ LaunchArgs make_args(const void* q, const void* k, const void* v, const int32_t*
 
 constexpr long long kMaxGrid = 2147483647LL;
 
+// Compute units of the current device, cached per device (the split-KV plan
+// depends on them).  0 on error, with the HIP error in *err.
+int current_cu_count(hipError_t* err) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  *err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (*err != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -95,6 +114,61 @@ klein_status_t klein_rope4d_attn_fwd_fp8(const void* q, const void* k, const voi
   if (klein::attn_fwd_fp8_grid(B, S, H) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
   try {
     LaunchArgs a = make_args(q, k, v, pos_thwl, out, B, S, H, D, stream);
+    a.descale[0] = q_descale; a.descale[1] = k_descale; a.descale[2] = v_descale;
+    return map_hip(klein::launch_attn_fwd_fp8(a));
+  } catch (...) {
+    return KLEIN_ERR_LAUNCH;
+  }
+}
+
+klein_status_t klein_attn_workspace_size(int B, int S, int H, int D, klein_dtype_t dtype,
+                                         size_t* bytes) {
+  if (!bytes) return KLEIN_ERR_INVALID_ARG;
+  if (dtype != KLEIN_DTYPE_BF16 && dtype != KLEIN_DTYPE_FP8_E4M3) return KLEIN_ERR_INVALID_ARG;
+  if (B < 1 || S < 1 || H < 1) return KLEIN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return KLEIN_ERR_UNSUPPORTED;
+  if (klein::attn_fwd_bf16_grid(B, S, H) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
+  try {
+    hipError_t e;
+    const int ncu = current_cu_count(&e);
+    if (e != hipSuccess) return map_hip(e);
+    *bytes = (size_t)klein::plan_split(B, S, H, D, ncu).bytes;
+    return KLEIN_OK;
+  } catch (...) {
+    return KLEIN_ERR_LAUNCH;
+  }
+}
+
+klein_status_t klein_rope4d_attn_fwd_ws(const void* q, const void* k, const void* v,
+                                        const int32_t* pos_thwl, void* out, int B, int S, int H,
+                                        int D, klein_dtype_t dtype, float q_descale,
+                                        float k_descale, float v_descale, void* workspace,
+                                        size_t workspace_bytes, klein_stream_t stream) {
+  if (dtype != KLEIN_DTYPE_BF16 && dtype != KLEIN_DTYPE_FP8_E4M3) return KLEIN_ERR_INVALID_ARG;
+  klein_status_t st = check_common(q, k, v, pos_thwl, out, B, S, H, D);
+  if (st != KLEIN_OK) return st;
+  const bool fp8 = dtype == KLEIN_DTYPE_FP8_E4M3;
+  if (fp8)
+    for (float s : {q_descale, k_descale, v_descale})
+      if (!(std::isfinite(s) && s > 0.f)) return KLEIN_ERR_INVALID_ARG;
+  if (klein::attn_fwd_bf16_grid(B, S, H) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return KLEIN_ERR_INVALID_ARG;
+  try {
+    hipError_t e;
+    const int ncu = current_cu_count(&e);
+    if (e != hipSuccess) return map_hip(e);
+    const klein::SplitPlan plan = klein::plan_split(B, S, H, D, ncu);
+    if (plan.bytes > 0 && (!workspace || workspace_bytes < (size_t)plan.bytes))
+      return KLEIN_ERR_INVALID_ARG;
+    LaunchArgs a = make_args(q, k, v, pos_thwl, out, B, S, H, D, stream);
+    if (plan.n_sk > 0) {
+      a.split.part = static_cast<float*>(workspace);
+      a.split.n_dp = plan.n_dp;
+      a.split.n_sk = plan.n_sk;
+      a.split.n_rem = plan.n_rem;
+      a.split.n_chunk = plan.n_chunk;
+    }
+    if (!fp8) return map_hip(klein::launch_attn_fwd_bf16(a));
     a.descale[0] = q_descale; a.descale[1] = k_descale; a.descale[2] = v_descale;
     return map_hip(klein::launch_attn_fwd_fp8(a));
   } catch (...) {
@@ -199,6 +273,6 @@ const char* klein_status_string(klein_status_t status) {
   return "unknown status";
 }
 
-int klein_version(void) { return 110; }
+int klein_version(void) { return 120; }
 
 }  // extern "C"

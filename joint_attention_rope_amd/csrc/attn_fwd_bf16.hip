@@ -75,12 +75,14 @@ __device__ __forceinline__ int key_to_row(int kk) {
 // PREROT: q and k arrive rotated, as fp16 (the projection's RoPE epilogue
 // emits them so); Q is only scaled and K tiles are copied to LDS as they
 // are, with no table, positions or rotation.
-template <int D, bool SPARSE, bool PREROT>
+// SPLIT: the split-KV schedule (SplitArgs): whole items first, then the key
+// chunks of the remaining items, merged through the workspace.
+template <int D, bool SPARSE, bool PREROT, bool SPLIT>
 __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ pos,
     uint16_t* __restrict__ out, int S, int H, int nqt, RopeFreqs fr, float qscale,
-    const uint8_t* __restrict__ bmask) {
+    const uint8_t* __restrict__ bmask, SplitArgs sp) {
   constexpr int BM = 256;              // queries per workgroup (8 waves x 32)
   constexpr int BN = 64;               // keys per tile
   constexpr int NT = 512;              // threads
@@ -98,6 +100,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   constexpr int TAB = kTabN * TROW;    // start of the fallback slots
   static_assert(KPT >= 1 && (BN * CPR) % NT == 0, "tile/thread split");
   static_assert(KPT == 1 || KPT % 2 == 0, "V^T store packs key pairs");
+  static_assert(!(SPARSE && SPLIT), "one schedule at a time");
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BN * VROW];
@@ -109,16 +112,21 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lr = lane & 31;
-
-  const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = work % nqt;
-  const int bh = work / nqt;
-  const int h = bh % H, b = bh / H;
+  const int nkt = (S + BN - 1) / BN;
   const size_t rs = (size_t)H * D;                       // token stride
-  const size_t base = (size_t)b * S * rs + (size_t)h * D;
-  const uint16_t* qb = q + base;
-  const uint16_t* kb = k + base;
-  const uint16_t* vb = v + base;
+
+  // ---- this workgroup's work: an item (b, h, query tile) and its key tiles
+  // [k0, k1): all of them, or with SPLIT past the whole items, chunk `chunk`
+  int work, k0 = 0, k1 = nkt, chunk = 0;
+  if (SPLIT && (int)blockIdx.x >= sp.n_dp) {
+    const int s = xcd_remap(blockIdx.x - sp.n_dp, sp.n_sk);
+    chunk = s / sp.n_rem;
+    work = sp.n_dp + s % sp.n_rem;
+    k0 = split_chunk_begin(chunk, nkt, sp.n_chunk);
+    k1 = split_chunk_begin(chunk + 1, nkt, sp.n_chunk);
+  } else {
+    work = xcd_remap(blockIdx.x, SPLIT ? sp.n_dp : gridDim.x);
+  }
 
   // ---- cos/sin table (the very values rope_chunk computes)
   if constexpr (!PREROT) {
@@ -128,6 +136,18 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
       cs_tab[p * TROW + j] = make_float2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
     }
   }
+
+  const int qt = work % nqt;
+  const int bh = work / nqt;
+  const int h = bh % H, b = bh / H;
+  const size_t base = (size_t)b * S * rs + (size_t)h * D;
+  const uint16_t* qb = q + base;
+  // keys, values and key positions from the segment's first tile on; Sk
+  // keys remain from there
+  const uint16_t* kb = k + base + (size_t)k0 * BN * rs;
+  const uint16_t* vb = v + base + (size_t)k0 * BN * rs;
+  const int32_t* kposb = pos + (size_t)k0 * BN * 4;
+  const int Sk = S - k0 * BN;
 
   // ---- this lane's query: rotate, scale by log2(e)/sqrt(D), fp16 in VGPRs.
   // Rows past S load row S-1 (in bounds) and are never stored.
@@ -163,7 +183,6 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   // byte offsets of key lk (key lk + it adds it * rowb, a scalar offset)
   const int voff = lk * rowb + 16 * lc;
   const int voff_p = (lk * 4 + la) * 4;
-  const int nkt = (S + BN - 1) / BN;
   // tile index of pipeline position t (the kept list when SPARSE)
   auto tl = [&](int t) -> int {
     if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)klist[t]);
@@ -174,7 +193,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   // ring slot kt & 1 holds tile kt's
   int kpos0[KPT], kpos1[KPT];
   auto tile_rows = [&](int kt) {
-    const int n = S - kt * BN;
+    const int n = Sk - kt * BN;
     return n < 0 ? 0 : (n > BN ? BN : n);
   };
   auto load_k = [&](int kt) {
@@ -185,7 +204,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   };
   auto load_pos = [&](int kt, int* slot) {
     if constexpr (PREROT) return;
-    const __amdgpu_buffer_rsrc_t rp = uniform_rsrc(pos + (size_t)kt * BN * 4, tile_rows(kt) * 16);
+    const __amdgpu_buffer_rsrc_t rp = uniform_rsrc(kposb + (size_t)kt * BN * 4, tile_rows(kt) * 16);
 #pragma unroll
     for (int it = 0; it < KPT; ++it)
       slot[it] = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, voff_p, it * 16, 0);
@@ -296,12 +315,12 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   // max rose more than TAU above m_run, m_run moves up by delta, O and l take
   // 2^-delta, and the relative scores of this tile shift by -delta
   auto softmax_max = [&](int t, f32x16_t* sc) {
-    if (t * BN + BN > S) {
+    if (t * BN + BN > Sk) {
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (t * BN + 32 * kbk + 16 * g + i >= S) sc[kbk][i] = kNegInf;
+          if (t * BN + 32 * kbk + 16 * g + i >= Sk) sc[kbk][i] = kNegInf;
     }
     const float mx = rowmax32(sc);
     if (__builtin_amdgcn_ballot_w64(mx > TAU)) {
@@ -420,7 +439,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     }
   };
 
-  int nsteps = nkt;
+  int nsteps = k1 - k0;
   if constexpr (SPARSE) {
     if (wave == 0) {
       const int n = build_kept_list(bmask + ((size_t)bh * nqt + qt) * nkt, nkt, klist, lane);
@@ -464,12 +483,12 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   // m_run starts at tile 0's exact row max (keys past S masked), so scores
   // are relative from the first tile on and no row can underflow
   const int kt0 = tl(0);
-  if (kt0 * BN + BN > S) {
+  if (kt0 * BN + BN > Sk) {
 #pragma unroll
     for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (kt0 * BN + 32 * kbk + 16 * g + i >= S) sa[kbk][i] = kNegInf;
+        if (kt0 * BN + 32 * kbk + 16 * g + i >= Sk) sa[kbk][i] = kNegInf;
   }
   m_run = rowmax32(sa);
 #pragma unroll
@@ -501,9 +520,17 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   }
   if (t < nsteps) step(t, sa, sb, kpos0);
 
-  // ---- epilogue: O / l, bf16, store (lane holds channels 32mb + 8(i/4) + 4g + i%4)
-  const float inv = 1.0f / pair_sum(l_run);
+  // ---- epilogue: O / l, bf16, store (lane holds channels 32mb + 8(i/4) + 4g + i%4);
+  // a chunk of a split item stores its partial instead (the merge kernel
+  // writes those rows)
+  const float lsum = pair_sum(l_run);
+  if constexpr (SPLIT)
+    if (k0 != 0 || k1 != nkt) {
+      split_store<MB>(o, m_run, lsum, sp, work - sp.n_dp, chunk);
+      return;
+    }
   if (qrow < S) {
+    const float inv = 1.0f / lsum;
     uint16_t* orow = out + base + (size_t)qrow * rs;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -518,19 +545,25 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   }
 }
 
-template <int D, bool SPARSE, bool PREROT = false>
+template <int D, bool SPARSE, bool PREROT = false, bool SPLIT = false>
 static hipError_t launch_bf16(const LaunchArgs& a) {
   constexpr int BM = 256;
   const int nqt = (a.S + BM - 1) / BM;
-  const long long n = (long long)a.B * a.H * nqt;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, SPARSE, PREROT>), dim3((unsigned)n), dim3(512), 0,
-                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     a.pos, (uint16_t*)a.out, a.S, a.H, nqt, a.freqs, a.qscale_log2, a.bmask);
+  const long long n = SPLIT ? (long long)a.split.n_dp + a.split.n_sk : (long long)a.B * a.H * nqt;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, SPARSE, PREROT, SPLIT>), dim3((unsigned)n), dim3(512),
+                     0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     a.pos, (uint16_t*)a.out, a.S, a.H, nqt, a.freqs, a.qscale_log2, a.bmask,
+                     a.split);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd_bf16(const LaunchArgs& a) {
   if (a.bmask) return a.D == 128 ? launch_bf16<128, true>(a) : launch_bf16<64, true>(a);
+  if (a.split.n_sk > 0) {
+    const hipError_t e = a.D == 128 ? launch_bf16<128, false, false, true>(a)
+                                    : launch_bf16<64, false, false, true>(a);
+    return e != hipSuccess ? e : launch_split_merge(a, 1.0f);
+  }
   return a.D == 128 ? launch_bf16<128, false>(a) : launch_bf16<64, false>(a);
 }
 

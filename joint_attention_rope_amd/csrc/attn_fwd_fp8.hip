@@ -104,12 +104,14 @@ __device__ __forceinline__ int rope_pair_fp8_h(uint32_t word, h2_t cs, int acc) 
 // SPARSE: block-sparse variant (one mask byte per batch, head, query tile of
 // 256 and key tile of 64; only kept key tiles stream through the pipeline, in
 // ascending order, so with every tile kept the result equals the dense one).
-template <int D, bool SPARSE>
+// SPLIT: the split-KV schedule (SplitArgs): whole items first, then the key
+// chunks of the remaining items, merged through the workspace.
+template <int D, bool SPARSE, bool SPLIT>
 __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     const int32_t* __restrict__ pos, uint16_t* __restrict__ out, int S, int H, int nqt,
     RopeFreqs fr, float q_mul, int sc_a, int sc_b, float o_scale,
-    const uint8_t* __restrict__ bmask) {
+    const uint8_t* __restrict__ bmask, SplitArgs sp) {
   constexpr int BM = 256;              // queries per workgroup (8 waves x 32)
   constexpr int BN = 64;               // keys per tile
   constexpr int NT = 512;              // threads
@@ -128,6 +130,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   constexpr float C0 = 0.80735492205760410f;   // log2(1.75)
   static_assert(NCH == NT || 2 * NCH == NT, "one K and one V chunk per thread (D 128) "
                                             "or one of either (D 64)");
+  static_assert(!(SPARSE && SPLIT), "one schedule at a time");
 
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][BN * KROW];
   __shared__ __attribute__((aligned(16))) uint8_t v_lds[2][BN * VROW];
@@ -140,17 +143,22 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lr = lane & 31;
-
-  const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = work % nqt;
-  const int bh = work / nqt;
-  const int h = bh % H, b = bh / H;
+  const int nkt = (S + BN - 1) / BN;
   const size_t rs = (size_t)H * D;                       // token stride (bytes)
-  const size_t base = (size_t)b * S * rs + (size_t)h * D;
-  const uint8_t* qb = q + base;
-  const uint8_t* kbase = k + base;
-  const uint8_t* vbase = v + base;
   const int rowb = (int)rs;
+
+  // ---- this workgroup's work: an item (b, h, query tile) and its key tiles
+  // [k0, k1): all of them, or with SPLIT past the whole items, chunk `chunk`
+  int work, k0 = 0, k1 = nkt, chunk = 0;
+  if (SPLIT && (int)blockIdx.x >= sp.n_dp) {
+    const int s = xcd_remap(blockIdx.x - sp.n_dp, sp.n_sk);
+    chunk = s / sp.n_rem;
+    work = sp.n_dp + s % sp.n_rem;
+    k0 = split_chunk_begin(chunk, nkt, sp.n_chunk);
+    k1 = split_chunk_begin(chunk + 1, nkt, sp.n_chunk);
+  } else {
+    work = xcd_remap(blockIdx.x, SPLIT ? sp.n_dp : gridDim.x);
+  }
 
   // ---- cos/sin table: entry p * TROW + j = (cos, sin)(p w_j) / 2
   for (int e = tid; e < kTabN * NJ; e += NT) {
@@ -158,6 +166,18 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
     const float2 c = rope_cs(p, fr.hi[j], fr.lo[j], kHalf);
     cs_tab[p * TROW + j] = (h2_t){(_Float16)c.x, (_Float16)c.y};
   }
+
+  const int qt = work % nqt;
+  const int bh = work / nqt;
+  const int h = bh % H, b = bh / H;
+  const size_t base = (size_t)b * S * rs + (size_t)h * D;
+  const uint8_t* qb = q + base;
+  // keys, values and key positions from the segment's first tile on; Sk
+  // keys remain from there
+  const uint8_t* kbase = k + base + (size_t)k0 * BN * rs;
+  const uint8_t* vbase = v + base + (size_t)k0 * BN * rs;
+  const int32_t* kposb = pos + (size_t)k0 * BN * 4;
+  const int Sk = S - k0 * BN;
 
   // ---- Q'': this lane's query, dims 64 ks + 32 g + [0, 32) per k-step.
   // Rows past S load row S-1 (in bounds) and are never stored.
@@ -195,7 +215,6 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   const int voff_v = vkey * rowb + 16 * vc;
   const int krow = (kkey & ~31) + key_to_row8(kkey & 31);
 
-  const int nkt = (S + BN - 1) / BN;
   // tile index of pipeline position t (the kept list when SPARSE)
   auto tl = [&](int t) -> int {
     if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)klist[t]);
@@ -207,7 +226,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   int kpos0 = 0, kpos1 = 0;
 
   auto tile_rows = [&](int kt) {
-    const int n = S - kt * BN;
+    const int n = Sk - kt * BN;
     return n < 0 ? 0 : (n > BN ? BN : n);
   };
   // global -> registers (rows past S read as zero through the descriptors)
@@ -220,7 +239,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   };
   auto load_pos = [&](int kt, int& slot) {
     if (kst) {
-      const __amdgpu_buffer_rsrc_t rp = uniform_rsrc(pos + (size_t)kt * BN * 4, tile_rows(kt) * 16);
+      const __amdgpu_buffer_rsrc_t rp = uniform_rsrc(kposb + (size_t)kt * BN * 4, tile_rows(kt) * 16);
       slot = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, voff_p, 0, 0);
     }
   };
@@ -304,12 +323,12 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
     for (int i = 0; i < 16; ++i) cinit[i] = C0 - m_run;
   };
   auto mask_tail = [&](int t, f32x16_t* sc) {
-    if (t * BN + BN > S) {
+    if (t * BN + BN > Sk) {
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (t * BN + 32 * kbk + 16 * g + i >= S) sc[kbk][i] = kNegInf;
+          if (t * BN + 32 * kbk + 16 * g + i >= Sk) sc[kbk][i] = kNegInf;
     }
   };
   auto softmax_max = [&](int t, f32x16_t* sc) {
@@ -401,7 +420,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
     }
   };
 
-  int nsteps = nkt;
+  int nsteps = k1 - k0;
   if constexpr (SPARSE) {
     if (wave == 0) {
       const int n = build_kept_list(bmask + ((size_t)bh * nqt + qt) * nkt, nkt, klist, lane);
@@ -476,9 +495,16 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   }
   if (t < nsteps) step(t, sa, sb, kpos0);
 
-  // ---- epilogue: O * dv / l -> bf16
-  const float inv = o_scale / pair_sum(l_run);
+  // ---- epilogue: O * dv / l -> bf16; a chunk of a split item stores its
+  // partial instead (the merge kernel writes those rows)
+  const float lsum = pair_sum(l_run);
+  if constexpr (SPLIT)
+    if (k0 != 0 || k1 != nkt) {
+      split_store<MB>(o, m_run, lsum, sp, work - sp.n_dp, chunk);
+      return;
+    }
   if (qrow < S) {
+    const float inv = o_scale / lsum;
     uint16_t* orow = out + (size_t)b * S * rs + (size_t)h * D + (size_t)qrow * rs;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -511,20 +537,24 @@ static Fp8Scales fp8_scales(const LaunchArgs& a) {
   return {(float)std::ldexp(G, -n), 127 + na, 127 + nb};
 }
 
-template <int D, bool SPARSE>
+template <int D, bool SPARSE, bool SPLIT = false>
 static hipError_t launch_fp8(const LaunchArgs& a) {
   const int nqt = (a.S + 255) / 256;
-  const long long n = (long long)a.B * a.H * nqt;
+  const long long n = SPLIT ? (long long)a.split.n_dp + a.split.n_sk : (long long)a.B * a.H * nqt;
   const Fp8Scales s = fp8_scales(a);
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, SPARSE>), dim3((unsigned)n), dim3(512), 0, a.stream,
-                     (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, a.pos,
-                     (uint16_t*)a.out, a.S, a.H, nqt, a.freqs, s.q_mul, s.sc_a, s.sc_b,
-                     a.descale[2], a.bmask);
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, SPARSE, SPLIT>), dim3((unsigned)n), dim3(512), 0,
+                     a.stream, (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v,
+                     a.pos, (uint16_t*)a.out, a.S, a.H, nqt, a.freqs, s.q_mul, s.sc_a, s.sc_b,
+                     a.descale[2], a.bmask, a.split);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd_fp8(const LaunchArgs& a) {
   if (a.bmask) return a.D == 128 ? launch_fp8<128, true>(a) : launch_fp8<64, true>(a);
+  if (a.split.n_sk > 0) {
+    const hipError_t e = a.D == 128 ? launch_fp8<128, false, true>(a) : launch_fp8<64, false, true>(a);
+    return e != hipSuccess ? e : launch_split_merge(a, a.descale[2]);
+  }
   return a.D == 128 ? launch_fp8<128, false>(a) : launch_fp8<64, false>(a);
 }
 

@@ -121,6 +121,54 @@ __device__ __forceinline__ int build_kept_list(const uint8_t* mrow, int nkt, uin
   return n;
 }
 
+// Split-KV schedule of the attention kernels (split variant).  The work list
+// holds B*H*ceil(S/256) items (one query tile each, all key tiles).  The
+// first n_dp items (whole rounds of the GPU) run one per workgroup.  Each of
+// the n_rem items that would fill only part of a last round is cut into
+// n_chunk chunks of key tiles at the same boundaries for every item, one
+// workgroup per (chunk, item); consecutive workgroups take the same chunk of
+// consecutive items, so the workgroups of one XCD stream the same keys and
+// values through its L2, as in the dense schedule.  A chunk stores its
+// unnormalised O, running max m and row sum l in the workspace slot
+// chunk * n_rem + item, and a second kernel on the same stream merges each
+// item's slots in chunk order into the output rows (the kernel boundary
+// orders the stores before the loads; the merge order is fixed, so the
+// result is deterministic).
+struct SplitArgs {
+  float* part;     // n_chunk * n_rem slots of split_slot_floats(D) floats
+  int n_dp;        // items run whole, by workgroups [0, n_dp)
+  int n_sk;        // split workgroups, [n_dp, n_dp + n_sk): n_chunk * n_rem
+  int n_rem;       // items split
+  int n_chunk;     // chunks per split item
+};
+
+// slot of a 256-query tile: O as [wave][32-row block][4][lane] float4 (the
+// accumulator registers of each lane, in order), then (m, l) as [wave][lane]
+// float2
+__host__ __device__ constexpr long long split_slot_floats(int D) { return 256LL * D + 1024; }
+
+// first key tile of chunk c of nkt tiles cut into n (c = n gives nkt)
+__host__ __device__ inline int split_chunk_begin(int c, int nkt, int n) {
+  return (int)((long long)c * nkt / n);
+}
+
+// Store this workgroup's partial (o, m, l: l already summed over the lane
+// pair) of chunk `chunk` of split item r.
+template <int MB>
+__device__ __forceinline__ void split_store(const f32x16_t* o, float m, float l,
+                                            const SplitArgs& sp, int r, int chunk) {
+  constexpr int D = 32 * MB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float* my = sp.part + (size_t)(chunk * sp.n_rem + r) * split_slot_floats(D);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4)
+      *reinterpret_cast<f32x4_t*>(my + 4 * (((wave * MB + mb) * 4 + i4) * 64 + lane)) =
+          (f32x4_t){o[mb][4 * i4], o[mb][4 * i4 + 1], o[mb][4 * i4 + 2], o[mb][4 * i4 + 3]};
+  *reinterpret_cast<f32x2_t*>(my + 256 * D + 2 * (wave * 64 + lane)) = (f32x2_t){m, l};
+}
+
 // Reduce a per-lane value with the lane 32 apart (lanes l and l^32 hold the
 // two halves of one query's keys in the 32x32 MFMA accumulator layout).
 __device__ __forceinline__ float pair_max(float x) {

@@ -22,7 +22,20 @@ struct LaunchArgs {
   // block-sparse mask [B][H][ceil(S/256)][ceil(S/64)] (nonzero = compute), or
   // null for dense attention
   const uint8_t* bmask = nullptr;
+  // split-KV schedule (n_sk > 0) over the caller's workspace, or none
+  SplitArgs split{};
 };
+
+// Split-KV cut of a dense call for a GPU of n_cu compute units (n_sk == 0:
+// whole items only, no workspace).  The workspace holds the partial slots.
+struct SplitPlan {
+  int n_dp, n_sk, n_rem, n_chunk;
+  long long bytes;
+};
+SplitPlan plan_split(int B, int S, int H, int D, int n_cu);
+// merges the split items' slots into their output rows (after the attention
+// kernel, on the same stream); o_scale multiplies O / l (v's descale for fp8)
+hipError_t launch_split_merge(const LaunchArgs& a, float o_scale);
 
 hipError_t launch_attn_fwd_bf16(const LaunchArgs& a);
 hipError_t launch_attn_fwd_prerotated(const LaunchArgs& a);

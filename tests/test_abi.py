@@ -22,8 +22,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "klein_rope4d_attn_fwd", "klein_rope4d_attn_fwd_fp8", "klein_rope4d_attn_fwd_blocksparse",
-        "klein_qkv_rope4d_proj", "klein_attn_fwd_prerotated",
-        "klein_rope4d_apply", "klein_status_string", "klein_version"])
+        "klein_qkv_rope4d_proj", "klein_attn_fwd_prerotated", "klein_rope4d_attn_fwd_ws",
+        "klein_attn_workspace_size", "klein_rope4d_apply", "klein_status_string",
+        "klein_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -103,3 +104,37 @@ def test_qkv_proj_and_prerotated_argument_checks():
     assert lib.klein_attn_fwd_prerotated(0, FAKE, FAKE, FAKE, 1, 8, 1, 64, None) == I
     assert lib.klein_attn_fwd_prerotated(FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 80, None) == U
     assert lib.klein_attn_fwd_prerotated(FAKE, FAKE, FAKE + 8, FAKE, 1, 8, 1, 64, None) == I
+
+
+@pytest.mark.parametrize("args,status", [
+    # q, k, v, pos, out, B, S, H, D, dtype, descales, workspace, bytes
+    ((0, FAKE, FAKE, FAKE, FAKE, 1, 4096, 1, 128, 0, 1.0, 1.0, 1.0, FAKE, 1 << 30),
+     _capi.KLEIN_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4096, 1, 128, 3, 1.0, 1.0, 1.0, FAKE, 1 << 30),
+     _capi.KLEIN_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4096, 1, 96, 0, 1.0, 1.0, 1.0, FAKE, 1 << 30),
+     _capi.KLEIN_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4096, 1, 128, 1, 1.0, 0.0, 1.0, FAKE, 1 << 30),
+     _capi.KLEIN_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4096, 1, 128, 0, 1.0, 1.0, 1.0, FAKE + 16, 1 << 30),
+     _capi.KLEIN_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4096, 1, 128, 0, 1.0, 1.0, 1.0, FAKE, 1 << 30),
+     _capi.KLEIN_ERR_INVALID_ARG),
+])
+def test_workspace_entry_argument_checks(args, status):
+    """Null tensors, bad dtype, unsupported D, bad fp8 descale, a workspace
+    not 256-byte aligned and sizes < 1 are rejected before any HIP call."""
+    assert _capi.lib().klein_rope4d_attn_fwd_ws(*args, None) == status
+
+
+def test_workspace_size_checks():
+    lib = _capi.lib()
+    n = ctypes.c_size_t(7)
+    assert lib.klein_attn_workspace_size(1, 4096, 1, 128, 0, None) == _capi.KLEIN_ERR_INVALID_ARG
+    assert lib.klein_attn_workspace_size(1, 4096, 1, 96, 0, ctypes.byref(n)) == \
+        _capi.KLEIN_ERR_UNSUPPORTED
+    assert lib.klein_attn_workspace_size(1, 4096, 0, 128, 0, ctypes.byref(n)) == \
+        _capi.KLEIN_ERR_INVALID_ARG
+    assert lib.klein_attn_workspace_size(1, 4096, 1, 128, 2, ctypes.byref(n)) == \
+        _capi.KLEIN_ERR_INVALID_ARG
+    assert n.value == 7                   # untouched on error
