@@ -5,6 +5,10 @@ One step = one call of the attention library on one batch of the 2048x2048
 text-to-image workload with CFG (cond + uncond batched): B=2, S=16,896
 (512 text + 128x128 image tokens), H=24, D=128, bf16 in/out, inputs resident
 in HBM before timing.  Throughput is attention TFLOP/s = 4*B*H*S^2*D / t.
+The timed call is klein_rope4d_attn_fwd_ws (the split-KV schedule: the
+attention kernel and its merge kernel), its workspace allocated before
+timing; the entry point without a workspace is timed beside it
+(no_workspace_entry_ms).
 
 Prints ONE JSON line.  Fields beyond the common ones:
   roofline      -- the attention kernel against dense bf16 MFMA peak, with the
@@ -28,18 +32,18 @@ sys.path.insert(0, ROOT)
 METRIC = "joint-attention TFLOP/s + % MFMA peak at 2048² (16,896 tok, 24 heads×128)"
 PEAK_BF16 = 2516.6      # dense bf16 MFMA, TFLOP/s (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_FP8 = 5033.2       # dense fp8 MFMA, TFLOP/s
-def stored_traffic(name, kernel):
-    """Memory bytes per launch from a committed rocprofv3 counter summary
+def stored_traffic(name, call):
+    """Memory bytes per call from a committed rocprofv3 counter summary
     (profiles/traffic_<name>.json), if it was taken on the current kernel
     sources; else None."""
-    from joint_attention_rope_amd.profiling import KERNEL_SOURCES, sources_hash
+    from joint_attention_rope_amd.profiling import CALLS, sources_hash
     path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("sources_hash") != sources_hash(KERNEL_SOURCES[kernel]):
+    if rec.get("call") != call or rec.get("sources_hash") != sources_hash(CALLS[call]["sources"]):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -67,6 +71,13 @@ def time_gpu(fn, steps, warmup, torch):
     stop.record()
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / steps          # ms per launch
+
+
+def workspace(kl, torch, cfg, dev):
+    """The split-KV workspace of a workload's shape (None if it needs none)."""
+    dt = kl.KLEIN_DTYPE_FP8_E4M3 if cfg.dtype == "fp8" else kl.KLEIN_DTYPE_BF16
+    n = kl.klein_attn_workspace_size(cfg.B, cfg.S, cfg.H, cfg.D, dt)
+    return torch.empty(n, dtype=torch.uint8, device=dev) if n else None
 
 
 def cpu_baseline(inp, cfg, target_s=15.0):
@@ -138,10 +149,16 @@ def main():
     inp = make_inputs(cfg)
     q, k, v, pos = to_device(inp, dev)
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
-    ms = time_gpu(lambda: kl.klein_rope4d_attn_fwd(q, k, v, pos, out), args.steps,
+    # the timed call: the split-KV entry point, its workspace allocated (and
+    # inputs resident) before timing; the entry point without a workspace is
+    # timed after it for reference
+    ws = workspace(kl, torch, cfg, dev)
+    ms = time_gpu(lambda: kl.klein_rope4d_attn_fwd_ws(q, k, v, pos, out, ws), args.steps,
                   args.warmup, torch)
+    dense_ms = time_gpu(lambda: kl.klein_rope4d_attn_fwd(q, k, v, pos, out),
+                        max(3, args.steps // 4), 2, torch)
     tflops = cfg.flops / (ms * 1e-3) / 1e12
-    traffic = stored_traffic("attn_fwd_bf16_2048px_t2i_cfg", "attn_fwd_bf16_kernel")
+    traffic = stored_traffic("attn_fwd_bf16_2048px_t2i_cfg", "attn_fwd_bf16_splitkv")
     rec = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -162,24 +179,33 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16, 4),
                      "traffic": traffic},
+        "entry_point": "klein_rope4d_attn_fwd_ws (split-KV schedule, workspace "
+                       f"{0 if ws is None else ws.numel() / 1e6:.1f} MB)",
+        "no_workspace_entry_ms": round(dense_ms, 4),
     }
-    del q, k, v, out
+    del q, k, v, out, ws
     if not args.no_fp8:
         try:
             cfg5 = get_config(5)
             inp5 = make_inputs(cfg5)
             q5, k5, v5, p5 = to_device(inp5, dev)
             o5 = torch.empty(q5.shape, dtype=torch.bfloat16, device=dev)
-            ms5 = time_gpu(lambda: kl.klein_rope4d_attn_fwd_fp8(q5, k5, v5, p5, o5, *inp5.descale),
+            ws5 = workspace(kl, torch, cfg5, dev)
+            ms5 = time_gpu(lambda: kl.klein_rope4d_attn_fwd_ws(q5, k5, v5, p5, o5, ws5,
+                                                               descales=inp5.descale),
                            max(3, args.steps // 2), max(1, args.warmup // 2), torch)
+            dense5 = time_gpu(lambda: kl.klein_rope4d_attn_fwd_fp8(q5, k5, v5, p5, o5,
+                                                                   *inp5.descale), 3, 1, torch)
             t5 = cfg5.flops / (ms5 * 1e-3) / 1e12
             rec["fp8"] = {"workload": "2048x2048 edit: B=1, S=33280 (512 text + 2 x 128x128), "
                                       "H=24, D=128, e4m3 in, bf16 out",
                           "ms_per_call": round(ms5, 4), "tflops": round(t5, 2),
                           "peak": PEAK_FP8, "frac": round(t5 / PEAK_FP8, 4),
                           "traffic": stored_traffic("attn_fwd_fp8_2048px_edit",
-                                                    "attn_fwd_fp8_kernel")}
-            del q5, k5, v5, o5
+                                                    "attn_fwd_fp8_splitkv"),
+                          "entry_point": "klein_rope4d_attn_fwd_ws",
+                          "no_workspace_entry_ms": round(dense5, 4)}
+            del q5, k5, v5, o5, ws5
         except kl.KleinError as e:
             rec["fp8"] = {"error": str(e)}
     if args.extra:
@@ -191,18 +217,45 @@ def main():
             print(f"[extra] timing {c.dtype} S={c.S}", file=sys.stderr, flush=True)
             xq, xk, xv, xp = to_device(xi, dev)
             xo = torch.empty(xq.shape, dtype=torch.bfloat16, device=dev)
+            xw = workspace(kl, torch, c, dev)
+            xms = time_gpu(lambda: kl.klein_rope4d_attn_fwd_ws(
+                xq, xk, xv, xp, xo, xw, descales=xi.descale or (1.0, 1.0, 1.0)), 5, 2, torch)
             if xi.descale is None:
                 call = lambda: kl.klein_rope4d_attn_fwd(xq, xk, xv, xp, xo)
             else:
                 call = lambda: kl.klein_rope4d_attn_fwd_fp8(xq, xk, xv, xp, xo, *xi.descale)
-            xms = time_gpu(call, 5, 2, torch)
+            dms = time_gpu(call, 3, 1, torch)
             xt = c.flops / (xms * 1e-3) / 1e12
             rec["extra"].append({
                 "workload": f"2048x2048 edit with {refs} references: B={c.B}, S={c.S} "
                             f"({c.text} text + {refs + 1} x 128x128), H={c.H}, D={c.D}, {c.dtype}",
                 "ms_per_call": round(xms, 4), "tflops": round(xt, 2), "peak": peak,
-                "frac": round(xt / peak, 4)})
-            del xq, xk, xv, xo
+                "frac": round(xt / peak, 4), "no_workspace_entry_ms": round(dms, 4)})
+            del xq, xk, xv, xo, xw
+        # one GPU's share of the 2048x2048 workload under sequence parallelism
+        # (heads split over GPUs after an all-to-all): 3 or 4 heads of one CFG
+        # branch (8- or 6-way), 6 heads of one branch (4-way), both branches
+        # with 3 heads; the workload's inputs and positions at that size
+        for B, H in ((1, 3), (1, 4), (1, 6), (2, 3)):
+            c = get_config(4, B=B, H=H, uncond_zero_text=B == 2)
+            print(f"[extra] shard B={B} H={H} S={c.S}", file=sys.stderr, flush=True)
+            xi = make_inputs(c)
+            xq, xk, xv, xp = to_device(xi, dev)
+            xo = torch.empty(xq.shape, dtype=torch.bfloat16, device=dev)
+            xw = workspace(kl, torch, c, dev)
+            # calls of ~0.5-1 ms: ~100 ms of warm-up first, so that the clock has
+            # left the idle state of the input generation before timing
+            xms = time_gpu(lambda: kl.klein_rope4d_attn_fwd_ws(xq, xk, xv, xp, xo, xw), 50, 150,
+                           torch)
+            dms = time_gpu(lambda: kl.klein_rope4d_attn_fwd(xq, xk, xv, xp, xo), 50, 150, torch)
+            xt = c.flops / (xms * 1e-3) / 1e12
+            rec["extra"].append({
+                "workload": f"one GPU's share of 2048x2048 t2i: B={B}, S={c.S}, H={H}, D={c.D}, "
+                            f"bf16 ({B * H * ((c.S + 255) // 256)} query tiles)",
+                "ms_per_call": round(xms, 4), "tflops": round(xt, 2), "peak": PEAK_BF16,
+                "frac": round(xt / PEAK_BF16, 4), "no_workspace_entry_ms": round(dms, 4),
+                "no_workspace_entry_tflops": round(c.flops / (dms * 1e-3) / 1e12, 2)})
+            del xq, xk, xv, xo, xw
         # block-sparse: the bench workloads with a seeded structured mask
         # (text blocks, a band around each query block, 30 % of the rest)
         from workloads import make_block_mask

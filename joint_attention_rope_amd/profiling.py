@@ -8,10 +8,11 @@ Three rocprofv3 runs of bench.py feed the trace/traffic summary (each with
   rocprofv3 --pmc WRITE_SIZE      --output-format csv -d WRITE -o run -- python3 bench.py ...
 
 FETCH_SIZE / WRITE_SIZE (KiB per dispatch, L2-to-memory traffic) are scaled by
-known_bytes / counter for the copy kernel, then reported per launch of the
-attention kernel next to its algorithmic bytes.
+known_bytes / counter for the copy kernel, then reported per call (the
+attention kernel plus, on the split-KV path, its merge kernel) next to the
+call's algorithmic bytes.
 
-  python -m joint_attention_rope_amd.profiling --kernel attn_fwd_bf16_kernel \
+  python -m joint_attention_rope_amd.profiling --call attn_fwd_bf16_splitkv \
       --name attn_fwd_bf16_2048px_t2i_cfg --workload 4 --stats STATS --fetch FETCH \
       --write WRITE --steps 5 --copy-mib 1024 --command "..."
 
@@ -29,9 +30,24 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 COPY_KERNEL = "MulFunctor"
 
-KERNEL_SOURCES = {
-    "attn_fwd_bf16_kernel": ["klein_device.hpp", "attn_fwd_bf16.hip"],
-    "attn_fwd_fp8_kernel": ["klein_device.hpp", "attn_fwd_fp8.hip"],
+# A profiled call of an entry point: its attention kernel (matched on the
+# demangled name, template arguments included) and, on the split-KV path, the
+# merge kernel dispatched right after it; the sources its measurement depends on.
+CALLS = {
+    "attn_fwd_bf16_splitkv": {
+        "kernel": "attn_fwd_bf16_kernel<128, false, false, true>",
+        "merge": "split_merge_kernel<128>",
+        "sources": ["klein_device.hpp", "attn_fwd_bf16.hip", "split_schedule.hip"]},
+    "attn_fwd_fp8_splitkv": {
+        "kernel": "attn_fwd_fp8_kernel<128, false, true>",
+        "merge": "split_merge_kernel<128>",
+        "sources": ["klein_device.hpp", "attn_fwd_fp8.hip", "split_schedule.hip"]},
+    "attn_fwd_bf16_dense": {
+        "kernel": "attn_fwd_bf16_kernel<128, false, false, false>", "merge": None,
+        "sources": ["klein_device.hpp", "attn_fwd_bf16.hip"]},
+    "attn_fwd_fp8_dense": {
+        "kernel": "attn_fwd_fp8_kernel<128, false, false>", "merge": None,
+        "sources": ["klein_device.hpp", "attn_fwd_fp8.hip"]},
 }
 
 
@@ -57,16 +73,46 @@ def _find(dirname, suffix):
     raise FileNotFoundError(f"no *{suffix} under {dirname}")
 
 
-def kernel_durations_ns(stats_dir, kernel):
+def _pair(ids_kernel, ids_merge):
+    """For each attention dispatch id, the first merge dispatch id after it
+    (and before the next attention dispatch), or None."""
+    ks = sorted(ids_kernel)
+    ms = sorted(ids_merge)
+    out = {}
+    for i, k in enumerate(ks):
+        nxt = ks[i + 1] if i + 1 < len(ks) else float("inf")
+        out[k] = next((m for m in ms if k < m < nxt), None)
+    return out
+
+
+def call_durations_ns(stats_dir, call):
+    """Per call, in dispatch order: (attention kernel ns, merge kernel ns)."""
+    c = CALLS[call]
     rows = _rows(_find(stats_dir, "kernel_trace.csv"))
-    return [int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-            for r in rows if kernel in r["Kernel_Name"]]
+    dur = {int(r["Dispatch_Id"]): int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows}
+    ks = [int(r["Dispatch_Id"]) for r in rows if c["kernel"] in r["Kernel_Name"]]
+    ms = [int(r["Dispatch_Id"]) for r in rows if c["merge"] and c["merge"] in r["Kernel_Name"]]
+    pairs = _pair(ks, ms)
+    return [(dur[k], dur[pairs[k]] if pairs[k] is not None else 0) for k in sorted(ks)]
 
 
 def counter_per_dispatch(pmc_dir, kernel, counter):
-    rows = _rows(_find(pmc_dir, "counter_collection.csv"))
-    return [float(r["Counter_Value"]) for r in rows
-            if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    """Counter value per dispatch of a kernel (summed over reporting units)."""
+    per = {}
+    for r in _rows(_find(pmc_dir, "counter_collection.csv")):
+        if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            k = int(r["Dispatch_Id"])
+            per[k] = per.get(k, 0.0) + float(r["Counter_Value"])
+    return per
+
+
+def call_counter(pmc_dir, call, counter):
+    """Per call: the counter of the attention kernel plus that of its merge."""
+    c = CALLS[call]
+    ks = counter_per_dispatch(pmc_dir, c["kernel"], counter)
+    ms = counter_per_dispatch(pmc_dir, c["merge"], counter) if c["merge"] else {}
+    pairs = _pair(list(ks), list(ms))
+    return [ks[k] + (ms[pairs[k]] if pairs[k] is not None else 0.0) for k in sorted(ks)]
 
 
 # Counter passes (8 SQ counters and one GRBM counter per pass at most).
@@ -175,13 +221,14 @@ def algorithmic_bytes(workload):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--kernel")
+    ap.add_argument("--call", choices=sorted(CALLS),
+                    help="the profiled call (attention kernel + its merge, if any)")
     ap.add_argument("--name")
     ap.add_argument("--workload", type=int)
     ap.add_argument("--stats")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
-    ap.add_argument("--steps", type=int, help="timed calls (last N dispatches)")
+    ap.add_argument("--steps", type=int, help="timed calls (the last N calls)")
     ap.add_argument("--copy-mib", type=int)
     ap.add_argument("--command")
     ap.add_argument("--bench-ms", type=float, default=None,
@@ -200,39 +247,44 @@ def main():
 
     import sys
     sys.path.insert(0, ROOT)
+    call = CALLS[args.call]
+    srcs = call["sources"]
+    shash = sources_hash(srcs)
+    kinds = f"`{call['kernel']}`" + (f" + `{call['merge']}`" if call["merge"] else "")
     if args.counters:
         from workloads import get_config
-        md = f"# {args.name} counters\n\nKernel `{args.kernel}`; sources hash " \
-             f"{sources_hash(KERNEL_SOURCES[args.kernel])}.\n\n" + \
-             counters_markdown(args.kernel, get_config(args.workload), args.counters, args.command)
+        md = f"# {args.name} counters\n\nKernel {kinds} (counters of the attention kernel); " \
+             f"sources hash {shash} ({', '.join(srcs)}).\n\n" + \
+             counters_markdown(call["kernel"], get_config(args.workload), args.counters, args.command)
         with open(os.path.join(ROOT, "profiles", f"{args.name}_counters.md"), "w") as f:
             f.write(md)
         print(md)
         return
     cfg, algo_read, algo_write = algorithmic_bytes(args.workload)
-    durs = kernel_durations_ns(args.stats, args.kernel)
-    timed = durs[-args.steps:]
+    calls = call_durations_ns(args.stats, args.call)
+    durs = [a + m for a, m in calls]
+    timed = calls[-args.steps:]
     avg_all = sum(durs) / len(durs) / 1e6
-    avg_timed = sum(timed) / len(timed) / 1e6
+    avg_timed = sum(a + m for a, m in timed) / len(timed) / 1e6
+    avg_attn = sum(a for a, _ in timed) / len(timed) / 1e6
+    avg_merge = sum(m for _, m in timed) / len(timed) / 1e6
 
     copy_bytes = args.copy_mib * (1 << 20)
-    cf = counter_per_dispatch(args.fetch, COPY_KERNEL, "FETCH_SIZE")
-    cw = counter_per_dispatch(args.write, COPY_KERNEL, "WRITE_SIZE")
+    cf = list(counter_per_dispatch(args.fetch, COPY_KERNEL, "FETCH_SIZE").values())
+    cw = list(counter_per_dispatch(args.write, COPY_KERNEL, "WRITE_SIZE").values())
     f_scale = copy_bytes / (sum(cf) / len(cf) * 1024.0)
     w_scale = copy_bytes / (sum(cw) / len(cw) * 1024.0)
-    kf = counter_per_dispatch(args.fetch, args.kernel, "FETCH_SIZE")
-    kw = counter_per_dispatch(args.write, args.kernel, "WRITE_SIZE")
+    kf = call_counter(args.fetch, args.call, "FETCH_SIZE")
+    kw = call_counter(args.write, args.call, "WRITE_SIZE")
     read_b = sum(kf) / len(kf) * 1024.0 * f_scale
     write_b = sum(kw) / len(kw) * 1024.0 * w_scale
     flops = cfg.flops
     tflops = flops / (avg_timed * 1e-3) / 1e12
-    srcs = KERNEL_SOURCES[args.kernel]
-    shash = sources_hash(srcs)
 
     md = f"""# {args.name}
 
-Kernel `{args.kernel}` on the workload {cfg.name}: B={cfg.B}, S={cfg.S}, H={cfg.H}, D={cfg.D}, {cfg.dtype}.
-Kernel sources hash {shash} ({', '.join(srcs)}).
+Call of {kinds} on the workload {cfg.name}: B={cfg.B}, S={cfg.S}, H={cfg.H}, D={cfg.D}, {cfg.dtype}.
+Sources hash {shash} ({', '.join(srcs)}).
 
 Commands (run from /tmp with TMPDIR=/tmp; R = repository root):
 
@@ -244,12 +296,14 @@ Commands (run from /tmp with TMPDIR=/tmp; R = repository root):
 
 | quantity | value |
 |---|---|
-| dispatches of the kernel | {len(durs)} |
-| average duration, all dispatches | {avg_all:.4f} ms |
-| average duration, last {args.steps} (the timed calls) | {avg_timed:.4f} ms |
-| min / max | {min(durs) / 1e6:.4f} / {max(durs) / 1e6:.4f} ms |
+| calls | {len(durs)} |
+| average duration per call, all calls | {avg_all:.4f} ms |
+| average duration per call, last {args.steps} (the timed calls) | {avg_timed:.4f} ms |
+| of which the attention kernel | {avg_attn:.4f} ms |
+| of which the merge kernel | {avg_merge:.4f} ms |
+| min / max per call | {min(durs) / 1e6:.4f} / {max(durs) / 1e6:.4f} ms |
 | bench.py ms per call in the same run | {args.bench_ms if args.bench_ms is not None else 'n/a'} |
-| attention flops per launch (4 B H S^2 D) | {flops:.4e} |
+| attention flops per call (4 B H S^2 D) | {flops:.4e} |
 | TFLOP/s at the timed average | {tflops:.1f} |
 
 ## Memory traffic (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)
@@ -258,7 +312,7 @@ Calibration: an elementwise fp32 copy of {copy_bytes} bytes read and written.
 FETCH_SIZE read {sum(cf) / len(cf):.0f} KiB for it (scale {f_scale:.4f}),
 WRITE_SIZE {sum(cw) / len(cw):.0f} KiB (scale {w_scale:.4f}).
 
-| per launch | counter (KiB) | scaled bytes | algorithmic bytes | ratio |
+| per call | counter (KiB) | scaled bytes | algorithmic bytes | ratio |
 |---|---|---|---|---|
 | read  | {sum(kf) / len(kf):.0f} | {read_b:.4e} | {algo_read:.4e} | {read_b / algo_read:.2f} |
 | write | {sum(kw) / len(kw):.0f} | {write_b:.4e} | {algo_write:.4e} | {write_b / algo_write:.2f} |
@@ -269,7 +323,7 @@ WRITE_SIZE {sum(cw) / len(cw):.0f} KiB (scale {w_scale:.4f}).
     with open(os.path.join(out_dir, f"{args.name}.md"), "w") as f:
         f.write(md)
     with open(os.path.join(out_dir, f"traffic_{args.name}.json"), "w") as f:
-        json.dump({"kernel": args.kernel, "sources_hash": shash,
+        json.dump({"call": args.call, "sources_hash": shash,
                    "hbm_bytes_per_launch": round(read_b + write_b),
                    "read_bytes": round(read_b), "write_bytes": round(write_b),
                    "algorithmic_bytes": algo_read + algo_write,
