@@ -43,6 +43,9 @@ Modules:
                 block) pairs, the reading of the pages' sparsified attention
                 (pinned: brute force, every block kept = dense, one kept block
                 = dense on that block's keys)
+  backward   -- gradients of q, k, v through the attention and the rotation,
+                and the softmax log-sum-exp (pinned: finite differences of the
+                forward, torch autograd at p = 0, softmax invariants)
 """
 
 from .joint_attention import (
@@ -53,6 +56,7 @@ from .joint_attention import (
     decode_inputs,
     rel_l2,
 )
+from .backward import attention_backward
 from .blocksparse import (
     attention_blocksparse,
     attention_blocksparse_inputs_rows,
@@ -64,6 +68,7 @@ from .rope4d import rope4d, rope_frequencies
 
 __all__ = [
     "attention",
+    "attention_backward",
     "attention_blocksparse",
     "attention_blocksparse_inputs_rows",
     "attention_blocksparse_rows",
