@@ -143,6 +143,52 @@ klein_status_t klein_attn_workspace_size(int B, int S, int H, int D, klein_dtype
                                          size_t* bytes);
 
 /*
+ * Training forward: klein_rope4d_attn_fwd for bfloat16 inputs that also
+ * writes the softmax statistic the backward needs,
+ *   lse[b][h][i] = log sum_j exp(<q'_i, k'_j> / sqrt(D))   (natural log),
+ * lse: DEVICE pointer, fp32 [B][H][S], 4-byte aligned, caller-owned.
+ * Training is the use the pages give for it: LoRA and DreamBooth-style
+ * training of the model ("Flux.3 Image Klein arrives in Diffusers with a
+ * modular architecture", sections "What happened" and "Key details").
+ */
+klein_status_t klein_rope4d_attn_fwd_lse(const void* q, const void* k, const void* v,
+                                         const int32_t* pos_thwl, void* out, float* lse,
+                                         int B, int S, int H, int D, klein_stream_t stream);
+
+/*
+ * Backward of the bf16 attention: given the forward's inputs, its output
+ * `out` and lse (klein_rope4d_attn_fwd_lse), and dout = dL/dout, writes the
+ * gradients of L with respect to the unrotated q, k and v:
+ *   dv_j = sum_i p_ij dout_i,  ds_ij = p_ij (<dout_i, v_j> - <dout_i, out_i>),
+ *   dq_i = R(pos_i)^T sum_j ds_ij k'_j / sqrt(D),
+ *   dk_j = R(pos_j)^T sum_i ds_ij q'_i / sqrt(D)
+ * with p_ij = exp(<q'_i, k'_j> / sqrt(D) - lse_i).  R^T turns each channel
+ * pair back by the same angle.
+ *   q, k, v, out, dout: [B][S][H][D] bfloat16; lse: fp32 [B][H][S];
+ *   dq, dk, dv: [B][S][H][D] bfloat16, written completely, must not alias
+ *   the inputs.  Accumulation is fp32; the recomputed scores use the same
+ *   fp16 rotated operands as the forward, P is rounded to bf16 and ds to
+ *   fp16 as MFMA operands.
+ *   workspace: DEVICE pointer, 256-byte aligned, caller-owned, at least
+ *   klein_attn_bwd_workspace_size bytes (the rotated q and k in fp16 and
+ *   <dout_i, out_i> in fp32); contents on entry do not matter.
+ * Two calls sharing one workspace on different streams race.  A smaller
+ * workspace is INVALID_ARG.
+ */
+klein_status_t klein_rope4d_attn_bwd(const void* q, const void* k, const void* v,
+                                     const int32_t* pos_thwl, const void* out, const void* dout,
+                                     const float* lse, void* dq, void* dk, void* dv,
+                                     int B, int S, int H, int D, void* workspace,
+                                     size_t workspace_bytes, klein_stream_t stream);
+
+/*
+ * Workspace bytes klein_rope4d_attn_bwd needs: 4 B S H D (rounded up to
+ * 256-byte multiples) + 4 B H S.  INVALID_ARG for a null `bytes` or sizes < 1,
+ * UNSUPPORTED for D not in {64, 128}.
+ */
+klein_status_t klein_attn_bwd_workspace_size(int B, int S, int H, int D, size_t* bytes);
+
+/*
  * Block-sparse variant: the same attention with each query attending only to
  * the keys of the kept blocks of its query block.  This is how this library
  * reads the sparsified attention of the Blackwell write-up ("How FLUX 3 Image

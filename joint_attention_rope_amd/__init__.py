@@ -21,7 +21,8 @@ __all__ = [
     "klein_version", "library_path", "KLEIN_DTYPE_BF16", "KLEIN_DTYPE_FP8_E4M3",
     "KLEIN_SPARSE_QBLOCK", "KLEIN_SPARSE_KBLOCK", "blocksparse_mask_shape",
     "klein_qkv_rope4d_proj", "klein_attn_fwd_prerotated", "klein_rope4d_attn_fwd_ws",
-    "klein_attn_workspace_size",
+    "klein_attn_workspace_size", "klein_rope4d_attn_fwd_lse", "klein_rope4d_attn_bwd",
+    "klein_attn_bwd_workspace_size",
 ]
 
 
@@ -165,6 +166,63 @@ def klein_rope4d_attn_fwd_ws(q, k, v, pos_thwl, out, workspace, dtype=None,
         B, S, H, D, int(dtype), dq, dk, dv, wp, wb, _stream(stream, q.device))
     _check(st, "klein_rope4d_attn_fwd_ws")
     return out
+
+
+def _same_bshd(ref, named, dtype=torch.bfloat16):
+    shape = _bshd(ref, "q")
+    for t, n in named:
+        if _bshd(t, n) != shape:
+            raise ValueError(f"{n} must have q's shape {shape}")
+        if t.dtype != dtype:
+            raise ValueError(f"{n} must be {dtype}")
+    return shape
+
+
+def _lse_tensor(lse, B, S, H):
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_cuda \
+            or not lse.is_contiguous():
+        raise ValueError(f"lse must be a contiguous float32 GPU tensor [B, H, S] = [{B}, {H}, {S}]")
+
+
+def klein_rope4d_attn_fwd_lse(q, k, v, pos_thwl, out, lse, stream=None):
+    """bf16 forward that also writes lse [B, H, S] (float32, natural log of the
+    softmax denominator) for klein_rope4d_attn_bwd."""
+    B, S, H, D = _same_bshd(q, ((q, "q"), (k, "k"), (v, "v"), (out, "out")))
+    _pos(pos_thwl, S)
+    _lse_tensor(lse, B, S, H)
+    st = _capi.lib().klein_rope4d_attn_fwd_lse(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), pos_thwl.data_ptr(), out.data_ptr(),
+        lse.data_ptr(), B, S, H, D, _stream(stream, q.device))
+    _check(st, "klein_rope4d_attn_fwd_lse")
+    return out, lse
+
+
+def klein_attn_bwd_workspace_size(B, S, H, D):
+    """Bytes of workspace klein_rope4d_attn_bwd needs."""
+    import ctypes
+    n = ctypes.c_size_t(0)
+    st = _capi.lib().klein_attn_bwd_workspace_size(int(B), int(S), int(H), int(D), ctypes.byref(n))
+    _check(st, "klein_attn_bwd_workspace_size")
+    return n.value
+
+
+def klein_rope4d_attn_bwd(q, k, v, pos_thwl, out, dout, lse, dq, dk, dv, workspace, stream=None):
+    """dq, dk, dv <- gradients of the RoPE-4D joint attention (bf16 [B, S, H, D])
+    given the forward's out and lse and dout = dL/dout.  workspace: a contiguous
+    GPU tensor of at least klein_attn_bwd_workspace_size(B, S, H, D) bytes."""
+    B, S, H, D = _same_bshd(q, ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout"),
+                                (dq, "dq"), (dk, "dk"), (dv, "dv")))
+    _pos(pos_thwl, S)
+    _lse_tensor(lse, B, S, H)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    st = _capi.lib().klein_rope4d_attn_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), pos_thwl.data_ptr(), out.data_ptr(),
+        dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, S, H, D,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream(stream, q.device))
+    _check(st, "klein_rope4d_attn_bwd")
+    return dq, dk, dv
 
 
 def blocksparse_mask_shape(B, S, H):

@@ -11,11 +11,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libklein_attn.so")
 SOURCES = ["api.cpp", "attn_fwd_bf16.hip", "attn_fwd_fp8.hip", "qkv_rope_proj.hip", "rope_apply.hip",
-           "split_schedule.hip"]
+           "split_schedule.hip", "attn_bwd.hip"]
 # Device kernels never see NaN inputs on purpose (a NaN in q/k/v propagates to
 # out either way), so min/max need no IEEE NaN canonicalisation.  The host
 # argument checks (std::isfinite on descales) keep full NaN semantics.
-KERNEL_FLAGS = {"attn_fwd_bf16.hip": ["-fno-honor-nans"], "attn_fwd_fp8.hip": ["-fno-honor-nans"]}
+KERNEL_FLAGS = {"attn_fwd_bf16.hip": ["-fno-honor-nans"], "attn_fwd_fp8.hip": ["-fno-honor-nans"],
+                "attn_bwd.hip": ["-fno-honor-nans"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

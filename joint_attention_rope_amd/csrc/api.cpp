@@ -121,6 +121,67 @@ klein_status_t klein_rope4d_attn_fwd_fp8(const void* q, const void* k, const voi
   }
 }
 
+klein_status_t klein_rope4d_attn_fwd_lse(const void* q, const void* k, const void* v,
+                                         const int32_t* pos_thwl, void* out, float* lse, int B,
+                                         int S, int H, int D, klein_stream_t stream) {
+  klein_status_t st = check_common(q, k, v, pos_thwl, out, B, S, H, D);
+  if (st != KLEIN_OK) return st;
+  if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u)) return KLEIN_ERR_INVALID_ARG;
+  if (klein::attn_fwd_bf16_grid(B, S, H) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
+  try {
+    LaunchArgs a = make_args(q, k, v, pos_thwl, out, B, S, H, D, stream);
+    a.lse = lse;
+    return map_hip(klein::launch_attn_fwd_bf16(a));
+  } catch (...) {
+    return KLEIN_ERR_LAUNCH;
+  }
+}
+
+klein_status_t klein_attn_bwd_workspace_size(int B, int S, int H, int D, size_t* bytes) {
+  if (!bytes) return KLEIN_ERR_INVALID_ARG;
+  if (B < 1 || S < 1 || H < 1) return KLEIN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return KLEIN_ERR_UNSUPPORTED;
+  *bytes = (size_t)klein::attn_bwd_workspace_bytes(B, S, H, D);
+  return KLEIN_OK;
+}
+
+klein_status_t klein_rope4d_attn_bwd(const void* q, const void* k, const void* v,
+                                     const int32_t* pos_thwl, const void* out, const void* dout,
+                                     const float* lse, void* dq, void* dk, void* dv, int B, int S,
+                                     int H, int D, void* workspace, size_t workspace_bytes,
+                                     klein_stream_t stream) {
+  klein_status_t st = check_common(q, k, v, pos_thwl, out, B, S, H, D);
+  if (st != KLEIN_OK) return st;
+  for (const void* p : {dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!p || !aligned16(p)) return KLEIN_ERR_INVALID_ARG;
+  if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u)) return KLEIN_ERR_INVALID_ARG;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return KLEIN_ERR_INVALID_ARG;
+  if (workspace_bytes < (size_t)klein::attn_bwd_workspace_bytes(B, S, H, D))
+    return KLEIN_ERR_INVALID_ARG;
+  const long long nb = (S + 127) / 128;
+  if ((long long)B * H * nb > kMaxGrid || (long long)B * S * H * D / 8 / 256 > kMaxGrid)
+    return KLEIN_ERR_UNSUPPORTED;
+  try {
+    const long long n = (long long)B * S * H * D;
+    const long long half = (n * 2 + 255) / 256 * 256;
+    char* ws = static_cast<char*>(workspace);
+    klein::BwdArgs a{};
+    a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
+    a.out = (const uint16_t*)out; a.dout = (const uint16_t*)dout; a.pos = pos_thwl; a.lse = lse;
+    a.dq = (uint16_t*)dq; a.dk = (uint16_t*)dk; a.dv = (uint16_t*)dv;
+    a.qr = reinterpret_cast<uint16_t*>(ws);
+    a.kr = reinterpret_cast<uint16_t*>(ws + half);
+    a.delta = reinterpret_cast<float*>(ws + 2 * half);
+    a.B = B; a.S = S; a.H = H; a.D = D;
+    a.qscale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+    a.freqs = make_freqs(D);
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    return map_hip(klein::launch_attn_bwd(a));
+  } catch (...) {
+    return KLEIN_ERR_LAUNCH;
+  }
+}
+
 klein_status_t klein_attn_workspace_size(int B, int S, int H, int D, klein_dtype_t dtype,
                                          size_t* bytes) {
   if (!bytes) return KLEIN_ERR_INVALID_ARG;
@@ -273,6 +334,6 @@ const char* klein_status_string(klein_status_t status) {
   return "unknown status";
 }
 
-int klein_version(void) { return 120; }
+int klein_version(void) { return 130; }
 
 }  // extern "C"

@@ -1,0 +1,455 @@
+// Backward of the RoPE-4D joint self-attention, bf16 in / bf16 gradients, for
+// gfx950.  Per batch entry and head, with q'_i = R_i q_i, k'_j = R_j k_j,
+// s_ij = <q'_i, k'_j> / sqrt(D), p = softmax_j(s), o = p v, and dout = dL/do:
+//
+//   dv_j = sum_i p_ij dout_i                 dp_ij = <dout_i, v_j>
+//   ds_ij = p_ij (dp_ij - delta_i),          delta_i = <dout_i, o_i>
+//   dq_i = R_i^T (1/sqrt(D)) sum_j ds_ij k'_j,  dk_j = R_j^T (1/sqrt(D)) sum_i ds_ij q'_i
+//
+// with p recomputed from the scores and the forward's log-sum-exp lse_i
+// (p_ij = exp(s_ij - lse_i)).  Three kernels, no atomics:
+//
+//   prep:  q'' = fp16(R q * log2(e)/sqrt(D)) and k' = fp16(R k), exactly the
+//          values the forward kernel forms on chip (so the recomputed scores
+//          match the ones lse was taken over), and delta_i;
+//   dk/dv: one workgroup per 128 keys (4 waves x 32 keys, the keys on the
+//          MFMA columns), streaming all queries in tiles of 64;
+//   dq:    one workgroup per 128 queries (4 waves x 32 queries), streaming all
+//          keys in tiles of 64.
+//
+// Each MFMA keeps the fast operand layout of the forward kernel: the tile
+// that streams through LDS is the A operand, read row-wise (rows of a
+// 32-row block stored in the permuted order of key_to_row, so that
+// accumulator register i of lane half g belongs to row 16g + i) or
+// transposed with ds_read_b64_tr_b16; the per-lane operand (this wave's keys
+// or queries) sits in registers.  The products whose k dimension is the
+// streamed rows take P or dS straight from the score accumulators as the B
+// operand, the k order matching the transposed reads.  The gradients leave
+// through the rotation's transpose (rotation by -p) in registers: in the
+// accumulators a lane holds the interleaved channel pairs (d, d+1) of one
+// token in adjacent registers.
+#include <cmath>
+
+#include "klein_device.hpp"
+#include "klein_launch.hpp"
+
+namespace klein {
+
+// one channel pair of an output gradient, rotated back: R(-phi) (x, y)
+__device__ __forceinline__ void rotate_back(float& x, float& y, int p, float whi, float wlo) {
+  const float fp = (float)p;
+  const float rev = __builtin_amdgcn_fractf(fp * whi) + fp * wlo;
+  const float s = __builtin_amdgcn_sinf(rev), c = __builtin_amdgcn_cosf(rev);
+  const float a = x, b = y;
+  x = a * c + b * s;
+  y = b * c - a * s;
+}
+
+// ---------------------------------------------------------------- prep
+// One thread per 16-byte chunk (8 channels) of a token row of one head.
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const int32_t* __restrict__ pos, const uint16_t* __restrict__ o,
+    const uint16_t* __restrict__ dout, uint16_t* __restrict__ qr, uint16_t* __restrict__ kr,
+    float* __restrict__ delta, int S, int H, long long nchunks, RopeFreqs fr, float qscale) {
+  constexpr int CPR = D / 8, DA = D / 4;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= nchunks) return;            // whole rows (CPR aligned lanes) leave together
+  const long long row = idx / CPR;       // (b S + s) H + h
+  const int c = (int)(idx % CPR);
+  const int h = (int)(row % H);
+  const long long bs = row / H;
+  const int s = (int)(bs % S), b = (int)(bs / S);
+  const size_t off = (size_t)idx * 8;
+  const int a = (8 * c) / DA, j0 = ((8 * c) % DA) / 2;
+  const int p = pos[4 * s + a];
+  *reinterpret_cast<u32x4_t*>(qr + off) =
+      rope_chunk<true>(*reinterpret_cast<const u32x4_t*>(q + off), p, &fr.hi[j0], &fr.lo[j0], qscale);
+  *reinterpret_cast<u32x4_t*>(kr + off) =
+      rope_chunk<true>(*reinterpret_cast<const u32x4_t*>(k + off), p, &fr.hi[j0], &fr.lo[j0], 1.0f);
+  const u32x4_t ov = *reinterpret_cast<const u32x4_t*>(o + off);
+  const u32x4_t dv = *reinterpret_cast<const u32x4_t*>(dout + off);
+  float sum = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) sum += bf16_lo(ov[w]) * bf16_lo(dv[w]) + bf16_hi(ov[w]) * bf16_hi(dv[w]);
+#pragma unroll
+  for (int m = 1; m < CPR; m <<= 1) sum += __shfl_xor(sum, m);
+  if (c == 0) delta[((size_t)b * H + h) * S + s] = sum;
+}
+
+// Per-lane base (16-bit elements) of the transposing reads of a 64-row tile
+// stored in key_to_row order within each 32-row block: lane L of a 16-lane
+// group points at row t = L/4 of its 4-row group (natural row 16g + t, stored
+// at 4g + t), channels 16 (group % 2) + 4 (L % 4); natural row + 4 is stored
+// 8 rows further, natural row + 8 16 rows further.  Two reads (+0, +8 rows)
+// hand lane i channel c0 + i of natural rows 16g + 8j + [0, 8) of the block.
+__device__ __forceinline__ int tr_base(int lane, int row_stride) {
+  return (4 * (lane >> 5) + ((lane & 15) >> 2)) * row_stride + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x8_t read_tr8(const uint16_t* p, int row_stride) {
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(p + 8 * row_stride));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ---------------------------------------------------------------- dk, dv
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
+    const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ pos, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    int S, int H, int nkb, RopeFreqs fr) {
+  constexpr int BK = 128;              // keys per workgroup (4 waves x 32)
+  constexpr int BQ = 64;               // queries per step
+  constexpr int NT = 256;
+  constexpr int KS = D / 16, MB = D / 32, DA = D / 4;
+  constexpr int ROW = D + 8;           // LDS row stride of the q'' and dout tiles (16-bit)
+  constexpr int CPR = D / 8;
+  constexpr int NCH = BQ * CPR / NT;   // 16-byte chunks per thread per tile, each tensor
+  static_assert(NCH >= 1 && BQ * CPR % NT == 0, "tile split");
+
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][BQ * ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t o_lds[2][BQ * ROW];
+  __shared__ __attribute__((aligned(16))) float st_lds[2][2 * BQ];   // lse2 (+inf past S), delta
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, lr = lane & 31;
+  const int work = xcd_remap(blockIdx.x, gridDim.x);
+  const int kb = work % nkb, bh = work / nkb;
+  const int h = bh % H, b = bh / H;
+  const size_t rs = (size_t)H * D;
+  const size_t base = (size_t)b * S * rs + (size_t)h * D;
+  const int rowb = (int)(rs * 2);
+  const int key = kb * BK + wave * 32 + lr;
+  const bool kval = key < S;
+
+  // this lane's key as the B operand of S = q'' k'^T and dP = dout v^T
+  f16x8_t kreg[KS];
+  bf16x8_t vreg[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const size_t e = base + (size_t)key * rs + 16 * ks + 8 * g;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    kreg[ks] = __builtin_bit_cast(f16x8_t, kval ? *reinterpret_cast<const u32x4_t*>(kr + e) : z);
+    vreg[ks] = __builtin_bit_cast(bf16x8_t, kval ? *reinterpret_cast<const u32x4_t*>(v + e) : z);
+  }
+  f32x16_t dva[MB], dka[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) dva[mb] = dka[mb] = (f32x16_t){};
+
+  const float* lse_bh = lse + (size_t)bh * S;
+  const float* dl_bh = delta + (size_t)bh * S;
+  u32x4_t sq[NCH], so[NCH];
+  float sl = 0.f, sd = 0.f;
+  auto load = [&](int qt) {
+    const int q0 = qt * BQ;
+    const int n = S - q0 < BQ ? S - q0 : BQ;
+    const __amdgpu_buffer_rsrc_t rq = uniform_rsrc(qr + base + (size_t)q0 * rs, n * rowb);
+    const __amdgpu_buffer_rsrc_t ro = uniform_rsrc(dout + base + (size_t)q0 * rs, n * rowb);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int j = tid + NT * i, row = j / CPR, ch = j % CPR;
+      const int off = row * rowb + 16 * ch;
+      sq[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+      so[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0));
+    }
+    if (tid < BQ) {
+      const int qi = q0 + tid;
+      sl = qi < S ? lse_bh[qi] * kLog2e : __builtin_huge_valf();
+      sd = qi < S ? dl_bh[qi] : 0.f;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int j = tid + NT * i, row = j / CPR, ch = j % CPR;
+      const int lrow = (row & ~31) + key_to_row(row & 31);
+      *reinterpret_cast<u32x4_t*>(&q_lds[buf][lrow * ROW + 8 * ch]) = sq[i];
+      *reinterpret_cast<u32x4_t*>(&o_lds[buf][lrow * ROW + 8 * ch]) = so[i];
+    }
+    if (tid < BQ) {
+      st_lds[buf][tid] = sl;
+      st_lds[buf][BQ + tid] = sd;
+    }
+  };
+
+  const int trb = tr_base(lane, ROW);
+  const int nqt = (S + BQ - 1) / BQ;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int qt = 0; qt < nqt; ++qt) {
+    const int buf = qt & 1;
+    if (qt + 1 < nqt) load(qt + 1);
+    f32x16_t sc[2], dp[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      // initial values -lse2 and -delta of rows 32 blk + 16 g + i
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&st_lds[buf][32 * blk + 16 * g + 4 * i4]);
+        const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&st_lds[buf][BQ + 32 * blk + 16 * g + 4 * i4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sc[blk][4 * i4 + e] = -l4[e];
+          dp[blk][4 * i4 + e] = -d4[e];
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = (32 * blk + lr) * ROW + 16 * ks + 8 * g;
+        const f16x8_t aq = *reinterpret_cast<const f16x8_t*>(&q_lds[buf][off]);
+        sc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aq, kreg[ks], sc[blk], 0, 0, 0);
+        const bf16x8_t ao = *reinterpret_cast<const bf16x8_t*>(&o_lds[buf][off]);
+        dp[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vreg[ks], dp[blk], 0, 0, 0);
+      }
+    }
+    // P = 2^(s2 - lse2) (bf16, for dV) and dS = P (dP - delta) (fp16, for dK)
+    uint32_t pw[2][8], sw[2][8];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const float p0 = __builtin_amdgcn_exp2f(sc[blk][2 * w]);
+        const float p1 = __builtin_amdgcn_exp2f(sc[blk][2 * w + 1]);
+        pw[blk][w] = pack_bf16x2(p0, p1);
+        sw[blk][w] = pack_f16x2(p0 * dp[blk][2 * w], p1 * dp[blk][2 * w + 1]);
+      }
+    // dV^T += dout^T P, dK'^T += q''^T dS: k = the 64 queries of the tile, in
+    // steps (blk, j) of 16: k slot (g, e) is query 32 blk + 16 g + 8 j + e
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8_t pb = __builtin_bit_cast(
+            bf16x8_t, (u32x4_t){pw[blk][4 * j], pw[blk][4 * j + 1], pw[blk][4 * j + 2], pw[blk][4 * j + 3]});
+        const f16x8_t sb = __builtin_bit_cast(
+            f16x8_t, (u32x4_t){sw[blk][4 * j], sw[blk][4 * j + 1], sw[blk][4 * j + 2], sw[blk][4 * j + 3]});
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int off = trb + (32 * blk + 16 * j) * ROW + 32 * mb;
+          const bf16x8_t ot = __builtin_bit_cast(bf16x8_t, read_tr8(&o_lds[buf][off], ROW));
+          dva[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot, pb, dva[mb], 0, 0, 0);
+          const f16x8_t qt8 = __builtin_bit_cast(f16x8_t, read_tr8(&q_lds[buf][off], ROW));
+          dka[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qt8, sb, dka[mb], 0, 0, 0);
+        }
+      }
+    if (qt + 1 < nqt) store(buf ^ 1);   // that buffer was last read before the previous barrier
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane = key, register i of block mb = channel 32 mb + 8 (i/4) + 4 g + i%4
+  if (!kval) return;
+  const size_t row = base + (size_t)key * rs;
+  const float kscale = 1.0f / kLog2e;    // q'' carries log2(e)/sqrt(D); dk' needs 1/sqrt(D)
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = 32 * mb + 8 * i4 + 4 * g;
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = dka[mb][4 * i4 + e] * kscale;
+      const int a = d / DA, jp = (d % DA) / 2;
+      const int p = pos[4 * key + a];
+      rotate_back(y[0], y[1], p, fr.hi[jp], fr.lo[jp]);
+      rotate_back(y[2], y[3], p, fr.hi[jp + 1], fr.lo[jp + 1]);
+      uint2 w;
+      w.x = pack_bf16x2(y[0], y[1]);
+      w.y = pack_bf16x2(y[2], y[3]);
+      *reinterpret_cast<uint2*>(dk + row + d) = w;
+      w.x = pack_bf16x2(dva[mb][4 * i4], dva[mb][4 * i4 + 1]);
+      w.y = pack_bf16x2(dva[mb][4 * i4 + 2], dva[mb][4 * i4 + 3]);
+      *reinterpret_cast<uint2*>(dv + row + d) = w;
+    }
+}
+
+// ---------------------------------------------------------------- dq
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
+    const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ pos, uint16_t* __restrict__ dq, int S, int H, int nqb,
+    RopeFreqs fr, float dqscale) {
+  constexpr int BQ = 128;              // queries per workgroup (4 waves x 32)
+  constexpr int BK = 64;               // keys per step
+  constexpr int NT = 256;
+  constexpr int KS = D / 16, MB = D / 32, DA = D / 4;
+  constexpr int ROW = D + 8;
+  constexpr int CPR = D / 8;
+  constexpr int NCH = BK * CPR / NT;
+  static_assert(NCH >= 1 && BK * CPR % NT == 0, "tile split");
+
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BK * ROW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, lr = lane & 31;
+  const int work = xcd_remap(blockIdx.x, gridDim.x);
+  const int qb = work % nqb, bh = work / nqb;
+  const int h = bh % H, b = bh / H;
+  const size_t rs = (size_t)H * D;
+  const size_t base = (size_t)b * S * rs + (size_t)h * D;
+  const int rowb = (int)(rs * 2);
+  const int query = qb * BQ + wave * 32 + lr;
+  const bool qval = query < S;
+
+  // this lane's query as the B operand of S^T = k' q''^T and dP^T = v dout^T
+  f16x8_t qreg[KS];
+  bf16x8_t oreg[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const size_t e = base + (size_t)query * rs + 16 * ks + 8 * g;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    qreg[ks] = __builtin_bit_cast(f16x8_t, qval ? *reinterpret_cast<const u32x4_t*>(qr + e) : z);
+    oreg[ks] = __builtin_bit_cast(bf16x8_t, qval ? *reinterpret_cast<const u32x4_t*>(dout + e) : z);
+  }
+  const float nlse2 = qval ? -lse[(size_t)bh * S + query] * kLog2e : 0.f;
+  const float ndl = qval ? -delta[(size_t)bh * S + query] : 0.f;
+  f32x16_t dqa[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) dqa[mb] = (f32x16_t){};
+
+  u32x4_t sk[NCH], sv[NCH];
+  auto load = [&](int kt) {
+    const int k0 = kt * BK;
+    const int n = S - k0 < BK ? S - k0 : BK;
+    const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(kr + base + (size_t)k0 * rs, n * rowb);
+    const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(v + base + (size_t)k0 * rs, n * rowb);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int j = tid + NT * i, row = j / CPR, ch = j % CPR;
+      const int off = row * rowb + 16 * ch;
+      sk[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+      sv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int j = tid + NT * i, row = j / CPR, ch = j % CPR;
+      const int lrow = (row & ~31) + key_to_row(row & 31);
+      *reinterpret_cast<u32x4_t*>(&k_lds[buf][lrow * ROW + 8 * ch]) = sk[i];
+      *reinterpret_cast<u32x4_t*>(&v_lds[buf][lrow * ROW + 8 * ch]) = sv[i];
+    }
+  };
+
+  const int trb = tr_base(lane, ROW);
+  const int nkt = (S + BK - 1) / BK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nkt) load(kt + 1);
+    f32x16_t sc[2], dp[2];
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sc[kbk][i] = nlse2;
+        dp[kbk][i] = ndl;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = (32 * kbk + lr) * ROW + 16 * ks + 8 * g;
+        const f16x8_t ak = *reinterpret_cast<const f16x8_t*>(&k_lds[buf][off]);
+        sc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, qreg[ks], sc[kbk], 0, 0, 0);
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&v_lds[buf][off]);
+        dp[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, oreg[ks], dp[kbk], 0, 0, 0);
+      }
+    }
+    // keys past S (last tile only): p = 0 (their k' rows read as zeros, but
+    // 2^(-lse2) alone could overflow)
+    if (kt * BK + BK > S) {
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kt * BK + 32 * kbk + 16 * g + i >= S) sc[kbk][i] = kNegInf;
+    }
+    uint32_t sw[2][8];
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const float p0 = __builtin_amdgcn_exp2f(sc[kbk][2 * w]);
+        const float p1 = __builtin_amdgcn_exp2f(sc[kbk][2 * w + 1]);
+        sw[kbk][w] = pack_f16x2(p0 * dp[kbk][2 * w], p1 * dp[kbk][2 * w + 1]);
+      }
+    // dQ'^T += k'^T dS^T: k = the 64 keys of the tile, slot (g, e) of step
+    // (kbk, j) is key 32 kbk + 16 g + 8 j + e
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const f16x8_t sb = __builtin_bit_cast(
+            f16x8_t, (u32x4_t){sw[kbk][4 * j], sw[kbk][4 * j + 1], sw[kbk][4 * j + 2], sw[kbk][4 * j + 3]});
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int off = trb + (32 * kbk + 16 * j) * ROW + 32 * mb;
+          const f16x8_t kt8 = __builtin_bit_cast(f16x8_t, read_tr8(&k_lds[buf][off], ROW));
+          dqa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kt8, sb, dqa[mb], 0, 0, 0);
+        }
+      }
+    if (kt + 1 < nkt) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!qval) return;
+  const size_t row = base + (size_t)query * rs;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = 32 * mb + 8 * i4 + 4 * g;
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = dqa[mb][4 * i4 + e] * dqscale;
+      const int a = d / DA, jp = (d % DA) / 2;
+      const int p = pos[4 * query + a];
+      rotate_back(y[0], y[1], p, fr.hi[jp], fr.lo[jp]);
+      rotate_back(y[2], y[3], p, fr.hi[jp + 1], fr.lo[jp + 1]);
+      uint2 w;
+      w.x = pack_bf16x2(y[0], y[1]);
+      w.y = pack_bf16x2(y[2], y[3]);
+      *reinterpret_cast<uint2*>(dq + row + d) = w;
+    }
+}
+
+template <int D>
+static hipError_t launch_bwd(const BwdArgs& a) {
+  const long long nchunks = (long long)a.B * a.S * a.H * (D / 8);
+  hipLaunchKernelGGL(attn_bwd_prep_kernel<D>, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0,
+                     a.stream, a.q, a.k, a.pos, a.out, a.dout, a.qr, a.kr, a.delta, a.S, a.H,
+                     nchunks, a.freqs, a.qscale_log2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nb = (a.S + 127) / 128;
+  const dim3 grid((unsigned)(a.B * a.H * nb));
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, grid, dim3(256), 0, a.stream, a.qr, a.kr, a.v,
+                     a.dout, a.lse, a.delta, a.pos, a.dk, a.dv, a.S, a.H, nb, a.freqs);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, grid, dim3(256), 0, a.stream, a.qr, a.kr, a.v, a.dout,
+                     a.lse, a.delta, a.pos, a.dq, a.S, a.H, nb, a.freqs,
+                     (float)(1.0 / std::sqrt((double)D)));
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd(const BwdArgs& a) {
+  return a.D == 128 ? launch_bwd<128>(a) : launch_bwd<64>(a);
+}
+
+long long attn_bwd_workspace_bytes(int B, int S, int H, int D) {
+  const long long n = (long long)B * S * H * D;
+  return 2 * ((n * 2 + 255) / 256 * 256) + ((long long)B * H * S * 4 + 255) / 256 * 256;
+}
+
+}  // namespace klein

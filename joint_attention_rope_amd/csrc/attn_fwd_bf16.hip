@@ -61,13 +61,6 @@ namespace klein {
 
 constexpr int kTabN = 256;        // positions covered by the cos/sin table
 
-// LDS row of key kk (0..31) of a 32-key block: the MFMA output row r holds
-// key 16*((r/4)&1) + 4*(r/8) + (r%4); this is the inverse map.
-__device__ __forceinline__ int key_to_row(int kk) {
-  const int g = kk >> 4, i = kk & 15;
-  return ((i >> 2) << 3) + (g << 2) + (i & 3);
-}
-
 // SPARSE: block-sparse variant; bmask holds one byte per (batch, head, query
 // tile of 256, key tile of 64), nonzero = compute, and only the kept key
 // tiles of a query tile stream through the pipeline (in ascending order, so
@@ -82,7 +75,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ pos,
     uint16_t* __restrict__ out, int S, int H, int nqt, RopeFreqs fr, float qscale,
-    const uint8_t* __restrict__ bmask, SplitArgs sp) {
+    const uint8_t* __restrict__ bmask, SplitArgs sp, float* __restrict__ lse) {
   constexpr int BM = 256;              // queries per workgroup (8 waves x 32)
   constexpr int BN = 64;               // keys per tile
   constexpr int NT = 512;              // threads
@@ -531,6 +524,10 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     }
   if (qrow < S) {
     const float inv = 1.0f / lsum;
+    // the softmax log-sum-exp (natural log of sum_j exp(s_ij)) for a backward
+    // pass: the scores are kept in log2 units relative to m_run
+    if (lse != nullptr && g == 0)
+      lse[((size_t)b * H + h) * S + qrow] = (m_run + __builtin_amdgcn_logf(lsum)) * kLn2;
     uint16_t* orow = out + base + (size_t)qrow * rs;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -553,7 +550,7 @@ static hipError_t launch_bf16(const LaunchArgs& a) {
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, SPARSE, PREROT, SPLIT>), dim3((unsigned)n), dim3(512),
                      0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      a.pos, (uint16_t*)a.out, a.S, a.H, nqt, a.freqs, a.qscale_log2, a.bmask,
-                     a.split);
+                     a.split, a.lse);
   return hipGetLastError();
 }
 
@@ -562,7 +559,7 @@ hipError_t launch_attn_fwd_bf16(const LaunchArgs& a) {
   if (a.split.n_sk > 0) {
     const hipError_t e = a.D == 128 ? launch_bf16<128, false, false, true>(a)
                                     : launch_bf16<64, false, false, true>(a);
-    return e != hipSuccess ? e : launch_split_merge(a, 1.0f);
+    return e != hipSuccess ? e : launch_split_merge(a, 1.0f, a.lse);
   }
   return a.D == 128 ? launch_bf16<128, false>(a) : launch_bf16<64, false>(a);
 }

@@ -553,7 +553,7 @@ hipError_t launch_attn_fwd_fp8(const LaunchArgs& a) {
   if (a.bmask) return a.D == 128 ? launch_fp8<128, true>(a) : launch_fp8<64, true>(a);
   if (a.split.n_sk > 0) {
     const hipError_t e = a.D == 128 ? launch_fp8<128, false, true>(a) : launch_fp8<64, false, true>(a);
-    return e != hipSuccess ? e : launch_split_merge(a, a.descale[2]);
+    return e != hipSuccess ? e : launch_split_merge(a, a.descale[2], nullptr);
   }
   return a.D == 128 ? launch_fp8<128, false>(a) : launch_fp8<64, false>(a);
 }

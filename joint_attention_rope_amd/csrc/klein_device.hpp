@@ -29,6 +29,8 @@ struct RopeFreqs {
 };
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kLog2e = 1.44269504088896341f;
 
 // Fourth word of a raw buffer descriptor on gfx9-family GPUs (32-bit data
 // format, no swizzle): loads past the descriptor's size return zero.
@@ -83,6 +85,15 @@ __device__ __forceinline__ u32x4_t rope_chunk(u32x4_t x, int p, const float* whi
     y[jj] = F16 ? pack_f16x2(u, w) : pack_bf16x2(u, w);
   }
   return y;
+}
+
+// LDS row of element kk (0..31) of a 32-row block such that, after a 32x32
+// MFMA whose A operand rows are read in LDS row order, accumulator register i
+// of lane half g holds element 16g + i: the MFMA output row r holds element
+// 16*((r/4)&1) + 4*(r/8) + (r%4), and this is the inverse map.
+__device__ __forceinline__ int key_to_row(int kk) {
+  const int g = kk >> 4, i = kk & 15;
+  return ((i >> 2) << 3) + (g << 2) + (i & 3);
 }
 
 // Workgroups are handed to the 8 XCDs round robin (block i -> XCD i % 8), and

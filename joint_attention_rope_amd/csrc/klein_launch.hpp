@@ -24,6 +24,9 @@ struct LaunchArgs {
   const uint8_t* bmask = nullptr;
   // split-KV schedule (n_sk > 0) over the caller's workspace, or none
   SplitArgs split{};
+  // bf16 dense/split paths: also write the softmax log-sum-exp, fp32
+  // [B][H][S], natural log (null: not written)
+  float* lse = nullptr;
 };
 
 // Split-KV cut of a dense call for a GPU of n_cu compute units (n_sk == 0:
@@ -35,7 +38,7 @@ struct SplitPlan {
 SplitPlan plan_split(int B, int S, int H, int D, int n_cu);
 // merges the split items' slots into their output rows (after the attention
 // kernel, on the same stream); o_scale multiplies O / l (v's descale for fp8)
-hipError_t launch_split_merge(const LaunchArgs& a, float o_scale);
+hipError_t launch_split_merge(const LaunchArgs& a, float o_scale, float* lse);
 
 hipError_t launch_attn_fwd_bf16(const LaunchArgs& a);
 hipError_t launch_attn_fwd_prerotated(const LaunchArgs& a);
@@ -43,6 +46,31 @@ long long attn_fwd_bf16_grid(int B, int S, int H);
 hipError_t launch_attn_fwd_fp8(const LaunchArgs& a);
 long long attn_fwd_fp8_grid(int B, int S, int H);
 hipError_t launch_rope4d_apply(const LaunchArgs& a);
+
+// Attention backward (bf16): q, k, v, out, dout [B][S][H][D] bf16, lse fp32
+// [B][H][S] (natural log) -> dq, dk, dv bf16; qr, kr (fp16 [B][S][H][D]) and
+// delta (fp32 [B][H][S]) in the caller's workspace.
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* out;
+  const uint16_t* dout;
+  const int32_t* pos;
+  const float* lse;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  uint16_t* qr;
+  uint16_t* kr;
+  float* delta;
+  int B, S, H, D;
+  float qscale_log2;
+  RopeFreqs freqs;
+  hipStream_t stream;
+};
+hipError_t launch_attn_bwd(const BwdArgs& a);
+long long attn_bwd_workspace_bytes(int B, int S, int H, int D);
 
 // QKV projection with the RoPE-4D epilogue: x [B S][C] bf16, w [3 H D][C]
 // bf16, bias [3 H D] bf16 or null -> q', k' fp16 and v bf16, [B][S][H][D].

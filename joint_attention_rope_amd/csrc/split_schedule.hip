@@ -58,7 +58,8 @@ SplitPlan plan_split(int B, int S, int H, int D, int n_cu) {
 template <int D>
 __global__ __launch_bounds__(256) void split_merge_kernel(const float* __restrict__ part,
                                                           uint16_t* __restrict__ out, int S, int H,
-                                                          int nqt, SplitArgs sp, float o_scale) {
+                                                          int nqt, SplitArgs sp, float o_scale,
+                                                          float* __restrict__ lse) {
   constexpr int MB = D / 32;
   constexpr long long SLOT = split_slot_floats(D);
   const int tid = threadIdx.x;
@@ -88,6 +89,8 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const float* __restric
     }
     if (row < S) {
       const float inv = o_scale / L;
+      // the log-sum-exp of the row (natural log), once per row (mb = i4 = 0, first lane half)
+      if (lse != nullptr && e < 32) lse[((size_t)b * H + h) * S + row] = (M + __builtin_amdgcn_logf(L)) * kLn2;
       uint2 v;
       v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
       v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
@@ -96,15 +99,15 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const float* __restric
   }
 }
 
-hipError_t launch_split_merge(const LaunchArgs& a, float o_scale) {
+hipError_t launch_split_merge(const LaunchArgs& a, float o_scale, float* lse) {
   const int nqt = (a.S + 255) / 256;
   const dim3 grid((unsigned)a.split.n_rem * 8);
   if (a.D == 128)
     hipLaunchKernelGGL(split_merge_kernel<128>, grid, dim3(256), 0, a.stream, a.split.part,
-                       (uint16_t*)a.out, a.S, a.H, nqt, a.split, o_scale);
+                       (uint16_t*)a.out, a.S, a.H, nqt, a.split, o_scale, lse);
   else
     hipLaunchKernelGGL(split_merge_kernel<64>, grid, dim3(256), 0, a.stream, a.split.part,
-                       (uint16_t*)a.out, a.S, a.H, nqt, a.split, o_scale);
+                       (uint16_t*)a.out, a.S, a.H, nqt, a.split, o_scale, lse);
   return hipGetLastError();
 }
 

@@ -23,7 +23,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "klein_rope4d_attn_fwd", "klein_rope4d_attn_fwd_fp8", "klein_rope4d_attn_fwd_blocksparse",
         "klein_qkv_rope4d_proj", "klein_attn_fwd_prerotated", "klein_rope4d_attn_fwd_ws",
-        "klein_attn_workspace_size", "klein_rope4d_apply", "klein_status_string",
+        "klein_attn_workspace_size", "klein_rope4d_attn_fwd_lse", "klein_rope4d_attn_bwd",
+        "klein_attn_bwd_workspace_size", "klein_rope4d_apply", "klein_status_string",
         "klein_version"])
 
 
@@ -138,3 +139,27 @@ def test_workspace_size_checks():
     assert lib.klein_attn_workspace_size(1, 4096, 1, 128, 2, ctypes.byref(n)) == \
         _capi.KLEIN_ERR_INVALID_ARG
     assert n.value == 7                   # untouched on error
+
+
+def test_backward_argument_checks():
+    lib = _capi.lib()
+    I, U = _capi.KLEIN_ERR_INVALID_ARG, _capi.KLEIN_ERR_UNSUPPORTED
+    n = ctypes.c_size_t(0)
+    assert lib.klein_attn_bwd_workspace_size(1, 100, 2, 64, ctypes.byref(n)) == _capi.KLEIN_OK
+    need = n.value
+    assert need >= 4 * 100 * 2 * 64 + 4 * 2 * 100
+    assert lib.klein_attn_bwd_workspace_size(1, 100, 2, 96, ctypes.byref(n)) == U
+    assert lib.klein_attn_bwd_workspace_size(0, 100, 2, 64, ctypes.byref(n)) == I
+    assert lib.klein_attn_bwd_workspace_size(1, 100, 2, 64, None) == I
+    # q, k, v, pos, out, dout, lse, dq, dk, dv, B, S, H, D, workspace, bytes
+    ok = [FAKE] * 10 + [1, 100, 2, 64, FAKE, need]
+    cases = [(5, 0, I), (6, 0, I), (6, FAKE + 2, I), (7, FAKE + 8, I), (14, 0, I),
+             (14, FAKE + 16, I), (15, need - 1, I), (13, 80, U), (10, 0, I)]
+    for i, val, st in cases:
+        args = list(ok)
+        args[i] = val
+        assert lib.klein_rope4d_attn_bwd(*args, None) == st, (i, val)
+    assert lib.klein_rope4d_attn_fwd_lse(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 8, 1, 64, None) == I
+    assert lib.klein_rope4d_attn_fwd_lse(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, 1, 8, 1, 64,
+                                         None) == I
+    assert lib.klein_rope4d_attn_fwd_lse(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 80, None) == U

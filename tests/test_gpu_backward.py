@@ -1,0 +1,115 @@
+"""GPU parity of the attention backward (klein_rope4d_attn_bwd) and of the
+training forward's log-sum-exp (klein_rope4d_attn_fwd_lse) against the oracle.
+
+Tolerances.  Each gradient is an fp32 sum rounded once to bf16 (relative
+error <= 2^-9); inside, P is rounded to bf16 for dv and ds = p (dp - delta) to
+fp16 for dq and dk, and the inputs of the backward (the forward's bf16 out and
+fp32 lse) carry the forward's own error.  Measured on seeded N(0, 1) inputs
+and on the 1024x1024 workload the relative L2 errors are 1.7e-3 (dq, dk) and
+2.0-2.4e-3 (dv); the bound is rel-L2 <= 6e-3 per gradient tensor.  The log-sum-exp is a p-weighted mean of score errors: the scores
+come from fp16 rotated q and k (relative 2^-11 each), |q'| |k'| / sqrt(D) ~
+sqrt(D) for N(0, 1) inputs, so score errors reach ~1e-3; the bound is 4e-3
+absolute.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import joint_attention_rope_amd as kl
+from helpers import bf16_tensor_to_f64, errors, random_inputs, to_device
+from workloads import bf16_bits_from_f32, get_config, make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+GRAD_REL_L2 = 6e-3
+LSE_ABS = 4e-3
+
+
+def bf16_from_f64(x):
+    bits = bf16_bits_from_f32(np.asarray(x, dtype=np.float32))
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV), \
+        (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def run_fwd_bwd(inp, dout_seed):
+    """GPU forward (out, lse) and backward on inp; returns the device results
+    and the float64 values of the inputs and of dout."""
+    import oracle
+    q, k, v, pos = to_device(inp)
+    B, S, H, D = q.shape
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(B, H, S, dtype=torch.float32, device=DEV)
+    kl.klein_rope4d_attn_fwd_lse(q, k, v, pos, out, lse)
+    rng = np.random.default_rng(dout_seed)
+    dout, dout64 = bf16_from_f64(rng.standard_normal(q.shape))
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(kl.klein_attn_bwd_workspace_size(B, S, H, D), dtype=torch.uint8, device=DEV)
+    kl.klein_rope4d_attn_bwd(q, k, v, pos, out, dout, lse, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    q64, k64, v64 = oracle.decode_inputs(inp)
+    return (out, lse, dq, dk, dv), (q64, k64, v64, dout64)
+
+
+def check_grads(gpu, ref, what):
+    worst = {}
+    for t, r, name in zip(gpu, ref, ("dq", "dk", "dv")):
+        got = bf16_tensor_to_f64(t)
+        assert np.isfinite(got).all(), f"{what} {name}: non-finite"
+        max_abs, rel = errors(got, r)
+        worst[name] = rel
+        print(f"{what} {name}: max_abs {max_abs:.3e} rel_l2 {rel:.3e}", flush=True)
+    for name, rel in worst.items():
+        assert rel <= GRAD_REL_L2, f"{what} {name}: rel_l2 {rel:.3e} > {GRAD_REL_L2}"
+
+
+@pytest.mark.parametrize("B,S,H,D", [
+    (1, 300, 2, 64),      # ragged query and key tiles
+    (2, 577, 3, 128),
+    (1, 65, 1, 64),       # one partial key block, two query tiles
+    (1, 1000, 2, 128),
+])
+def test_backward_matches_oracle(B, S, H, D):
+    import oracle
+    inp = random_inputs(B, S, H, D, seed=S + 7 * D)
+    (out, lse, dq, dk, dv), (q, k, v, dout) = run_fwd_bwd(inp, dout_seed=S)
+    rq, rk, rv, rlse = oracle.attention_backward(q, k, v, inp.pos, dout)
+    lse_err = float(np.max(np.abs(lse.cpu().numpy() - rlse)))
+    print(f"B={B} S={S} H={H} D={D} lse max_abs {lse_err:.3e}", flush=True)
+    check_grads((dq, dk, dv), (rq, rk, rv), f"B={B} S={S} H={H} D={D}")
+    assert lse_err <= LSE_ABS
+
+
+def test_forward_with_lse_equals_forward():
+    inp = random_inputs(2, 700, 3, 128, seed=41)
+    q, k, v, pos = to_device(inp)
+    a = torch.empty(q.shape, dtype=torch.bfloat16, device=DEV)
+    b = torch.empty_like(a)
+    lse = torch.empty(2, 3, 700, dtype=torch.float32, device=DEV)
+    kl.klein_rope4d_attn_fwd(q, k, v, pos, a)
+    kl.klein_rope4d_attn_fwd_lse(q, k, v, pos, b, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_workload_2_sampled_heads():
+    # the 1024x1024 text-to-image shape (S = 4608, H = 24, scaled inputs with
+    # x8 outlier key channels); the oracle runs two whole heads
+    import oracle
+    cfg = get_config(2)
+    inp = make_inputs(cfg)
+    (out, lse, dq, dk, dv), (q, k, v, dout) = run_fwd_bwd(inp, dout_seed=2)
+    for h in (0, 17):
+        rq, rk, rv, rlse = oracle.attention_backward(q[:, :, h:h + 1], k[:, :, h:h + 1],
+                                                     v[:, :, h:h + 1], inp.pos, dout[:, :, h:h + 1])
+        assert np.max(np.abs(lse[:, h:h + 1].cpu().numpy() - rlse)) <= LSE_ABS
+        check_grads((dq[:, :, h:h + 1], dk[:, :, h:h + 1], dv[:, :, h:h + 1]), (rq, rk, rv),
+                    f"workload 2 head {h}")
+
+
+def test_repeat_bitwise_identical():
+    inp = random_inputs(1, 900, 2, 128, seed=43)
+    a, _ = run_fwd_bwd(inp, dout_seed=5)
+    b, _ = run_fwd_bwd(inp, dout_seed=5)
+    for x, y in zip(a[2:], b[2:]):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
