@@ -73,6 +73,22 @@ def time_gpu(fn, steps, warmup, torch):
     return start.elapsed_time(stop) / steps          # ms per launch
 
 
+def time_gpu_calls(fn, steps, warmup, torch):
+    """Like time_gpu, with an event between every timed call: returns the mean
+    ms per call over the whole timed region and the per-call durations."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[steps]) / steps, per
+
+
 def workspace(kl, torch, cfg, dev):
     """The split-KV workspace of a workload's shape (None if it needs none)."""
     dt = kl.KLEIN_DTYPE_FP8_E4M3 if cfg.dtype == "fp8" else kl.KLEIN_DTYPE_BF16
@@ -153,8 +169,8 @@ def main():
     # inputs resident) before timing; the entry point without a workspace is
     # timed after it for reference
     ws = workspace(kl, torch, cfg, dev)
-    ms = time_gpu(lambda: kl.klein_rope4d_attn_fwd_ws(q, k, v, pos, out, ws), args.steps,
-                  args.warmup, torch)
+    ms, per_call = time_gpu_calls(lambda: kl.klein_rope4d_attn_fwd_ws(q, k, v, pos, out, ws),
+                                  args.steps, args.warmup, torch)
     dense_ms = time_gpu(lambda: kl.klein_rope4d_attn_fwd(q, k, v, pos, out),
                         max(3, args.steps // 4), 2, torch)
     tflops = cfg.flops / (ms * 1e-3) / 1e12
@@ -182,6 +198,8 @@ def main():
         "entry_point": "klein_rope4d_attn_fwd_ws (split-KV schedule, workspace "
                        f"{0 if ws is None else ws.numel() / 1e6:.1f} MB)",
         "no_workspace_entry_ms": round(dense_ms, 4),
+        "ms_per_call_median": round(sorted(per_call)[len(per_call) // 2], 4),
+        "ms_per_call_min": round(min(per_call), 4),
     }
     del q, k, v, out, ws
     if not args.no_fp8:
@@ -323,6 +341,62 @@ def main():
             "peak": PEAK_BF16, "frac": round(c.flops / (ams * 1e-3) / 1e12 / PEAK_BF16, 4),
             "fused_rotation_ms": round(ms, 4)})
         del xx, ww, bb, qo, ko, vo, oo, yy
+    if args.extra:
+        # the 1024x1024 workloads, warm (back to back) and cold (a 1 GiB buffer
+        # written before each call, so no input is left in the caches)
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        for cid in (2, 3):
+            c = get_config(cid)
+            xi = make_inputs(c)
+            xq, xk, xv, xp = to_device(xi, dev)
+            xo = torch.empty(xq.shape, dtype=torch.bfloat16, device=dev)
+            xw = workspace(kl, torch, c, dev)
+            call = lambda: kl.klein_rope4d_attn_fwd_ws(xq, xk, xv, xp, xo, xw)
+            wms, wper = time_gpu_calls(call, 50, 100, torch)
+            cold = []
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for _ in range(30):
+                flush.fill_(1.0)
+                e0.record()
+                call()
+                e1.record()
+                torch.cuda.synchronize()
+                cold.append(e0.elapsed_time(e1))
+            med = lambda xs: sorted(xs)[len(xs) // 2]
+            rec["extra"].append({
+                "workload": f"{c.name}: B={c.B}, S={c.S}, H={c.H}, D={c.D}, bf16 (split-KV entry)",
+                "warm_ms_median": round(med(wper), 4), "warm_ms_min": round(min(wper), 4),
+                "cold_ms_median": round(med(cold), 4), "cold_ms_min": round(min(cold), 4),
+                "warm_tflops": round(c.flops / (med(wper) * 1e-3) / 1e12, 2),
+                "cold_tflops": round(c.flops / (med(cold) * 1e-3) / 1e12, 2), "peak": PEAK_BF16})
+            del xq, xk, xv, xo, xw
+        del flush
+        # attention backward (training: LoRA / DreamBooth-style edit training
+        # on 1024x1024 triples, and the 2048x2048 shape): forward with lse
+        # once, then the timed backward call (prep + dK/dV + dQ kernels);
+        # flops counted as 2.5x the forward's (the five S^2-sized products)
+        for cid in (3, 4):
+            c = get_config(cid)
+            print(f"[extra] backward S={c.S}", file=sys.stderr, flush=True)
+            xi = make_inputs(c)
+            xq, xk, xv, xp = to_device(xi, dev)
+            xo = torch.empty(xq.shape, dtype=torch.bfloat16, device=dev)
+            xl = torch.empty(c.B, c.H, c.S, dtype=torch.float32, device=dev)
+            kl.klein_rope4d_attn_fwd_lse(xq, xk, xv, xp, xo, xl)
+            g = torch.Generator(device=dev).manual_seed(505)
+            xd = torch.randn(xq.shape, device=dev, generator=g).to(torch.bfloat16)
+            gq, gk, gv = (torch.empty_like(xq) for _ in range(3))
+            xw = torch.empty(kl.klein_attn_bwd_workspace_size(c.B, c.S, c.H, c.D),
+                             dtype=torch.uint8, device=dev)
+            bms = time_gpu(lambda: kl.klein_rope4d_attn_bwd(xq, xk, xv, xp, xo, xd, xl, gq, gk, gv,
+                                                            xw), 10, 3, torch)
+            bf = 2.5 * c.flops
+            rec["extra"].append({
+                "workload": f"attention backward (dq, dk, dv through RoPE-4D), {c.name}: B={c.B}, "
+                            f"S={c.S}, H={c.H}, D={c.D}, bf16",
+                "ms_per_call": round(bms, 4), "tflops": round(bf / (bms * 1e-3) / 1e12, 2),
+                "peak": PEAK_BF16, "frac": round(bf / (bms * 1e-3) / 1e12 / PEAK_BF16, 4)})
+            del xq, xk, xv, xo, xl, xd, gq, gk, gv, xw
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)

@@ -143,6 +143,15 @@ def counter_means(dirs, kernel):
     return out
 
 
+def mean_duration_ns(pmc_dir, kernel):
+    """Mean dispatch duration of a kernel in a counter run."""
+    per = {}
+    for r in _rows(_find(pmc_dir, "counter_collection.csv")):
+        if kernel in r["Kernel_Name"]:
+            per[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return sum(per.values()) / len(per) if per else None
+
+
 def counters_markdown(kernel, cfg, dirs, command):
     """Instruction mix per wave-tile (one wave's 32 queries against one
     64-key tile) and MFMA utilisation from the SQ counter passes."""
@@ -171,6 +180,10 @@ def counters_markdown(kernel, cfg, dirs, command):
                 f"= {c['SQ_VALU_MFMA_BUSY_CYCLES']:.4e} / ({busy:.4e} x {SIMDS}) = "
                 f"**{100 * c['SQ_VALU_MFMA_BUSY_CYCLES'] / (busy * SIMDS):.1f} %** of the cycles the "
                 f"GPU was busy with the dispatch.\n")
+        dur = mean_duration_ns(dirs[0], kernel)
+        if dur:
+            util += (f"\nEffective engine clock = (GRBM_GUI_ACTIVE / 8 XCDs) / mean dispatch duration "
+                     f"= {busy:.4e} / {dur:.4e} ns = **{busy / dur * 1e3:.0f} MHz** (peak 2400).\n")
     return (f"## Counters (rocprofv3 --pmc, two passes)\n\nWave-tiles per dispatch: {tiles} "
             f"(B x H x {nqt} query tiles x 8 waves x {nkt} key tiles).\n\n```\n{command}\n```\n\n"
             + "\n".join(lines) + "\n" + util)
