@@ -65,6 +65,21 @@ LaunchArgs make_args(const void* q, const void* k, const void* v, const int32_t*
 
 constexpr long long kMaxGrid = 2147483647LL;
 
+// Workspace of klein_rope4d_attn_fwd_ws: k rotated once (bf16 path, fp16
+// [B][S][H][D]) and the split-KV partials.
+struct WsLayout {
+  long long krot_bytes;       // 0 for fp8
+  klein::SplitPlan plan;      // partials at offset krot_bytes
+  long long total;
+};
+WsLayout ws_layout(int B, int S, int H, int D, klein_dtype_t dtype, int ncu) {
+  WsLayout w{};
+  w.krot_bytes = dtype == KLEIN_DTYPE_BF16 ? ((long long)B * S * H * D * 2 + 255) / 256 * 256 : 0;
+  w.plan = klein::plan_split(B, S, H, D, ncu);
+  w.total = w.krot_bytes + w.plan.bytes;
+  return w;
+}
+
 // Compute units of the current device, cached per device (the split-KV plan
 // depends on them).  0 on error, with the HIP error in *err.
 int current_cu_count(hipError_t* err) {
@@ -193,7 +208,7 @@ klein_status_t klein_attn_workspace_size(int B, int S, int H, int D, klein_dtype
     hipError_t e;
     const int ncu = current_cu_count(&e);
     if (e != hipSuccess) return map_hip(e);
-    *bytes = (size_t)klein::plan_split(B, S, H, D, ncu).bytes;
+    *bytes = (size_t)ws_layout(B, S, H, D, dtype, ncu).total;
     return KLEIN_OK;
   } catch (...) {
     return KLEIN_ERR_LAUNCH;
@@ -218,12 +233,14 @@ klein_status_t klein_rope4d_attn_fwd_ws(const void* q, const void* k, const void
     hipError_t e;
     const int ncu = current_cu_count(&e);
     if (e != hipSuccess) return map_hip(e);
-    const klein::SplitPlan plan = klein::plan_split(B, S, H, D, ncu);
-    if (plan.bytes > 0 && (!workspace || workspace_bytes < (size_t)plan.bytes))
+    const WsLayout w = ws_layout(B, S, H, D, dtype, ncu);
+    const klein::SplitPlan& plan = w.plan;
+    if (w.total > 0 && (!workspace || workspace_bytes < (size_t)w.total))
       return KLEIN_ERR_INVALID_ARG;
     LaunchArgs a = make_args(q, k, v, pos_thwl, out, B, S, H, D, stream);
+    if (w.krot_bytes > 0) a.krot = workspace;
     if (plan.n_sk > 0) {
-      a.split.part = static_cast<float*>(workspace);
+      a.split.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.krot_bytes);
       a.split.n_dp = plan.n_dp;
       a.split.n_sk = plan.n_sk;
       a.split.n_rem = plan.n_rem;

@@ -38,7 +38,7 @@ namespace klein {
 // one channel pair of an output gradient, rotated back: R(-phi) (x, y)
 __device__ __forceinline__ void rotate_back(float& x, float& y, int p, float whi, float wlo) {
   const float fp = (float)p;
-  const float rev = __builtin_amdgcn_fractf(fp * whi) + fp * wlo;
+  const float rev = rope_rev(fp, whi, wlo);
   const float s = __builtin_amdgcn_sinf(rev), c = __builtin_amdgcn_cosf(rev);
   const float a = x, b = y;
   x = a * c + b * s;

@@ -65,12 +65,17 @@ constexpr int kTabN = 256;        // positions covered by the cos/sin table
 // tile of 256, key tile of 64), nonzero = compute, and only the kept key
 // tiles of a query tile stream through the pipeline (in ascending order, so
 // with every tile kept the result is bit-identical to the dense kernel).
-// PREROT: q and k arrive rotated, as fp16 (the projection's RoPE epilogue
-// emits them so); Q is only scaled and K tiles are copied to LDS as they
-// are, with no table, positions or rotation.
+// ROT: where the rotation happens.  kRotInKernel: Q once per workgroup and
+// every K tile on its way to LDS (cos/sin from an LDS table).  kRotKPre: k
+// arrives rotated, as fp16 (one elementwise pass over K before the call, so
+// each key is rotated once instead of once per query tile); Q is rotated in
+// the kernel.  kRotBothPre: q and k both arrive rotated as fp16 (the
+// projection's RoPE epilogue emits them so); Q is only scaled.  With k
+// pre-rotated, K tiles are copied to LDS as they are, with no table,
+// positions or rotation.
 // SPLIT: the split-KV schedule (SplitArgs): whole items first, then the key
 // chunks of the remaining items, merged through the workspace.
-template <int D, bool SPARSE, bool PREROT, bool SPLIT>
+template <int D, bool SPARSE, int ROT, bool SPLIT>
 __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ pos,
@@ -94,6 +99,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   static_assert(KPT >= 1 && (BN * CPR) % NT == 0, "tile/thread split");
   static_assert(KPT == 1 || KPT % 2 == 0, "V^T store packs key pairs");
   static_assert(!(SPARSE && SPLIT), "one schedule at a time");
+  constexpr bool QPRE = ROT == kRotBothPre;     // q arrives rotated (fp16)
+  constexpr bool KPRE = ROT != kRotInKernel;    // k arrives rotated (fp16)
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BN * VROW];
@@ -122,10 +129,10 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   }
 
   // ---- cos/sin table (the very values rope_chunk computes)
-  if constexpr (!PREROT) {
+  if constexpr (!KPRE) {
     for (int e = tid; e < kTabN * NJ; e += NT) {
       const int j = e % NJ, p = e / NJ;
-      const float rev = __builtin_amdgcn_fractf((float)p * fr.hi[j]) + (float)p * fr.lo[j];
+      const float rev = rope_rev((float)p, fr.hi[j], fr.lo[j]);
       cs_tab[p * TROW + j] = make_float2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
     }
   }
@@ -152,7 +159,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     const int d0 = 16 * ks + 8 * g;
     const int a = d0 / DA, j0 = (d0 % DA) / 2;
     const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qb + (size_t)qload * rs + d0);
-    if constexpr (PREROT) {
+    if constexpr (QPRE) {
       typedef float f32x8v_t __attribute__((ext_vector_type(8)));
       const f32x8v_t xf = __builtin_convertvector(__builtin_bit_cast(f16x8_t, x), f32x8v_t);
       qreg[ks] = __builtin_convertvector(xf * qscale, f16x8_t);
@@ -196,7 +203,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
       kx[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, voff, it * rowb, 0));
   };
   auto load_pos = [&](int kt, int* slot) {
-    if constexpr (PREROT) return;
+    if constexpr (KPRE) return;
     const __amdgpu_buffer_rsrc_t rp = uniform_rsrc(kposb + (size_t)kt * BN * 4, tile_rows(kt) * 16);
 #pragma unroll
     for (int it = 0; it < KPT; ++it)
@@ -207,14 +214,14 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   // own slots, filled here in a divergent branch that waves whose positions
   // all lie in the table skip.
   auto key_cs_index = [&](const int* kp, int it) {
-    if constexpr (PREROT) return 0;
+    if constexpr (KPRE) return 0;
     const bool oob = (unsigned)kp[it] >= (unsigned)kTabN;
     if (oob) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         int j = lj0 + jj;
         asm volatile("" : "+v"(j));      // keep the loads in this rare path
-        const float rev = __builtin_amdgcn_fractf((float)kp[it] * fr.hi[j]) + (float)kp[it] * fr.lo[j];
+        const float rev = rope_rev((float)kp[it], fr.hi[j], fr.lo[j]);
         cs_tab[TAB + TSLOT * tid + 4 * it + jj] =
             make_float2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
       }
@@ -223,8 +230,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   };
   // one rotated pair (x, y) -> (x c - y s, x s + y c), fp16
   auto rot_pair = [&](uint32_t xw, float2 cs) {
-    const float xa = bf16_lo(xw), xb = bf16_hi(xw);
-    return pack_f16x2(xa * cs.x - xb * cs.y, xa * cs.y + xb * cs.x);
+    const f32x2_t r = rope_rot(bf16_lo(xw), bf16_hi(xw), cs.x, cs.y);
+    return pack_f16x2(r[0], r[1]);
   };
   auto load_v = [&](int kt) {
     const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(vb + (size_t)kt * BN * rs, tile_rows(kt) * rowb);
@@ -239,7 +246,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
       const int key = lk + it;
       const int row = (key & ~31) + key_to_row(key & 31);
       u32x4_t y;
-      if constexpr (PREROT) {
+      if constexpr (KPRE) {
         y = kx[it];
       } else {
         const int ci = key_cs_index(kp, it);
@@ -372,13 +379,13 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   // (RoPE-4D, one pair per slice) and V(t+1) spread over the MFMAs; then the
   // loads of K(t+3), V(t+2).
   constexpr int NB = 4 * MB;                 // MFMAs in region B
-  constexpr int NROT = PREROT ? KPT : 4 * KPT;   // RoPE pairs (or K chunks) to stage
+  constexpr int NROT = KPRE ? KPT : 4 * KPT;   // RoPE pairs (or K chunks) to stage
   constexpr int NVW = KPT;                   // V chunks to stage
   constexpr int NIT = NROT + NVW;
   auto region_b = [&](int vbuf, int kdst, int vdst, const uint32_t (*pw)[8], const int* ci) {
     float2 kcs[NROT];
     auto read_cs = [&](int item) {
-      if constexpr (!PREROT)
+      if constexpr (!KPRE)
         if (item < NROT) kcs[item] = cs_tab[ci[item / 4] + item % 4];
     };
     read_cs(0);
@@ -410,7 +417,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
 #pragma unroll
       for (int item = i * NIT / NB; item < (i + 1) * NIT / NB; ++item) {
         read_cs(item + 2);
-        if (PREROT && item < NROT) {
+        if (KPRE && item < NROT) {
           // one pre-rotated K chunk, copied
           const int key = lk + item;
           const int row = (key & ~31) + key_to_row(key & 31);
@@ -542,30 +549,43 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   }
 }
 
-template <int D, bool SPARSE, bool PREROT = false, bool SPLIT = false>
+template <int D, bool SPARSE, int ROT = kRotInKernel, bool SPLIT = false>
 static hipError_t launch_bf16(const LaunchArgs& a) {
   constexpr int BM = 256;
   const int nqt = (a.S + BM - 1) / BM;
   const long long n = SPLIT ? (long long)a.split.n_dp + a.split.n_sk : (long long)a.B * a.H * nqt;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, SPARSE, PREROT, SPLIT>), dim3((unsigned)n), dim3(512),
-                     0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, SPARSE, ROT, SPLIT>), dim3((unsigned)n), dim3(512),
+                     0, a.stream, (const uint16_t*)a.q,
+                     (const uint16_t*)(ROT == kRotKPre ? a.krot : a.k), (const uint16_t*)a.v,
                      a.pos, (uint16_t*)a.out, a.S, a.H, nqt, a.freqs, a.qscale_log2, a.bmask,
                      a.split, a.lse);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fwd_bf16(const LaunchArgs& a) {
-  if (a.bmask) return a.D == 128 ? launch_bf16<128, true>(a) : launch_bf16<64, true>(a);
-  if (a.split.n_sk > 0) {
-    const hipError_t e = a.D == 128 ? launch_bf16<128, false, false, true>(a)
-                                    : launch_bf16<64, false, false, true>(a);
+template <int D>
+static hipError_t launch_bf16_dense(const LaunchArgs& a) {
+  if (a.krot) {
+    // k rotated once into the workspace, then the kernel without K rotation
+    hipError_t e = launch_rope4d_fp16(a.k, a.pos, a.krot, a.B, a.S, a.H, D, a.freqs, 1.0f, a.stream);
+    if (e != hipSuccess) return e;
+    if (a.split.n_sk == 0) return launch_bf16<D, false, kRotKPre>(a);
+    e = launch_bf16<D, false, kRotKPre, true>(a);
     return e != hipSuccess ? e : launch_split_merge(a, 1.0f, a.lse);
   }
-  return a.D == 128 ? launch_bf16<128, false>(a) : launch_bf16<64, false>(a);
+  if (a.split.n_sk > 0) {
+    const hipError_t e = launch_bf16<D, false, kRotInKernel, true>(a);
+    return e != hipSuccess ? e : launch_split_merge(a, 1.0f, a.lse);
+  }
+  return launch_bf16<D, false>(a);
+}
+
+hipError_t launch_attn_fwd_bf16(const LaunchArgs& a) {
+  if (a.bmask) return a.D == 128 ? launch_bf16<128, true>(a) : launch_bf16<64, true>(a);
+  return a.D == 128 ? launch_bf16_dense<128>(a) : launch_bf16_dense<64>(a);
 }
 
 hipError_t launch_attn_fwd_prerotated(const LaunchArgs& a) {
-  return a.D == 128 ? launch_bf16<128, false, true>(a) : launch_bf16<64, false, true>(a);
+  return a.D == 128 ? launch_bf16<128, false, kRotBothPre>(a) : launch_bf16<64, false, kRotBothPre>(a);
 }
 
 long long attn_fwd_bf16_grid(int B, int S, int H) {

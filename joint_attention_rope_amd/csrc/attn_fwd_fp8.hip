@@ -72,7 +72,7 @@ __device__ __forceinline__ int key_to_row8(int kk) {
 // (cos, sin) * scale of the angle pos * w (w in revolutions, split hi + lo)
 __device__ __forceinline__ float2 rope_cs(int p, float whi, float wlo, float scale) {
   const float fp = (float)p;
-  const float rev = __builtin_amdgcn_fractf(fp * whi) + fp * wlo;
+  const float rev = rope_rev(fp, whi, wlo);
   return make_float2(__builtin_amdgcn_cosf(rev) * scale, __builtin_amdgcn_sinf(rev) * scale);
 }
 

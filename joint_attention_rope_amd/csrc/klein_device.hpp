@@ -64,6 +64,19 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Angle of RoPE pair j at integer position p, in revolutions (v_sin_f32 and
+// v_cos_f32 take revolutions): fract(p * hi) + p * lo, one explicit fma, so
+// that every kernel forms bit-identical angles whatever the compiler contracts.
+__device__ __forceinline__ float rope_rev(float fp, float whi, float wlo) {
+  return __builtin_fmaf(fp, wlo, __builtin_amdgcn_fractf(fp * whi));
+}
+
+// One pair (x, y) -> (x c - y s, x s + y c), with explicit fmas (same bits in
+// every kernel that rotates).
+__device__ __forceinline__ f32x2_t rope_rot(float x, float y, float c, float s) {
+  return (f32x2_t){__builtin_fmaf(x, c, -(y * s)), __builtin_fmaf(x, s, y * c)};
+}
+
 // Rotate one 16-byte chunk of bf16: 8 consecutive channels = 4 interleaved
 // pairs of a single axis block, pairs j0 .. j0+3, at integer position p on
 // that axis.  Each pair (x, y) -> (x cos - y sin, x sin + y cos), then
@@ -76,12 +89,11 @@ __device__ __forceinline__ u32x4_t rope_chunk(u32x4_t x, int p, const float* whi
   u32x4_t y;
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
-    const float rev = __builtin_amdgcn_fractf(fp * whi[jj]) + fp * wlo[jj];
+    const float rev = rope_rev(fp, whi[jj], wlo[jj]);
     const float s = __builtin_amdgcn_sinf(rev);
     const float c = __builtin_amdgcn_cosf(rev);
-    const float a = bf16_lo(x[jj]);
-    const float b = bf16_hi(x[jj]);
-    const float u = (a * c - b * s) * scale, w = (a * s + b * c) * scale;
+    const f32x2_t r = rope_rot(bf16_lo(x[jj]), bf16_hi(x[jj]), c, s);
+    const float u = r[0] * scale, w = r[1] * scale;
     y[jj] = F16 ? pack_f16x2(u, w) : pack_bf16x2(u, w);
   }
   return y;

@@ -27,7 +27,19 @@ struct LaunchArgs {
   // bf16 dense/split paths: also write the softmax log-sum-exp, fp32
   // [B][H][S], natural log (null: not written)
   float* lse = nullptr;
+  // bf16 dense/split paths: workspace for k rotated once (fp16 [B][S][H][D])
+  // before the attention kernel, or null (rotate every K tile in the kernel)
+  void* krot = nullptr;
 };
+
+// where the attention kernels rotate (see attn_fwd_bf16.hip)
+constexpr int kRotInKernel = 0;
+constexpr int kRotKPre = 1;
+constexpr int kRotBothPre = 2;
+
+// y = fp16(R(pos) x * scale) for bf16 x [B][S][H][D] (the kernels' rotation routine)
+hipError_t launch_rope4d_fp16(const void* x, const int32_t* pos, void* y, int B, int S, int H,
+                              int D, const RopeFreqs& fr, float scale, hipStream_t stream);
 
 // Split-KV cut of a dense call for a GPU of n_cu compute units (n_sk == 0:
 // whole items only, no workspace).  The workspace holds the partial slots.

@@ -159,11 +159,11 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
 #pragma unroll
           for (int pr = 0; pr < 2; ++pr) {
             const int j = j0 + pr;
-            const float rev = __builtin_amdgcn_fractf(fp * fr.hi[j]) + fp * fr.lo[j];
+            const float rev = rope_rev(fp, fr.hi[j], fr.lo[j]);
             const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
-            const float xa = y[2 * pr], xb = y[2 * pr + 1];
-            y[2 * pr] = xa * cs - xb * sn;
-            y[2 * pr + 1] = xa * sn + xb * cs;
+            const f32x2_t r = rope_rot(y[2 * pr], y[2 * pr + 1], cs, sn);
+            y[2 * pr] = r[0];
+            y[2 * pr + 1] = r[1];
           }
           outw.x = pack_f16x2(y[0], y[1]);
           outw.y = pack_f16x2(y[2], y[3]);
