@@ -115,9 +115,10 @@ klein_status_t klein_rope4d_attn_fwd_fp8(const void* q, const void* k, const voi
  * differ by the rounding of the probabilities against each chunk's own
  * running max and the fp32 merge, within the same error bounds.  The result
  * is deterministic (fixed merge order).
- * For bf16 the keys are also rotated once, into fp16 in `workspace`, before
- * the attention kernel (the dense entry points rotate every key tile once per
- * tile of 256 queries); the values equal those the dense kernels form.
+ * The keys are also rotated once, into `workspace` (fp16 for bf16 inputs,
+ * E4M3 codes of R k / 2 for fp8), before the attention kernel; the dense
+ * entry points rotate every key tile once per tile of 256 queries.  The
+ * values equal those the dense kernels form.
  *   workspace      : DEVICE pointer, 256-byte aligned, caller-owned, at least
  *                    the size klein_attn_workspace_size reports for the same
  *                    shape on the current device (may be NULL when that is 0).
@@ -135,8 +136,8 @@ klein_status_t klein_rope4d_attn_fwd_ws(const void* q, const void* k, const void
 
 /*
  * Workspace bytes klein_rope4d_attn_fwd_ws needs for this shape on the
- * current HIP device: for bf16, the rotated keys (B*S*H*D*2 bytes, rounded up
- * to a multiple of 256), then for either dtype the split partials (0 when the
+ * current HIP device: the rotated keys (B*S*H*D*2 bytes for bf16, B*S*H*D
+ * for fp8, rounded up to a multiple of 256), then the split partials (0 when the
  * tiles fill whole rounds, or the sequence is shorter than 2048 keys, and
  * nothing is split; at most 4 * (number of compute units) * (256 * D + 1024)
  * * 4 bytes, 138 MB for D = 128 on 256 compute units).  Writes *bytes; INVALID_ARG for a

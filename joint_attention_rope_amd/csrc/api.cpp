@@ -65,16 +65,17 @@ LaunchArgs make_args(const void* q, const void* k, const void* v, const int32_t*
 
 constexpr long long kMaxGrid = 2147483647LL;
 
-// Workspace of klein_rope4d_attn_fwd_ws: k rotated once (bf16 path, fp16
-// [B][S][H][D]) and the split-KV partials.
+// Workspace of klein_rope4d_attn_fwd_ws: k rotated once (fp16 for bf16
+// inputs, e4m3 codes for fp8, [B][S][H][D]) and the split-KV partials.
 struct WsLayout {
-  long long krot_bytes;       // 0 for fp8
+  long long krot_bytes;
   klein::SplitPlan plan;      // partials at offset krot_bytes
   long long total;
 };
 WsLayout ws_layout(int B, int S, int H, int D, klein_dtype_t dtype, int ncu) {
   WsLayout w{};
-  w.krot_bytes = dtype == KLEIN_DTYPE_BF16 ? ((long long)B * S * H * D * 2 + 255) / 256 * 256 : 0;
+  const int elem = dtype == KLEIN_DTYPE_BF16 ? 2 : 1;      // fp16 or e4m3 rotated keys
+  w.krot_bytes = ((long long)B * S * H * D * elem + 255) / 256 * 256;
   w.plan = klein::plan_split(B, S, H, D, ncu);
   w.total = w.krot_bytes + w.plan.bytes;
   return w;

@@ -104,9 +104,12 @@ __device__ __forceinline__ int rope_pair_fp8_h(uint32_t word, h2_t cs, int acc) 
 // SPARSE: block-sparse variant (one mask byte per batch, head, query tile of
 // 256 and key tile of 64; only kept key tiles stream through the pipeline, in
 // ascending order, so with every tile kept the result equals the dense one).
+// KPRE: the key codes arrive rotated (K'' = e4m3(R k / 2), written once per
+// call by rope4d_fp8_kernel with the very arithmetic of the in-kernel path),
+// and K tiles are copied to LDS as they are: no table, positions or rotation.
 // SPLIT: the split-KV schedule (SplitArgs): whole items first, then the key
 // chunks of the remaining items, merged through the workspace.
-template <int D, bool SPARSE, bool SPLIT>
+template <int D, bool SPARSE, bool KPRE, bool SPLIT>
 __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     const int32_t* __restrict__ pos, uint16_t* __restrict__ out, int S, int H, int nqt,
@@ -161,10 +164,12 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   }
 
   // ---- cos/sin table: entry p * TROW + j = (cos, sin)(p w_j) / 2
-  for (int e = tid; e < kTabN * NJ; e += NT) {
-    const int j = e % NJ, p = e / NJ;
-    const float2 c = rope_cs(p, fr.hi[j], fr.lo[j], kHalf);
-    cs_tab[p * TROW + j] = (h2_t){(_Float16)c.x, (_Float16)c.y};
+  if constexpr (!KPRE) {
+    for (int e = tid; e < kTabN * NJ; e += NT) {
+      const int j = e % NJ, p = e / NJ;
+      const float2 c = rope_cs(p, fr.hi[j], fr.lo[j], kHalf);
+      cs_tab[p * TROW + j] = (h2_t){(_Float16)c.x, (_Float16)c.y};
+    }
   }
 
   const int qt = work % nqt;
@@ -238,6 +243,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
     }
   };
   auto load_pos = [&](int kt, int& slot) {
+    if constexpr (KPRE) return;
     if (kst) {
       const __amdgpu_buffer_rsrc_t rp = uniform_rsrc(kposb + (size_t)kt * BN * 4, tile_rows(kt) * 16);
       slot = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, voff_p, 0, 0);
@@ -257,6 +263,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   // table) its own 8 slots past the table, filled here.  The branch is
   // divergent and skipped by waves whose positions all lie in the table.
   auto key_cs_index = [&](int kp) {
+    if constexpr (KPRE) return 0;
     const bool oob = kst && (unsigned)kp >= (unsigned)kTabN;
     if (oob) {
 #pragma unroll
@@ -272,6 +279,10 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   // one rotated pair of the K chunk; the 16-byte LDS store after the last
   u32x4_t ky;
   auto rope_item = [&](int kdst, int jj, h2_t cs) {
+    if constexpr (KPRE) {              // a rotated chunk: one copy
+      if (jj == 0 && kst) *reinterpret_cast<u32x4_t*>(&k_lds[kdst][krow * KROW + 16 * kc]) = kx;
+      return;
+    }
     const int w = jj >> 1;
     ky[w] = (uint32_t)((jj & 1) ? rope_pair_fp8_h<true>(kx[w], cs, (int)ky[w])
                                 : rope_pair_fp8_h<false>(kx[w], cs, (int)ky[w]));
@@ -280,7 +291,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   auto stage_k = [&](int buf, int kp) {
     const int ci = key_cs_index(kp);
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) rope_item(buf, jj, cs_tab[ci + jj]);
+    for (int jj = 0; jj < 8; ++jj) rope_item(buf, jj, KPRE ? h2_t{} : cs_tab[ci + jj]);
   };
   // lane base of the transposing V reads: lane L of group G = L / 16 reads
   // row 16 (G / 2) + (L % 16) / 2, channels 16 (G % 2) + 8 (L % 2) .. + 7
@@ -404,15 +415,17 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
     h2_t kcs[8];
     vop[0] = read_v(vbuf, 0);
     vop[1] = read_v(vbuf, 1);
-    kcs[0] = cs_tab[ci];
-    kcs[1] = cs_tab[ci + 1];
+    if constexpr (!KPRE) {
+      kcs[0] = cs_tab[ci];
+      kcs[1] = cs_tab[ci + 1];
+    }
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       if (i + 2 < MB) vop[i + 2] = read_v(vbuf, i + 2);
       o[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[i], pb, o[i], 0, 0, 0, 0, 0, 0);
 #pragma unroll
       for (int item = i * NIT / MB; item < (i + 1) * NIT / MB; ++item) {
-        if (item + 2 < 8) kcs[item + 2] = cs_tab[ci + item + 2];
+        if (!KPRE && item + 2 < 8) kcs[item + 2] = cs_tab[ci + item + 2];
         if (item < 8) rope_item(kdst, item, kcs[item]);
         else stage_v(vdst);
       }
@@ -537,25 +550,73 @@ static Fp8Scales fp8_scales(const LaunchArgs& a) {
   return {(float)std::ldexp(G, -n), 127 + na, 127 + nb};
 }
 
-template <int D, bool SPARSE, bool SPLIT = false>
+// K'' = e4m3(R k / 2) for the whole key tensor, one thread per 16-byte chunk
+// (16 codes = 8 pairs of one axis block): the same table values, (cos, sin)/2
+// in fp16, and the same packed-fp16 rotation as the kernel's staging of K.
+template <int D>
+__global__ __launch_bounds__(256) void rope4d_fp8_kernel(const uint8_t* __restrict__ k,
+                                                         const int32_t* __restrict__ pos,
+                                                         uint8_t* __restrict__ kr, long long nchunks,
+                                                         int S, int H, RopeFreqs fr) {
+  constexpr int CPK = D / 16, DA = D / 4;
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long c = (long long)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks; c += stride) {
+    const int kc = (int)(c % CPK);
+    const int s = (int)((c / CPK / H) % S);
+    const int a = (16 * kc) / DA, j0 = ((16 * kc) % DA) / 2;
+    const int p = pos[4 * s + a];
+    const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(k + 16 * c);
+    u32x4_t ky = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const float2 cf = rope_cs(p, fr.hi[j0 + jj], fr.lo[j0 + jj], kHalf);
+      const h2_t cs = {(_Float16)cf.x, (_Float16)cf.y};
+      const int w = jj >> 1;
+      ky[w] = (uint32_t)((jj & 1) ? rope_pair_fp8_h<true>(kx[w], cs, (int)ky[w])
+                                  : rope_pair_fp8_h<false>(kx[w], cs, (int)ky[w]));
+    }
+    *reinterpret_cast<u32x4_t*>(kr + 16 * c) = ky;
+  }
+}
+
+template <int D, bool SPARSE, bool KPRE = false, bool SPLIT = false>
 static hipError_t launch_fp8(const LaunchArgs& a) {
   const int nqt = (a.S + 255) / 256;
   const long long n = SPLIT ? (long long)a.split.n_dp + a.split.n_sk : (long long)a.B * a.H * nqt;
   const Fp8Scales s = fp8_scales(a);
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, SPARSE, SPLIT>), dim3((unsigned)n), dim3(512), 0,
-                     a.stream, (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v,
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, SPARSE, KPRE, SPLIT>), dim3((unsigned)n), dim3(512), 0,
+                     a.stream, (const uint8_t*)a.q, (const uint8_t*)(KPRE ? a.krot : a.k),
+                     (const uint8_t*)a.v,
                      a.pos, (uint16_t*)a.out, a.S, a.H, nqt, a.freqs, s.q_mul, s.sc_a, s.sc_b,
                      a.descale[2], a.bmask, a.split);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fwd_fp8(const LaunchArgs& a) {
-  if (a.bmask) return a.D == 128 ? launch_fp8<128, true>(a) : launch_fp8<64, true>(a);
-  if (a.split.n_sk > 0) {
-    const hipError_t e = a.D == 128 ? launch_fp8<128, false, true>(a) : launch_fp8<64, false, true>(a);
+template <int D>
+static hipError_t launch_fp8_dense(const LaunchArgs& a) {
+  if (a.krot) {
+    // key codes rotated once into the workspace, then the kernel without K rotation
+    const long long nchunks = (long long)a.B * a.S * a.H * (D / 16);
+    long long blocks = (nchunks + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(rope4d_fp8_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, a.stream,
+                       (const uint8_t*)a.k, a.pos, (uint8_t*)a.krot, nchunks, a.S, a.H, a.freqs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.split.n_sk == 0) return launch_fp8<D, false, true>(a);
+    e = launch_fp8<D, false, true, true>(a);
     return e != hipSuccess ? e : launch_split_merge(a, a.descale[2], nullptr);
   }
-  return a.D == 128 ? launch_fp8<128, false>(a) : launch_fp8<64, false>(a);
+  if (a.split.n_sk > 0) {
+    const hipError_t e = launch_fp8<D, false, false, true>(a);
+    return e != hipSuccess ? e : launch_split_merge(a, a.descale[2], nullptr);
+  }
+  return launch_fp8<D, false>(a);
+}
+
+hipError_t launch_attn_fwd_fp8(const LaunchArgs& a) {
+  if (a.bmask) return a.D == 128 ? launch_fp8<128, true>(a) : launch_fp8<64, true>(a);
+  return a.D == 128 ? launch_fp8_dense<128>(a) : launch_fp8_dense<64>(a);
 }
 
 long long attn_fwd_fp8_grid(int B, int S, int H) {

@@ -1,9 +1,9 @@
 """GPU checks of klein_rope4d_attn_fwd_ws, the split-KV schedule.
 
 Query tiles that run whole (the full rounds of the GPU) go through the same
-arithmetic as the dense entry point (for bf16 the keys are rotated once
-before the call, to the very fp16 values the dense kernel forms per tile), so
-their rows must be bit-identical to it.  Rows of split tiles round P to bf16 relative to each chunk's own
+arithmetic as the dense entry point (the keys are rotated once before the
+call, to the very fp16 values, or e4m3 codes, the dense kernels form per
+tile), so their rows must be bit-identical to it.  Rows of split tiles round P to bf16 relative to each chunk's own
 running max and merge fp32 partial sums, so they differ from the dense rows
 at the level of the kernel's rounding error; they must match the oracle
 within the hot path's tolerances.  Results must not depend on which
@@ -128,15 +128,15 @@ def test_repeat_calls_bitwise_identical():
 
 @pytest.mark.parametrize("D", [64, 128])
 def test_unsplit_call_equals_dense(D):
-    # S < 2048: nothing is split; bf16 keys are still rotated once into the
-    # workspace (fp16, the values the kernel's cos/sin table gives), so the
-    # result equals the dense entry point bit for bit; fp8 needs no workspace
+    # S < 2048: nothing is split; the keys are still rotated once into the
+    # workspace (fp16, or e4m3 codes for fp8: the values the kernels' cos/sin
+    # tables give), so the result equals the dense entry point bit for bit
     inp = random_inputs(2, 1000, 3, D, seed=98)
     assert kl.klein_attn_workspace_size(2, 1000, 3, D) == 2 * 1000 * 3 * D * 2
     out, _ = run_ws(inp)
     assert torch.equal(out.view(torch.int16), run_attention(inp).view(torch.int16))
     inp8 = random_fp8_inputs(1, 1000, 2, D, seed=99)
-    assert kl.klein_attn_workspace_size(1, 1000, 2, D, kl.KLEIN_DTYPE_FP8_E4M3) == 0
+    assert kl.klein_attn_workspace_size(1, 1000, 2, D, kl.KLEIN_DTYPE_FP8_E4M3) == 1000 * 2 * D
     out8, _ = run_ws(inp8)
     assert torch.equal(out8.view(torch.int16), run_attention(inp8).view(torch.int16))
 
