@@ -30,23 +30,28 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 COPY_KERNEL = "MulFunctor"
 
-# A profiled call of an entry point: its attention kernel (matched on the
-# demangled name, template arguments included) and, on the split-KV path, the
-# merge kernel dispatched right after it; the sources its measurement depends on.
+# A profiled call of an entry point: the elementwise pass that rotates the
+# keys once (dispatched before the attention kernel), the attention kernel
+# (matched on the demangled name, template arguments included) and, on the
+# split-KV path, the merge kernel dispatched after it; and the sources the
+# measurement depends on.
 CALLS = {
     "attn_fwd_bf16_splitkv": {
-        "kernel": "attn_fwd_bf16_kernel<128, false, false, true>",
+        "before": "rope4d_fp16_kernel<128>",
+        "kernel": "attn_fwd_bf16_kernel<128, false, 1, true>",
         "merge": "split_merge_kernel<128>",
-        "sources": ["klein_device.hpp", "attn_fwd_bf16.hip", "split_schedule.hip"]},
+        "sources": ["klein_device.hpp", "attn_fwd_bf16.hip", "split_schedule.hip",
+                    "rope_apply.hip"]},
     "attn_fwd_fp8_splitkv": {
-        "kernel": "attn_fwd_fp8_kernel<128, false, true>",
+        "before": "rope4d_fp8_kernel<128>",
+        "kernel": "attn_fwd_fp8_kernel<128, false, true, true>",
         "merge": "split_merge_kernel<128>",
         "sources": ["klein_device.hpp", "attn_fwd_fp8.hip", "split_schedule.hip"]},
     "attn_fwd_bf16_dense": {
-        "kernel": "attn_fwd_bf16_kernel<128, false, false, false>", "merge": None,
+        "before": None, "kernel": "attn_fwd_bf16_kernel<128, false, 0, false>", "merge": None,
         "sources": ["klein_device.hpp", "attn_fwd_bf16.hip"]},
     "attn_fwd_fp8_dense": {
-        "kernel": "attn_fwd_fp8_kernel<128, false, false>", "merge": None,
+        "before": None, "kernel": "attn_fwd_fp8_kernel<128, false, false, false>", "merge": None,
         "sources": ["klein_device.hpp", "attn_fwd_fp8.hip"]},
 }
 
@@ -73,27 +78,39 @@ def _find(dirname, suffix):
     raise FileNotFoundError(f"no *{suffix} under {dirname}")
 
 
-def _pair(ids_kernel, ids_merge):
-    """For each attention dispatch id, the first merge dispatch id after it
-    (and before the next attention dispatch), or None."""
+def _pair(ids_kernel, ids_other, after=True):
+    """For each attention dispatch id, the nearest dispatch id of the other
+    kernel after it (before the next attention dispatch), or with after=False
+    before it (after the previous attention dispatch); None if there is none."""
     ks = sorted(ids_kernel)
-    ms = sorted(ids_merge)
+    os_ = sorted(ids_other)
     out = {}
     for i, k in enumerate(ks):
-        nxt = ks[i + 1] if i + 1 < len(ks) else float("inf")
-        out[k] = next((m for m in ms if k < m < nxt), None)
+        if after:
+            nxt = ks[i + 1] if i + 1 < len(ks) else float("inf")
+            out[k] = next((m for m in os_ if k < m < nxt), None)
+        else:
+            prv = ks[i - 1] if i > 0 else -1
+            cand = [m for m in os_ if prv < m < k]
+            out[k] = cand[-1] if cand else None
     return out
 
 
+def _ids(rows, name):
+    return [int(r["Dispatch_Id"]) for r in rows if name and name in r["Kernel_Name"]]
+
+
 def call_durations_ns(stats_dir, call):
-    """Per call, in dispatch order: (attention kernel ns, merge kernel ns)."""
+    """Per call, in dispatch order: (rotation pass ns, attention kernel ns,
+    merge kernel ns)."""
     c = CALLS[call]
     rows = _rows(_find(stats_dir, "kernel_trace.csv"))
     dur = {int(r["Dispatch_Id"]): int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows}
-    ks = [int(r["Dispatch_Id"]) for r in rows if c["kernel"] in r["Kernel_Name"]]
-    ms = [int(r["Dispatch_Id"]) for r in rows if c["merge"] and c["merge"] in r["Kernel_Name"]]
-    pairs = _pair(ks, ms)
-    return [(dur[k], dur[pairs[k]] if pairs[k] is not None else 0) for k in sorted(ks)]
+    ks = _ids(rows, c["kernel"])
+    pm = _pair(ks, _ids(rows, c["merge"]))
+    pb = _pair(ks, _ids(rows, c["before"]), after=False)
+    get = lambda d: dur[d] if d is not None else 0
+    return [(get(pb[k]), dur[k], get(pm[k])) for k in sorted(ks)]
 
 
 def counter_per_dispatch(pmc_dir, kernel, counter):
@@ -107,12 +124,16 @@ def counter_per_dispatch(pmc_dir, kernel, counter):
 
 
 def call_counter(pmc_dir, call, counter):
-    """Per call: the counter of the attention kernel plus that of its merge."""
+    """Per call: the counter of the attention kernel plus those of its
+    rotation pass and merge."""
     c = CALLS[call]
     ks = counter_per_dispatch(pmc_dir, c["kernel"], counter)
     ms = counter_per_dispatch(pmc_dir, c["merge"], counter) if c["merge"] else {}
-    pairs = _pair(list(ks), list(ms))
-    return [ks[k] + (ms[pairs[k]] if pairs[k] is not None else 0.0) for k in sorted(ks)]
+    bs = counter_per_dispatch(pmc_dir, c["before"], counter) if c["before"] else {}
+    pm = _pair(list(ks), list(ms))
+    pb = _pair(list(ks), list(bs), after=False)
+    return [ks[k] + (ms[pm[k]] if pm[k] is not None else 0.0) + (bs[pb[k]] if pb[k] is not None else 0.0)
+            for k in sorted(ks)]
 
 
 # Counter passes (8 SQ counters and one GRBM counter per pass at most).
@@ -263,7 +284,8 @@ def main():
     call = CALLS[args.call]
     srcs = call["sources"]
     shash = sources_hash(srcs)
-    kinds = f"`{call['kernel']}`" + (f" + `{call['merge']}`" if call["merge"] else "")
+    kinds = (f"`{call['before']}` + " if call["before"] else "") + f"`{call['kernel']}`" + \
+        (f" + `{call['merge']}`" if call["merge"] else "")
     if args.counters:
         from workloads import get_config
         md = f"# {args.name} counters\n\nKernel {kinds} (counters of the attention kernel); " \
@@ -275,12 +297,13 @@ def main():
         return
     cfg, algo_read, algo_write = algorithmic_bytes(args.workload)
     calls = call_durations_ns(args.stats, args.call)
-    durs = [a + m for a, m in calls]
+    durs = [sum(c) for c in calls]
     timed = calls[-args.steps:]
     avg_all = sum(durs) / len(durs) / 1e6
-    avg_timed = sum(a + m for a, m in timed) / len(timed) / 1e6
-    avg_attn = sum(a for a, _ in timed) / len(timed) / 1e6
-    avg_merge = sum(m for _, m in timed) / len(timed) / 1e6
+    avg_timed = sum(sum(c) for c in timed) / len(timed) / 1e6
+    avg_rot = sum(c[0] for c in timed) / len(timed) / 1e6
+    avg_attn = sum(c[1] for c in timed) / len(timed) / 1e6
+    avg_merge = sum(c[2] for c in timed) / len(timed) / 1e6
 
     copy_bytes = args.copy_mib * (1 << 20)
     cf = list(counter_per_dispatch(args.fetch, COPY_KERNEL, "FETCH_SIZE").values())
@@ -312,6 +335,7 @@ Commands (run from /tmp with TMPDIR=/tmp; R = repository root):
 | calls | {len(durs)} |
 | average duration per call, all calls | {avg_all:.4f} ms |
 | average duration per call, last {args.steps} (the timed calls) | {avg_timed:.4f} ms |
+| of which the key rotation pass | {avg_rot:.4f} ms |
 | of which the attention kernel | {avg_attn:.4f} ms |
 | of which the merge kernel | {avg_merge:.4f} ms |
 | min / max per call | {min(durs) / 1e6:.4f} / {max(durs) / 1e6:.4f} ms |
