@@ -12,10 +12,11 @@
 //   prep:  q'' = fp16(R q * log2(e)/sqrt(D)) and k' = fp16(R k), exactly the
 //          values the forward kernel forms on chip (so the recomputed scores
 //          match the ones lse was taken over), and delta_i;
-//   dk/dv: one workgroup per 128 keys (4 waves x 32 keys, the keys on the
-//          MFMA columns), streaming all queries in tiles of 64;
-//   dq:    one workgroup per 128 queries (4 waves x 32 queries), streaming all
-//          keys in tiles of 64.
+//   dk/dv: one workgroup per 256 keys (8 waves x 32 keys, two per SIMD; the
+//          keys on the MFMA columns), streaming all queries in tiles of 32
+//          (64 for D = 64);
+//   dq:    one workgroup per 256 queries (8 waves x 32 queries, two per SIMD),
+//          streaming all keys in tiles of 64.
 //
 // Each MFMA keeps the fast operand layout of the forward kernel: the tile
 // that streams through LDS is the A operand, read row-wise (rows of a
@@ -98,15 +99,16 @@ __device__ __forceinline__ s16x8_t read_tr8(const uint16_t* p, int row_stride) {
 
 // ---------------------------------------------------------------- dk, dv
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ pos, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
     int S, int H, int nkb, RopeFreqs fr) {
-  constexpr int BK = 128;              // keys per workgroup (4 waves x 32)
-  constexpr int BQ = 64;               // queries per step
-  constexpr int NT = 256;
+  constexpr int BK = 256;              // keys per workgroup (8 waves x 32)
+  constexpr int NBLK = D == 128 ? 1 : 2;   // 32-query blocks per step (one staging chunk a thread)
+  constexpr int BQ = 32 * NBLK;        // queries per step
+  constexpr int NT = 512;
   constexpr int KS = D / 16, MB = D / 32, DA = D / 4;
   constexpr int ROW = D + 8;           // LDS row stride of the q'' and dout tiles (16-bit)
   constexpr int CPR = D / 8;
@@ -186,9 +188,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   for (int qt = 0; qt < nqt; ++qt) {
     const int buf = qt & 1;
     if (qt + 1 < nqt) load(qt + 1);
-    f32x16_t sc[2], dp[2];
+    f32x16_t sc[NBLK], dp[NBLK];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+    for (int blk = 0; blk < NBLK; ++blk) {
       // initial values -lse2 and -delta of rows 32 blk + 16 g + i
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
@@ -210,9 +212,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
       }
     }
     // P = 2^(s2 - lse2) (bf16, for dV) and dS = P (dP - delta) (fp16, for dK)
-    uint32_t pw[2][8], sw[2][8];
+    uint32_t pw[NBLK][8], sw[NBLK][8];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+    for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const float p0 = __builtin_amdgcn_exp2f(sc[blk][2 * w]);
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     // dV^T += dout^T P, dK'^T += q''^T dS: k = the 64 queries of the tile, in
     // steps (blk, j) of 16: k slot (g, e) is query 32 blk + 16 g + 8 j + e
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+    for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const bf16x8_t pb = __builtin_bit_cast(
@@ -271,15 +273,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 
 // ---------------------------------------------------------------- dq
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ pos, uint16_t* __restrict__ dq, int S, int H, int nqb,
     RopeFreqs fr, float dqscale) {
-  constexpr int BQ = 128;              // queries per workgroup (4 waves x 32)
+  constexpr int BQ = 256;              // queries per workgroup (8 waves x 32)
   constexpr int BK = 64;               // keys per step
-  constexpr int NT = 256;
+  constexpr int NT = 512;
   constexpr int KS = D / 16, MB = D / 32, DA = D / 4;
   constexpr int ROW = D + 8;
   constexpr int CPR = D / 8;
@@ -431,14 +433,15 @@ static hipError_t launch_bwd(const BwdArgs& a) {
                      nchunks, a.freqs, a.qscale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nb = (a.S + 127) / 128;
+  const int nb = (a.S + 255) / 256;
   const dim3 grid((unsigned)(a.B * a.H * nb));
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, grid, dim3(256), 0, a.stream, a.qr, a.kr, a.v,
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, grid, dim3(512), 0, a.stream, a.qr, a.kr, a.v,
                      a.dout, a.lse, a.delta, a.pos, a.dk, a.dv, a.S, a.H, nb, a.freqs);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, grid, dim3(256), 0, a.stream, a.qr, a.kr, a.v, a.dout,
-                     a.lse, a.delta, a.pos, a.dq, a.S, a.H, nb, a.freqs,
+  const int nqb = (a.S + 255) / 256;
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3((unsigned)(a.B * a.H * nqb)), dim3(512), 0, a.stream,
+                     a.qr, a.kr, a.v, a.dout, a.lse, a.delta, a.pos, a.dq, a.S, a.H, nqb, a.freqs,
                      (float)(1.0 / std::sqrt((double)D)));
   return hipGetLastError();
 }
