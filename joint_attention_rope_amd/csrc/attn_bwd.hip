@@ -110,13 +110,20 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
   constexpr int BQ = 32 * NBLK;        // queries per step
   constexpr int NT = 512;
   constexpr int KS = D / 16, MB = D / 32, DA = D / 4;
-  constexpr int ROW = D + 8;           // LDS row stride of the q'' and dout tiles (16-bit)
+  // Each tile sits in LDS twice: rows padded by 16 bytes for the row-wise
+  // 16-byte reads (16 lanes of a phase on 16 consecutive rows hit disjoint
+  // banks), and by 64 bytes for the transposing reads (the 4 rows x 64 bytes
+  // of a phase on disjoint banks); no one stride serves both.
+  constexpr int ROW = D + 8;           // row-read copy stride (16-bit elements)
+  constexpr int TROW = D + 32;         // transposed-read copy stride
   constexpr int CPR = D / 8;
   constexpr int NCH = BQ * CPR / NT;   // 16-byte chunks per thread per tile, each tensor
   static_assert(NCH >= 1 && BQ * CPR % NT == 0, "tile split");
 
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][BQ * ROW];
   __shared__ __attribute__((aligned(16))) uint16_t o_lds[2][BQ * ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t qt_lds[2][BQ * TROW];
+  __shared__ __attribute__((aligned(16))) uint16_t ot_lds[2][BQ * TROW];
   __shared__ __attribute__((aligned(16))) float st_lds[2][2 * BQ];   // lse2 (+inf past S), delta
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -173,6 +180,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
       const int lrow = (row & ~31) + key_to_row(row & 31);
       *reinterpret_cast<u32x4_t*>(&q_lds[buf][lrow * ROW + 8 * ch]) = sq[i];
       *reinterpret_cast<u32x4_t*>(&o_lds[buf][lrow * ROW + 8 * ch]) = so[i];
+      *reinterpret_cast<u32x4_t*>(&qt_lds[buf][lrow * TROW + 8 * ch]) = sq[i];
+      *reinterpret_cast<u32x4_t*>(&ot_lds[buf][lrow * TROW + 8 * ch]) = so[i];
     }
     if (tid < BQ) {
       st_lds[buf][tid] = sl;
@@ -180,7 +189,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
     }
   };
 
-  const int trb = tr_base(lane, ROW);
+  const int trb = tr_base(lane, TROW);
   const int nqt = (S + BQ - 1) / BQ;
   load(0);
   store(0);
@@ -234,10 +243,10 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
             f16x8_t, (u32x4_t){sw[blk][4 * j], sw[blk][4 * j + 1], sw[blk][4 * j + 2], sw[blk][4 * j + 3]});
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const int off = trb + (32 * blk + 16 * j) * ROW + 32 * mb;
-          const bf16x8_t ot = __builtin_bit_cast(bf16x8_t, read_tr8(&o_lds[buf][off], ROW));
+          const int off = trb + (32 * blk + 16 * j) * TROW + 32 * mb;
+          const bf16x8_t ot = __builtin_bit_cast(bf16x8_t, read_tr8(&ot_lds[buf][off], TROW));
           dva[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot, pb, dva[mb], 0, 0, 0);
-          const f16x8_t qt8 = __builtin_bit_cast(f16x8_t, read_tr8(&q_lds[buf][off], ROW));
+          const f16x8_t qt8 = __builtin_bit_cast(f16x8_t, read_tr8(&qt_lds[buf][off], TROW));
           dka[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qt8, sb, dka[mb], 0, 0, 0);
         }
       }
@@ -283,13 +292,15 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
   constexpr int BK = 64;               // keys per step
   constexpr int NT = 512;
   constexpr int KS = D / 16, MB = D / 32, DA = D / 4;
-  constexpr int ROW = D + 8;
+  constexpr int ROW = D + 8;           // row-read copy stride (as in the dk/dv kernel)
+  constexpr int TROW = D + 32;         // transposed-read copy stride (k' only)
   constexpr int CPR = D / 8;
   constexpr int NCH = BK * CPR / NT;
   static_assert(NCH >= 1 && BK * CPR % NT == 0, "tile split");
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * ROW];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BK * ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t kt_lds[2][BK * TROW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lr = lane & 31;
@@ -339,10 +350,11 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
       const int lrow = (row & ~31) + key_to_row(row & 31);
       *reinterpret_cast<u32x4_t*>(&k_lds[buf][lrow * ROW + 8 * ch]) = sk[i];
       *reinterpret_cast<u32x4_t*>(&v_lds[buf][lrow * ROW + 8 * ch]) = sv[i];
+      *reinterpret_cast<u32x4_t*>(&kt_lds[buf][lrow * TROW + 8 * ch]) = sk[i];
     }
   };
 
-  const int trb = tr_base(lane, ROW);
+  const int trb = tr_base(lane, TROW);
   const int nkt = (S + BK - 1) / BK;
   load(0);
   store(0);
@@ -395,8 +407,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
             f16x8_t, (u32x4_t){sw[kbk][4 * j], sw[kbk][4 * j + 1], sw[kbk][4 * j + 2], sw[kbk][4 * j + 3]});
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const int off = trb + (32 * kbk + 16 * j) * ROW + 32 * mb;
-          const f16x8_t kt8 = __builtin_bit_cast(f16x8_t, read_tr8(&k_lds[buf][off], ROW));
+          const int off = trb + (32 * kbk + 16 * j) * TROW + 32 * mb;
+          const f16x8_t kt8 = __builtin_bit_cast(f16x8_t, read_tr8(&kt_lds[buf][off], TROW));
           dqa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kt8, sb, dqa[mb], 0, 0, 0);
         }
       }
