@@ -124,7 +124,9 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t o_lds[2][BQ * ROW];
   __shared__ __attribute__((aligned(16))) uint16_t qt_lds[2][BQ * TROW];
   __shared__ __attribute__((aligned(16))) uint16_t ot_lds[2][BQ * TROW];
-  __shared__ __attribute__((aligned(16))) float st_lds[2][2 * BQ];   // lse2 (+inf past S), delta
+  // -lse2 (-inf past S) and -delta of the tile's queries: the MFMA initial
+  // values as they are
+  __shared__ __attribute__((aligned(16))) float st_lds[2][2 * BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lr = lane & 31;
@@ -169,8 +171,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
     }
     if (tid < BQ) {
       const int qi = q0 + tid;
-      sl = qi < S ? lse_bh[qi] * kLog2e : __builtin_huge_valf();
-      sd = qi < S ? dl_bh[qi] : 0.f;
+      sl = qi < S ? -lse_bh[qi] * kLog2e : kNegInf;
+      sd = qi < S ? -dl_bh[qi] : 0.f;
     }
   };
   auto store = [&](int buf) {
@@ -207,8 +209,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
         const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&st_lds[buf][BQ + 32 * blk + 16 * g + 4 * i4]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sc[blk][4 * i4 + e] = -l4[e];
-          dp[blk][4 * i4 + e] = -d4[e];
+          sc[blk][4 * i4 + e] = l4[e];
+          dp[blk][4 * i4 + e] = d4[e];
         }
       }
 #pragma unroll
