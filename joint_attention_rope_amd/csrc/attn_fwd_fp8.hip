@@ -143,6 +143,9 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   __shared__ __attribute__((aligned(16))) h2_t cs_tab[TAB + TSLOT * NT];
   __shared__ uint16_t klist[SPARSE ? kSparseMaxTiles + kSparsePad : 1];
   __shared__ int klist_n;
+  // E4M3 ones: the A operand of the row-sum MFMA (read by every lane)
+  __shared__ __attribute__((aligned(16))) uint32_t ones_lds[4];
+  if (threadIdx.x < 4) ones_lds[threadIdx.x] = 0x38383838u;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lr = lane & 31;
@@ -301,7 +304,10 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   f32x16_t o[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) o[mb] = (f32x16_t){};
-  float m_run = 0.f, l_run = 0.f;
+  float m_run = 0.f;
+  // row sums of P8 on the MFMA: ones^T P8 puts the sum over the tile's keys
+  // of this lane's query in every register
+  f32x16_t lacc = {};
 
   auto read_k = [&](int kbuf, int kbk, int ks) {
     const uint8_t* src = &k_lds[kbuf][(32 * kbk + lr) * KROW + 64 * ks + 32 * g];
@@ -349,7 +355,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
       const float delta = __builtin_fmaxf(mx - C0, 0.f);
       const float alpha = __builtin_amdgcn_exp2f(-delta);
       m_run += delta;
-      l_run *= alpha;
+      lacc *= alpha;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) o[mb] *= alpha;
 #pragma unroll
@@ -359,7 +365,8 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   };
 
   // Region A: S(t+1) (2 KS MFMAs, K'' operands read two ahead) with the
-  // softmax of S(t) in 8 slices of 4 scores (one P8 word each).
+  // softmax of S(t) in 8 slices of 4 scores (one P8 word each).  The row
+  // sums are taken in region B, from P8 itself.
   constexpr int NA = 2 * KS;
   auto region_a = [&](int kbuf, const f32x16_t* cur, f32x16_t* nxt, i32x8_t& pb) {
     i32x8_t kop[NA];
@@ -367,7 +374,6 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
     nxt[1] = cinit;
     kop[0] = read_k(kbuf, 0 / KS, 0 % KS);
     if (NA > 1) kop[1 % NA] = read_k(kbuf, 1 / KS, 1 % KS);
-    float ls4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       if (i + 2 < NA) kop[i + 2] = read_k(kbuf, (i + 2) / KS, (i + 2) % KS);
@@ -378,10 +384,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
         const int kb2 = sl >> 2, w = sl & 3;
         float p[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(cur[kb2][4 * w + e]);
-          ls4[e] += p[e];
-        }
+        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(cur[kb2][4 * w + e]);
         // both halves of the word are rewritten: the old word only fills
         // the operand that the conversion keeps
         int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pb[4 * kb2 + w], false);
@@ -389,15 +392,15 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    l_run += (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
     // Pin the score MFMAs here: their results are only read in the next
     // step, and without a use here they would be sunk to it, away from the
     // softmax work they are meant to overlap.
     asm volatile("" : "+v"(nxt[0]), "+v"(nxt[1]));
   };
 
-  // Region B: O^T += V(t)^T P8^T (MB MFMAs, V^T operands read two ahead) with
-  // the staging of K''(t+2) (8 rotated pairs) and V(t+1) spread over them.
+  // Region B: O^T += V(t)^T P8^T (MB MFMAs, V^T operands read two ahead) and
+  // the row sums (one more MFMA) with the staging of K''(t+2) (8 rotated
+  // pairs) and V(t+1) spread over them.
   auto read_v = [&](int vbuf, int mb) {
     typedef int i32x2v_t __attribute__((ext_vector_type(2)));
     i32x2v_t r[4];
@@ -431,6 +434,10 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    const u32x4_t on = *reinterpret_cast<const u32x4_t*>(ones_lds);
+    const i32x8_t ones = {(int)on[0], (int)on[1], (int)on[2], (int)on[3],
+                          (int)on[0], (int)on[1], (int)on[2], (int)on[3]};
+    lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb, lacc, 0, 0, 0, 0, 0, 0);
   };
 
   int nsteps = k1 - k0;
@@ -510,7 +517,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
 
   // ---- epilogue: O * dv / l -> bf16; a chunk of a split item stores its
   // partial instead (the merge kernel writes those rows)
-  const float lsum = pair_sum(l_run);
+  const float lsum = lacc[0];
   if constexpr (SPLIT)
     if (k0 != 0 || k1 != nkt) {
       split_store<MB>(o, m_run, lsum, sp, work - sp.n_dp, chunk);
