@@ -39,9 +39,11 @@
 //
 // Softmax runs in the exp2 domain (Q carries log2(e)/sqrt(D)).  The score
 // MFMA chains start from -m (the running row max) rather than zero, so the
-// accumulators hold s - m directly.  O and l are rescaled only when a row's
-// max grows by more than TAU = 8, so p = 2^(s - m) <= 2^8 in between; the
-// final O / l is the same either way.
+// accumulators hold s - m directly.  No row max is taken per tile: m moves
+// (and O and l are rescaled) only when a tile's p = 2^(s - m), summed over the
+// 32 keys a lane holds, exceeds 2^16, so p <= 2^16 in between (or on overflow
+// to inf); the tile's P is then recomputed from its scores.  The final O / l
+// is the same either way.
 //
 // V stays row-major in LDS ([key][d], staged with plain 16-byte copies) and
 // the V^T operand of O^T += V^T P^T is read with ds_read_b64_tr_b16: inside a
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   constexpr int KROW = D + 8;          // LDS row stride of K' (16-bit), padded
   constexpr int VROW = D + 32;         // LDS row stride of V (bf16), padded
   constexpr int DA = D / 4;            // channels per RoPE axis
-  constexpr float TAU = 8.0f;
+  constexpr float kSumLimit = 65536.0f;   // 2^16: the rescale trigger
   constexpr int NJ = D / 8;            // rotation pairs per axis
   constexpr int TROW = NJ + 1;         // cos/sin table row stride (float2)
   constexpr int TSLOT = 4 * KPT + 1;   // per-thread fallback slot stride
@@ -311,10 +313,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) cinit[i] = -m_run;
   };
-  // mask keys past S (last tile only), then the rare rescale: when some row's
-  // max rose more than TAU above m_run, m_run moves up by delta, O and l take
-  // 2^-delta, and the relative scores of this tile shift by -delta
-  auto softmax_max = [&](int t, f32x16_t* sc) {
+  // keys past S (last tile only) take -inf before the exponent
+  auto mask_tail = [&](int t, f32x16_t* sc) {
     if (t * BN + BN > Sk) {
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk)
@@ -322,25 +322,43 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
         for (int i = 0; i < 16; ++i)
           if (t * BN + 32 * kbk + 16 * g + i >= Sk) sc[kbk][i] = kNegInf;
     }
-    const float mx = rowmax32(sc);
-    if (__builtin_amdgcn_ballot_w64(mx > TAU)) {
-      const float delta = __builtin_fmaxf(mx, 0.f);
-      const float alpha = __builtin_amdgcn_exp2f(-delta);
-      m_run += delta;
-      l_run *= alpha;
+  };
+  const bf16x2_t kOnesBf16x2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+  // The rare rescale, once a tile's P (from S(t) = cur) came out too large:
+  // m_run moves up to the tile's row max where that is higher, O and l take
+  // 2^-delta, S(t) and S(t+1) (already formed against the old m) shift by
+  // -delta, and P(t) and this lane's sum of it are recomputed.
+  auto rescale = [&](f32x16_t* cur, f32x16_t* nxt, uint32_t (*pw)[8]) {
+    const float delta = __builtin_fmaxf(rowmax32(cur), 0.f);
+    const float alpha = __builtin_amdgcn_exp2f(-delta);
+    m_run += delta;
+    l_run *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) o[mb] *= alpha;
+    for (int mb = 0; mb < MB; ++mb) o[mb] *= alpha;
 #pragma unroll
-      for (int kbk = 0; kbk < 2; ++kbk) sc[kbk] -= delta;
-      set_cinit();
+    for (int kbk = 0; kbk < 2; ++kbk) {
+      cur[kbk] -= delta;
+      nxt[kbk] -= delta;
     }
+    set_cinit();
+    float ls = 0.f;
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const uint32_t pk = pack_bf16x2(__builtin_amdgcn_exp2f(cur[kbk][2 * w]),
+                                        __builtin_amdgcn_exp2f(cur[kbk][2 * w + 1]));
+        pw[kbk][w] = pk;
+        ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), kOnesBf16x2, ls, false);
+      }
+    return ls;
   };
 
   // Region A: S(t+1) = K'(t+1) Q'^T (2 KS MFMAs, operands read two MFMAs
   // ahead) with one slice of the softmax of S(t) after each MFMA; the
   // sched_barrier fences keep the compiler from regrouping the slices.
+  // Returns this lane's sum of P(t).
   constexpr int NA = 2 * KS;                 // MFMAs in region A
-  const bf16x2_t kOnesBf16x2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
   constexpr int SA = 16;                     // softmax slices (2 scores each)
   auto region_a = [&](int kbuf, const f32x16_t* cur, f32x16_t* nxt, uint32_t (*pw)[8]) {
     f16x8_t ka[NA];
@@ -372,7 +390,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    l_run += (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
+    return (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
   };
 
   // Region B: O^T += V(t)^T P(t)^T (4 MB MFMAs) with the staging of K'(t+2)
@@ -497,14 +515,15 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
 
   // one pipeline step; `cur` holds S(t), `nxt` receives S(t+1)
   // `kps` holds the positions of K(t+2) and receives those of K(t+4).  The
-  // rare branches (rotation fallback, rescale) come first, so that regions
-  // A and B form one block whose interleaving the compiler keeps.
+  // rare branches (rotation fallback, rescale) sit between the regions.
   auto step = [&](int t, f32x16_t* cur, f32x16_t* nxt, int* kps) {
     int ci[KPT];
 #pragma unroll
     for (int it = 0; it < KPT; ++it) ci[it] = key_cs_index(kps, it);
-    softmax_max(tl(t), cur);
-    region_a((t + 1) & 1, cur, nxt, pw);
+    mask_tail(tl(t), cur);
+    float lt = region_a((t + 1) & 1, cur, nxt, pw);
+    if (__builtin_amdgcn_ballot_w64(lt > kSumLimit)) lt = rescale(cur, nxt, pw);
+    l_run += lt;
     // K(t+2) into buffer t&1 (it held K(t), consumed last step); V(t+1) into
     // buffer (t+1)&1 (it held V(t-1), consumed last step)
     region_b(t & 1, t & 1, (t + 1) & 1, pw, ci);

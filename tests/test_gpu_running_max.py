@@ -1,0 +1,87 @@
+"""GPU parity when the running row max has to move during the key stream.
+
+Seeded inputs whose scores grow along the key axis (a ramp: every few tiles
+the softmax mass moves to later keys) or carry one huge key late in the
+sequence (a spike: 2^(s - m) overflows fp32 against the max of the earlier
+tiles).  Positions are zero, so the rotation is the identity and the score
+structure survives it.  Both dtypes, the plain and the workspace entry (the
+latter with the split-KV schedule at S = 4000), against the oracle at the hot
+path's tolerances.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import joint_attention_rope_amd as kl
+from helpers import assert_bf16_close, assert_fp8_close, bf16_tensor_to_f64, oracle_full, to_device
+from workloads import Inputs, bf16_bits_from_f32, e4m3_encode, get_config
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def float_inputs(pattern, S, H, D, seed):
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    shape = (1, S, H, D)
+    q = 0.3 * rng.standard_normal(shape) + 8.0 * u
+    k = 0.3 * rng.standard_normal(shape)
+    v = rng.standard_normal(shape)
+    if pattern == "ramp":
+        # scores from about -14 to +70 (natural log units) along the keys
+        k += np.linspace(-20.0, 100.0, S)[None, :, None, None] * u
+    else:
+        k += rng.standard_normal(shape)
+        for j in (S // 2, S - 5):
+            k[:, j] = 300.0 * u
+    return q, k, v
+
+
+def make(pattern, dtype, S, H, D, seed):
+    q, k, v = float_inputs(pattern, S, H, D, seed)
+    pos = np.zeros((S, 4), dtype=np.int32)
+    if dtype == "bf16":
+        b = lambda x: bf16_bits_from_f32(x.astype(np.float32))
+        return Inputs(get_config(1, B=1, H=H, D=D), b(q), b(k), b(v), pos)
+    codes, scales = [], []
+    for x in (q, k, v):
+        xb = (bf16_bits_from_f32(x.astype(np.float32)).astype(np.uint32) << np.uint32(16)).view(np.float32)
+        sc = float(np.float32(np.max(np.abs(xb)) / 448.0))
+        codes.append(e4m3_encode(xb.astype(np.float64) / sc))
+        scales.append(sc)
+    return Inputs(get_config(5, B=1, H=H, D=D), *codes, pos, descale=tuple(scales))
+
+
+def run(inp, workspace):
+    q, k, v, pos = to_device(inp, DEV)
+    B, S, H, D = q.shape
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=DEV)
+    if workspace:
+        dt = kl.KLEIN_DTYPE_BF16 if inp.descale is None else kl.KLEIN_DTYPE_FP8_E4M3
+        ws = torch.empty(kl.klein_attn_workspace_size(B, S, H, D, dt), dtype=torch.uint8, device=DEV)
+        kl.klein_rope4d_attn_fwd_ws(q, k, v, pos, out, ws, dtype=dt,
+                                    descales=inp.descale or (1.0, 1.0, 1.0))
+    elif inp.descale is None:
+        kl.klein_rope4d_attn_fwd(q, k, v, pos, out)
+    else:
+        kl.klein_rope4d_attn_fwd_fp8(q, k, v, pos, out, *inp.descale)
+    torch.cuda.synchronize()
+    return bf16_tensor_to_f64(out)
+
+
+@pytest.mark.parametrize("workspace", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("pattern", ["ramp", "spike"])
+@pytest.mark.parametrize("S,H,D", [(1000, 2, 128), (4000, 1, 128), (700, 3, 64)])
+def test_running_max_moves(pattern, dtype, workspace, S, H, D):
+    inp = make(pattern, dtype, S, H, D, seed=S + D)
+    print(f"[case] {pattern} {dtype} ws={workspace} S={S} H={H} D={D}", flush=True)
+    got = run(inp, workspace)
+    ref = oracle_full(inp)
+    what = f"{pattern} {dtype} ws={workspace} S={S} H={H} D={D}"
+    if dtype == "bf16":
+        assert_bf16_close(got, ref, what)
+    else:
+        assert_fp8_close(got, ref, what)
