@@ -15,7 +15,8 @@
 //   P8  = e4m3(p)                        when a row grows by more than TAU = 8,
 //                                        so p <= 1.75 * 2^8 = 448
 //   O^T += V^T P8^T                      V row-major in LDS, read transposed
-//   out = O * dv / l,                    l = sum of p (fp32; the 1.75 cancels)
+//   l  += ones^T P8^T                    row sums of P8, on the MFMA as well
+//   out = O * dv / l                     (the 1.75 cancels)
 //
 // with G = 2 dq dk log2(e) / sqrt(D): the exp2-domain score of query i and
 // key j is dq dk log2(e)/sqrt(D) <R q_i, R k_j> = G <R q_i, K''_j>, and n is
@@ -31,13 +32,13 @@
 //
 // Schedule (per wave; K'' and V double-buffered in LDS, one barrier a tile):
 //   softmax max of S(t); rare rescale of O and l
-//   region A:  S(t+1) MFMAs      interleaved with  p = 2^S(t), P8, row sums
+//   region A:  S(t+1) MFMAs      interleaved with  p = 2^S(t), P8
 //   region B:  O^T += V(t)^T P8  interleaved with  staging K''(t+2) and
-//                                                   V(t+1) into LDS
+//              and l += 1^T P8                      V(t+1) into LDS
 //   buffer loads of K(t+3), V(t+2); barrier
 //
 // Rotation of keys: cos and sin (times 1/2) of every (position, pair)
-// with position in [0, 512) come from an LDS table built once per workgroup;
+// with position in [0, 1024) come from an LDS table built once per workgroup;
 // a wave that holds any other position computes them directly instead.
 //
 // MFMA operands: the score MFMA puts keys on rows and queries on columns, and
