@@ -30,6 +30,7 @@
 // accumulators a lane holds the interleaved channel pairs (d, d+1) of one
 // token in adjacent registers.
 #include <cmath>
+#include <type_traits>
 
 #include "klein_device.hpp"
 #include "klein_launch.hpp"
@@ -361,9 +362,13 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
   load(0);
   store(0);
   __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
+  // one key tile; the last one (LAST) masks keys past S and prefetches
+  // nothing, so the others form one branch-free block that the compiler can
+  // interleave (MFMAs of one 32-key block with the exponentials of the other)
+  auto step = [&](int kt, auto last) {
+    constexpr bool LAST = decltype(last)::value;
     const int buf = kt & 1;
-    if (kt + 1 < nkt) load(kt + 1);
+    if constexpr (!LAST) load(kt + 1);
     f32x16_t sc[2], dp[2];
 #pragma unroll
     for (int kbk = 0; kbk < 2; ++kbk) {
@@ -383,7 +388,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
     }
     // keys past S (last tile only): p = 0 (their k' rows read as zeros, but
     // 2^(-lse2) alone could overflow)
-    if (kt * BK + BK > S) {
+    if constexpr (LAST) {
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
@@ -414,9 +419,13 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
           dqa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kt8, sb, dqa[mb], 0, 0, 0);
         }
       }
-    if (kt + 1 < nkt) store(buf ^ 1);
-    __syncthreads();
-  }
+    if constexpr (!LAST) {
+      store(buf ^ 1);
+      __syncthreads();
+    }
+  };
+  for (int kt = 0; kt + 1 < nkt; ++kt) step(kt, std::false_type{});
+  step(nkt - 1, std::true_type{});
 
   if (!qval) return;
   const size_t row = base + (size_t)query * rs;
