@@ -7,9 +7,9 @@
 // workgroup barrier per tile separates producers from consumers:
 //
 //   iteration t (S(t) already in registers):
-//     softmax max of S(t); rare rescale of O and l
 //     region A:  S(t+1) = K'(t+1) Q'^T  (16 MFMAs)       interleaved with
 //                P(t) = 2^(S(t) - m), row sums, bf16 pack   (VALU)
+//     rare rescale of O, l and P(t) when P(t) came out too large
 //     region B:  O^T += V(t)^T P(t)^T  (16 MFMAs)        interleaved with
 //                staging K'(t+2) (RoPE-4D) and V(t+1)^T into LDS, and the
 //                buffer loads of K(t+3), V(t+2) from HBM
