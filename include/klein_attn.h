@@ -148,6 +148,30 @@ klein_status_t klein_attn_workspace_size(int B, int S, int H, int D, klein_dtype
                                          size_t* bytes);
 
 /*
+ * The split-KV plan that klein_rope4d_attn_fwd_ws follows for this shape on a
+ * GPU with n_cu compute units.  Host-only: touches no device, so it also
+ * serves to inspect the schedule for other GPUs.  With
+ *   items = B * H * ceil(S / 256)      (one workgroup each: 256 queries)
+ *   nkt   = ceil(S / 64)               (64-key tiles per item)
+ *   rem   = items mod n_cu             (items of the last, partial round)
+ * nothing is cut when nkt < 32 or rem == 0.  Otherwise each chunk count
+ * c = 2, 3, ... with 8 c <= nkt and c * rem <= 4 * n_cu is priced at
+ *   cost(c) = ceil(c * rem / n_cu) * (nkt / c + 6)   tile steps
+ * against cost(1) = nkt for whole items; the cheapest c (the smallest on a
+ * tie) is taken if its cost is at most 0.85 * nkt, else nothing is cut.
+ * On return:
+ *   plan[0] = items run whole (first, in whole rounds when anything is cut)
+ *   plan[1] = items cut into key chunks (rem, or 0)
+ *   plan[2] = chunks per cut item (c, or 0)
+ *   *partial_bytes = c * rem * (256 * D + 1024) * 4, the fp32 partials'
+ *                    share of the workspace (0 when nothing is cut)
+ * INVALID_ARG for null outputs or sizes < 1 (n_cu included), UNSUPPORTED
+ * for D not in {64, 128} or a grid past 2^31 - 1 workgroups.
+ */
+klein_status_t klein_splitkv_plan(int B, int S, int H, int D, int n_cu, int* plan,
+                                  size_t* partial_bytes);
+
+/*
  * Training forward: klein_rope4d_attn_fwd for bfloat16 inputs that also
  * writes the softmax statistic the backward needs,
  *   lse[b][h][i] = log sum_j exp(<q'_i, k'_j> / sqrt(D))   (natural log),

@@ -21,8 +21,8 @@ __all__ = [
     "klein_version", "library_path", "KLEIN_DTYPE_BF16", "KLEIN_DTYPE_FP8_E4M3",
     "KLEIN_SPARSE_QBLOCK", "KLEIN_SPARSE_KBLOCK", "blocksparse_mask_shape",
     "klein_qkv_rope4d_proj", "klein_attn_fwd_prerotated", "klein_rope4d_attn_fwd_ws",
-    "klein_attn_workspace_size", "klein_rope4d_attn_fwd_lse", "klein_rope4d_attn_bwd",
-    "klein_attn_bwd_workspace_size",
+    "klein_attn_workspace_size", "klein_splitkv_plan", "klein_rope4d_attn_fwd_lse",
+    "klein_rope4d_attn_bwd", "klein_attn_bwd_workspace_size",
 ]
 
 
@@ -123,13 +123,26 @@ def klein_rope4d_attn_fwd_fp8(q, k, v, pos_thwl, out, q_descale, k_descale, v_de
 
 def klein_attn_workspace_size(B, S, H, D, dtype=KLEIN_DTYPE_BF16):
     """Bytes of workspace klein_rope4d_attn_fwd_ws needs for this shape on the
-    current device (0: nothing is split)."""
+    current device: the rotated keys, then the split partials (if any)."""
     import ctypes
     n = ctypes.c_size_t(0)
     st = _capi.lib().klein_attn_workspace_size(int(B), int(S), int(H), int(D), int(dtype),
                                                ctypes.byref(n))
     _check(st, "klein_attn_workspace_size")
     return n.value
+
+
+def klein_splitkv_plan(B, S, H, D, n_cu):
+    """The split-KV plan of klein_rope4d_attn_fwd_ws on a GPU with n_cu compute
+    units (host only): (whole items, cut items, chunks per cut item, partial
+    bytes)."""
+    import ctypes
+    plan = (ctypes.c_int * 3)()
+    n = ctypes.c_size_t(0)
+    st = _capi.lib().klein_splitkv_plan(int(B), int(S), int(H), int(D), int(n_cu), plan,
+                                        ctypes.byref(n))
+    _check(st, "klein_splitkv_plan")
+    return plan[0], plan[1], plan[2], n.value
 
 
 def klein_rope4d_attn_fwd_ws(q, k, v, pos_thwl, out, workspace, dtype=None,

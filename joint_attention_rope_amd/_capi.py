@@ -35,6 +35,8 @@ SIGNATURES = {
                                         _f32, _f32, _f32, _vp, ctypes.c_size_t, _vp]),
     "klein_attn_workspace_size": (_int, [_int, _int, _int, _int, _int,
                                          ctypes.POINTER(ctypes.c_size_t)]),
+    "klein_splitkv_plan": (_int, [_int, _int, _int, _int, _int, ctypes.POINTER(ctypes.c_int),
+                                  ctypes.POINTER(ctypes.c_size_t)]),
     "klein_rope4d_attn_fwd_lse": (_int, [_vp, _vp, _vp, _i32p, _vp, _vp, _int, _int, _int, _int,
                                          _vp]),
     "klein_rope4d_attn_bwd": (_int, [_vp, _vp, _vp, _i32p, _vp, _vp, _vp, _vp, _vp, _vp, _int,

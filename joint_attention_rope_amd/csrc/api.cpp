@@ -216,6 +216,20 @@ klein_status_t klein_attn_workspace_size(int B, int S, int H, int D, klein_dtype
   }
 }
 
+klein_status_t klein_splitkv_plan(int B, int S, int H, int D, int n_cu, int* plan,
+                                  size_t* partial_bytes) {
+  if (!plan || !partial_bytes) return KLEIN_ERR_INVALID_ARG;
+  if (B < 1 || S < 1 || H < 1 || n_cu < 1) return KLEIN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return KLEIN_ERR_UNSUPPORTED;
+  if (klein::attn_fwd_bf16_grid(B, S, H) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
+  const klein::SplitPlan p = klein::plan_split(B, S, H, D, n_cu);
+  plan[0] = p.n_sk > 0 ? p.n_dp : (int)klein::attn_fwd_bf16_grid(B, S, H);
+  plan[1] = p.n_sk > 0 ? p.n_rem : 0;
+  plan[2] = p.n_sk > 0 ? p.n_chunk : 0;
+  *partial_bytes = (size_t)p.bytes;
+  return KLEIN_OK;
+}
+
 klein_status_t klein_rope4d_attn_fwd_ws(const void* q, const void* k, const void* v,
                                         const int32_t* pos_thwl, void* out, int B, int S, int H,
                                         int D, klein_dtype_t dtype, float q_descale,
@@ -352,6 +366,6 @@ const char* klein_status_string(klein_status_t status) {
   return "unknown status";
 }
 
-int klein_version(void) { return 130; }
+int klein_version(void) { return 131; }
 
 }  // extern "C"
