@@ -173,3 +173,16 @@ def test_graph_capture_replays():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {i}"
+
+
+@pytest.mark.parametrize("B,S,H,D,fp8", [(2, 16896, 24, 128, False), (1, 33280, 24, 128, True),
+                                         (1, 16896, 4, 128, False), (1, 1000, 3, 64, False)])
+def test_workspace_size_is_keys_plus_planned_partials(B, S, H, D, fp8):
+    # the size query on this GPU = the rotated keys (256-aligned) + the
+    # partials of the plan for this GPU's compute-unit count
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    dtype = kl.KLEIN_DTYPE_FP8_E4M3 if fp8 else kl.KLEIN_DTYPE_BF16
+    keys = B * S * H * D * (1 if fp8 else 2)
+    keys = (keys + 255) // 256 * 256
+    assert kl.klein_attn_workspace_size(B, S, H, D, dtype) == \
+        keys + kl.klein_splitkv_plan(B, S, H, D, ncu)[3]
