@@ -334,6 +334,34 @@ def main():
             "peak": PEAK_BF16, "frac": round(gf / (pms * 1e-3) / 1e12 / PEAK_BF16, 4),
             "torch_addmm_ms": round(tms, 4),
             "torch_addmm_tflops": round(gf / (tms * 1e-3) / 1e12, 2)})
+        # the same projection on E4M3 operands (per-tensor amax/448 scales),
+        # against torch's fp8 GEMM (torch._scaled_mm, hipBLASLt) on the codes
+        sx = float(xx.float().abs().max()) / 448.0
+        sw = float(ww.float().abs().max()) / 448.0
+        x8 = (xx.float() / sx).to(torch.float8_e4m3fn)
+        w8 = (ww.float() / sw).to(torch.float8_e4m3fn)
+        xq, wq = x8.view(torch.uint8), w8.view(torch.uint8)
+        fms = time_gpu(lambda: kl.klein_qkv_rope4d_proj(xq, wq, bb, pp, qo, ko, vo,
+                                                        descales=(sx, sw)), 10, 3, torch)
+        rec_fp8 = {
+            "workload": f"QKV projection + RoPE-4D epilogue, FP8 operands: x [{c.B}, {c.S}, {C}] "
+                        f"and W [{3 * C}, {C}] E4M3 with per-tensor scales, bf16 bias; "
+                        f"q', k' fp16, v bf16",
+            "ms_per_call": round(fms, 4), "tflops": round(gf / (fms * 1e-3) / 1e12, 2),
+            "peak": PEAK_FP8, "frac": round(gf / (fms * 1e-3) / 1e12 / PEAK_FP8, 4)}
+        try:
+            one = torch.ones((), device=dev)
+            sa_, sb_ = one * sx, one * sw
+            x8m = x8.view(-1, C)
+            yy8 = lambda: torch._scaled_mm(x8m, w8.t(), scale_a=sa_, scale_b=sb_,
+                                           out_dtype=torch.bfloat16)
+            sms = time_gpu(yy8, 10, 3, torch)
+            rec_fp8["torch_scaled_mm_ms"] = round(sms, 4)
+            rec_fp8["torch_scaled_mm_tflops"] = round(gf / (sms * 1e-3) / 1e12, 2)
+        except Exception as e:     # the comparison only; the projection is timed above
+            rec_fp8["torch_scaled_mm"] = f"unavailable: {e}"
+        rec["extra"].append(rec_fp8)
+        del x8, w8, xq, wq
         rec["extra"].append({
             "workload": f"attention on pre-rotated fp16 q', k' (bf16 v): {c.name}, B={c.B}, "
                         f"S={c.S}, H={c.H}, D={c.D}",

@@ -271,6 +271,25 @@ klein_status_t klein_qkv_rope4d_proj(const void* x, const void* w, const void* b
                                      klein_stream_t stream);
 
 /*
+ * The same projection with FP8 operands (the quantised GEMMs of "How FLUX 3
+ * Image Klein was made 3-4x faster on NVIDIA Blackwell", section "Method 1",
+ * in the E4M3 format this library's FP8 attention takes):
+ *   x : [B][S][C] E4M3FN codes, value = decode(code) * x_descale
+ *   w : [3*H*D][C] E4M3FN codes, value = decode(code) * w_descale
+ *   y = (sum_c x_code w_code) * x_descale * w_descale (+ bias), fp32
+ *   accumulation; bias bfloat16 as above; outputs, rotation and rounding as
+ *   klein_qkv_rope4d_proj (fp16 q', k', bfloat16 v).
+ * C must be a multiple of 128 (UNSUPPORTED otherwise) and at most 65536;
+ * descales finite and > 0 (else INVALID_ARG).  Device pointers, 16-byte
+ * aligned (bias 8), caller-owned; nothing allocated.
+ */
+klein_status_t klein_qkv_rope4d_proj_fp8(const void* x, const void* w, const void* bias,
+                                         const int32_t* pos_thwl, void* q_out, void* k_out,
+                                         void* v_out, int B, int S, int C, int H, int D,
+                                         float x_descale, float w_descale,
+                                         klein_stream_t stream);
+
+/*
  * Joint attention of queries and keys that are already rotated (as
  * klein_qkv_rope4d_proj emits them): out_i = sum_j softmax_j(<q_i, k_j> /
  * sqrt(D)) v_j over all j, no mask -- the definition above with the rotation

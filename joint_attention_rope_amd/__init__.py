@@ -278,13 +278,18 @@ def klein_rope4d_attn_fwd_blocksparse(q, k, v, pos_thwl, out, block_mask, dtype=
     return out
 
 
-def klein_qkv_rope4d_proj(x, w, bias, pos_thwl, q_out, k_out, v_out, stream=None):
+def klein_qkv_rope4d_proj(x, w, bias, pos_thwl, q_out, k_out, v_out, stream=None,
+                          descales=None):
     """q_out, k_out (fp16, rotated), v_out (bf16) [B, S, H, D] <- x W^T + bias.
 
-    x: bf16 [B, S, C]; w: bf16 [3 H D, C]; bias: bf16 [3 H D] or None.
+    x: bf16 [B, S, C]; w: bf16 [3 H D, C]; bias: bf16 [3 H D] or None.  With
+    descales = (x_descale, w_descale), x and w are E4M3 codes (uint8 tensors)
+    and the FP8 entry point computes (x_code w_code^T) x_descale w_descale.
     """
-    if x.dim() != 3 or x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
-        raise ValueError("x must be a contiguous bfloat16 GPU tensor [B, S, C]")
+    fp8 = descales is not None
+    xt = torch.uint8 if fp8 else torch.bfloat16
+    if x.dim() != 3 or x.dtype != xt or not x.is_cuda or not x.is_contiguous():
+        raise ValueError(f"x must be a contiguous {xt} GPU tensor [B, S, C]")
     B, S, C = x.shape
     Bq, Sq, H, D = _bshd(q_out, "q_out")
     if (Bq, Sq) != (B, S) or _bshd(k_out, "k_out") != (B, S, H, D) \
@@ -292,18 +297,23 @@ def klein_qkv_rope4d_proj(x, w, bias, pos_thwl, q_out, k_out, v_out, stream=None
         raise ValueError("q_out, k_out, v_out must be [B, S, H, D] for x's B, S")
     if q_out.dtype != torch.float16 or k_out.dtype != torch.float16 or v_out.dtype != torch.bfloat16:
         raise ValueError("q_out and k_out must be float16, v_out bfloat16")
-    if w.dtype != torch.bfloat16 or tuple(w.shape) != (3 * H * D, C) or not w.is_cuda \
+    if w.dtype != xt or tuple(w.shape) != (3 * H * D, C) or not w.is_cuda \
             or not w.is_contiguous():
-        raise ValueError(f"w must be a contiguous bfloat16 GPU tensor [{3 * H * D}, {C}]")
+        raise ValueError(f"w must be a contiguous {xt} GPU tensor [{3 * H * D}, {C}]")
     if bias is not None and (bias.dtype != torch.bfloat16 or tuple(bias.shape) != (3 * H * D,)
                              or not bias.is_cuda or not bias.is_contiguous()):
         raise ValueError(f"bias must be None or a bfloat16 GPU tensor [{3 * H * D}]")
     _pos(pos_thwl, S)
-    st = _capi.lib().klein_qkv_rope4d_proj(
-        x.data_ptr(), w.data_ptr(), 0 if bias is None else bias.data_ptr(), pos_thwl.data_ptr(),
-        q_out.data_ptr(), k_out.data_ptr(), v_out.data_ptr(), B, S, C, H, D,
-        _stream(stream, x.device))
-    _check(st, "klein_qkv_rope4d_proj")
+    ptrs = (x.data_ptr(), w.data_ptr(), 0 if bias is None else bias.data_ptr(),
+            pos_thwl.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), v_out.data_ptr(),
+            B, S, C, H, D)
+    if fp8:
+        st = _capi.lib().klein_qkv_rope4d_proj_fp8(*ptrs, float(descales[0]), float(descales[1]),
+                                                   _stream(stream, x.device))
+        _check(st, "klein_qkv_rope4d_proj_fp8")
+    else:
+        st = _capi.lib().klein_qkv_rope4d_proj(*ptrs, _stream(stream, x.device))
+        _check(st, "klein_qkv_rope4d_proj")
     return q_out, k_out, v_out
 
 

@@ -45,6 +45,8 @@ SIGNATURES = {
                                              ctypes.POINTER(ctypes.c_size_t)]),
     "klein_qkv_rope4d_proj": (_int, [_vp, _vp, _vp, _i32p, _vp, _vp, _vp, _int, _int, _int,
                                      _int, _int, _vp]),
+    "klein_qkv_rope4d_proj_fp8": (_int, [_vp, _vp, _vp, _i32p, _vp, _vp, _vp, _int, _int, _int,
+                                         _int, _int, _f32, _f32, _vp]),
     "klein_attn_fwd_prerotated": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp]),
     "klein_rope4d_apply": (_int, [_vp, _i32p, _vp, _int, _int, _int, _int, _vp]),
     "klein_status_string": (ctypes.c_char_p, [_int]),

@@ -314,14 +314,17 @@ klein_status_t klein_attn_fwd_prerotated(const void* q, const void* k, const voi
   }
 }
 
-klein_status_t klein_qkv_rope4d_proj(const void* x, const void* w, const void* bias,
-                                     const int32_t* pos_thwl, void* q_out, void* k_out,
-                                     void* v_out, int B, int S, int C, int H, int D,
-                                     klein_stream_t stream) {
+static klein_status_t qkv_proj(const void* x, const void* w, const void* bias,
+                               const int32_t* pos_thwl, void* q_out, void* k_out, void* v_out,
+                               int B, int S, int C, int H, int D, bool fp8, float x_descale,
+                               float w_descale, klein_stream_t stream) {
   if (!x || !w || !pos_thwl || !q_out || !k_out || !v_out) return KLEIN_ERR_INVALID_ARG;
   if (B < 1 || S < 1 || C < 1 || H < 1) return KLEIN_ERR_INVALID_ARG;
+  if (fp8 && !(std::isfinite(x_descale) && x_descale > 0.f && std::isfinite(w_descale) &&
+               w_descale > 0.f))
+    return KLEIN_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return KLEIN_ERR_UNSUPPORTED;
-  if (C % 64 != 0 || C > 65536) return KLEIN_ERR_UNSUPPORTED;
+  if (C % (fp8 ? 128 : 64) != 0 || C > 65536) return KLEIN_ERR_UNSUPPORTED;
   for (const void* p : {x, w, (const void*)q_out, (const void*)k_out, (const void*)v_out,
                         (const void*)pos_thwl})
     if (!aligned16(p)) return KLEIN_ERR_INVALID_ARG;
@@ -330,7 +333,8 @@ klein_status_t klein_qkv_rope4d_proj(const void* x, const void* w, const void* b
   if ((long long)B * S * H * D * 3 >= (1LL << 40)) return KLEIN_ERR_UNSUPPORTED;
   try {
     klein::QkvArgs a{};
-    a.x = (const uint16_t*)x; a.w = (const uint16_t*)w; a.bias = (const uint16_t*)bias;
+    a.x = x; a.w = w; a.bias = (const uint16_t*)bias;
+    a.fp8 = fp8; a.x_descale = x_descale; a.w_descale = w_descale;
     a.pos = pos_thwl;
     a.q = (uint16_t*)q_out; a.k = (uint16_t*)k_out; a.v = (uint16_t*)v_out;
     a.B = B; a.S = S; a.C = C; a.H = H; a.D = D;
@@ -340,6 +344,23 @@ klein_status_t klein_qkv_rope4d_proj(const void* x, const void* w, const void* b
   } catch (...) {
     return KLEIN_ERR_LAUNCH;
   }
+}
+
+klein_status_t klein_qkv_rope4d_proj(const void* x, const void* w, const void* bias,
+                                     const int32_t* pos_thwl, void* q_out, void* k_out,
+                                     void* v_out, int B, int S, int C, int H, int D,
+                                     klein_stream_t stream) {
+  return qkv_proj(x, w, bias, pos_thwl, q_out, k_out, v_out, B, S, C, H, D, false, 1.f, 1.f,
+                  stream);
+}
+
+klein_status_t klein_qkv_rope4d_proj_fp8(const void* x, const void* w, const void* bias,
+                                         const int32_t* pos_thwl, void* q_out, void* k_out,
+                                         void* v_out, int B, int S, int C, int H, int D,
+                                         float x_descale, float w_descale,
+                                         klein_stream_t stream) {
+  return qkv_proj(x, w, bias, pos_thwl, q_out, k_out, v_out, B, S, C, H, D, true, x_descale,
+                  w_descale, stream);
 }
 
 klein_status_t klein_rope4d_apply(const void* x, const int32_t* pos_thwl, void* y, int B, int S,

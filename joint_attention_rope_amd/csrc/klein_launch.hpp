@@ -85,10 +85,13 @@ hipError_t launch_attn_bwd(const BwdArgs& a);
 long long attn_bwd_workspace_bytes(int B, int S, int H, int D);
 
 // QKV projection with the RoPE-4D epilogue: x [B S][C] bf16, w [3 H D][C]
-// bf16, bias [3 H D] bf16 or null -> q', k' fp16 and v bf16, [B][S][H][D].
+// bf16 (or both E4M3 codes with descales, fp8), bias [3 H D] bf16 or null
+// -> q', k' fp16 and v bf16, [B][S][H][D].
 struct QkvArgs {
-  const uint16_t* x;
-  const uint16_t* w;
+  const void* x;
+  const void* w;
+  bool fp8;
+  float x_descale, w_descale;
   const uint16_t* bias;
   const int32_t* pos;
   uint16_t* q;

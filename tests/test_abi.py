@@ -22,7 +22,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "klein_rope4d_attn_fwd", "klein_rope4d_attn_fwd_fp8", "klein_rope4d_attn_fwd_blocksparse",
-        "klein_qkv_rope4d_proj", "klein_attn_fwd_prerotated", "klein_rope4d_attn_fwd_ws",
+        "klein_qkv_rope4d_proj", "klein_qkv_rope4d_proj_fp8", "klein_attn_fwd_prerotated",
+        "klein_rope4d_attn_fwd_ws",
         "klein_attn_workspace_size", "klein_splitkv_plan", "klein_rope4d_attn_fwd_lse",
         "klein_rope4d_attn_bwd", "klein_attn_bwd_workspace_size", "klein_rope4d_apply",
         "klein_status_string", "klein_version"])

@@ -1,10 +1,13 @@
-"""GPU parity of the QKV projection with its RoPE-4D epilogue and of the
-attention on pre-rotated queries and keys, each against the oracle.
+"""GPU parity of the QKV projection with its RoPE-4D epilogue (bf16 and FP8
+operands) and of the attention on pre-rotated queries and keys, each against
+the oracle.
 
 Tolerances of the projection: its outputs are fp32 sums rounded once, to
 fp16 (q', k': relative rounding error <= 2^-11) or bf16 (v: <= 2^-8), so the
 relative L2 error over a tensor is bounded by those with margin: 1e-3 for
-q', k' and 5e-3 for v.  The attention keeps the bf16 bounds of the hot path.
+q', k' and 5e-3 for v.  With FP8 operands every product of two E4M3 values
+is exact in fp32, so the same bounds hold against the projection of the
+decoded codes.  The attention keeps the bf16 bounds of the hot path.
 """
 
 import numpy as np
@@ -95,3 +98,60 @@ def test_pipeline_matches_fused_definition():
     ref = oracle.attention(y[:, :, 0], y[:, :, 1], y[:, :, 2], pos)
     max_abs, rel = errors(bf16_tensor_to_f64(out), ref)
     assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2, (max_abs, rel)
+
+
+def fp8_case(B, S, C, H, D, bias, seed):
+    """E4M3 codes of N(0, 1) x and N(0, 1/C) W with per-tensor amax/448
+    scales, and their float64 values (code x descale) for the oracle."""
+    import oracle
+    from workloads import e4m3_encode
+    rng = np.random.default_rng(seed)
+    codes, vals, scales = [], [], []
+    for shape, sd in (((B, S, C), 1.0), ((3 * H * D, C), 1.0 / np.sqrt(C))):
+        a = (rng.standard_normal(shape) * sd).astype(np.float32).astype(np.float64)
+        sc = float(np.float32(np.max(np.abs(a)) / 448.0))
+        c = e4m3_encode(a / sc)
+        codes.append(torch.from_numpy(c).to(DEV))
+        vals.append(oracle.e4m3_decode(c) * sc)
+        scales.append(sc)
+    b_t, b = bf16_dev(rng.standard_normal(3 * H * D) * 0.1) if bias else (None, None)
+    pos = rng.integers(-50, 600, size=(S, 4)).astype(np.int32)
+    dev = (codes[0], codes[1], b_t, torch.from_numpy(pos).to(DEV))
+    return dev, tuple(scales), (vals[0], vals[1], b, pos)
+
+
+@pytest.mark.parametrize("B,S,C,H,D,bias", [
+    (2, 300, 128, 2, 64, True),      # one K step, partial feature and token tiles
+    (1, 513, 256, 4, 128, False),
+    (1, 1000, 3072, 2, 128, True),   # the hidden size of the bench shape
+    (3, 77, 384, 3, 64, True),
+])
+def test_fp8_projection_matches_oracle(B, S, C, H, D, bias):
+    import oracle
+    dev_args, descales, host = fp8_case(B, S, C, H, D, bias, seed=S + C + 1)
+    q = torch.empty(B, S, H, D, dtype=torch.float16, device=DEV)
+    k = torch.empty_like(q)
+    v = torch.empty(B, S, H, D, dtype=torch.bfloat16, device=DEV)
+    kl.klein_qkv_rope4d_proj(*dev_args, q, k, v, descales=descales)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.qkv_rope4d_proj(*host, H, D)
+    for got, ref, bound, name in ((f16_to_f64(q), rq, 1e-3, "q'"), (f16_to_f64(k), rk, 1e-3, "k'"),
+                                  (bf16_tensor_to_f64(v), rv, 5e-3, "v")):
+        _, rel = errors(got, ref)
+        assert np.isfinite(got).all() and rel <= bound, f"{name}: rel_l2 {rel:.3e} > {bound}"
+
+
+def test_fp8_projection_rejects_bad_descales_and_width():
+    dev_args, _, _ = fp8_case(1, 64, 128, 1, 64, False, seed=5)
+    q = torch.empty(1, 64, 1, 64, dtype=torch.float16, device=DEV)
+    k = torch.empty_like(q)
+    v = torch.empty(1, 64, 1, 64, dtype=torch.bfloat16, device=DEV)
+    for d in ((0.0, 1.0), (1.0, float("inf")), (-1.0, 1.0)):
+        with pytest.raises(kl.KleinError) as e:
+            kl.klein_qkv_rope4d_proj(*dev_args, q, k, v, descales=d)
+        assert e.value.status == kl.KLEIN_ERR_INVALID_ARG
+    x64 = torch.zeros(1, 64, 64, dtype=torch.uint8, device=DEV)     # C = 64: not a multiple of 128
+    w64 = torch.zeros(3 * 64, 64, dtype=torch.uint8, device=DEV)
+    with pytest.raises(kl.KleinError) as e:
+        kl.klein_qkv_rope4d_proj(x64, w64, None, dev_args[3], q, k, v, descales=(1.0, 1.0))
+    assert e.value.status == kl.KLEIN_ERR_UNSUPPORTED
