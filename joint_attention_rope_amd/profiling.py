@@ -253,6 +253,47 @@ def algorithmic_bytes(workload):
     return cfg, 3 * n * elem + 16 * cfg.S, 2 * n
 
 
+BWD_SOURCES = ["klein_device.hpp", "attn_bwd.hip"]
+BWD_KERNELS = (("prep", "attn_bwd_prep_kernel<128>"), ("dK/dV", "attn_bwd_dkdv_kernel<128>"),
+               ("dQ", "attn_bwd_dq_kernel<128>"))
+
+
+def backward_markdown(stats_dir, workloads, command):
+    """Per-kernel durations of the backward's three kernels, one table per
+    workload; a workload's dispatches are told apart by their grids (prep:
+    one work-item per 8 channels of B S H D, rounded up to 256; dK/dV and dQ:
+    B H ceil(S / 256) workgroups of 512)."""
+    from workloads import get_config
+    rows = _rows(_find(stats_dir, "kernel_trace.csv"))
+    size = lambda r: int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+    md = [f"# attn_bwd kernels\n\nThe backward's kernels (prep, dK/dV, dQ) at D = 128; sources "
+          f"hash {sources_hash(BWD_SOURCES)} ({', '.join(BWD_SOURCES)}).\n\nCommand (run from "
+          f"/tmp with TMPDIR=/tmp; R = repository root):\n\n```\n{command}\n```\n"]
+    for w in workloads:
+        cfg = get_config(w)
+        grids = {"prep": -(-cfg.B * cfg.S * cfg.H * cfg.D // 8 // 256) * 256,
+                 "dK/dV": cfg.B * cfg.H * -(-cfg.S // 256) * 512,
+                 "dQ": cfg.B * cfg.H * -(-cfg.S // 256) * 512}
+        durs = {label: [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in rows
+                        if name in r["Kernel_Name"] and size(r) == grids[label]]
+                for label, name in BWD_KERNELS}
+        if not all(durs.values()):
+            continue
+        mean = {k: sum(v) / len(v) for k, v in durs.items()}
+        unit = cfg.B * cfg.H * cfg.S * cfg.S * cfg.D
+        total = sum(mean.values())
+        md.append(f"\n## {cfg.name}: B={cfg.B}, S={cfg.S}, H={cfg.H}, D={cfg.D}\n\n"
+                  f"| kernel | dispatches | mean ms | MFMA flops (x B H S^2 D) | TFLOP/s on them |\n"
+                  f"|---|---|---|---|---|\n")
+        for label, units in (("prep", 0), ("dK/dV", 8), ("dQ", 6)):
+            rate = f"{units * unit / (mean[label] * 1e-3) / 1e12:.1f}" if units else "-"
+            md.append(f"| {label} | {len(durs[label])} | {mean[label]:.4f} | {units or '-'} | "
+                      f"{rate} |\n")
+        md.append(f"| the backward (sum of the means) | | {total:.4f} | 10 (algorithmic) | "
+                  f"{10 * unit / (total * 1e-3) / 1e12:.1f} |\n")
+    return "".join(md)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--call", choices=sorted(CALLS),
@@ -269,9 +310,20 @@ def main():
                     help="ms per call that bench.py printed in the stats run")
     ap.add_argument("--counters", nargs=2, metavar=("PASS1", "PASS2"),
                     help="write profiles/<name>_counters.md from two --pmc runs instead")
+    ap.add_argument("--backward", metavar="STATS",
+                    help="write profiles/attn_bwd_kernels.md from a kernel trace of "
+                         "bench.py --extra (the backward at workloads 3 and 4)")
     ap.add_argument("--gemm-ceiling", action="store_true",
                     help="measure vendor GEMM throughput on the GPU and print a markdown table")
     args = ap.parse_args()
+    if args.backward:
+        import sys
+        sys.path.insert(0, ROOT)
+        md = backward_markdown(args.backward, (3, 4), args.command)
+        with open(os.path.join(ROOT, "profiles", "attn_bwd_kernels.md"), "w") as f:
+            f.write(md)
+        print(md)
+        return
     if args.gemm_ceiling:
         print("| M = N = K | bf16, random | bf16, zeros | fp8 e4m3 (scaled_mm), random |")
         print("|---|---|---|---|")
