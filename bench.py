@@ -297,13 +297,22 @@ def main():
             kn = np.minimum(64, c.S - 64 * np.arange(mask.shape[3]))
             pairs = float(np.einsum("bhij,i,j->", mask.astype(np.float64), qn, kn))
             eff = 4.0 * c.D * pairs / (sms * 1e-3) / 1e12
+            # the same with the keys rotated once into a workspace
+            dt = kl.KLEIN_DTYPE_BF16 if xi.descale is None else kl.KLEIN_DTYPE_FP8_E4M3
+            xw = torch.empty(kl.klein_attn_workspace_size(c.B, c.S, c.H, c.D, dt),
+                             dtype=torch.uint8, device=dev)
+            wms = time_gpu(lambda: kl.klein_rope4d_attn_fwd_blocksparse(
+                xq, xk, xv, xp, xo, xm, descales=desc, workspace=xw), 5, 2, torch)
+            weff = 4.0 * c.D * pairs / (wms * 1e-3) / 1e12
             rec["extra"].append({
                 "workload": f"block-sparse {c.name}: B={c.B}, S={c.S}, H={c.H}, D={c.D}, "
                             f"{c.dtype}; mask keeps {100 * mask.mean():.1f} % of 256x64 blocks",
                 "ms_per_call": round(sms, 4), "dense_ms_per_call": round(dms, 4),
                 "speedup_vs_dense": round(dms / sms, 3),
-                "effective_tflops": round(eff, 2), "peak": peak, "frac": round(eff / peak, 4)})
-            del xq, xk, xv, xo, xm
+                "effective_tflops": round(eff, 2), "peak": peak, "frac": round(eff / peak, 4),
+                "keys_rotated_once_ms": round(wms, 4),
+                "keys_rotated_once_effective_tflops": round(weff, 2)})
+            del xq, xk, xv, xo, xm, xw
     if args.extra:
         # QKV projection with the RoPE-4D epilogue at the bench shape (hidden
         # C = H D = 3072, an assumption: the pages give no width), against

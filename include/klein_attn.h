@@ -249,6 +249,29 @@ klein_status_t klein_rope4d_attn_fwd_blocksparse(const void* q, const void* k, c
                                                  klein_stream_t stream);
 
 /*
+ * The block-sparse variant with the keys rotated once into a caller-owned
+ * workspace first (as klein_rope4d_attn_fwd_ws does) instead of once per
+ * query tile; the result equals klein_rope4d_attn_fwd_blocksparse's bit for
+ * bit.  Nothing is split.
+ *   workspace      : DEVICE pointer, 256-byte aligned, caller-owned, at least
+ *                    B*S*H*D*2 bytes for bf16 (B*S*H*D for fp8), rounded up
+ *                    to a multiple of 256 (klein_attn_workspace_size for the
+ *                    same shape is always enough); contents on entry do not
+ *                    matter; calls that share one at the same time race.
+ *   workspace_bytes: its size; smaller than required, or a null or
+ *                    misaligned workspace, is INVALID_ARG.
+ * Other arguments and errors as klein_rope4d_attn_fwd_blocksparse.
+ */
+klein_status_t klein_rope4d_attn_fwd_blocksparse_ws(const void* q, const void* k, const void* v,
+                                                    const int32_t* pos_thwl, void* out,
+                                                    int B, int S, int H, int D,
+                                                    klein_dtype_t dtype, float q_descale,
+                                                    float k_descale, float v_descale,
+                                                    const uint8_t* block_mask, void* workspace,
+                                                    size_t workspace_bytes,
+                                                    klein_stream_t stream);
+
+/*
  * QKV projection with the RoPE-4D rotation fused into its epilogue -- the
  * step that feeds the attention in each joint block ("Flux.3 Image Klein
  * arrives in Diffusers with a modular architecture", section "How it works";

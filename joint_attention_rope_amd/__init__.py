@@ -244,13 +244,16 @@ def blocksparse_mask_shape(B, S, H):
 
 
 def klein_rope4d_attn_fwd_blocksparse(q, k, v, pos_thwl, out, block_mask, dtype=None,
-                                      descales=(1.0, 1.0, 1.0), stream=None):
+                                      descales=(1.0, 1.0, 1.0), stream=None, workspace=None):
     """Block-sparse RoPE-4D joint attention: queries of query block I attend to
     the keys of the blocks J with block_mask[b, h, I, J] != 0 only.
 
     block_mask: uint8 (or bool) GPU tensor of blocksparse_mask_shape(B, S, H).
     dtype: KLEIN_DTYPE_BF16 or KLEIN_DTYPE_FP8_E4M3 (inferred from q.dtype when
     None); descales (q, k, v) apply to fp8 only.  out: bfloat16 [B, S, H, D].
+    workspace: None, or a uint8 GPU tensor (klein_attn_workspace_size bytes is
+    enough) into which the keys are rotated once (klein_rope4d_attn_fwd_blocksparse_ws;
+    the same result).
     """
     B, S, H, D = _bshd(q, "q")
     for t, n in ((k, "k"), (v, "v"), (out, "out")):
@@ -271,10 +274,17 @@ def klein_rope4d_attn_fwd_blocksparse(q, k, v, pos_thwl, out, block_mask, dtype=
         raise ValueError("block_mask must be a contiguous uint8/bool GPU tensor of shape "
                          f"{blocksparse_mask_shape(B, S, H)}")
     dq, dk, dv = (float(x) for x in descales)
-    st = _capi.lib().klein_rope4d_attn_fwd_blocksparse(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), pos_thwl.data_ptr(), out.data_ptr(),
-        B, S, H, D, int(dtype), dq, dk, dv, block_mask.data_ptr(), _stream(stream, q.device))
-    _check(st, "klein_rope4d_attn_fwd_blocksparse")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), pos_thwl.data_ptr(), out.data_ptr(),
+            B, S, H, D, int(dtype), dq, dk, dv, block_mask.data_ptr())
+    if workspace is None:
+        st = _capi.lib().klein_rope4d_attn_fwd_blocksparse(*args, _stream(stream, q.device))
+        _check(st, "klein_rope4d_attn_fwd_blocksparse")
+    else:
+        if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+        st = _capi.lib().klein_rope4d_attn_fwd_blocksparse_ws(
+            *args, workspace.data_ptr(), workspace.numel(), _stream(stream, q.device))
+        _check(st, "klein_rope4d_attn_fwd_blocksparse_ws")
     return out
 
 

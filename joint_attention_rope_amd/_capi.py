@@ -31,6 +31,9 @@ SIGNATURES = {
                                          _f32, _f32, _f32, _vp]),
     "klein_rope4d_attn_fwd_blocksparse": (_int, [_vp, _vp, _vp, _i32p, _vp, _int, _int, _int,
                                                  _int, _int, _f32, _f32, _f32, _vp, _vp]),
+    "klein_rope4d_attn_fwd_blocksparse_ws": (_int, [_vp, _vp, _vp, _i32p, _vp, _int, _int,
+                                                    _int, _int, _int, _f32, _f32, _f32, _vp, _vp,
+                                                    ctypes.c_size_t, _vp]),
     "klein_rope4d_attn_fwd_ws": (_int, [_vp, _vp, _vp, _i32p, _vp, _int, _int, _int, _int, _int,
                                         _f32, _f32, _f32, _vp, ctypes.c_size_t, _vp]),
     "klein_attn_workspace_size": (_int, [_int, _int, _int, _int, _int,

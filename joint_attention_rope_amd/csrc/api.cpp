@@ -269,12 +269,11 @@ klein_status_t klein_rope4d_attn_fwd_ws(const void* q, const void* k, const void
   }
 }
 
-klein_status_t klein_rope4d_attn_fwd_blocksparse(const void* q, const void* k, const void* v,
-                                                 const int32_t* pos_thwl, void* out, int B,
-                                                 int S, int H, int D, klein_dtype_t dtype,
-                                                 float q_descale, float k_descale,
-                                                 float v_descale, const uint8_t* block_mask,
-                                                 klein_stream_t stream) {
+static klein_status_t blocksparse(const void* q, const void* k, const void* v,
+                                  const int32_t* pos_thwl, void* out, int B, int S, int H, int D,
+                                  klein_dtype_t dtype, float q_descale, float k_descale,
+                                  float v_descale, const uint8_t* block_mask, void* workspace,
+                                  size_t workspace_bytes, bool use_ws, klein_stream_t stream) {
   if (dtype != KLEIN_DTYPE_BF16 && dtype != KLEIN_DTYPE_FP8_E4M3) return KLEIN_ERR_INVALID_ARG;
   klein_status_t st = check_common(q, k, v, pos_thwl, out, B, S, H, D);
   if (st != KLEIN_OK) return st;
@@ -287,15 +286,43 @@ klein_status_t klein_rope4d_attn_fwd_blocksparse(const void* q, const void* k, c
       if (!(std::isfinite(s) && s > 0.f)) return KLEIN_ERR_INVALID_ARG;
   if ((fp8 ? klein::attn_fwd_fp8_grid(B, S, H) : klein::attn_fwd_bf16_grid(B, S, H)) > kMaxGrid)
     return KLEIN_ERR_UNSUPPORTED;
+  if (use_ws) {
+    const long long need = ((long long)B * S * H * D * (fp8 ? 1 : 2) + 255) / 256 * 256;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) ||
+        workspace_bytes < (size_t)need)
+      return KLEIN_ERR_INVALID_ARG;
+  }
   try {
     LaunchArgs a = make_args(q, k, v, pos_thwl, out, B, S, H, D, stream);
     a.bmask = block_mask;
+    if (use_ws) a.krot = workspace;
     if (!fp8) return map_hip(klein::launch_attn_fwd_bf16(a));
     a.descale[0] = q_descale; a.descale[1] = k_descale; a.descale[2] = v_descale;
     return map_hip(klein::launch_attn_fwd_fp8(a));
   } catch (...) {
     return KLEIN_ERR_LAUNCH;
   }
+}
+
+klein_status_t klein_rope4d_attn_fwd_blocksparse(const void* q, const void* k, const void* v,
+                                                 const int32_t* pos_thwl, void* out, int B,
+                                                 int S, int H, int D, klein_dtype_t dtype,
+                                                 float q_descale, float k_descale,
+                                                 float v_descale, const uint8_t* block_mask,
+                                                 klein_stream_t stream) {
+  return blocksparse(q, k, v, pos_thwl, out, B, S, H, D, dtype, q_descale, k_descale, v_descale,
+                     block_mask, nullptr, 0, false, stream);
+}
+
+klein_status_t klein_rope4d_attn_fwd_blocksparse_ws(const void* q, const void* k, const void* v,
+                                                    const int32_t* pos_thwl, void* out, int B,
+                                                    int S, int H, int D, klein_dtype_t dtype,
+                                                    float q_descale, float k_descale,
+                                                    float v_descale, const uint8_t* block_mask,
+                                                    void* workspace, size_t workspace_bytes,
+                                                    klein_stream_t stream) {
+  return blocksparse(q, k, v, pos_thwl, out, B, S, H, D, dtype, q_descale, k_descale, v_descale,
+                     block_mask, workspace, workspace_bytes, true, stream);
 }
 
 klein_status_t klein_attn_fwd_prerotated(const void* q, const void* k, const void* v, void* out,

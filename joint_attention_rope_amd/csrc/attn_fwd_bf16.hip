@@ -598,8 +598,17 @@ static hipError_t launch_bf16_dense(const LaunchArgs& a) {
   return launch_bf16<D, false>(a);
 }
 
+template <int D>
+static hipError_t launch_bf16_sparse(const LaunchArgs& a) {
+  if (!a.krot) return launch_bf16<D, true>(a);
+  // k rotated once into the workspace, then the block-sparse kernel without K rotation
+  const hipError_t e = launch_rope4d_fp16(a.k, a.pos, a.krot, a.B, a.S, a.H, D, a.freqs, 1.0f,
+                                          a.stream);
+  return e != hipSuccess ? e : launch_bf16<D, true, kRotKPre>(a);
+}
+
 hipError_t launch_attn_fwd_bf16(const LaunchArgs& a) {
-  if (a.bmask) return a.D == 128 ? launch_bf16<128, true>(a) : launch_bf16<64, true>(a);
+  if (a.bmask) return a.D == 128 ? launch_bf16_sparse<128>(a) : launch_bf16_sparse<64>(a);
   return a.D == 128 ? launch_bf16_dense<128>(a) : launch_bf16_dense<64>(a);
 }
 

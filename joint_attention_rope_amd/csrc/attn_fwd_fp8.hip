@@ -600,16 +600,29 @@ static hipError_t launch_fp8(const LaunchArgs& a) {
   return hipGetLastError();
 }
 
+// the key codes rotated once into the workspace (a.krot)
+template <int D>
+static hipError_t rotate_keys_fp8(const LaunchArgs& a) {
+  const long long nchunks = (long long)a.B * a.S * a.H * (D / 16);
+  long long blocks = (nchunks + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(rope4d_fp8_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, a.stream,
+                     (const uint8_t*)a.k, a.pos, (uint8_t*)a.krot, nchunks, a.S, a.H, a.freqs);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_fp8_sparse(const LaunchArgs& a) {
+  if (!a.krot) return launch_fp8<D, true>(a);
+  const hipError_t e = rotate_keys_fp8<D>(a);
+  return e != hipSuccess ? e : launch_fp8<D, true, true>(a);
+}
+
 template <int D>
 static hipError_t launch_fp8_dense(const LaunchArgs& a) {
   if (a.krot) {
     // key codes rotated once into the workspace, then the kernel without K rotation
-    const long long nchunks = (long long)a.B * a.S * a.H * (D / 16);
-    long long blocks = (nchunks + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(rope4d_fp8_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, a.stream,
-                       (const uint8_t*)a.k, a.pos, (uint8_t*)a.krot, nchunks, a.S, a.H, a.freqs);
-    hipError_t e = hipGetLastError();
+    hipError_t e = rotate_keys_fp8<D>(a);
     if (e != hipSuccess) return e;
     if (a.split.n_sk == 0) return launch_fp8<D, false, true>(a);
     e = launch_fp8<D, false, true, true>(a);
@@ -623,7 +636,7 @@ static hipError_t launch_fp8_dense(const LaunchArgs& a) {
 }
 
 hipError_t launch_attn_fwd_fp8(const LaunchArgs& a) {
-  if (a.bmask) return a.D == 128 ? launch_fp8<128, true>(a) : launch_fp8<64, true>(a);
+  if (a.bmask) return a.D == 128 ? launch_fp8_sparse<128>(a) : launch_fp8_sparse<64>(a);
   return a.D == 128 ? launch_fp8_dense<128>(a) : launch_fp8_dense<64>(a);
 }
 

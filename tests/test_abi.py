@@ -22,6 +22,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "klein_rope4d_attn_fwd", "klein_rope4d_attn_fwd_fp8", "klein_rope4d_attn_fwd_blocksparse",
+        "klein_rope4d_attn_fwd_blocksparse_ws",
         "klein_qkv_rope4d_proj", "klein_qkv_rope4d_proj_fp8", "klein_attn_fwd_prerotated",
         "klein_rope4d_attn_fwd_ws",
         "klein_attn_workspace_size", "klein_splitkv_plan", "klein_rope4d_attn_fwd_lse",

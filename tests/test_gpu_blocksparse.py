@@ -18,12 +18,18 @@ pytestmark = pytest.mark.gpu
 QB, KB = kl.KLEIN_SPARSE_QBLOCK, kl.KLEIN_SPARSE_KBLOCK
 
 
-def run_sparse(inp, mask, dev="cuda:0"):
+def run_sparse(inp, mask, dev="cuda:0", workspace=False):
     q, k, v, pos = to_device(inp, dev)
+    B, S, H, D = q.shape
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     m = torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).to(dev)
+    ws = None
+    if workspace:
+        dt = kl.KLEIN_DTYPE_BF16 if inp.descale is None else kl.KLEIN_DTYPE_FP8_E4M3
+        ws = torch.empty(kl.klein_attn_workspace_size(B, S, H, D, dt), dtype=torch.uint8,
+                         device=dev)
     kl.klein_rope4d_attn_fwd_blocksparse(q, k, v, pos, out, m,
-                                         descales=inp.descale or (1.0, 1.0, 1.0))
+                                         descales=inp.descale or (1.0, 1.0, 1.0), workspace=ws)
     torch.cuda.synchronize()
     return out
 
@@ -93,6 +99,35 @@ def test_single_tile_lists_and_deterministic():
     b = run_sparse(inp, mask)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert_bf16_close(bf16_tensor_to_f64(a), oracle_sparse(inp, mask), "one tile per block")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("S,D", [(1000, 128), (577, 64), (4000, 128)])
+def test_keys_rotated_once_equals_per_tile_bitwise(S, D, fp8):
+    # the workspace variant rotates every key once, to the very values the
+    # per-tile rotation forms, so the results agree bit for bit
+    rng = np.random.default_rng(S + D + fp8)
+    inp = (random_fp8_inputs if fp8 else random_inputs)(2, S, 3, D, seed=S + 3 * D + fp8)
+    mask = rand_mask(rng, 2, 3, S, 0.45)
+    a = run_sparse(inp, mask)
+    b = run_sparse(inp, mask, workspace=True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_workspace_variant_checks_the_workspace():
+    inp = random_inputs(1, 300, 2, 128, seed=67)
+    q, k, v, pos = to_device(inp)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    m = torch.ones(kl.blocksparse_mask_shape(1, 300, 2), dtype=torch.uint8, device=q.device)
+    need = (300 * 2 * 128 * 2 + 255) // 256 * 256
+    small = torch.empty(need - 256, dtype=torch.uint8, device=q.device)
+    with pytest.raises(kl.KleinError) as e:
+        kl.klein_rope4d_attn_fwd_blocksparse(q, k, v, pos, out, m, workspace=small)
+    assert e.value.status == kl.KLEIN_ERR_INVALID_ARG
+    exact = torch.empty(need, dtype=torch.uint8, device=q.device)
+    kl.klein_rope4d_attn_fwd_blocksparse(q, k, v, pos, out, m, workspace=exact)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), run_attention(inp).view(torch.int16))
 
 
 def test_workload_4_structured_mask_sampled_rows():
