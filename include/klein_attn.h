@@ -185,6 +185,19 @@ klein_status_t klein_rope4d_attn_fwd_lse(const void* q, const void* k, const voi
                                          int B, int S, int H, int D, klein_stream_t stream);
 
 /*
+ * klein_rope4d_attn_fwd_lse on the schedule of klein_rope4d_attn_fwd_ws (keys
+ * rotated once into the workspace, the last round's query tiles split over
+ * key chunks and merged, lse written by the kernel for whole tiles and by the
+ * merge for split ones).  Workspace as klein_rope4d_attn_fwd_ws with dtype
+ * BF16; lse as klein_rope4d_attn_fwd_lse.  Tiles that run whole give the
+ * same out and lse bits as klein_rope4d_attn_fwd_lse.
+ */
+klein_status_t klein_rope4d_attn_fwd_lse_ws(const void* q, const void* k, const void* v,
+                                            const int32_t* pos_thwl, void* out, float* lse,
+                                            int B, int S, int H, int D, void* workspace,
+                                            size_t workspace_bytes, klein_stream_t stream);
+
+/*
  * Backward of the bf16 attention: given the forward's inputs, its output
  * `out` and lse (klein_rope4d_attn_fwd_lse), and dout = dL/dout, writes the
  * gradients of L with respect to the unrotated q, k and v:

@@ -197,16 +197,25 @@ def _lse_tensor(lse, B, S, H):
         raise ValueError(f"lse must be a contiguous float32 GPU tensor [B, H, S] = [{B}, {H}, {S}]")
 
 
-def klein_rope4d_attn_fwd_lse(q, k, v, pos_thwl, out, lse, stream=None):
+def klein_rope4d_attn_fwd_lse(q, k, v, pos_thwl, out, lse, stream=None, workspace=None):
     """bf16 forward that also writes lse [B, H, S] (float32, natural log of the
-    softmax denominator) for klein_rope4d_attn_bwd."""
+    softmax denominator) for klein_rope4d_attn_bwd.  With a workspace (a uint8
+    GPU tensor of klein_attn_workspace_size bytes) it runs on the split-KV
+    schedule of klein_rope4d_attn_fwd_ws (klein_rope4d_attn_fwd_lse_ws)."""
     B, S, H, D = _same_bshd(q, ((q, "q"), (k, "k"), (v, "v"), (out, "out")))
     _pos(pos_thwl, S)
     _lse_tensor(lse, B, S, H)
-    st = _capi.lib().klein_rope4d_attn_fwd_lse(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), pos_thwl.data_ptr(), out.data_ptr(),
-        lse.data_ptr(), B, S, H, D, _stream(stream, q.device))
-    _check(st, "klein_rope4d_attn_fwd_lse")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), pos_thwl.data_ptr(), out.data_ptr(),
+            lse.data_ptr(), B, S, H, D)
+    if workspace is None:
+        st = _capi.lib().klein_rope4d_attn_fwd_lse(*args, _stream(stream, q.device))
+        _check(st, "klein_rope4d_attn_fwd_lse")
+    else:
+        if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+        st = _capi.lib().klein_rope4d_attn_fwd_lse_ws(*args, workspace.data_ptr(),
+                                                      workspace.numel(), _stream(stream, q.device))
+        _check(st, "klein_rope4d_attn_fwd_lse_ws")
     return out, lse
 
 

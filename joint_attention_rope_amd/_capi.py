@@ -42,6 +42,8 @@ SIGNATURES = {
                                   ctypes.POINTER(ctypes.c_size_t)]),
     "klein_rope4d_attn_fwd_lse": (_int, [_vp, _vp, _vp, _i32p, _vp, _vp, _int, _int, _int, _int,
                                          _vp]),
+    "klein_rope4d_attn_fwd_lse_ws": (_int, [_vp, _vp, _vp, _i32p, _vp, _vp, _int, _int, _int,
+                                            _int, _vp, ctypes.c_size_t, _vp]),
     "klein_rope4d_attn_bwd": (_int, [_vp, _vp, _vp, _i32p, _vp, _vp, _vp, _vp, _vp, _vp, _int,
                                      _int, _int, _int, _vp, ctypes.c_size_t, _vp]),
     "klein_attn_bwd_workspace_size": (_int, [_int, _int, _int, _int,

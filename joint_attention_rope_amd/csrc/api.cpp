@@ -230,11 +230,11 @@ klein_status_t klein_splitkv_plan(int B, int S, int H, int D, int n_cu, int* pla
   return KLEIN_OK;
 }
 
-klein_status_t klein_rope4d_attn_fwd_ws(const void* q, const void* k, const void* v,
-                                        const int32_t* pos_thwl, void* out, int B, int S, int H,
-                                        int D, klein_dtype_t dtype, float q_descale,
-                                        float k_descale, float v_descale, void* workspace,
-                                        size_t workspace_bytes, klein_stream_t stream) {
+static klein_status_t attn_ws(const void* q, const void* k, const void* v,
+                              const int32_t* pos_thwl, void* out, float* lse, int B, int S, int H,
+                              int D, klein_dtype_t dtype, float q_descale, float k_descale,
+                              float v_descale, void* workspace, size_t workspace_bytes,
+                              klein_stream_t stream) {
   if (dtype != KLEIN_DTYPE_BF16 && dtype != KLEIN_DTYPE_FP8_E4M3) return KLEIN_ERR_INVALID_ARG;
   klein_status_t st = check_common(q, k, v, pos_thwl, out, B, S, H, D);
   if (st != KLEIN_OK) return st;
@@ -253,6 +253,7 @@ klein_status_t klein_rope4d_attn_fwd_ws(const void* q, const void* k, const void
     if (w.total > 0 && (!workspace || workspace_bytes < (size_t)w.total))
       return KLEIN_ERR_INVALID_ARG;
     LaunchArgs a = make_args(q, k, v, pos_thwl, out, B, S, H, D, stream);
+    a.lse = lse;
     if (w.krot_bytes > 0) a.krot = workspace;
     if (plan.n_sk > 0) {
       a.split.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.krot_bytes);
@@ -267,6 +268,24 @@ klein_status_t klein_rope4d_attn_fwd_ws(const void* q, const void* k, const void
   } catch (...) {
     return KLEIN_ERR_LAUNCH;
   }
+}
+
+klein_status_t klein_rope4d_attn_fwd_ws(const void* q, const void* k, const void* v,
+                                        const int32_t* pos_thwl, void* out, int B, int S, int H,
+                                        int D, klein_dtype_t dtype, float q_descale,
+                                        float k_descale, float v_descale, void* workspace,
+                                        size_t workspace_bytes, klein_stream_t stream) {
+  return attn_ws(q, k, v, pos_thwl, out, nullptr, B, S, H, D, dtype, q_descale, k_descale,
+                 v_descale, workspace, workspace_bytes, stream);
+}
+
+klein_status_t klein_rope4d_attn_fwd_lse_ws(const void* q, const void* k, const void* v,
+                                            const int32_t* pos_thwl, void* out, float* lse,
+                                            int B, int S, int H, int D, void* workspace,
+                                            size_t workspace_bytes, klein_stream_t stream) {
+  if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u)) return KLEIN_ERR_INVALID_ARG;
+  return attn_ws(q, k, v, pos_thwl, out, lse, B, S, H, D, KLEIN_DTYPE_BF16, 1.f, 1.f, 1.f,
+                 workspace, workspace_bytes, stream);
 }
 
 static klein_status_t blocksparse(const void* q, const void* k, const void* v,

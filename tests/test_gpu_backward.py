@@ -113,3 +113,35 @@ def test_repeat_bitwise_identical():
     b, _ = run_fwd_bwd(inp, dout_seed=5)
     for x, y in zip(a[2:], b[2:]):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("B,S,H", [(1, 2500, 4), (2, 900, 3)])
+def test_forward_with_lse_on_the_split_schedule(B, S, H):
+    # the workspace variant: tiles that run whole give the same bits as the
+    # plain training forward, split tiles match the oracle (out and lse)
+    import oracle
+    inp = random_inputs(B, S, H, 128, seed=S + H)
+    q, k, v, pos = to_device(inp)
+    a = torch.empty(q.shape, dtype=torch.bfloat16, device=DEV)
+    b = torch.empty_like(a)
+    la = torch.empty(B, H, S, dtype=torch.float32, device=DEV)
+    lb = torch.empty_like(la)
+    kl.klein_rope4d_attn_fwd_lse(q, k, v, pos, a, la)
+    ws = torch.empty(kl.klein_attn_workspace_size(B, S, H, 128), dtype=torch.uint8, device=DEV)
+    kl.klein_rope4d_attn_fwd_lse(q, k, v, pos, b, lb, workspace=ws)
+    torch.cuda.synchronize()
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    whole, cut, _, _ = kl.klein_splitkv_plan(B, S, H, 128, ncu)
+    nqt = -(-S // 256)
+    for item in range(whole):                    # items in (b, h, query tile) order
+        bb, hh, t = item // (H * nqt), (item // nqt) % H, item % nqt
+        r0, r1 = 256 * t, min(S, 256 * t + 256)
+        assert torch.equal(a[bb, r0:r1, hh].view(torch.int16), b[bb, r0:r1, hh].view(torch.int16))
+        assert torch.equal(la[bb, hh, r0:r1], lb[bb, hh, r0:r1])
+    q64, k64, v64 = oracle.decode_inputs(inp)
+    ref = oracle.attention(q64, k64, v64, inp.pos)
+    got = bf16_tensor_to_f64(b)
+    max_abs, rel = errors(got, ref)
+    assert max_abs <= 2e-2 and rel <= 5e-3, (max_abs, rel)
+    _, _, _, rlse = oracle.attention_backward(q64, k64, v64, inp.pos, np.zeros_like(q64))
+    assert np.max(np.abs(lb.cpu().numpy() - rlse)) <= LSE_ABS
