@@ -8,15 +8,16 @@
 //
 //   Q'' = e4m3(R(q_code) * c)            registers, once; c = G / 2^n
 //   K'' = e4m3(R(k_code) / 2)            LDS, per tile
-//   S^T = 2^n K'' Q''^T + c0 - m         the 2^n is the MFMA's E8M0 operand
-//                                        scale, c0 - m the chain's initial
-//                                        value, c0 = log2(1.75)
-//   p   = 2^S = 1.75 * 2^(s - m)         m is the running row max, raised only
-//   P8  = e4m3(p)                        when a row grows by more than TAU = 8,
-//                                        so p <= 1.75 * 2^8 = 448
+//   Y^T = 2^(n+3) K'' Q''^T + 94 - 8m    the 2^(n+3) is the MFMA's E8M0
+//                                        operand scale, 94 - 8m the chain's
+//                                        initial value: Y = 8 (s - m) + 94
+//   P8  = code rne(clamp(Y, 0, 255))     an E4M3 code read as an integer
+//                                        (v_cvt_pk_u8_f32); m is the running
+//                                        row max, raised only when a row grows
+//                                        by more than 4, so Y <= 126 (448)
 //   O^T += V^T P8^T                      V row-major in LDS, read transposed
 //   l  += ones^T P8^T                    row sums of P8, on the MFMA as well
-//   out = O * dv / l                     (the 1.75 cancels)
+//   out = O * dv / l
 //
 // with G = 2 dq dk log2(e) / sqrt(D): the exp2-domain score of query i and
 // key j is dq dk log2(e)/sqrt(D) <R q_i, R k_j> = G <R q_i, K''_j>, and n is
@@ -25,14 +26,24 @@
 // 317, and neither re-quantisation leaves the E4M3 range.  Halving K (a power
 // of two) keeps the channels the rotation leaves alone -- the t and l axis
 // blocks of image tokens, at position 0 -- exact codes, which is worth a
-// fifth of the fp8 path's error against the oracle.  Softmax therefore needs no VALU
-// multiply at all: one v_exp_f32 and half a conversion per score.  The 1.75
-// (folded into the chain's start) lifts p so that the full E4M3 range is used
-// and fewer small probabilities fall to its subnormals.
+// fifth of the fp8 path's error against the oracle.
+//
+// Softmax without an exponential: an E4M3 code c of a normal number is
+// 8 (e + 7) + f for the value 2^e (1 + f/8), so c / 8 - 7 is log2 of the
+// value within the binade's linear interpolation (at most 0.086 off, i.e. at
+// most 6.2 % too large).  The code nearest to 8 x + 94 therefore encodes
+// about 2^(x + 4.75), with x = s - m the exp2-domain score against the
+// running max: one full-rate conversion per score replaces a quarter-rate
+// v_exp_f32 and half an fp8 conversion.  O and l take the very same P8, so
+// the common factor cancels and only the interpolation's variation within a
+// binade remains (rel-L2 on the 2048^2 edit workload 4.1e-2 -> 4.4e-2, by a
+// CPU emulation of these roundings).  With 94 for the max, P8 stays a normal
+// number down to x = -10.75; codes below 0 clamp to 0 (a masked key's -inf
+// as well).
 //
 // Schedule (per wave; K'' and V double-buffered in LDS, one barrier a tile):
 //   softmax max of S(t); rare rescale of O and l
-//   region A:  S(t+1) MFMAs      interleaved with  p = 2^S(t), P8
+//   region A:  Y(t+1) MFMAs      interleaved with  the P8 codes of Y(t)
 //   region B:  O^T += V(t)^T P8  interleaved with  staging K''(t+2) and
 //              and l += 1^T P8                      V(t+1) into LDS
 //   buffer loads of K(t+3), V(t+2); barrier
@@ -130,8 +141,8 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   constexpr int TROW = NJ + 2;         // cos/sin table row stride (half2)
   constexpr int TSLOT = 10;            // per-thread fallback slot stride
   constexpr int TAB = kTabN * TROW;    // start of the fallback slots
-  constexpr float TAU = 8.0f;          // 1.75 * 2^TAU = 448
-  constexpr float C0 = 0.80735492205760410f;   // log2(1.75)
+  constexpr float YM = 94.0f;          // code of a score equal to the running max
+  constexpr float YMAX = 126.0f;       // largest finite E4M3 code (448)
   static_assert(NCH == NT || 2 * NCH == NT, "one K and one V chunk per thread (D 128) "
                                             "or one of either (D 64)");
   static_assert(!(SPARSE && SPLIT), "one schedule at a time");
@@ -305,7 +316,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   f32x16_t o[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) o[mb] = (f32x16_t){};
-  float m_run = 0.f;
+  float m8 = 0.f;                      // running row max, in code units (8 m)
   // row sums of P8 on the MFMA: ones^T P8 puts the sum over the tile's keys
   // of this lane's query in every register
   f32x16_t lacc = {};
@@ -338,7 +349,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   f32x16_t cinit;
   auto set_cinit = [&]() {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) cinit[i] = C0 - m_run;
+    for (int i = 0; i < 16; ++i) cinit[i] = YM - m8;
   };
   auto mask_tail = [&](int t, f32x16_t* sc) {
     if (t * BN + BN > Sk) {
@@ -351,11 +362,11 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   };
   auto softmax_max = [&](int t, f32x16_t* sc) {
     mask_tail(t, sc);
-    const float mx = rowmax32(sc);              // (row max relative to m) + C0
-    if (__builtin_amdgcn_ballot_w64(mx > TAU + C0)) {
-      const float delta = __builtin_fmaxf(mx - C0, 0.f);
-      const float alpha = __builtin_amdgcn_exp2f(-delta);
-      m_run += delta;
+    const float mx = rowmax32(sc);              // code of the row's largest score
+    if (__builtin_amdgcn_ballot_w64(mx > YMAX)) {
+      const float delta = __builtin_fmaxf(mx - YM, 0.f);
+      const float alpha = __builtin_amdgcn_exp2f(-0.125f * delta);
+      m8 += delta;
       lacc *= alpha;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) o[mb] *= alpha;
@@ -383,13 +394,13 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
 #pragma unroll
       for (int sl = i * 8 / NA; sl < (i + 1) * 8 / NA; ++sl) {
         const int kb2 = sl >> 2, w = sl & 3;
-        float p[4];
+        // four codes, each rounded to nearest even and clamped to [0, 255]
+        // into its byte of the word
+        uint32_t word = __builtin_amdgcn_cvt_pk_u8_f32(cur[kb2][4 * w], 0u, 0u);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(cur[kb2][4 * w + e]);
-        // both halves of the word are rewritten: the old word only fills
-        // the operand that the conversion keeps
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pb[4 * kb2 + w], false);
-        pb[4 * kb2 + w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+        for (int e = 1; e < 4; ++e)
+          word = __builtin_amdgcn_cvt_pk_u8_f32(cur[kb2][4 * w + e], (unsigned)e, word);
+        pb[4 * kb2 + w] = (int)word;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -488,9 +499,9 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   __syncthreads();                     // K'' buffer 0 is refilled in iteration 0
   // m starts at tile 0's exact row max, so scores are relative from the start
   mask_tail(tl(0), sa);
-  m_run = rowmax32(sa);
+  m8 = rowmax32(sa);
 #pragma unroll
-  for (int kbk = 0; kbk < 2; ++kbk) sa[kbk] -= m_run - C0;
+  for (int kbk = 0; kbk < 2; ++kbk) sa[kbk] -= m8 - YM;
   set_cinit();
 
   i32x8_t pb = {};
@@ -521,7 +532,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   const float lsum = lacc[0];
   if constexpr (SPLIT)
     if (k0 != 0 || k1 != nkt) {
-      split_store<MB>(o, m_run, lsum, sp, work - sp.n_dp, chunk);
+      split_store<MB>(o, 0.125f * m8, lsum, sp, work - sp.n_dp, chunk);
       return;
     }
   if (qrow < S) {
@@ -541,9 +552,10 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
 }
 
 // Score scale split: G = 2 dq dk log2(e) / sqrt(D) = c * 2^n with c in
-// (1/(2 sqrt 2), 1/sqrt 2]; 2^n goes to the MFMA as two E8M0 operand scales
-// (each in [2^-127, 2^127]).  |n| > 254 is clamped (descale products that far
-// out underflow or overflow fp32 scores anyway).
+// (1/(2 sqrt 2), 1/sqrt 2]; 2^(n+3) (the 8 turns exp2-domain scores into
+// E4M3 code units) goes to the MFMA as two E8M0 operand scales (each in
+// [2^-127, 2^127]).  |n + 3| > 254 is clamped (descale products that far out
+// underflow or overflow fp32 scores anyway).
 struct Fp8Scales {
   float q_mul;
   int sc_a, sc_b;
@@ -551,10 +563,11 @@ struct Fp8Scales {
 static Fp8Scales fp8_scales(const LaunchArgs& a) {
   const double G = (double)a.descale[0] * (double)a.descale[1] *
                    1.4426950408889634 * 2.0 / std::sqrt((double)a.D);
-  int n = (int)std::ceil(std::log2(G * 1.4142135623730951));
-  if (n > 254) n = 254;
-  if (n < -254) n = -254;
-  const int na = n / 2, nb = n - na;
+  const int n = (int)std::ceil(std::log2(G * 1.4142135623730951));
+  int e = n + 3;
+  if (e > 254) e = 254;
+  if (e < -254) e = -254;
+  const int na = e / 2, nb = e - na;
   return {(float)std::ldexp(G, -n), 127 + na, 127 + nb};
 }
 
