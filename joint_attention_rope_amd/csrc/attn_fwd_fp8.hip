@@ -155,9 +155,9 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   __shared__ __attribute__((aligned(16))) h2_t cs_tab[TAB + TSLOT * NT];
   __shared__ uint16_t klist[SPARSE ? kSparseMaxTiles + kSparsePad : 1];
   __shared__ int klist_n;
-  // E4M3 ones: the A operand of the row-sum MFMA (read by every lane)
-  __shared__ __attribute__((aligned(16))) uint32_t ones_lds[4];
-  if (threadIdx.x < 4) ones_lds[threadIdx.x] = 0x38383838u;
+  // A operand of the row-sum MFMA: E4M3 ones (words 0-3) or zeros (4-7)
+  __shared__ __attribute__((aligned(16))) uint32_t ones_lds[8];
+  if (threadIdx.x < 8) ones_lds[threadIdx.x] = threadIdx.x < 4 ? 0x38383838u : 0u;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lr = lane & 31;
@@ -317,9 +317,15 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) o[mb] = (f32x16_t){};
   float m8 = 0.f;                      // running row max, in code units (8 m)
-  // row sums of P8 on the MFMA: ones^T P8 puts the sum over the tile's keys
-  // of this lane's query in every register
-  f32x16_t lacc = {};
+  // Row sums of P8 on a 16x16x128 MFMA that reads the P8 operand of the
+  // 32x32x64 one as it is.  Lane 16b + n of that operand holds 32 keys of
+  // query 16 (b & 1) + n, so an A operand whose lane 16b + r is all ones
+  // exactly when bit 2 of r equals bit 0 of b makes output row r, column n
+  // the row sum of query 16 ((r >> 2) & 1) + n -- and output lane L, which
+  // holds rows 4 (L / 16) + [0, 4) of column L % 16, gets the sum of its own
+  // query L % 32 in all 4 registers.
+  f32x4_t lacc = {};
+  const int ones_off = ((lane >> 2) & 1) == ((lane >> 4) & 1) ? 0 : 4;
 
   auto read_k = [&](int kbuf, int kbk, int ks) {
     const uint8_t* src = &k_lds[kbuf][(32 * kbk + lr) * KROW + 64 * ks + 32 * g];
@@ -446,10 +452,10 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    const u32x4_t on = *reinterpret_cast<const u32x4_t*>(ones_lds);
+    const u32x4_t on = *reinterpret_cast<const u32x4_t*>(ones_lds + ones_off);
     const i32x8_t ones = {(int)on[0], (int)on[1], (int)on[2], (int)on[3],
                           (int)on[0], (int)on[1], (int)on[2], (int)on[3]};
-    lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb, lacc, 0, 0, 0, 0, 0, 0);
+    lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pb, lacc, 0, 0, 0, 0, 0, 0);
   };
 
   int nsteps = k1 - k0;
