@@ -98,6 +98,27 @@ def test_e4m3_decode_all_codes():
     assert np.array_equal(e4m3_encode(e4m3_decode(fin)), fin)
 
 
+def test_e4m3_code_is_a_log2_of_its_value():
+    """The fp8 attention turns scores into probabilities by rounding 8 x + 94 to an
+    integer and reading it as an E4M3 code.  That rests on a property of the format:
+    a positive normal code c (8..126) encodes 2^(c/8 - 7) times a factor in
+    [1, 1 + 0.0616] (linear interpolation inside a binade against the exponential),
+    exact at the binade starts; the subnormal codes 1..7 are c * 2^-9, and 0 is zero."""
+    codes = np.arange(8, 127)
+    vals = e4m3_decode(codes.astype(np.uint8))
+    ratio = vals / np.exp2(codes / 8.0 - 7.0)
+    assert ratio.min() == 1.0 and ratio.max() < 1.0616
+    assert np.all(ratio[codes % 8 == 0] == 1.0)
+    # the largest factor, max over f of (1 + f) / 2^f at f = 1/ln 2 - 1, sampled at f = 4/8
+    assert abs(ratio.max() - 1.5 / np.sqrt(2.0)) < 1e-12
+    # monotone: a larger score never gives a smaller probability
+    assert np.all(np.diff(vals) > 0)
+    sub = np.arange(0, 8)
+    assert np.array_equal(e4m3_decode(sub.astype(np.uint8)), sub * 2.0 ** -9)
+    assert e4m3_decode(np.array([126], dtype=np.uint8))[0] == 448.0
+    assert np.isnan(e4m3_decode(np.array([127], dtype=np.uint8))[0])
+
+
 def test_generator_is_seeded_and_follows_recipe():
     a = make_inputs(get_config(1))
     b = make_inputs(get_config(1))
