@@ -157,7 +157,7 @@ klein_status_t klein_attn_bwd_workspace_size(int B, int S, int H, int D, size_t*
   if (!bytes) return KLEIN_ERR_INVALID_ARG;
   if (B < 1 || S < 1 || H < 1) return KLEIN_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return KLEIN_ERR_UNSUPPORTED;
-  *bytes = (size_t)klein::attn_bwd_workspace_bytes(B, S, H, D);
+  *bytes = (size_t)klein::attn_bwd_workspace(B, S, H, D).total;
   return KLEIN_OK;
 }
 
@@ -172,22 +172,22 @@ klein_status_t klein_rope4d_attn_bwd(const void* q, const void* k, const void* v
     if (!p || !aligned16(p)) return KLEIN_ERR_INVALID_ARG;
   if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u)) return KLEIN_ERR_INVALID_ARG;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return KLEIN_ERR_INVALID_ARG;
-  if (workspace_bytes < (size_t)klein::attn_bwd_workspace_bytes(B, S, H, D))
-    return KLEIN_ERR_INVALID_ARG;
+  const klein::BwdWorkspace wl = klein::attn_bwd_workspace(B, S, H, D);
+  if (workspace_bytes < (size_t)wl.total) return KLEIN_ERR_INVALID_ARG;
   const long long nb = (S + 127) / 128;
   if ((long long)B * H * nb > kMaxGrid || (long long)B * S * H * D / 8 / 256 > kMaxGrid)
     return KLEIN_ERR_UNSUPPORTED;
   try {
-    const long long n = (long long)B * S * H * D;
-    const long long half = (n * 2 + 255) / 256 * 256;
     char* ws = static_cast<char*>(workspace);
     klein::BwdArgs a{};
     a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
     a.out = (const uint16_t*)out; a.dout = (const uint16_t*)dout; a.pos = pos_thwl; a.lse = lse;
     a.dq = (uint16_t*)dq; a.dk = (uint16_t*)dk; a.dv = (uint16_t*)dv;
     a.qr = reinterpret_cast<uint16_t*>(ws);
-    a.kr = reinterpret_cast<uint16_t*>(ws + half);
-    a.delta = reinterpret_cast<float*>(ws + 2 * half);
+    a.kr = reinterpret_cast<uint16_t*>(ws + wl.kr);
+    a.delta = reinterpret_cast<float*>(ws + wl.delta);
+    a.norm2 = reinterpret_cast<float*>(ws + wl.norm2);
+    a.escale = reinterpret_cast<float*>(ws + wl.escale);
     a.B = B; a.S = S; a.H = H; a.D = D;
     a.qscale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
     a.freqs = make_freqs(D);

@@ -11,12 +11,27 @@
 //
 //   prep:  q'' = fp16(R q * log2(e)/sqrt(D)) and k' = fp16(R k), exactly the
 //          values the forward kernel forms on chip (so the recomputed scores
-//          match the ones lse was taken over), and delta_i;
+//          match the ones lse was taken over), delta_i, and the squared row
+//          norms of dout and v;
+//   scale: per (batch, head), the power of two 2^e that puts the largest
+//          possible |ds| near 2^14 (below);
 //   dk/dv: one workgroup per 256 keys (8 waves x 32 keys, two per SIMD; the
 //          keys on the MFMA columns), streaming all queries in tiles of 32
 //          (64 for D = 64);
 //   dq:    one workgroup per 256 queries (8 waves x 32 queries, two per SIMD),
 //          streaming all keys in tiles of 64.
+//
+// Range of ds.  ds enters its MFMAs as fp16, whose normal range (2^-14 ..
+// 65504) is far narrower than fp32's: with small gradients (|dout| ~ 1e-4
+// and below, common in fine-tuning) most ds would fall into fp16's subnormals
+// or to zero, with large ones they would overflow.  So both gradient kernels
+// work with 2^e p and 2^e ds instead: e is added to the score MFMA's initial
+// value (-lse2 + e), so exp2 already returns 2^e p, and the epilogues
+// multiply the accumulated gradients by 2^-e, exactly.  Since sum_j p_ij = 1,
+// |delta_i| <= max_j |dp_ij|, and |ds_ij| <= 2 max_i |dout_i| max_j |v_j|
+// (Cauchy-Schwarz); e puts that bound just under 2^14, a quarter of fp16's
+// largest value.  The same e serves the whole (batch, head), because dk and
+// dv sum over all its queries.
 //
 // Each MFMA keeps the fast operand layout of the forward kernel: the tile
 // that streams through LDS is the A operand, read row-wise (rows of a
@@ -52,9 +67,10 @@ __device__ __forceinline__ void rotate_back(float& x, float& y, int p, float whi
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const int32_t* __restrict__ pos, const uint16_t* __restrict__ o,
-    const uint16_t* __restrict__ dout, uint16_t* __restrict__ qr, uint16_t* __restrict__ kr,
-    float* __restrict__ delta, int S, int H, long long nchunks, RopeFreqs fr, float qscale) {
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ pos,
+    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
+    uint16_t* __restrict__ qr, uint16_t* __restrict__ kr, float* __restrict__ delta,
+    float* __restrict__ norm2, int S, int H, long long nchunks, RopeFreqs fr, float qscale) {
   constexpr int CPR = D / 8, DA = D / 4;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= nchunks) return;            // whole rows (CPR aligned lanes) leave together
@@ -72,12 +88,70 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(
       rope_chunk<true>(*reinterpret_cast<const u32x4_t*>(k + off), p, &fr.hi[j0], &fr.lo[j0], 1.0f);
   const u32x4_t ov = *reinterpret_cast<const u32x4_t*>(o + off);
   const u32x4_t dv = *reinterpret_cast<const u32x4_t*>(dout + off);
-  float sum = 0.f;
+  const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(v + off);
+  float sum = 0.f, dd = 0.f, vn = 0.f;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) sum += bf16_lo(ov[w]) * bf16_lo(dv[w]) + bf16_hi(ov[w]) * bf16_hi(dv[w]);
+  for (int w = 0; w < 4; ++w) {
+    sum += bf16_lo(ov[w]) * bf16_lo(dv[w]) + bf16_hi(ov[w]) * bf16_hi(dv[w]);
+    dd += bf16_lo(dv[w]) * bf16_lo(dv[w]) + bf16_hi(dv[w]) * bf16_hi(dv[w]);
+    vn += bf16_lo(vv[w]) * bf16_lo(vv[w]) + bf16_hi(vv[w]) * bf16_hi(vv[w]);
+  }
 #pragma unroll
-  for (int m = 1; m < CPR; m <<= 1) sum += __shfl_xor(sum, m);
-  if (c == 0) delta[((size_t)b * H + h) * S + s] = sum;
+  for (int m = 1; m < CPR; m <<= 1) {
+    sum += __shfl_xor(sum, m);
+    dd += __shfl_xor(dd, m);
+    vn += __shfl_xor(vn, m);
+  }
+  if (c == 0) {
+    const size_t r = ((size_t)b * H + h) * S + s;
+    delta[r] = sum;
+    norm2[r] = dd;                                   // |dout_i|^2 [B][H][S], then
+    norm2[nchunks / CPR + r] = vn;                   // |v_i|^2 [B][H][S]
+  }
+}
+
+// ---------------------------------------------------------------- scale
+// One workgroup per (batch, head): e = 14 - ceil(log2(2 max|dout_i| max|v_j|))
+// (see "Range of ds" above), clamped to [-100, 100]; as a float, in
+// escale[bh].  A zero bound (dout or v all zero, so ds = 0) gives e = 14.
+__global__ __launch_bounds__(256) void attn_bwd_scale_kernel(const float* __restrict__ norm2,
+                                                             float* __restrict__ escale, int S,
+                                                             long long rows) {
+  __shared__ float red[2][4];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const float* nd = norm2 + (size_t)bh * S;
+  const float* nv = nd + rows;
+  float md = 0.f, mv = 0.f;
+  for (int i = tid; i < S; i += 256) {
+    md = __builtin_fmaxf(md, nd[i]);
+    mv = __builtin_fmaxf(mv, nv[i]);
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    md = __builtin_fmaxf(md, __shfl_xor(md, m));
+    mv = __builtin_fmaxf(mv, __shfl_xor(mv, m));
+  }
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = md;
+    red[1][tid >> 6] = mv;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    md = __builtin_fmaxf(__builtin_fmaxf(red[0][0], red[0][1]), __builtin_fmaxf(red[0][2], red[0][3]));
+    mv = __builtin_fmaxf(__builtin_fmaxf(red[1][0], red[1][1]), __builtin_fmaxf(red[1][2], red[1][3]));
+    // 2 sqrt(md) sqrt(mv), 1/256 larger for the rounding of the norms
+    const float bound = 2.f * __builtin_sqrtf(md) * __builtin_sqrtf(mv) * (1.f + 1.f / 256.f);
+    int e = 14;
+    if (!(bound < __builtin_huge_valf())) {
+      e = -100;
+    } else if (bound > 0.f) {
+      int ex = 0;
+      (void)__builtin_frexpf(bound, &ex);             // bound < 2^ex
+      e = 14 - ex;
+      e = e < -100 ? -100 : (e > 100 ? 100 : e);
+    }
+    escale[bh] = (float)e;
+  }
 }
 
 // Per-lane base (16-bit elements) of the transposing reads of a 64-row tile
@@ -104,8 +178,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta,
-    const int32_t* __restrict__ pos, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-    int S, int H, int nkb, RopeFreqs fr) {
+    const float* __restrict__ escale, const int32_t* __restrict__ pos,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int S, int H, int nkb, RopeFreqs fr) {
   constexpr int BK = 256;              // keys per workgroup (8 waves x 32)
   constexpr int NBLK = D == 128 ? 1 : 2;   // 32-query blocks per step (one staging chunk a thread)
   constexpr int BQ = 32 * NBLK;        // queries per step
@@ -156,6 +230,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
 
   const float* lse_bh = lse + (size_t)bh * S;
   const float* dl_bh = delta + (size_t)bh * S;
+  const float e2 = escale[bh];                   // P and dS carry 2^e2
   u32x4_t sq[NCH], so[NCH];
   float sl = 0.f, sd = 0.f;
   auto load = [&](int qt) {
@@ -172,7 +247,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
     }
     if (tid < BQ) {
       const int qi = q0 + tid;
-      sl = qi < S ? -lse_bh[qi] * kLog2e : kNegInf;
+      sl = qi < S ? e2 - lse_bh[qi] * kLog2e : kNegInf;
       sd = qi < S ? -dl_bh[qi] : 0.f;
     }
   };
@@ -223,7 +298,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
         dp[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vreg[ks], dp[blk], 0, 0, 0);
       }
     }
-    // P = 2^(s2 - lse2) (bf16, for dV) and dS = P (dP - delta) (fp16, for dK)
+    // P = 2^(s2 - lse2 + e2) (bf16, for dV) and dS = P (dP - delta) (fp16,
+    // for dK), both carrying 2^e2
     uint32_t pw[NBLK][8], sw[NBLK][8];
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk)
@@ -260,7 +336,9 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
   // ---- epilogue: lane = key, register i of block mb = channel 32 mb + 8 (i/4) + 4 g + i%4
   if (!kval) return;
   const size_t row = base + (size_t)key * rs;
-  const float kscale = 1.0f / kLog2e;    // q'' carries log2(e)/sqrt(D); dk' needs 1/sqrt(D)
+  // q'' carries log2(e)/sqrt(D) (dk' needs 1/sqrt(D)); dS and P carry 2^e2
+  const float vscale = __builtin_ldexpf(1.0f, -(int)e2);
+  const float kscale = vscale / kLog2e;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -277,8 +355,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
       w.x = pack_bf16x2(y[0], y[1]);
       w.y = pack_bf16x2(y[2], y[3]);
       *reinterpret_cast<uint2*>(dk + row + d) = w;
-      w.x = pack_bf16x2(dva[mb][4 * i4], dva[mb][4 * i4 + 1]);
-      w.y = pack_bf16x2(dva[mb][4 * i4 + 2], dva[mb][4 * i4 + 3]);
+      w.x = pack_bf16x2(dva[mb][4 * i4] * vscale, dva[mb][4 * i4 + 1] * vscale);
+      w.y = pack_bf16x2(dva[mb][4 * i4 + 2] * vscale, dva[mb][4 * i4 + 3] * vscale);
       *reinterpret_cast<uint2*>(dv + row + d) = w;
     }
 }
@@ -289,8 +367,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta,
-    const int32_t* __restrict__ pos, uint16_t* __restrict__ dq, int S, int H, int nqb,
-    RopeFreqs fr, float dqscale) {
+    const float* __restrict__ escale, const int32_t* __restrict__ pos,
+    uint16_t* __restrict__ dq, int S, int H, int nqb, RopeFreqs fr, float dqscale) {
   constexpr int BQ = 256;              // queries per workgroup (8 waves x 32)
   constexpr int BK = 64;               // keys per step
   constexpr int NT = 512;
@@ -326,7 +404,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
     qreg[ks] = __builtin_bit_cast(f16x8_t, qval ? *reinterpret_cast<const u32x4_t*>(qr + e) : z);
     oreg[ks] = __builtin_bit_cast(bf16x8_t, qval ? *reinterpret_cast<const u32x4_t*>(dout + e) : z);
   }
-  const float nlse2 = qval ? -lse[(size_t)bh * S + query] * kLog2e : 0.f;
+  const float e2 = escale[bh];                   // dS carries 2^e2
+  const float nlse2 = qval ? e2 - lse[(size_t)bh * S + query] * kLog2e : 0.f;
   const float ndl = qval ? -delta[(size_t)bh * S + query] : 0.f;
   f32x16_t dqa[MB];
 #pragma unroll
@@ -429,6 +508,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
 
   if (!qval) return;
   const size_t row = base + (size_t)query * rs;
+  const float qscale = __builtin_ldexpf(dqscale, -(int)e2);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -436,7 +516,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
       const int d = 32 * mb + 8 * i4 + 4 * g;
       float y[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = dqa[mb][4 * i4 + e] * dqscale;
+      for (int e = 0; e < 4; ++e) y[e] = dqa[mb][4 * i4 + e] * qscale;
       const int a = d / DA, jp = (d % DA) / 2;
       const int p = pos[4 * query + a];
       rotate_back(y[0], y[1], p, fr.hi[jp], fr.lo[jp]);
@@ -452,20 +532,24 @@ template <int D>
 static hipError_t launch_bwd(const BwdArgs& a) {
   const long long nchunks = (long long)a.B * a.S * a.H * (D / 8);
   hipLaunchKernelGGL(attn_bwd_prep_kernel<D>, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0,
-                     a.stream, a.q, a.k, a.pos, a.out, a.dout, a.qr, a.kr, a.delta, a.S, a.H,
-                     nchunks, a.freqs, a.qscale_log2);
+                     a.stream, a.q, a.k, a.v, a.pos, a.out, a.dout, a.qr, a.kr, a.delta, a.norm2,
+                     a.S, a.H, nchunks, a.freqs, a.qscale_log2);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_scale_kernel, dim3((unsigned)(a.B * a.H)), dim3(256), 0, a.stream,
+                     a.norm2, a.escale, a.S, (long long)a.B * a.H * a.S);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nb = (a.S + 255) / 256;
   const dim3 grid((unsigned)(a.B * a.H * nb));
   hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, grid, dim3(512), 0, a.stream, a.qr, a.kr, a.v,
-                     a.dout, a.lse, a.delta, a.pos, a.dk, a.dv, a.S, a.H, nb, a.freqs);
+                     a.dout, a.lse, a.delta, a.escale, a.pos, a.dk, a.dv, a.S, a.H, nb, a.freqs);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqb = (a.S + 255) / 256;
   hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3((unsigned)(a.B * a.H * nqb)), dim3(512), 0, a.stream,
-                     a.qr, a.kr, a.v, a.dout, a.lse, a.delta, a.pos, a.dq, a.S, a.H, nqb, a.freqs,
-                     (float)(1.0 / std::sqrt((double)D)));
+                     a.qr, a.kr, a.v, a.dout, a.lse, a.delta, a.escale, a.pos, a.dq, a.S, a.H, nqb,
+                     a.freqs, (float)(1.0 / std::sqrt((double)D)));
   return hipGetLastError();
 }
 
@@ -473,9 +557,16 @@ hipError_t launch_attn_bwd(const BwdArgs& a) {
   return a.D == 128 ? launch_bwd<128>(a) : launch_bwd<64>(a);
 }
 
-long long attn_bwd_workspace_bytes(int B, int S, int H, int D) {
-  const long long n = (long long)B * S * H * D;
-  return 2 * ((n * 2 + 255) / 256 * 256) + ((long long)B * H * S * 4 + 255) / 256 * 256;
+BwdWorkspace attn_bwd_workspace(int B, int S, int H, int D) {
+  const auto up = [](long long x) { return (x + 255) / 256 * 256; };
+  const long long n = (long long)B * S * H * D, rows = (long long)B * H * S;
+  BwdWorkspace w{};
+  w.kr = up(n * 2);                       // qr at 0, then kr: fp16 [B][S][H][D] each
+  w.delta = 2 * w.kr;                     // fp32 [B][H][S]
+  w.norm2 = w.delta + up(rows * 4);       // fp32 [2][B][H][S]
+  w.escale = w.norm2 + up(rows * 8);      // fp32 [B][H]
+  w.total = w.escale + up((long long)B * H * 4);
+  return w;
 }
 
 }  // namespace klein

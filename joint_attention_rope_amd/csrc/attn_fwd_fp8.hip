@@ -8,13 +8,13 @@
 //
 //   Q'' = e4m3(R(q_code) * c)            registers, once; c = G / 2^n
 //   K'' = e4m3(R(k_code) / 2)            LDS, per tile
-//   Y^T = 2^(n+3) K'' Q''^T + 94 - 8m    the 2^(n+3) is the MFMA's E8M0
-//                                        operand scale, 94 - 8m the chain's
-//                                        initial value: Y = 8 (s - m) + 94
+//   Y^T = 2^(n+3) K'' Q''^T + 118 - 8m   the 2^(n+3) is the MFMA's E8M0
+//                                        operand scale, 118 - 8m the chain's
+//                                        initial value: Y = 8 (s - m) + 118
 //   P8  = code rne(clamp(Y, 0, 255))     an E4M3 code read as an integer
 //                                        (v_cvt_pk_u8_f32); m is the running
 //                                        row max, raised only when a row grows
-//                                        by more than 4, so Y <= 126 (448)
+//                                        by more than 1, so Y <= 126 (448)
 //   O^T += V^T P8^T                      V row-major in LDS, read transposed
 //   l  += ones^T P8^T                    row sums of P8, on the MFMA as well
 //   out = O * dv / l
@@ -31,15 +31,23 @@
 // Softmax without an exponential: an E4M3 code c of a normal number is
 // 8 (e + 7) + f for the value 2^e (1 + f/8), so c / 8 - 7 is log2 of the
 // value within the binade's linear interpolation (at most 0.086 off, i.e. at
-// most 6.2 % too large).  The code nearest to 8 x + 94 therefore encodes
-// about 2^(x + 4.75), with x = s - m the exp2-domain score against the
+// most 6.2 % too large).  The code nearest to 8 x + 118 therefore encodes
+// about 2^(x + 7.75), with x = s - m the exp2-domain score against the
 // running max: one full-rate conversion per score replaces a quarter-rate
 // v_exp_f32 and half an fp8 conversion.  O and l take the very same P8, so
 // the common factor cancels and only the interpolation's variation within a
-// binade remains (rel-L2 on the 2048^2 edit workload 4.1e-2 -> 4.4e-2, by a
-// CPU emulation of these roundings).  With 94 for the max, P8 stays a normal
-// number down to x = -10.75; codes below 0 clamp to 0 (a masked key's -inf
-// as well).
+// binade remains (rel-L2 on the 2048^2 edit workload 4.1e-2 -> 4.5e-2, by a
+// CPU model of these roundings).
+// Range: with the max at code 118 (224) and at most one binade of growth
+// before a rescale, P8 stays a normal number down to x = -13.75, within a
+// binade of what an exact exponential scaled to 448 keeps; below code 8 the
+// codes are subnormals (value c 2^-9, no longer 2^(c/8 - 7)), and below
+// x = -14.7 they round to 0 (a masked key's -inf as well).  A key that far
+// below the row max carries a weight of at most 2^-14.7 of it, which matters
+// only when thousands of such keys face one dominant key.  The lazy
+// headroom costs rescales: about one wave-tile in 20 on N(0, 1) scores of
+// the 2048^2 edit workload, against one in 800 with the max at code 94 and
+// four binades of headroom, which cut keys off at x = -11.7.
 //
 // Schedule (per wave; K'' and V double-buffered in LDS, one barrier a tile):
 //   softmax max of S(t); rare rescale of O and l
@@ -141,7 +149,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   constexpr int TROW = NJ + 2;         // cos/sin table row stride (half2)
   constexpr int TSLOT = 10;            // per-thread fallback slot stride
   constexpr int TAB = kTabN * TROW;    // start of the fallback slots
-  constexpr float YM = 94.0f;          // code of a score equal to the running max
+  constexpr float YM = 118.0f;         // code of a score equal to the running max
   constexpr float YMAX = 126.0f;       // largest finite E4M3 code (448)
   static_assert(NCH == NT || 2 * NCH == NT, "one K and one V chunk per thread (D 128) "
                                             "or one of either (D 64)");

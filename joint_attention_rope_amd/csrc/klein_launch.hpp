@@ -60,8 +60,10 @@ long long attn_fwd_fp8_grid(int B, int S, int H);
 hipError_t launch_rope4d_apply(const LaunchArgs& a);
 
 // Attention backward (bf16): q, k, v, out, dout [B][S][H][D] bf16, lse fp32
-// [B][H][S] (natural log) -> dq, dk, dv bf16; qr, kr (fp16 [B][S][H][D]) and
-// delta (fp32 [B][H][S]) in the caller's workspace.
+// [B][H][S] (natural log) -> dq, dk, dv bf16; qr, kr (fp16 [B][S][H][D]),
+// delta (fp32 [B][H][S]), the squared row norms of dout and v (fp32
+// [2][B][H][S]) and the per-head exponent of the ds scale (fp32 [B][H]) in
+// the caller's workspace.
 struct BwdArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -76,13 +78,19 @@ struct BwdArgs {
   uint16_t* qr;
   uint16_t* kr;
   float* delta;
+  float* norm2;
+  float* escale;
   int B, S, H, D;
   float qscale_log2;
   RopeFreqs freqs;
   hipStream_t stream;
 };
 hipError_t launch_attn_bwd(const BwdArgs& a);
-long long attn_bwd_workspace_bytes(int B, int S, int H, int D);
+// byte offsets of the backward's workspace parts (qr at 0) and its size
+struct BwdWorkspace {
+  long long kr, delta, norm2, escale, total;
+};
+BwdWorkspace attn_bwd_workspace(int B, int S, int H, int D);
 
 // QKV projection with the RoPE-4D epilogue: x [B S][C] bf16, w [3 H D][C]
 // bf16 (or both E4M3 codes with descales, fp8), bias [3 H D] bf16 or null

@@ -4,7 +4,9 @@ compare with the oracle at the tolerances of the hot path.
 Tolerances (bf16 inputs, bf16 output): max |gpu - oracle| <= 2e-2 and
 ||gpu - oracle||_2 / ||oracle||_2 <= 5e-3 over the compared elements.
 fp8 inputs: relative L2 <= 6e-2 against the exact attention of the dequantised
-codes.  A derivation of why these bound the kernel's rounding (bf16 Q'/K'/P and
+codes, and every output row within 0.15 relative L2 of its reference row (a
+CPU model of the fp8 kernel's roundings puts the largest row at 0.10 on these
+inputs, and at 0.08-0.13 on rows that face one dominant key).  A derivation of why these bound the kernel's rounding (bf16 Q'/K'/P and
 output, e4m3 Q'/K'/P) is in the design notes.
 """
 
@@ -17,6 +19,7 @@ from workloads import Inputs
 BF16_MAX_ABS = 2e-2
 BF16_REL_L2 = 5e-3
 FP8_REL_L2 = 6e-2
+FP8_ROW_REL_L2 = 0.15
 
 
 def to_device(inp: Inputs, dev="cuda:0"):
@@ -109,8 +112,37 @@ def random_fp8_inputs(B, S, H, D, seed, pos_lo=-50, pos_hi=600, unit_scale=False
                   descale=tuple(scales))
 
 
+def row_rel_l2(gpu, ref):
+    """Relative L2 error of every output row (over the last axis)."""
+    den = np.linalg.norm(ref, axis=-1)
+    num = np.linalg.norm(gpu - ref, axis=-1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+
 def assert_fp8_close(gpu, ref, what=""):
     max_abs, rel = errors(gpu, ref)
     assert np.isfinite(gpu).all(), f"{what}: non-finite output"
     assert rel <= FP8_REL_L2, f"{what}: rel_l2 {rel:.3e} (<= {FP8_REL_L2}), max_abs {max_abs:.3e}"
+    rows = row_rel_l2(gpu, ref)
+    worst = np.unravel_index(int(np.argmax(rows)), rows.shape) if rows.size else ()
+    assert rows.size == 0 or rows[worst] <= FP8_ROW_REL_L2, \
+        f"{what}: row {worst} rel_l2 {rows[worst]:.3e} (<= {FP8_ROW_REL_L2})"
     return max_abs, rel
+
+
+def assert_elementwise(got, ref, rel, floor, what="", rms_axes=None):
+    """|got - ref| <= rel * |ref| + floor * rms(ref) for every element.
+
+    rms(ref) is taken over ``rms_axes`` (kept as broadcast dimensions), e.g.
+    over the tokens and channels of each (batch, head) of a [B, S, H, D]
+    tensor, or over the whole tensor when None.  The relative term covers the
+    final rounding of each element, the floor the error of its sums."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = np.sqrt(np.mean(ref * ref, axis=rms_axes, keepdims=rms_axes is not None))
+    excess = np.abs(got - ref) - (rel * np.abs(ref) + floor * rms)
+    worst = np.unravel_index(int(np.argmax(excess)), excess.shape) if excess.size else ()
+    assert excess.size == 0 or excess[worst] <= 0, (
+        f"{what}: element {worst}: got {got[worst]:.6g}, ref {ref[worst]:.6g}, "
+        f"bound {rel:g} |ref| + {floor:g} rms")
+

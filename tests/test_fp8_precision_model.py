@@ -1,0 +1,137 @@
+"""The FP8 attention's precision choices, priced on the CPU (no GPU).
+
+tests/fp8_kernel_model.py restates the fp8 kernel's rounding steps (E4M3
+Q''/K'', scores as E4M3 codes relative to a lazily raised running max,
+integer-code probabilities, fp32 sums); these tests compare it with the
+float64 oracle on the decoded inputs:
+
+* on the FP8 edit workload's recipe (and at its full 2048^2 size, sampled
+  rows) the model stays inside the 6e-2 relative-L2 bound;
+* a row with one dominant key 12 binades above 8,192 others: with the running
+  max at code 94 and four binades of lazy headroom (the earlier kernel) the
+  other keys round to code 0 and the row's error is of order 1; with the max
+  at code 118 and one binade of headroom (the kernel now) they stay normal
+  E4M3 numbers and the row is as close as an exact exponential rounded to
+  e4m3(448 p) gets;
+* the model's cut-off: a key is kept down to 14.7 binades below the max and
+  dropped below it.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import fp8_kernel_model as M
+from workloads import e4m3_encode, get_config, make_inputs, make_positions
+
+FP8_REL_L2 = 6e-2
+KERNEL_YM = 118.0
+
+
+def rows_error(got, ref):
+    """(relative L2 over all rows, largest per-row relative L2)."""
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    per_row = np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+    return rel, float(per_row.max())
+
+
+def oracle_head(inp, b, h, rows):
+    q, k, v = oracle.decode_inputs(inp, b, h)
+    return oracle.attention_rows(q[None, :, None], k[None, :, None], v[None, :, None],
+                                 inp.pos, rows)[0, :, 0]
+
+
+def test_model_on_the_edit_recipe():
+    # the FP8 edit workload's recipe at a 32 x 32 grid: 512 text + 2 x 1,024
+    inp = make_inputs(get_config(5, grid=32))
+    S = inp.q.shape[1]
+    rows = np.arange(0, S, 7)
+    num = den = 0.0
+    for h in (0, 11, 23):
+        got = M.attention_head(*M.decode_codes(inp, 0, h), inp.pos, inp.descale, rows,
+                               ym=KERNEL_YM)
+        ref = oracle_head(inp, 0, h, rows)
+        num += float(np.sum((got - ref) ** 2))
+        den += float(np.sum(ref ** 2))
+        assert rows_error(got, ref)[1] <= 0.15
+    rel = np.sqrt(num / den)
+    print(f"edit recipe, 32 x 32 grid: rel-L2 {rel:.3e}")
+    assert 0.03 <= rel <= FP8_REL_L2
+
+
+def test_model_on_the_full_2048_edit_workload():
+    # S = 33,280: sampled rows of two heads (every wave holding one is modelled whole)
+    cfg = get_config(5)
+    inp = make_inputs(cfg)
+    rows = np.array([0, 511, 512, 9000, 17407, 25000, 33279])
+    num = den = 0.0
+    for h in (3, 20):
+        got = M.attention_head(*M.decode_codes(inp, 0, h), inp.pos, inp.descale, rows,
+                               ym=KERNEL_YM)
+        ref = oracle_head(inp, 0, h, rows)
+        num += float(np.sum((got - ref) ** 2))
+        den += float(np.sum(ref ** 2))
+    rel = np.sqrt(num / den)
+    print(f"2048^2 edit workload, sampled rows: rel-L2 {rel:.3e}")
+    assert rel <= FP8_REL_L2
+
+
+def dominant_key_case(gap_binades, n_others=8192, D=128, seed=0):
+    """fp8 inputs where queries 0..63 see key 5 (first tile) gap_binades (log2
+    units of the softmax) above n_others keys of nearly equal score.  All
+    tokens are image tokens (t = l = 0), and the signal lies in the l axis
+    block, which their positions leave unrotated."""
+    rng = np.random.default_rng(seed)
+    pos = make_positions(0, 128, 0)[: n_others + 1]
+    S = pos.shape[0]
+    q = rng.standard_normal((S, D)) * 0.3
+    k = rng.standard_normal((S, D)) * 0.3
+    v = rng.standard_normal((S, D))
+    u = np.zeros(D)
+    u[3 * D // 4:] = 1.0 / np.sqrt(D // 4)
+    q[:64] += 6.0 * u
+    k[5] = gap_binades * np.sqrt(D) / (6.0 * M.LOG2E) * u
+    codes, descale = [], []
+    for x in (q, k, v):
+        s = float(np.float32(np.max(np.abs(x)) / 448.0))
+        codes.append(e4m3_encode(x / s))
+        descale.append(s)
+    return codes, tuple(descale), pos
+
+
+def dominant_errors(gap, ym):
+    codes, descale, pos = dominant_key_case(gap)
+    qc, kc, vc = (oracle.e4m3_decode(c) for c in codes)
+    q, k, v = (oracle.e4m3_decode(c) * s for c, s in zip(codes, descale))
+    rows = np.arange(0, 64, 3)
+    ref = oracle.attention_rows(q[None, :, None], k[None, :, None], v[None, :, None],
+                                pos, rows)[0, :, 0]
+    got = M.attention_head(qc, kc, vc, pos, descale, rows, ym=ym)
+    c, n = M.score_split(descale, q.shape[1])
+    q2 = M.rotate_q(qc, pos, c)[rows]
+    s2 = 2.0 ** n * (q2 @ M.rotate_k(kc, pos).T)
+    p8 = M.e4m3(448.0 * np.exp2(s2 - s2.max(axis=1, keepdims=True)))
+    ideal = M.bf16(p8 @ vc * descale[2] / p8.sum(axis=1, keepdims=True))
+    return rows_error(got, ref)[1], rows_error(ideal, ref)[1]
+
+
+@pytest.mark.parametrize("gap", [11.0, 12.0, 12.5])
+def test_dominant_key_row(gap):
+    old, _ = dominant_errors(gap, ym=94.0)
+    new, ideal = dominant_errors(gap, ym=KERNEL_YM)
+    print(f"gap {gap} binades: per-row rel-L2 max: max at code 94 {old:.3f}, "
+          f"at code 118 {new:.3f}, exact exp2 then e4m3(448 p) {ideal:.3f}")
+    assert old > 1.0
+    assert new <= 0.15
+    assert new <= ideal + 0.05
+
+
+def test_range_cut_off():
+    # one key at x = s - m below the running max: kept above -14.7 binades
+    # (code 0.5 after the shift by 118), dropped below
+    for x, kept in ((-13.75, True), (-14.6, True), (-14.8, False)):
+        y = 8.0 * x + KERNEL_YM
+        code = int(np.rint(np.clip(y, 0.0, 255.0)))
+        assert (oracle.e4m3_decode(np.array([code], dtype=np.uint8))[0] > 0) == kept
+    # the smallest normal code, 8, sits at x = -13.75
+    assert 8.0 * -13.75 + KERNEL_YM == 8.0

@@ -6,7 +6,13 @@ error <= 2^-9); inside, P is rounded to bf16 for dv and ds = p (dp - delta) to
 fp16 for dq and dk, and the inputs of the backward (the forward's bf16 out and
 fp32 lse) carry the forward's own error.  Measured on seeded N(0, 1) inputs
 and on the 1024x1024 workload the relative L2 errors are 1.7e-3 (dq, dk) and
-2.0-2.4e-3 (dv); the bound is rel-L2 <= 6e-3 per gradient tensor.  The log-sum-exp is a p-weighted mean of score errors: the scores
+2.0-2.4e-3 (dv); the bound is rel-L2 <= 6e-3 per gradient tensor.  Each
+element must also satisfy |got - ref| <= 2^-7 |ref| + 0.02 rms, rms taken over
+its (batch, head): a CPU model of the kernels' roundings puts the largest
+excess over the rounding term at 0.009 rms.  ds carries a per-head power of
+two that keeps it inside fp16's range, so these bounds hold for gradients of
+any size; cases with dout scaled by 1e-4, 1e-6 (fine-tuning gradients) and
+1e5 check that.  The log-sum-exp is a p-weighted mean of score errors: the scores
 come from fp16 rotated q and k (relative 2^-11 each), |q'| |k'| / sqrt(D) ~
 sqrt(D) for N(0, 1) inputs, so score errors reach ~1e-3; the bound is 4e-3
 absolute.
@@ -17,12 +23,14 @@ import pytest
 import torch
 
 import joint_attention_rope_amd as kl
-from helpers import bf16_tensor_to_f64, errors, random_inputs, to_device
+from helpers import assert_elementwise, bf16_tensor_to_f64, errors, random_inputs, to_device
 from workloads import bf16_bits_from_f32, get_config, make_inputs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 GRAD_REL_L2 = 6e-3
+GRAD_ELEM_REL = 2.0 ** -7
+GRAD_ELEM_FLOOR = 0.02
 LSE_ABS = 4e-3
 
 
@@ -32,9 +40,9 @@ def bf16_from_f64(x):
         (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
-def run_fwd_bwd(inp, dout_seed):
+def run_fwd_bwd(inp, dout_seed, dout_scale=1.0):
     """GPU forward (out, lse) and backward on inp; returns the device results
-    and the float64 values of the inputs and of dout."""
+    and the float64 values of the inputs and of dout (N(0, dout_scale^2))."""
     import oracle
     q, k, v, pos = to_device(inp)
     B, S, H, D = q.shape
@@ -42,7 +50,7 @@ def run_fwd_bwd(inp, dout_seed):
     lse = torch.empty(B, H, S, dtype=torch.float32, device=DEV)
     kl.klein_rope4d_attn_fwd_lse(q, k, v, pos, out, lse)
     rng = np.random.default_rng(dout_seed)
-    dout, dout64 = bf16_from_f64(rng.standard_normal(q.shape))
+    dout, dout64 = bf16_from_f64(rng.standard_normal(q.shape) * dout_scale)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     ws = torch.empty(kl.klein_attn_bwd_workspace_size(B, S, H, D), dtype=torch.uint8, device=DEV)
     kl.klein_rope4d_attn_bwd(q, k, v, pos, out, dout, lse, dq, dk, dv, ws)
@@ -57,10 +65,12 @@ def check_grads(gpu, ref, what):
         got = bf16_tensor_to_f64(t)
         assert np.isfinite(got).all(), f"{what} {name}: non-finite"
         max_abs, rel = errors(got, r)
-        worst[name] = rel
+        worst[name] = (got, r, rel)
         print(f"{what} {name}: max_abs {max_abs:.3e} rel_l2 {rel:.3e}", flush=True)
-    for name, rel in worst.items():
+    for name, (got, r, rel) in worst.items():
         assert rel <= GRAD_REL_L2, f"{what} {name}: rel_l2 {rel:.3e} > {GRAD_REL_L2}"
+        assert_elementwise(got, r, GRAD_ELEM_REL, GRAD_ELEM_FLOOR, f"{what} {name}",
+                           rms_axes=(1, 3))
 
 
 @pytest.mark.parametrize("B,S,H,D", [
@@ -78,6 +88,18 @@ def test_backward_matches_oracle(B, S, H, D):
     print(f"B={B} S={S} H={H} D={D} lse max_abs {lse_err:.3e}", flush=True)
     check_grads((dq, dk, dv), (rq, rk, rv), f"B={B} S={S} H={H} D={D}")
     assert lse_err <= LSE_ABS
+
+
+@pytest.mark.parametrize("dout_scale", [1e-4, 1e-6, 1e5])
+def test_backward_gradient_size(dout_scale):
+    # fine-tuning gradients are small: with ds rounded to fp16 as it is, most
+    # of it would fall into fp16's subnormals at 1e-4 and below (and overflow
+    # at 1e5); the per-head scale keeps the error where it is at dout ~ 1
+    import oracle
+    inp = random_inputs(1, 1000, 2, 128, seed=77)
+    (out, lse, dq, dk, dv), (q, k, v, dout) = run_fwd_bwd(inp, dout_seed=78, dout_scale=dout_scale)
+    rq, rk, rv, _ = oracle.attention_backward(q, k, v, inp.pos, dout)
+    check_grads((dq, dk, dv), (rq, rk, rv), f"dout x {dout_scale:g}")
 
 
 def test_forward_with_lse_equals_forward():
