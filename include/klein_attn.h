@@ -183,6 +183,35 @@ klein_status_t klein_splitkv_plan(int B, int S, int H, int D, int n_cu, int* pla
                                   size_t* partial_bytes);
 
 /*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the call
+ * klein_rope4d_attn_fwd_ws makes (same arguments, same kernels, same
+ * result bit for bit), with its workspace replaced by a scratch array that
+ * the library holds in static device memory, one per GPU.  The call itself
+ * allocates nothing and calls no allocating routine.
+ *   Scratch: KLEIN_NOALLOC_SCRATCH_BYTES (320 MiB) per GPU, taken when the
+ *   process first calls this function on that GPU and held until the
+ *   process ends.  A call whose klein_attn_workspace_size is larger returns
+ *   UNSUPPORTED before any device work (e.g. B = 4, S = 16,896, H = 24,
+ *   D = 128, bf16 needs 517 MB; the 2048^2 shapes with B = 2 bf16 or B = 1
+ *   fp8 fit).
+ *   Every call on one GPU uses that GPU's single array: two calls that run
+ *   at the same time on one GPU (different streams, threads or processes
+ *   sharing a context) race, and their results are undefined; calls in
+ *   stream order are fine.  The array keeps the last call's contents; no
+ *   part of it needs to start at zero (every byte a call reads, it has
+ *   written before, in stream order).
+ * Other arguments and errors as klein_rope4d_attn_fwd_ws (dtype BF16
+ * ignores the descales); NO_DEVICE without a usable GPU.
+ */
+#define KLEIN_NOALLOC_SCRATCH_BYTES (320LL * 1024 * 1024)
+klein_status_t klein_rope4d_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                                             const int32_t* pos_thwl, void* out,
+                                             int B, int S, int H, int D, klein_dtype_t dtype,
+                                             float q_descale, float k_descale,
+                                             float v_descale, klein_stream_t stream);
+
+/*
  * Training forward: klein_rope4d_attn_fwd for bfloat16 inputs that also
  * writes the softmax statistic the backward needs,
  *   lse[b][h][i] = log sum_j exp(<q'_i, k'_j> / sqrt(D))   (natural log),

@@ -13,7 +13,7 @@ import torch
 from . import _capi
 from ._capi import (KLEIN_DTYPE_BF16, KLEIN_DTYPE_FP8_E4M3, KLEIN_ERR_INVALID_ARG,
                     KLEIN_ERR_LAUNCH, KLEIN_ERR_NO_DEVICE, KLEIN_ERR_UNSUPPORTED, KLEIN_OK,
-                    KLEIN_SPARSE_KBLOCK, KLEIN_SPARSE_QBLOCK)
+                    KLEIN_NOALLOC_SCRATCH_BYTES, KLEIN_SPARSE_KBLOCK, KLEIN_SPARSE_QBLOCK)
 
 __all__ = [
     "KleinError", "klein_rope4d_attn_fwd", "klein_rope4d_attn_fwd_fp8",
@@ -22,7 +22,8 @@ __all__ = [
     "KLEIN_SPARSE_QBLOCK", "KLEIN_SPARSE_KBLOCK", "blocksparse_mask_shape",
     "klein_qkv_rope4d_proj", "klein_attn_fwd_prerotated", "klein_rope4d_attn_fwd_ws",
     "klein_attn_workspace_size", "klein_splitkv_plan", "klein_rope4d_attn_fwd_lse",
-    "klein_rope4d_attn_bwd", "klein_attn_bwd_workspace_size",
+    "klein_rope4d_attn_bwd", "klein_attn_bwd_workspace_size", "klein_rope4d_attn_fwd_noalloc",
+    "KLEIN_NOALLOC_SCRATCH_BYTES",
 ]
 
 
@@ -145,15 +146,8 @@ def klein_splitkv_plan(B, S, H, D, n_cu):
     return plan[0], plan[1], plan[2], n.value
 
 
-def klein_rope4d_attn_fwd_ws(q, k, v, pos_thwl, out, workspace, dtype=None,
-                             descales=(1.0, 1.0, 1.0), stream=None):
-    """The dense attention on the split-KV schedule (whole rounds of query
-    tiles, then the remaining tiles cut into key chunks over every compute unit).
-
-    workspace: a contiguous GPU tensor (any dtype) of at least
-    klein_attn_workspace_size(B, S, H, D, dtype) bytes, or None when that is 0.
-    dtype: inferred from q.dtype when None; descales (q, k, v) apply to fp8 only.
-    """
+def _ws_call_args(q, k, v, pos_thwl, out, dtype):
+    """Shape and dtype checks of the split-KV entry points: (B, S, H, D, dtype)."""
     B, S, H, D = _bshd(q, "q")
     for t, n in ((k, "k"), (v, "v"), (out, "out")):
         if _bshd(t, n) != (B, S, H, D):
@@ -167,6 +161,34 @@ def klein_rope4d_attn_fwd_ws(q, k, v, pos_thwl, out, workspace, dtype=None,
             raise ValueError(f"{n} has dtype {t.dtype}, which does not match the dtype code {dtype}")
     if out.dtype != torch.bfloat16:
         raise ValueError("out must be bfloat16")
+    return B, S, H, D, dtype
+
+
+def klein_rope4d_attn_fwd_noalloc(q, k, v, pos_thwl, out, dtype=None,
+                                  descales=(1.0, 1.0, 1.0), stream=None):
+    """klein_rope4d_attn_fwd_ws with the library's static per-GPU scratch
+    (KLEIN_NOALLOC_SCRATCH_BYTES) as its workspace: allocates nothing.
+    Calls that overlap on one GPU race.  A shape whose workspace exceeds the
+    scratch raises KleinError (status UNSUPPORTED)."""
+    B, S, H, D, dtype = _ws_call_args(q, k, v, pos_thwl, out, dtype)
+    dq, dk, dv = (float(x) for x in descales)
+    st = _capi.lib().klein_rope4d_attn_fwd_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), pos_thwl.data_ptr(), out.data_ptr(),
+        B, S, H, D, int(dtype), dq, dk, dv, _stream(stream, q.device))
+    _check(st, "klein_rope4d_attn_fwd_noalloc")
+    return out
+
+
+def klein_rope4d_attn_fwd_ws(q, k, v, pos_thwl, out, workspace, dtype=None,
+                             descales=(1.0, 1.0, 1.0), stream=None):
+    """The dense attention on the split-KV schedule (whole rounds of query
+    tiles, then the remaining tiles cut into key chunks over every compute unit).
+
+    workspace: a contiguous GPU tensor (any dtype) of at least
+    klein_attn_workspace_size(B, S, H, D, dtype) bytes, or None when that is 0.
+    dtype: inferred from q.dtype when None; descales (q, k, v) apply to fp8 only.
+    """
+    B, S, H, D, dtype = _ws_call_args(q, k, v, pos_thwl, out, dtype)
     if workspace is None:
         wp, wb = 0, 0
     else:

@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libklein_attn.so")
 SOURCES = ["api.cpp", "attn_fwd_bf16.hip", "attn_fwd_fp8.hip", "qkv_rope_proj.hip", "rope_apply.hip",
-           "split_schedule.hip", "attn_bwd.hip"]
+           "split_schedule.hip", "attn_bwd.hip", "noalloc.hip"]
 # Device kernels never see NaN inputs on purpose (a NaN in q/k/v propagates to
 # out either way), so min/max need no IEEE NaN canonicalisation.  The host
 # argument checks (std::isfinite on descales) keep full NaN semantics.

@@ -230,19 +230,30 @@ klein_status_t klein_splitkv_plan(int B, int S, int H, int D, int n_cu, int* pla
   return KLEIN_OK;
 }
 
+// The checks of the split-KV entry points that need no device.
+static klein_status_t check_ws_call(const void* q, const void* k, const void* v,
+                                    const int32_t* pos_thwl, const void* out, int B, int S, int H,
+                                    int D, klein_dtype_t dtype, float q_descale, float k_descale,
+                                    float v_descale) {
+  if (dtype != KLEIN_DTYPE_BF16 && dtype != KLEIN_DTYPE_FP8_E4M3) return KLEIN_ERR_INVALID_ARG;
+  klein_status_t st = check_common(q, k, v, pos_thwl, out, B, S, H, D);
+  if (st != KLEIN_OK) return st;
+  if (dtype == KLEIN_DTYPE_FP8_E4M3)
+    for (float s : {q_descale, k_descale, v_descale})
+      if (!(std::isfinite(s) && s > 0.f)) return KLEIN_ERR_INVALID_ARG;
+  if (klein::attn_fwd_bf16_grid(B, S, H) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
+  return KLEIN_OK;
+}
+
 static klein_status_t attn_ws(const void* q, const void* k, const void* v,
                               const int32_t* pos_thwl, void* out, float* lse, int B, int S, int H,
                               int D, klein_dtype_t dtype, float q_descale, float k_descale,
                               float v_descale, void* workspace, size_t workspace_bytes,
                               klein_stream_t stream) {
-  if (dtype != KLEIN_DTYPE_BF16 && dtype != KLEIN_DTYPE_FP8_E4M3) return KLEIN_ERR_INVALID_ARG;
-  klein_status_t st = check_common(q, k, v, pos_thwl, out, B, S, H, D);
+  klein_status_t st = check_ws_call(q, k, v, pos_thwl, out, B, S, H, D, dtype, q_descale,
+                                    k_descale, v_descale);
   if (st != KLEIN_OK) return st;
   const bool fp8 = dtype == KLEIN_DTYPE_FP8_E4M3;
-  if (fp8)
-    for (float s : {q_descale, k_descale, v_descale})
-      if (!(std::isfinite(s) && s > 0.f)) return KLEIN_ERR_INVALID_ARG;
-  if (klein::attn_fwd_bf16_grid(B, S, H) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
   if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return KLEIN_ERR_INVALID_ARG;
   try {
     hipError_t e;
@@ -277,6 +288,32 @@ klein_status_t klein_rope4d_attn_fwd_ws(const void* q, const void* k, const void
                                         size_t workspace_bytes, klein_stream_t stream) {
   return attn_ws(q, k, v, pos_thwl, out, nullptr, B, S, H, D, dtype, q_descale, k_descale,
                  v_descale, workspace, workspace_bytes, stream);
+}
+
+klein_status_t klein_rope4d_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                                             const int32_t* pos_thwl, void* out, int B, int S,
+                                             int H, int D, klein_dtype_t dtype, float q_descale,
+                                             float k_descale, float v_descale,
+                                             klein_stream_t stream) {
+  static_assert(KLEIN_NOALLOC_SCRATCH_BYTES == klein::kNoallocScratchBytes,
+                "the header states the scratch size");
+  const klein_status_t st = check_ws_call(q, k, v, pos_thwl, out, B, S, H, D, dtype, q_descale,
+                                          k_descale, v_descale);
+  if (st != KLEIN_OK) return st;
+  try {
+    hipError_t e;
+    const int ncu = current_cu_count(&e);
+    if (e != hipSuccess) return map_hip(e);
+    if (ws_layout(B, S, H, D, dtype, ncu).total > klein::kNoallocScratchBytes)
+      return KLEIN_ERR_UNSUPPORTED;
+    void* scratch = nullptr;
+    e = klein::noalloc_scratch(&scratch);
+    if (e != hipSuccess) return map_hip(e);
+    return attn_ws(q, k, v, pos_thwl, out, nullptr, B, S, H, D, dtype, q_descale, k_descale,
+                   v_descale, scratch, (size_t)klein::kNoallocScratchBytes, stream);
+  } catch (...) {
+    return KLEIN_ERR_LAUNCH;
+  }
 }
 
 klein_status_t klein_rope4d_attn_fwd_lse_ws(const void* q, const void* k, const void* v,
@@ -426,7 +463,7 @@ const char* klein_status_string(klein_status_t status) {
   switch (status) {
     case KLEIN_OK: return "ok";
     case KLEIN_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, size < 1, bad dtype or descale)";
-    case KLEIN_ERR_UNSUPPORTED: return "unsupported (head dim must be 64 or 128; grid or block mask too large)";
+    case KLEIN_ERR_UNSUPPORTED: return "unsupported (head dim must be 64 or 128; grid or block mask too large; or, for klein_rope4d_attn_fwd_noalloc, the call needs more than its fixed scratch)";
     case KLEIN_ERR_NO_DEVICE: return "no usable GPU";
     case KLEIN_ERR_LAUNCH: return "kernel launch failed";
   }

@@ -92,6 +92,12 @@ struct BwdWorkspace {
 };
 BwdWorkspace attn_bwd_workspace(int B, int S, int H, int D);
 
+// Scratch of the no-allocation entry point (noalloc.hip): the device address,
+// on the current GPU, of a static array of kNoallocScratchBytes, looked up
+// once per GPU.  Calls that use it at the same time on one GPU race.
+constexpr long long kNoallocScratchBytes = 320LL << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // QKV projection with the RoPE-4D epilogue: x [B S][C] bf16, w [3 H D][C]
 // bf16 (or both E4M3 codes with descales, fp8), bias [3 H D] bf16 or null
 // -> q', k' fp16 and v bf16, [B][S][H][D].

@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
         "klein_attn_workspace_size", "klein_splitkv_plan", "klein_rope4d_attn_fwd_lse",
         "klein_rope4d_attn_fwd_lse_ws",
         "klein_rope4d_attn_bwd", "klein_attn_bwd_workspace_size", "klein_rope4d_apply",
-        "klein_status_string", "klein_version"])
+        "klein_rope4d_attn_fwd_noalloc", "klein_status_string", "klein_version"])
 
 
 def test_library_exports_every_declared_symbol():
