@@ -98,9 +98,10 @@ klein_status_t klein_rope4d_attn_fwd(const void* q, const void* k, const void* v
  * reads a code as the log2 of its value: within a binade this is a linear
  * interpolation of 2^x, up to 6.2 % high, and the same codes give the row
  * sums, so only the variation of that bias is left in out.  The row max is
- * raised lazily (when a row grows by more than one binade), so a key is kept
- * as a normal E4M3 number down to 13.75 binades (9.5 nats) below its row's
- * max, as a subnormal to 14.7, and as 0 below that.  On N(0, 1) inputs of
+ * raised lazily, only when a row's code would pass 126 (448), and then to
+ * code 110: a key is kept as a normal E4M3 number down to 13.75 binades
+ * (9.5 nats) below its row's first max (12.75 below a raised one), as a
+ * subnormal about one binade further, and as 0 below that.  On N(0, 1) inputs of
  * the 2048^2 edit workload the result is within 4.5e-2 relative L2 of exact
  * attention of the decoded inputs (bound 6e-2).
  */

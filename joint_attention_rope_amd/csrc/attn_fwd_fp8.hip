@@ -13,8 +13,9 @@
 //                                        initial value: Y = 8 (s - m) + 118
 //   P8  = code rne(clamp(Y, 0, 255))     an E4M3 code read as an integer
 //                                        (v_cvt_pk_u8_f32); m is the running
-//                                        row max, raised only when a row grows
-//                                        by more than 1, so Y <= 126 (448)
+//                                        row max, raised only when a row's
+//                                        code would pass 126 (448), and then
+//                                        to code 110
 //   O^T += V^T P8^T                      V row-major in LDS, read transposed
 //   l  += ones^T P8^T                    row sums of P8, on the MFMA as well
 //   out = O * dv / l
@@ -38,16 +39,18 @@
 // the common factor cancels and only the interpolation's variation within a
 // binade remains (rel-L2 on the 2048^2 edit workload 4.1e-2 -> 4.5e-2, by a
 // CPU model of these roundings).
-// Range: with the max at code 118 (224) and at most one binade of growth
-// before a rescale, P8 stays a normal number down to x = -13.75, within a
-// binade of what an exact exponential scaled to 448 keeps; below code 8 the
-// codes are subnormals (value c 2^-9, no longer 2^(c/8 - 7)), and below
-// x = -14.7 they round to 0 (a masked key's -inf as well).  A key that far
-// below the row max carries a weight of at most 2^-14.7 of it, which matters
-// only when thousands of such keys face one dominant key.  The lazy
-// headroom costs rescales: about one wave-tile in 20 on N(0, 1) scores of
-// the 2048^2 edit workload, against one in 800 with the max at code 94 and
-// four binades of headroom, which cut keys off at x = -11.7.
+// Range: the first max (tile 0's exact row max) sits at code 118 (224): P8
+// stays a normal number down to x = -13.75, within a binade of what an
+// exact exponential scaled to 448 keeps.  A raise puts the new max at code
+// 110, leaving two binades of headroom (12.75 binades of normals below it):
+// rescales then come about once in 45 wave-tiles on N(0, 1) scores of the
+// 2048^2 edit workload (once in 20 with the raised max at 118, once in 800
+// with the max at 94 and four binades of headroom, which cut keys off at
+// x = -11.7).  Below code 8 the codes are subnormals (value c 2^-9, no longer
+// 2^(c/8 - 7)), and codes below 0.5 round to 0 (a masked key's -inf as
+// well).  A key that far below the row max carries a weight of at most
+// 2^-12.7 of it, which matters only when thousands of such keys face one
+// dominant key.
 //
 // Schedule (per wave; K'' and V double-buffered in LDS, one barrier a tile):
 //   softmax max of S(t); rare rescale of O and l
@@ -149,7 +152,8 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   constexpr int TROW = NJ + 2;         // cos/sin table row stride (half2)
   constexpr int TSLOT = 10;            // per-thread fallback slot stride
   constexpr int TAB = kTabN * TROW;    // start of the fallback slots
-  constexpr float YM = 118.0f;         // code of a score equal to the running max
+  constexpr float YM = 118.0f;         // code of a score equal to the first running max
+  constexpr float YR = 110.0f;         // code of the running max after a raise
   constexpr float YMAX = 126.0f;       // largest finite E4M3 code (448)
   static_assert(NCH == NT || 2 * NCH == NT, "one K and one V chunk per thread (D 128) "
                                             "or one of either (D 64)");
@@ -378,7 +382,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
     mask_tail(t, sc);
     const float mx = rowmax32(sc);              // code of the row's largest score
     if (__builtin_amdgcn_ballot_w64(mx > YMAX)) {
-      const float delta = __builtin_fmaxf(mx - YM, 0.f);
+      const float delta = __builtin_fmaxf(mx - YR, 0.f);
       const float alpha = __builtin_amdgcn_exp2f(-0.125f * delta);
       m8 += delta;
       lacc *= alpha;

@@ -13,10 +13,11 @@ its precision choices can be priced against the float64 oracle on the CPU:
 The running max starts at the exact row max of the first 64-key tile.  A wave
 of 32 queries checks each tile's row maxima; when any of its rows has a code
 above 126 (E4M3's largest finite value, 448), every row of the wave moves its
-max to its own tile max where that is higher than ym below it (delta =
-max(Ymax - ym, 0)), and O and l are scaled by 2^(-delta/8).  Codes below 0.5
-round to 0: a key more than about (ym + 0.5)/8 binades below the running
-max contributes nothing.  The split-KV schedule's chunks follow the same
+max to code ym_post where its tile max lies higher (delta = max(Ymax -
+ym_post, 0)), and O and l are scaled by 2^(-delta/8).  Codes below 0.5 round
+to 0: a key more than about (ym + 0.5)/8 binades below the first running
+max, or (ym_post + 0.5)/8 below a raised one, contributes nothing.  The
+kernel's values: ym = 118, ym_post = 110.  The split-KV schedule's chunks follow the same
 rules from their own first tile; this model covers the whole-tile path.
 """
 
@@ -84,13 +85,15 @@ def rotate_k(kc, pos):
     return out
 
 
-def attention_head(qc, kc, vc, pos, descale, rows, ym=94.0, stats=None):
+def attention_head(qc, kc, vc, pos, descale, rows, ym=118.0, stats=None, ym_post=110.0):
     """Output rows ``rows`` of one head (float64 values of the bf16 result).
 
     qc, kc, vc: float64 E4M3 code values [S, D] (no descale); every wave that
     holds one of ``rows`` is modelled in full (its rescale decisions depend
     on all 32 of its queries).  ``stats`` (a dict), if given, receives the
-    number of rescales per wave and tile."""
+    number of rescales per wave and tile.  ``ym_post``: the code a rescale
+    moves a row's max to (None: ym)."""
+    ym_post = ym if ym_post is None else ym_post
     S, D = qc.shape
     c, n = score_split(descale, D)
     waves = np.unique(np.asarray(rows) // WAVE)
@@ -113,7 +116,7 @@ def attention_head(qc, kc, vc, pos, descale, rows, ym=94.0, stats=None):
         mx = y.max(axis=2)
         hit = (mx > YMAX).any(axis=1)                                        # per wave
         if hit.any():
-            delta = np.where(hit[:, None], np.maximum(mx - ym, 0.0), 0.0)
+            delta = np.where(hit[:, None], np.maximum(mx - ym_post, 0.0), 0.0)
             alpha = np.exp2(-delta / 8.0)
             m8 += delta
             o *= alpha[..., None]

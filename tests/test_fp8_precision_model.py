@@ -9,10 +9,10 @@ float64 oracle on the decoded inputs:
   rows) the model stays inside the 6e-2 relative-L2 bound;
 * a row with one dominant key 12 binades above 8,192 others: with the running
   max at code 94 and four binades of lazy headroom (the earlier kernel) the
-  other keys round to code 0 and the row's error is of order 1; with the max
-  at code 118 and one binade of headroom (the kernel now) they stay normal
-  E4M3 numbers and the row is as close as an exact exponential rounded to
-  e4m3(448 p) gets;
+  other keys round to code 0 and the row's error is of order 1; with the
+  first max at code 118 (the kernel now) they stay normal E4M3 numbers and
+  the row is as close as an exact exponential rounded to e4m3(448 p) gets;
+  a dominant key met mid-sequence (a raised max, at code 110) as well;
 * the model's cut-off: a key is kept down to 14.7 binades below the max and
   dropped below it.
 """
@@ -25,7 +25,8 @@ import fp8_kernel_model as M
 from workloads import e4m3_encode, get_config, make_inputs, make_positions
 
 FP8_REL_L2 = 6e-2
-KERNEL_YM = 118.0
+KERNEL_YM = 118.0          # code of the first running max
+KERNEL_YR = 110.0          # code of a raised running max
 
 
 def rows_error(got, ref):
@@ -49,7 +50,7 @@ def test_model_on_the_edit_recipe():
     num = den = 0.0
     for h in (0, 11, 23):
         got = M.attention_head(*M.decode_codes(inp, 0, h), inp.pos, inp.descale, rows,
-                               ym=KERNEL_YM)
+                               ym=KERNEL_YM, ym_post=KERNEL_YR)
         ref = oracle_head(inp, 0, h, rows)
         num += float(np.sum((got - ref) ** 2))
         den += float(np.sum(ref ** 2))
@@ -67,7 +68,7 @@ def test_model_on_the_full_2048_edit_workload():
     num = den = 0.0
     for h in (3, 20):
         got = M.attention_head(*M.decode_codes(inp, 0, h), inp.pos, inp.descale, rows,
-                               ym=KERNEL_YM)
+                               ym=KERNEL_YM, ym_post=KERNEL_YR)
         ref = oracle_head(inp, 0, h, rows)
         num += float(np.sum((got - ref) ** 2))
         den += float(np.sum(ref ** 2))
@@ -76,11 +77,11 @@ def test_model_on_the_full_2048_edit_workload():
     assert rel <= FP8_REL_L2
 
 
-def dominant_key_case(gap_binades, n_others=8192, D=128, seed=0):
-    """fp8 inputs where queries 0..63 see key 5 (first tile) gap_binades (log2
-    units of the softmax) above n_others keys of nearly equal score.  All
-    tokens are image tokens (t = l = 0), and the signal lies in the l axis
-    block, which their positions leave unrotated."""
+def dominant_key_case(gap_binades, n_others=8192, D=128, seed=0, dom=5):
+    """fp8 inputs where queries 0..63 see key `dom` (5: the first tile)
+    gap_binades (log2 units of the softmax) above n_others keys of nearly
+    equal score.  All tokens are image tokens (t = l = 0), and the signal
+    lies in the l axis block, which their positions leave unrotated."""
     rng = np.random.default_rng(seed)
     pos = make_positions(0, 128, 0)[: n_others + 1]
     S = pos.shape[0]
@@ -90,7 +91,7 @@ def dominant_key_case(gap_binades, n_others=8192, D=128, seed=0):
     u = np.zeros(D)
     u[3 * D // 4:] = 1.0 / np.sqrt(D // 4)
     q[:64] += 6.0 * u
-    k[5] = gap_binades * np.sqrt(D) / (6.0 * M.LOG2E) * u
+    k[dom] = gap_binades * np.sqrt(D) / (6.0 * M.LOG2E) * u
     codes, descale = [], []
     for x in (q, k, v):
         s = float(np.float32(np.max(np.abs(x)) / 448.0))
@@ -99,14 +100,14 @@ def dominant_key_case(gap_binades, n_others=8192, D=128, seed=0):
     return codes, tuple(descale), pos
 
 
-def dominant_errors(gap, ym):
-    codes, descale, pos = dominant_key_case(gap)
+def dominant_errors(gap, ym, ym_post=None, dom=5):
+    codes, descale, pos = dominant_key_case(gap, dom=dom)
     qc, kc, vc = (oracle.e4m3_decode(c) for c in codes)
     q, k, v = (oracle.e4m3_decode(c) * s for c, s in zip(codes, descale))
     rows = np.arange(0, 64, 3)
     ref = oracle.attention_rows(q[None, :, None], k[None, :, None], v[None, :, None],
                                 pos, rows)[0, :, 0]
-    got = M.attention_head(qc, kc, vc, pos, descale, rows, ym=ym)
+    got = M.attention_head(qc, kc, vc, pos, descale, rows, ym=ym, ym_post=ym_post)
     c, n = M.score_split(descale, q.shape[1])
     q2 = M.rotate_q(qc, pos, c)[rows]
     s2 = 2.0 ** n * (q2 @ M.rotate_k(kc, pos).T)
@@ -117,13 +118,25 @@ def dominant_errors(gap, ym):
 
 @pytest.mark.parametrize("gap", [11.0, 12.0, 12.5])
 def test_dominant_key_row(gap):
-    old, _ = dominant_errors(gap, ym=94.0)
-    new, ideal = dominant_errors(gap, ym=KERNEL_YM)
+    old, _ = dominant_errors(gap, ym=94.0, ym_post=94.0)
+    new, ideal = dominant_errors(gap, ym=KERNEL_YM, ym_post=KERNEL_YR)
     print(f"gap {gap} binades: per-row rel-L2 max: max at code 94 {old:.3f}, "
           f"at code 118 {new:.3f}, exact exp2 then e4m3(448 p) {ideal:.3f}")
     assert old > 1.0
     assert new <= 0.15
     assert new <= ideal + 0.05
+
+
+@pytest.mark.parametrize("gap", [11.0, 12.0])
+def test_dominant_key_met_mid_sequence(gap):
+    # the dominant key in tile 64: the rows' max is raised to code 110 there,
+    # with half the other keys still to come below it
+    old, _ = dominant_errors(gap, ym=94.0, ym_post=94.0, dom=4096 + 5)
+    new, ideal = dominant_errors(gap, ym=KERNEL_YM, ym_post=KERNEL_YR, dom=4096 + 5)
+    print(f"gap {gap} binades, key mid-sequence: max at code 94 {old:.3f}, "
+          f"kernel {new:.3f}, exact exp2 then e4m3(448 p) {ideal:.3f}")
+    assert old > 0.3
+    assert new <= 0.15
 
 
 def test_range_cut_off():

@@ -73,21 +73,22 @@ def test_fp8_deterministic():
 
 
 @pytest.mark.parametrize("entry", ["plain", "workspace"])
-@pytest.mark.parametrize("gap", [11.0, 12.0])
-def test_fp8_dominant_key_row(entry, gap):
-    """Queries 0..63 face one key (in the first key tile) gap binades above
-    8,192 others.  The probabilities are E4M3 codes relative to the running
-    max; the max sits at code 118 with one binade of headroom, so the other
-    keys stay normal E4M3 numbers (with the max at code 94 they rounded to 0
-    and the row's error was of order 1)."""
+@pytest.mark.parametrize("gap,dom", [(11.0, 5), (12.0, 5), (12.0, 4101)])
+def test_fp8_dominant_key_row(entry, gap, dom):
+    """Queries 0..63 face one key gap binades above 8,192 others, in the
+    first key tile (dom 5) or mid-sequence (dom 4101, where the running max
+    is raised).  The probabilities are E4M3 codes relative to the running
+    max, which sits at code 118 (110 after a raise), so the other keys stay
+    normal E4M3 numbers (with the max at code 94 they rounded to 0 and the
+    row's error was of order 1)."""
     from test_fp8_precision_model import dominant_key_case
     from workloads import Inputs
-    codes, descale, pos = dominant_key_case(gap)
+    codes, descale, pos = dominant_key_case(gap, dom=dom)
     S, D = pos.shape[0], 128
     shape = (1, S, 1, D)
     inp = Inputs(get_config(5, B=1, H=1, D=D), *(c.reshape(shape) for c in codes), pos,
                  descale=descale)
-    print(f"[case] fp8 dominant key gap {gap} entry {entry}", flush=True)
+    print(f"[case] fp8 dominant key gap {gap} key {dom} entry {entry}", flush=True)
     q, k, v, p = to_device(inp)
     out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
     if entry == "plain":
@@ -102,6 +103,6 @@ def test_fp8_dominant_key_row(entry, gap):
     gpu = bf16_tensor_to_f64(out[:, :64])
     ref = oracle_rows(inp, rows)
     worst = float(row_rel_l2(gpu, ref).max())
-    print(f"gap {gap} {entry}: worst dominant row rel-L2 {worst:.3e}", flush=True)
+    print(f"gap {gap} key {dom} {entry}: worst dominant row rel-L2 {worst:.3e}", flush=True)
     assert worst <= FP8_ROW_REL_L2
 
