@@ -56,9 +56,13 @@
 extern "C" {
 #endif
 
+/* Both enums carry one more enumerator, at INT_MIN, that is no value of the
+ * type: it makes each type span every int, so that any int a caller passes
+ * (and the library rejects) is a valid value of the type in C++ too. */
 typedef enum {
   KLEIN_DTYPE_BF16 = 0,      /* q, k, v are bfloat16 */
-  KLEIN_DTYPE_FP8_E4M3 = 1   /* q, k, v are OCP FP8 E4M3FN codes, descale 1 */
+  KLEIN_DTYPE_FP8_E4M3 = 1,  /* q, k, v are OCP FP8 E4M3FN codes, descale 1 */
+  KLEIN_DTYPE_SPAN_INT_ = -0x7fffffff - 1
 } klein_dtype_t;
 
 typedef enum {
@@ -66,7 +70,8 @@ typedef enum {
   KLEIN_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, size < 1, bad dtype, bad descale */
   KLEIN_ERR_UNSUPPORTED = 2,  /* D not in {64, 128}, or grid too large */
   KLEIN_ERR_NO_DEVICE = 3,    /* the HIP runtime found no usable GPU */
-  KLEIN_ERR_LAUNCH = 4        /* the kernel launch itself failed */
+  KLEIN_ERR_LAUNCH = 4,       /* the kernel launch itself failed */
+  KLEIN_STATUS_SPAN_INT_ = -0x7fffffff - 1
 } klein_status_t;
 
 /* Opaque stream handle: a hipStream_t passed as a pointer. */

@@ -466,6 +466,7 @@ const char* klein_status_string(klein_status_t status) {
     case KLEIN_ERR_UNSUPPORTED: return "unsupported (head dim must be 64 or 128; grid or block mask too large; or, for klein_rope4d_attn_fwd_noalloc, the call needs more than its fixed scratch)";
     case KLEIN_ERR_NO_DEVICE: return "no usable GPU";
     case KLEIN_ERR_LAUNCH: return "kernel launch failed";
+    case KLEIN_STATUS_SPAN_INT_: break;
   }
   return "unknown status";
 }
