@@ -54,7 +54,6 @@ from .joint_attention import (
     attention_rows,
     bf16_to_f64,
     decode_inputs,
-    rel_l2,
 )
 from .backward import attention_backward
 from .blocksparse import (
@@ -78,7 +77,6 @@ __all__ = [
     "decode_inputs",
     "e4m3_decode",
     "qkv_rope4d_proj",
-    "rel_l2",
     "rope4d",
     "rope_frequencies",
 ]

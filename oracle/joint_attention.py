@@ -147,12 +147,3 @@ def _run(task, jobs, workers):
         else:
             with ThreadPoolExecutor(max_workers=n) as ex:
                 list(ex.map(task, jobs))
-
-
-def rel_l2(a, ref) -> float:
-    """||a - ref||_2 / ||ref||_2 over the whole array (float64)."""
-    a = np.asarray(a, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    den = np.linalg.norm(ref.ravel())
-    num = np.linalg.norm((a - ref).ravel())
-    return float(num / den) if den > 0 else float(num)
