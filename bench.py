@@ -17,13 +17,22 @@ Prints ONE JSON line.  Fields beyond the common ones:
   cpu_baseline  -- the fp64 CPU oracle timed on a bounded sample of the same
                    workload (a seeded subset of query rows), scaled to TFLOP/s;
   fp8           -- the FP8 E4M3 variant on the 2048x2048 edit workload
-                   (S = 33,280), against dense fp8 MFMA peak.
+                   (S = 33,280), against dense fp8 MFMA peak;
+  clock         -- the engine clock the attention kernels ran at, from a short
+                   rocprofv3 counter run of this script right after the timing
+                   (GRBM_GUI_ACTIVE per XCD over the dispatch duration), and
+                   the fraction of the MFMA peak at that clock;
+  next          -- the adjacent workloads: the attention backward at the
+                   headline shape, the 1024x1024 workloads warm and cold, and
+                   a 2048x2048 edit with two references.
 """
 
 import argparse
 import json
 import os
+import subprocess
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -46,6 +55,18 @@ def stored_traffic(name, call):
     if rec.get("call") != call or rec.get("sources_hash") != sources_hash(CALLS[call]["sources"]):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def traffic_source(name):
+    """Where a stored traffic figure comes from: the summary file and the
+    hash of the kernel sources it was taken on."""
+    try:
+        with open(os.path.join(ROOT, "profiles", f"traffic_{name}.json")) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return f"profiles/traffic_{name}.json (rocprofv3 FETCH_SIZE + WRITE_SIZE passes, " \
+           f"kernel sources hash {rec.get('sources_hash')})"
 
 
 def to_device(inp, dev):
@@ -102,7 +123,11 @@ def cpu_baseline(inp, cfg, target_s=15.0):
     import numpy as np
     import oracle
     from workloads import Inputs
-    workers = min(16, len(os.sched_getaffinity(0)))
+    visible = len(os.sched_getaffinity(0))
+    # a GPU machine gives each GPU a share of 16 host threads, whatever the
+    # affinity mask shows (OMP_NUM_THREADS says the same there)
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    workers = min(visible, share) if share > 0 else visible
     sub = Inputs(cfg, inp.q[:1], inp.k[:1], inp.v[:1], inp.pos, inp.descale)
     rng = np.random.default_rng(12345)
     # a discarded warm-up (thread pool, BLAS), then a calibration sample that
@@ -128,10 +153,160 @@ def cpu_baseline(inp, cfg, target_s=15.0):
         "value": round(flops / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": workers,
+        "cores_visible": visible,
         "kind": "oracle",
         "sample": f"{n} seeded query rows x {cfg.H} heads of batch entry 0 "
                   f"(all {cfg.S} keys each), float64 NumPy, {dt:.1f} s",
     }
+
+
+# kernels whose engine clock the counter run reports
+CLOCK_KERNELS = {"bf16": "attn_fwd_bf16_kernel", "fp8": "attn_fwd_fp8_kernel"}
+
+
+def clock_child(torch, kl, dev):
+    """--clock-child: a few calls of the two timed entry points on their
+    workloads, for the counter run that observed_clock() makes of this."""
+    from workloads import get_config, make_inputs
+    for cid in (4, 5):
+        c = get_config(cid)
+        print(f"[clock] {c.dtype} S={c.S}: generating inputs", file=sys.stderr, flush=True)
+        xi = make_inputs(c)
+        xq, xk, xv, xp = to_device(xi, dev)
+        xo = torch.empty(xq.shape, dtype=torch.bfloat16, device=dev)
+        xw = workspace(kl, torch, c, dev)
+        for _ in range(5):
+            kl.klein_rope4d_attn_fwd_ws(xq, xk, xv, xp, xo, xw, descales=xi.descale or (1.0, 1.0, 1.0))
+        torch.cuda.synchronize()
+        print(f"[clock] {c.dtype}: 5 calls done", file=sys.stderr, flush=True)
+        del xq, xk, xv, xo, xw
+
+
+def observed_clock():
+    """Engine clock while the attention kernels run: one rocprofv3 counter
+    pass (GRBM_GUI_ACTIVE, the busy cycles of each XCD) over a child run of
+    this script (--clock-child), divided by each dispatch's duration; the mean
+    over the last three dispatches of each kernel, in MHz.  The profiler runs
+    as a child process (never in place of this one)."""
+    import csv
+    import shutil
+    prof = shutil.which("rocprofv3") or "/opt/rocm/bin/rocprofv3"
+    out = tempfile.mkdtemp(prefix="klein_clock_", dir="/tmp")
+    cmd = [prof, "--log-level", "error", "--pmc", "GRBM_GUI_ACTIVE", "--output-format", "csv",
+           "-d", out, "-o", "clk", "--", sys.executable, os.path.join(ROOT, "bench.py"),
+           "--clock-child"]
+    print("[clock] counter run: " + " ".join(cmd[:8]) + " ... -- bench.py --clock-child",
+          file=sys.stderr, flush=True)
+    res = {"method": "rocprofv3 --pmc GRBM_GUI_ACTIVE over a child run of bench.py --clock-child "
+                     "right after the timed region: busy cycles per XCD / dispatch duration, "
+                     "mean of the last 3 dispatches"}
+    try:
+        r = subprocess.run(cmd, cwd="/tmp", env=dict(os.environ, TMPDIR="/tmp"),
+                           stdout=subprocess.DEVNULL, timeout=240)
+        # the profiler can end with a signal after the program's results are
+        # complete; the counters file decides
+        found = [os.path.join(dp, f) for dp, _, fs in os.walk(out) for f in fs
+                 if f.endswith("counter_collection.csv")]
+        if not found:
+            res["error"] = f"no counter output (exit status {r.returncode})"
+            return res
+        per = {}
+        with open(found[0]) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != "GRBM_GUI_ACTIVE":
+                    continue
+                for key, name in CLOCK_KERNELS.items():
+                    if name in row["Kernel_Name"]:
+                        d = per.setdefault(key, {}).setdefault(
+                            int(row["Dispatch_Id"]),
+                            [0.0, int(row["End_Timestamp"]) - int(row["Start_Timestamp"])])
+                        d[0] += float(row["Counter_Value"])
+        for key, disp in per.items():
+            last = [disp[k] for k in sorted(disp)][-3:]
+            res[f"{key}_mhz"] = round(sum(c / 8 / ns * 1e3 for c, ns in last) / len(last), 1)
+        return res
+    except (OSError, subprocess.SubprocessError, ValueError, KeyError) as e:
+        res["error"] = f"{type(e).__name__}: {e}"
+        return res
+    finally:
+        shutil.rmtree(out, ignore_errors=True)
+
+
+def next_rows(torch, kl, dev, inp4, steps):
+    """The adjacent workloads, each against its MFMA peak: the attention
+    backward at the headline shape (LoRA / DreamBooth-style training), the
+    1024x1024 workloads warm and cold, and a 2048x2048 edit with two
+    references (tokens grow by one image grid per reference)."""
+    from workloads import get_config, make_inputs
+    rows = []
+    # backward at the 2048x2048 CFG shape: forward with lse once, then the
+    # timed backward call (prep, scale, dK/dV and dQ kernels); flops counted
+    # as 2.5x the forward's (the five S^2-sized products)
+    c = get_config(4)
+    print(f"[next] backward S={c.S}", file=sys.stderr, flush=True)
+    xq, xk, xv, xp = to_device(inp4, dev)
+    xo = torch.empty(xq.shape, dtype=torch.bfloat16, device=dev)
+    xl = torch.empty(c.B, c.H, c.S, dtype=torch.float32, device=dev)
+    kl.klein_rope4d_attn_fwd_lse(xq, xk, xv, xp, xo, xl)
+    g = torch.Generator(device=dev).manual_seed(505)
+    xd = torch.randn(xq.shape, device=dev, generator=g).to(torch.bfloat16)
+    gq, gk, gv = (torch.empty_like(xq) for _ in range(3))
+    xw = torch.empty(kl.klein_attn_bwd_workspace_size(c.B, c.S, c.H, c.D), dtype=torch.uint8,
+                     device=dev)
+    bms = time_gpu(lambda: kl.klein_rope4d_attn_bwd(xq, xk, xv, xp, xo, xd, xl, gq, gk, gv, xw),
+                   max(3, steps // 2), 2, torch)
+    bf = 2.5 * c.flops
+    rows.append({"workload": f"attention backward (dq, dk, dv through RoPE-4D), {c.name}: "
+                             f"B={c.B}, S={c.S}, H={c.H}, D={c.D}, bf16",
+                 "ms_per_call": round(bms, 4), "tflops": round(bf / (bms * 1e-3) / 1e12, 2),
+                 "peak": PEAK_BF16, "frac": round(bf / (bms * 1e-3) / 1e12 / PEAK_BF16, 4)})
+    del xq, xk, xv, xo, xl, xd, gq, gk, gv, xw
+    # the 1024x1024 workloads, warm (back to back) and cold (a 1 GiB buffer
+    # written before each call, so no input is left in L2 or the Infinity Cache)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    for cid in (2, 3):
+        c = get_config(cid)
+        print(f"[next] {c.name} warm and cold", file=sys.stderr, flush=True)
+        xi = make_inputs(c)
+        xq, xk, xv, xp = to_device(xi, dev)
+        xo = torch.empty(xq.shape, dtype=torch.bfloat16, device=dev)
+        xw = workspace(kl, torch, c, dev)
+        call = lambda: kl.klein_rope4d_attn_fwd_ws(xq, xk, xv, xp, xo, xw)
+        _, wper = time_gpu_calls(call, 50, 100, torch)
+        cold = []
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(30):
+            flush.fill_(1.0)
+            e0.record()
+            call()
+            e1.record()
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        wt, ct = c.flops / (med(wper) * 1e-3) / 1e12, c.flops / (med(cold) * 1e-3) / 1e12
+        rows.append({"workload": f"{c.name}: B={c.B}, S={c.S}, H={c.H}, D={c.D}, bf16 "
+                                 f"(split-KV entry)",
+                     "warm_ms_median": round(med(wper), 4), "cold_ms_median": round(med(cold), 4),
+                     "warm_tflops": round(wt, 2), "cold_tflops": round(ct, 2),
+                     "peak": PEAK_BF16, "warm_frac": round(wt / PEAK_BF16, 4),
+                     "cold_frac": round(ct / PEAK_BF16, 4)})
+        del xq, xk, xv, xo, xw
+    del flush
+    # a 2048x2048 edit with two reference images (t = 1, 2), bf16
+    c = get_config(3, grid=128, refs=2)
+    print(f"[next] 2048x2048 edit, 2 references, S={c.S}", file=sys.stderr, flush=True)
+    xi = make_inputs(c)
+    xq, xk, xv, xp = to_device(xi, dev)
+    xo = torch.empty(xq.shape, dtype=torch.bfloat16, device=dev)
+    xw = workspace(kl, torch, c, dev)
+    xms = time_gpu(lambda: kl.klein_rope4d_attn_fwd_ws(xq, xk, xv, xp, xo, xw), 5, 2, torch)
+    xt = c.flops / (xms * 1e-3) / 1e12
+    rows.append({"workload": f"2048x2048 edit with 2 references: B={c.B}, S={c.S} ({c.text} "
+                             f"text + 3 x 128x128), H={c.H}, D={c.D}, bf16 (split-KV entry)",
+                 "ms_per_call": round(xms, 4), "tflops": round(xt, 2), "peak": PEAK_BF16,
+                 "frac": round(xt / PEAK_BF16, 4)})
+    del xq, xk, xv, xo, xw
+    return rows
 
 
 def main():
@@ -143,8 +318,14 @@ def main():
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--extra", action="store_true",
-                    help="also time multi-reference 2048x2048 edits (bf16, 2 references; "
-                         "fp8, 3 references) and report them under 'extra'")
+                    help="also time an fp8 2048x2048 edit with 3 references, one GPU's share "
+                         "of sharded shapes, block-sparse attention and the QKV projection, "
+                         "and report them under 'extra'")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the counter run that measures the engine clock")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the adjacent workloads (backward, 1024x1024, multi-reference)")
+    ap.add_argument("--clock-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, run an elementwise fp32 copy of MIB MiB three "
                          "times (a kernel of known HBM traffic for scaling counters)")
@@ -161,6 +342,9 @@ def main():
     from workloads import get_config, make_inputs
 
     dev = "cuda:0"
+    if args.clock_child:
+        clock_child(torch, kl, dev)
+        return
     cfg = get_config(4)
     inp = make_inputs(cfg)
     q, k, v, pos = to_device(inp, dev)
@@ -173,6 +357,10 @@ def main():
                                   args.steps, args.warmup, torch)
     dense_ms = time_gpu(lambda: kl.klein_rope4d_attn_fwd(q, k, v, pos, out),
                         max(3, args.steps // 4), 2, torch)
+    # the same schedule as the timed call with the library's static scratch
+    # instead of a caller workspace (the entry point that allocates nothing)
+    noalloc_ms = time_gpu(lambda: kl.klein_rope4d_attn_fwd_noalloc(q, k, v, pos, out),
+                          max(3, args.steps // 4), 2, torch)
     tflops = cfg.flops / (ms * 1e-3) / 1e12
     traffic = stored_traffic("attn_fwd_bf16_2048px_t2i_cfg", "attn_fwd_bf16_splitkv")
     rec = {
@@ -194,10 +382,13 @@ def main():
                    "head_dim": cfg.D, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16, 4),
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     "traffic_source": traffic_source("attn_fwd_bf16_2048px_t2i_cfg")
+                     if traffic is not None else None},
         "entry_point": "klein_rope4d_attn_fwd_ws (split-KV schedule, workspace "
                        f"{0 if ws is None else ws.numel() / 1e6:.1f} MB)",
         "no_workspace_entry_ms": round(dense_ms, 4),
+        "noalloc_entry_ms": round(noalloc_ms, 4),
         "ms_per_call_median": round(sorted(per_call)[len(per_call) // 2], 4),
         "ms_per_call_min": round(min(per_call), 4),
     }
@@ -221,14 +412,27 @@ def main():
                           "peak": PEAK_FP8, "frac": round(t5 / PEAK_FP8, 4),
                           "traffic": stored_traffic("attn_fwd_fp8_2048px_edit",
                                                     "attn_fwd_fp8_splitkv"),
+                          "traffic_source": traffic_source("attn_fwd_fp8_2048px_edit"),
                           "entry_point": "klein_rope4d_attn_fwd_ws",
                           "no_workspace_entry_ms": round(dense5, 4)}
             del q5, k5, v5, o5, ws5
         except kl.KleinError as e:
             rec["fp8"] = {"error": str(e)}
+    if not args.no_clock:
+        clk = observed_clock()
+        for key, t, peak in (("bf16", tflops, PEAK_BF16),
+                             ("fp8", rec.get("fp8", {}).get("tflops"), PEAK_FP8)):
+            mhz = clk.get(f"{key}_mhz")
+            if mhz and t:
+                # the same rate against the MFMA peak at the clock observed
+                clk[f"{key}_frac_at_observed_clock"] = round(t / (peak * mhz / 2400.0), 4)
+        rec["clock"] = clk
+    if not args.no_next:
+        rec["next"] = next_rows(torch, kl, dev, inp, args.steps)
     if args.extra:
         rec["extra"] = []
-        for cid, refs, peak in ((3, 2, PEAK_BF16), (5, 3, PEAK_FP8)):
+        # (the bf16 edit with 2 references is in "next")
+        for cid, refs, peak in ((5, 3, PEAK_FP8),):
             c = get_config(cid, grid=128, refs=refs)
             print(f"[extra] generating {c.dtype} S={c.S} inputs", file=sys.stderr, flush=True)
             xi = make_inputs(c)
@@ -378,62 +582,6 @@ def main():
             "peak": PEAK_BF16, "frac": round(c.flops / (ams * 1e-3) / 1e12 / PEAK_BF16, 4),
             "fused_rotation_ms": round(ms, 4)})
         del xx, ww, bb, qo, ko, vo, oo, yy
-    if args.extra:
-        # the 1024x1024 workloads, warm (back to back) and cold (a 1 GiB buffer
-        # written before each call, so no input is left in the caches)
-        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        for cid in (2, 3):
-            c = get_config(cid)
-            xi = make_inputs(c)
-            xq, xk, xv, xp = to_device(xi, dev)
-            xo = torch.empty(xq.shape, dtype=torch.bfloat16, device=dev)
-            xw = workspace(kl, torch, c, dev)
-            call = lambda: kl.klein_rope4d_attn_fwd_ws(xq, xk, xv, xp, xo, xw)
-            wms, wper = time_gpu_calls(call, 50, 100, torch)
-            cold = []
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            for _ in range(30):
-                flush.fill_(1.0)
-                e0.record()
-                call()
-                e1.record()
-                torch.cuda.synchronize()
-                cold.append(e0.elapsed_time(e1))
-            med = lambda xs: sorted(xs)[len(xs) // 2]
-            rec["extra"].append({
-                "workload": f"{c.name}: B={c.B}, S={c.S}, H={c.H}, D={c.D}, bf16 (split-KV entry)",
-                "warm_ms_median": round(med(wper), 4), "warm_ms_min": round(min(wper), 4),
-                "cold_ms_median": round(med(cold), 4), "cold_ms_min": round(min(cold), 4),
-                "warm_tflops": round(c.flops / (med(wper) * 1e-3) / 1e12, 2),
-                "cold_tflops": round(c.flops / (med(cold) * 1e-3) / 1e12, 2), "peak": PEAK_BF16})
-            del xq, xk, xv, xo, xw
-        del flush
-        # attention backward (training: LoRA / DreamBooth-style edit training
-        # on 1024x1024 triples, and the 2048x2048 shape): forward with lse
-        # once, then the timed backward call (prep + dK/dV + dQ kernels);
-        # flops counted as 2.5x the forward's (the five S^2-sized products)
-        for cid in (3, 4):
-            c = get_config(cid)
-            print(f"[extra] backward S={c.S}", file=sys.stderr, flush=True)
-            xi = make_inputs(c)
-            xq, xk, xv, xp = to_device(xi, dev)
-            xo = torch.empty(xq.shape, dtype=torch.bfloat16, device=dev)
-            xl = torch.empty(c.B, c.H, c.S, dtype=torch.float32, device=dev)
-            kl.klein_rope4d_attn_fwd_lse(xq, xk, xv, xp, xo, xl)
-            g = torch.Generator(device=dev).manual_seed(505)
-            xd = torch.randn(xq.shape, device=dev, generator=g).to(torch.bfloat16)
-            gq, gk, gv = (torch.empty_like(xq) for _ in range(3))
-            xw = torch.empty(kl.klein_attn_bwd_workspace_size(c.B, c.S, c.H, c.D),
-                             dtype=torch.uint8, device=dev)
-            bms = time_gpu(lambda: kl.klein_rope4d_attn_bwd(xq, xk, xv, xp, xo, xd, xl, gq, gk, gv,
-                                                            xw), 10, 3, torch)
-            bf = 2.5 * c.flops
-            rec["extra"].append({
-                "workload": f"attention backward (dq, dk, dv through RoPE-4D), {c.name}: B={c.B}, "
-                            f"S={c.S}, H={c.H}, D={c.D}, bf16",
-                "ms_per_call": round(bms, 4), "tflops": round(bf / (bms * 1e-3) / 1e12, 2),
-                "peak": PEAK_BF16, "frac": round(bf / (bms * 1e-3) / 1e12 / PEAK_BF16, 4)})
-            del xq, xk, xv, xo, xl, xd, gq, gk, gv, xw
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
