@@ -246,9 +246,13 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
       so[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0));
     }
     if (tid < BQ) {
-      const int qi = q0 + tid;
-      sl = qi < S ? e2 - lse_bh[qi] * kLog2e : kNegInf;
-      sd = qi < S ? -dl_bh[qi] : 0.f;
+      // through wave-uniform descriptors: no per-lane 64-bit addresses to keep
+      const __amdgpu_buffer_rsrc_t rl = uniform_rsrc(lse_bh + q0, n * 4);
+      const __amdgpu_buffer_rsrc_t rd = uniform_rsrc(dl_bh + q0, n * 4);
+      const float l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * tid, 0, 0));
+      const float d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, 4 * tid, 0, 0));
+      sl = tid < n ? e2 - l * kLog2e : kNegInf;
+      sd = tid < n ? -d : 0.f;
     }
   };
   auto store = [&](int buf) {

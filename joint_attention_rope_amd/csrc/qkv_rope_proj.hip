@@ -52,7 +52,19 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lr = lane & 31;
   const int wn = wave & 1, wm = wave >> 1;     // 2 x 4 waves: 128 features x 64 tokens
-  const int tn = blockIdx.x % ntile_n, tmi = blockIdx.x / ntile_n;
+  // Tile order: each XCD (own L2) takes a contiguous range of the tile list
+  // (xcd_remap), and the list runs through groups of kGroupM token tiles,
+  // token tile fastest: the 32 workgroups an XCD runs at once then cover
+  // 8 token tiles x 4 feature tiles, so 12 operand panels (8 of x, 4 of W,
+  // 1.5 MB each at C = 3072) are shared in its L2 instead of 1 of x and 32
+  // of W.
+  constexpr int kGroupM = 8;
+  const int ntile_m = (M + TM - 1) / TM;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int gsz = kGroupM * ntile_n;
+  const int m_first = (L / gsz) * kGroupM;
+  const int gm = min(ntile_m - m_first, kGroupM);
+  const int tmi = m_first + (L % gsz) % gm, tn = (L % gsz) / gm;
   const int n0 = tn * TN, m0 = tmi * TM;
   const int HD = H * D;
 
