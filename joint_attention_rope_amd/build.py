@@ -1,4 +1,7 @@
-"""Build the gfx950 HIP library libklein_attn.so in-tree with hipcc.
+"""Build the gfx950 HIP library libklein_attn.so in-tree with hipcc, and the
+measurement harness step_clock (the bf16 attention kernel with per-region
+cycle counters, linked with the library's other objects; not part of the
+library).
 
 Usage: python -m joint_attention_rope_amd.build
 """
@@ -10,6 +13,9 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libklein_attn.so")
+STEP_CLOCK = os.path.join(PKG, "step_clock")
+# the harness replaces this source (it includes it with the cycle counters on)
+STEP_CLOCK_REPLACES = "attn_fwd_bf16.hip"
 SOURCES = ["api.cpp", "attn_fwd_bf16.hip", "attn_fwd_fp8.hip", "qkv_rope_proj.hip", "rope_apply.hip",
            "split_schedule.hip", "attn_bwd.hip", "noalloc.hip"]
 # Device kernels never see NaN inputs on purpose (a NaN in q/k/v propagates to
@@ -41,19 +47,24 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     """Compile every source (always) and link libklein_attn.so."""
     tag = "%d" % os.getpid()
-    objs = []
+    objs = {}
     try:
-        for src in SOURCES:
+        cflags = [f for f in FLAGS if f != "-shared"]
+        for src in SOURCES + ["step_clock.hip"]:
             obj = os.path.join(CSRC, src + ".o" + tag)
-            cflags = [f for f in FLAGS if f != "-shared"]
-            _run([HIPCC, *cflags, *KERNEL_FLAGS.get(src, []), "-c", "-o", obj,
-                  os.path.join(CSRC, src)], verbose)
-            objs.append(obj)
+            flags = KERNEL_FLAGS.get(STEP_CLOCK_REPLACES if src == "step_clock.hip" else src, [])
+            _run([HIPCC, *cflags, *flags, "-c", "-o", obj, os.path.join(CSRC, src)], verbose)
+            objs[src] = obj
+        lib_objs = [objs[s] for s in SOURCES]
         tmp = LIB + ".tmp" + tag
-        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *lib_objs], verbose)
         os.replace(tmp, LIB)
+        clock_objs = [objs[s] for s in SOURCES if s != STEP_CLOCK_REPLACES] + [objs["step_clock.hip"]]
+        tmp = STEP_CLOCK + ".tmp" + tag
+        _run([HIPCC, "--offload-arch=gfx950", "-o", tmp, *clock_objs], verbose)
+        os.replace(tmp, STEP_CLOCK)
     finally:
-        for o in objs:
+        for o in objs.values():
             if os.path.exists(o):
                 os.remove(o)
     return LIB

@@ -61,6 +61,42 @@
 
 namespace klein {
 
+// Per-region cycle counts of the pipeline step, for a measurement build
+// only: defined by the step_clock.hip harness, never by the library.  Each
+// wave sums, over its steps, the shader-clock cycles (s_memtime) between
+// marks at the step start, after region A, after the rescale check, after
+// region B, after the buffer loads and after the barrier, and lane 0
+// writes them, with the step count, the cycles of the whole loop and its
+// fixed-rate timestamps (s_memrealtime), to klein_step_clock_out[8 wg +
+// wave][0..9].
+#ifdef KLEIN_STEP_CLOCK
+__device__ unsigned long long* klein_step_clock_out;
+#define KLEIN_CLOCK_START                                                    \
+  unsigned long long clk_sum[6] = {0, 0, 0, 0, 0, 0};                        \
+  const unsigned long long clk_real0 = __builtin_amdgcn_s_memrealtime();     \
+  unsigned long long clk_prev = __builtin_amdgcn_s_memtime();                \
+  const unsigned long long clk_start = clk_prev;
+#define KLEIN_CLOCK_MARK(i)                                                  \
+  do {                                                                       \
+    const unsigned long long clk_now = __builtin_amdgcn_s_memtime();         \
+    clk_sum[i] += clk_now - clk_prev;                                        \
+    clk_prev = clk_now;                                                      \
+  } while (0)
+#define KLEIN_CLOCK_STORE(nsteps)                                            \
+  if (klein_step_clock_out != nullptr && lane == 0) {                        \
+    unsigned long long* co = klein_step_clock_out + ((size_t)blockIdx.x * 8 + wave) * 10; \
+    for (int i = 0; i < 6; ++i) co[i] = clk_sum[i];                          \
+    co[6] = (unsigned long long)(nsteps);                                    \
+    co[7] = clk_prev - clk_start;                                            \
+    co[8] = clk_real0;                                                       \
+    co[9] = __builtin_amdgcn_s_memrealtime();                                \
+  }
+#else
+#define KLEIN_CLOCK_START
+#define KLEIN_CLOCK_MARK(i) do {} while (0)
+#define KLEIN_CLOCK_STORE(nsteps)
+#endif
+
 constexpr int kTabN = 256;        // positions covered by the cos/sin table
 
 // SPARSE: block-sparse variant; bmask holds one byte per (batch, head, query
@@ -516,21 +552,28 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   // one pipeline step; `cur` holds S(t), `nxt` receives S(t+1)
   // `kps` holds the positions of K(t+2) and receives those of K(t+4).  The
   // rare branches (rotation fallback, rescale) sit between the regions.
+  KLEIN_CLOCK_START
   auto step = [&](int t, f32x16_t* cur, f32x16_t* nxt, int* kps) {
     int ci[KPT];
 #pragma unroll
     for (int it = 0; it < KPT; ++it) ci[it] = key_cs_index(kps, it);
     mask_tail(tl(t), cur);
+    KLEIN_CLOCK_MARK(0);
     float lt = region_a((t + 1) & 1, cur, nxt, pw);
+    KLEIN_CLOCK_MARK(1);
     if (__builtin_amdgcn_ballot_w64(lt > kSumLimit)) lt = rescale(cur, nxt, pw);
     l_run += lt;
+    KLEIN_CLOCK_MARK(2);
     // K(t+2) into buffer t&1 (it held K(t), consumed last step); V(t+1) into
     // buffer (t+1)&1 (it held V(t-1), consumed last step)
     region_b(t & 1, t & 1, (t + 1) & 1, pw, ci);
+    KLEIN_CLOCK_MARK(3);
     load_k(tl(t + 3));
     load_pos(tl(t + 4), kps);
     load_v(tl(t + 2));
+    KLEIN_CLOCK_MARK(4);
     __syncthreads();
+    KLEIN_CLOCK_MARK(5);
   };
   int t = 0;
   for (; t + 1 < nsteps; t += 2) {
@@ -538,6 +581,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     step(t + 1, sb, sa, kpos1);
   }
   if (t < nsteps) step(t, sa, sb, kpos0);
+  KLEIN_CLOCK_STORE(nsteps)
 
   // ---- epilogue: O / l, bf16, store (lane holds channels 32mb + 8(i/4) + 4g + i%4);
   // a chunk of a split item stores its partial instead (the merge kernel

@@ -173,13 +173,20 @@ def mean_duration_ns(pmc_dir, kernel):
     return sum(per.values()) / len(per) if per else None
 
 
-def counters_markdown(kernel, cfg, dirs, command):
+def counters_markdown(kernel, cfg, dirs, command, units=None, unit_name=None):
     """Instruction mix per wave-tile (one wave's 32 queries against one
-    64-key tile) and MFMA utilisation from the SQ counter passes."""
+    64-key tile; or per `units` of `unit_name` when given) and MFMA
+    utilisation from the SQ counter passes."""
     c = counter_means(dirs, kernel)
-    nqt = (cfg.S + 255) // 256
-    nkt = (cfg.S + 63) // 64
-    tiles = cfg.B * cfg.H * nqt * 8 * nkt
+    if units:
+        tiles = units
+        per = f"Units per dispatch: {units} ({unit_name})."
+    else:
+        nqt = (cfg.S + 255) // 256
+        nkt = (cfg.S + 63) // 64
+        tiles = cfg.B * cfg.H * nqt * 8 * nkt
+        per = (f"Wave-tiles per dispatch: {tiles} (B x H x {nqt} query tiles x 8 waves x "
+               f"{nkt} key tiles).")
     rows = [("SQ_INSTS_MFMA", "MFMA instructions"), ("SQ_INSTS_VALU", "VALU instructions (incl. MFMA)"),
             ("SQ_INSTS_VALU_TRANS_F32", "transcendental VALU (exp, sin, cos)"),
             ("SQ_INSTS_LDS", "LDS instructions"), ("SQ_LDS_BANK_CONFLICT", "LDS bank-conflict cycles"),
@@ -188,7 +195,8 @@ def counters_markdown(kernel, cfg, dirs, command):
             ("SQ_WAIT_INST_LDS", "cycles waiting for LDS data (x4)"),
             ("SQ_WAIT_INST_ANY", "cycles waiting for any dependency (x4)"),
             ("SQ_WAVE_CYCLES", "wave cycles (x4)")]
-    lines = ["| counter | meaning | per dispatch | per wave-tile |", "|---|---|---|---|"]
+    lines = [f"| counter | meaning | per dispatch | per {'unit' if units else 'wave-tile'} |",
+             "|---|---|---|---|"]
     for k, m in rows:
         if k in c:
             lines.append(f"| {k} | {m} | {c[k]:.4e} | {c[k] / tiles:.2f} |")
@@ -205,8 +213,7 @@ def counters_markdown(kernel, cfg, dirs, command):
         if dur:
             util += (f"\nEffective engine clock = (GRBM_GUI_ACTIVE / 8 XCDs) / mean dispatch duration "
                      f"= {busy:.4e} / {dur:.4e} ns = **{busy / dur * 1e3:.0f} MHz** (peak 2400).\n")
-    return (f"## Counters (rocprofv3 --pmc, two passes)\n\nWave-tiles per dispatch: {tiles} "
-            f"(B x H x {nqt} query tiles x 8 waves x {nkt} key tiles).\n\n```\n{command}\n```\n\n"
+    return (f"## Counters (rocprofv3 --pmc, two passes)\n\n{per}\n\n```\n{command}\n```\n\n"
             + "\n".join(lines) + "\n" + util)
 
 
@@ -254,29 +261,33 @@ def algorithmic_bytes(workload):
 
 
 BWD_SOURCES = ["klein_device.hpp", "attn_bwd.hip"]
-BWD_KERNELS = (("prep", "attn_bwd_prep_kernel<128>"), ("dK/dV", "attn_bwd_dkdv_kernel<128>"),
-               ("dQ", "attn_bwd_dq_kernel<128>"))
+BWD_KERNELS = (("prep", "attn_bwd_prep_kernel<128>"), ("scale", "attn_bwd_scale_kernel"),
+               ("dK/dV", "attn_bwd_dkdv_kernel<128>"), ("dQ", "attn_bwd_dq_kernel<128>"))
 
 
-def backward_markdown(stats_dir, workloads, command):
-    """Per-kernel durations of the backward's three kernels, one table per
-    workload; a workload's dispatches are told apart by their grids (prep:
-    one work-item per 8 channels of B S H D, rounded up to 256; dK/dV and dQ:
-    B H ceil(S / 256) workgroups of 512)."""
+def backward_markdown(stats_dir, workloads, command, last=None):
+    """Per-kernel durations of the backward's kernels (their last `last`
+    dispatches, or all), one table per workload; a workload's dispatches are
+    told apart by their grids (prep: one work-item per 8 channels of B S H D,
+    rounded up to 256; scale: B H workgroups of 256; dK/dV and dQ: B H
+    ceil(S / 256) workgroups of 512)."""
     from workloads import get_config
     rows = _rows(_find(stats_dir, "kernel_trace.csv"))
     size = lambda r: int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
-    md = [f"# attn_bwd kernels\n\nThe backward's kernels (prep, dK/dV, dQ) at D = 128; sources "
+    md = [f"# attn_bwd kernels\n\nThe backward's kernels (prep, scale, dK/dV, dQ) at D = 128; sources "
           f"hash {sources_hash(BWD_SOURCES)} ({', '.join(BWD_SOURCES)}).\n\nCommand (run from "
           f"/tmp with TMPDIR=/tmp; R = repository root):\n\n```\n{command}\n```\n"]
     for w in workloads:
         cfg = get_config(w)
         grids = {"prep": -(-cfg.B * cfg.S * cfg.H * cfg.D // 8 // 256) * 256,
+                 "scale": cfg.B * cfg.H * 256,
                  "dK/dV": cfg.B * cfg.H * -(-cfg.S // 256) * 512,
                  "dQ": cfg.B * cfg.H * -(-cfg.S // 256) * 512}
         durs = {label: [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in rows
                         if name in r["Kernel_Name"] and size(r) == grids[label]]
                 for label, name in BWD_KERNELS}
+        if last:
+            durs = {k: v[-last:] for k, v in durs.items()}
         if not all(durs.values()):
             continue
         mean = {k: sum(v) / len(v) for k, v in durs.items()}
@@ -285,12 +296,120 @@ def backward_markdown(stats_dir, workloads, command):
         md.append(f"\n## {cfg.name}: B={cfg.B}, S={cfg.S}, H={cfg.H}, D={cfg.D}\n\n"
                   f"| kernel | dispatches | mean ms | MFMA flops (x B H S^2 D) | TFLOP/s on them |\n"
                   f"|---|---|---|---|---|\n")
-        for label, units in (("prep", 0), ("dK/dV", 8), ("dQ", 6)):
+        for label, units in (("prep", 0), ("scale", 0), ("dK/dV", 8), ("dQ", 6)):
             rate = f"{units * unit / (mean[label] * 1e-3) / 1e12:.1f}" if units else "-"
             md.append(f"| {label} | {len(durs[label])} | {mean[label]:.4f} | {units or '-'} | "
                       f"{rate} |\n")
         md.append(f"| the backward (sum of the means) | | {total:.4f} | 10 (algorithmic) | "
                   f"{10 * unit / (total * 1e-3) / 1e12:.1f} |\n")
+    return "".join(md)
+
+
+def drive(what, steps):
+    """Calls to trace or count on their own (run under rocprofv3): 'qkv' =
+    the QKV projection with its RoPE epilogue at the 2048x2048 CFG shape
+    (x [2, 16896, 3072] -> q', k', v), bf16 then FP8 operands, each followed
+    by the vendor GEMM on the same operands (torch.addmm, torch._scaled_mm);
+    'sparse' = the block-sparse attention with keys rotated once, on the
+    bench workloads with their seeded masks (bf16 workload 4, fp8 workload
+    5); 'bwd' = the attention backward at the 2048x2048 CFG shape (the
+    forward with lse once, then the backward calls).  `steps` calls of each
+    after ten warm-up calls."""
+    import sys
+    import torch
+    sys.path.insert(0, ROOT)
+    import joint_attention_rope_amd as kl
+    from workloads import get_config, make_block_mask, make_inputs
+    dev = "cuda:0"
+
+    def run(fn):
+        # ten warm-up calls: the clock ramps up over the first calls after
+        # the idle input preparation
+        for _ in range(10 + steps):
+            fn()
+        torch.cuda.synchronize()
+
+    if what == "qkv":
+        c = get_config(4)
+        C = c.H * c.D
+        g = torch.Generator(device=dev).manual_seed(404)
+        xx = torch.randn(c.B, c.S, C, device=dev, generator=g).to(torch.bfloat16)
+        ww = (torch.randn(3 * C, C, device=dev, generator=g) / C ** 0.5).to(torch.bfloat16)
+        bb = (torch.randn(3 * C, device=dev, generator=g) * 0.1).to(torch.bfloat16)
+        pp = torch.from_numpy(make_inputs(get_config(4, B=1, H=1)).pos).to(dev)
+        qo = torch.empty(c.B, c.S, c.H, c.D, dtype=torch.float16, device=dev)
+        ko = torch.empty_like(qo)
+        vo = torch.empty(c.B, c.S, c.H, c.D, dtype=torch.bfloat16, device=dev)
+        yy = torch.empty(c.B * c.S, 3 * C, dtype=torch.bfloat16, device=dev)
+        run(lambda: kl.klein_qkv_rope4d_proj(xx, ww, bb, pp, qo, ko, vo))
+        run(lambda: torch.addmm(bb, xx.view(-1, C), ww.t(), out=yy))
+        sx = float(xx.float().abs().max()) / 448.0
+        sw = float(ww.float().abs().max()) / 448.0
+        x8 = (xx.float() / sx).to(torch.float8_e4m3fn)
+        w8 = (ww.float() / sw).to(torch.float8_e4m3fn)
+        run(lambda: kl.klein_qkv_rope4d_proj(x8.view(torch.uint8), w8.view(torch.uint8), bb, pp,
+                                             qo, ko, vo, descales=(sx, sw)))
+        one = torch.ones((), device=dev)
+        run(lambda: torch._scaled_mm(x8.view(-1, C), w8.t(), scale_a=one * sx, scale_b=one * sw,
+                                     out_dtype=torch.bfloat16))
+    elif what == "sparse":
+        for cid in (4, 5):
+            c = get_config(cid)
+            xi = make_inputs(c)
+            if xi.descale is None:
+                conv = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+            else:
+                conv = lambda a: torch.from_numpy(a).to(dev)
+            q, k, v = conv(xi.q), conv(xi.k), conv(xi.v)
+            p = torch.from_numpy(xi.pos).to(dev)
+            o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+            m = torch.from_numpy(make_block_mask(c.B, c.H, c.S, c.text, 0.3, seed=cid)).to(dev)
+            dt = kl.KLEIN_DTYPE_BF16 if xi.descale is None else kl.KLEIN_DTYPE_FP8_E4M3
+            w = torch.empty(kl.klein_attn_workspace_size(c.B, c.S, c.H, c.D, dt),
+                            dtype=torch.uint8, device=dev)
+            run(lambda: kl.klein_rope4d_attn_fwd_blocksparse(
+                q, k, v, p, o, m, descales=xi.descale or (1.0, 1.0, 1.0), workspace=w))
+    elif what == "bwd":
+        c = get_config(4)
+        xi = make_inputs(c)
+        q, k, v = (torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+                   for a in (xi.q, xi.k, xi.v))
+        p = torch.from_numpy(xi.pos).to(dev)
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(c.B, c.H, c.S, dtype=torch.float32, device=dev)
+        kl.klein_rope4d_attn_fwd_lse(q, k, v, p, o, lse)
+        g = torch.Generator(device=dev).manual_seed(505)
+        do = torch.randn(q.shape, device=dev, generator=g).to(torch.bfloat16)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        w = torch.empty(kl.klein_attn_bwd_workspace_size(c.B, c.S, c.H, c.D), dtype=torch.uint8,
+                        device=dev)
+        run(lambda: kl.klein_rope4d_attn_bwd(q, k, v, p, o, do, lse, dq, dk, dv, w))
+    else:
+        raise ValueError(what)
+
+
+def kernels_markdown(name, stats_dir, kernels, command, note="", last=None):
+    """Mean duration of each listed kernel (label=name-substring; its last
+    `last` dispatches, or all) from a kernel trace, with TFLOP/s when a flop
+    count is given as label=substring=flops."""
+    rows = _rows(_find(stats_dir, "kernel_trace.csv"))
+    md = [f"# {name}\n\n{note}\n\nCommand (run from /tmp with TMPDIR=/tmp; R = repository "
+          f"root):\n\n```\n{command}\n```\n\n| kernel | dispatches | mean ms | min ms | "
+          f"TFLOP/s at the mean |\n|---|---|---|---|---|\n"]
+    for spec in kernels:
+        parts = spec.split("=")
+        label, pat = parts[0], parts[1]
+        flops = float(parts[2]) if len(parts) > 2 else None
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in rows
+             if pat in r["Kernel_Name"]]
+        if last:
+            d = d[-last:]
+        if not d:
+            md.append(f"| {label} | 0 | - | - | - |\n")
+            continue
+        mean = sum(d) / len(d)
+        rate = f"{flops / (mean * 1e-3) / 1e12:.1f}" if flops else "-"
+        md.append(f"| {label} (`{pat}`) | {len(d)} | {mean:.4f} | {min(d):.4f} | {rate} |\n")
     return "".join(md)
 
 
@@ -303,7 +422,9 @@ def main():
     ap.add_argument("--stats")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
-    ap.add_argument("--steps", type=int, help="timed calls (the last N calls)")
+    ap.add_argument("--steps", type=int, help="timed calls (after the warm-up calls)")
+    ap.add_argument("--warmup", type=int, default=0,
+                    help="warm-up calls of the profiled entry point before the timed ones")
     ap.add_argument("--copy-mib", type=int)
     ap.add_argument("--command")
     ap.add_argument("--bench-ms", type=float, default=None,
@@ -312,14 +433,35 @@ def main():
                     help="write profiles/<name>_counters.md from two --pmc runs instead")
     ap.add_argument("--backward", metavar="STATS",
                     help="write profiles/attn_bwd_kernels.md from a kernel trace of "
-                         "bench.py --extra (the backward at workloads 3 and 4)")
+                         "--drive bwd (the backward at the 2048x2048 CFG shape; with --steps, "
+                         "its last dispatches)")
     ap.add_argument("--gemm-ceiling", action="store_true",
                     help="measure vendor GEMM throughput on the GPU and print a markdown table")
+    ap.add_argument("--drive", choices=["qkv", "sparse", "bwd"],
+                    help="run the QKV projection, the block-sparse attention or the backward "
+                         "--steps times after ten warm-up calls (for rocprofv3)")
+    ap.add_argument("--kernels", nargs="+", metavar="LABEL=PATTERN[=FLOPS]",
+                    help="write profiles/<name>.md: mean duration of each kernel in --stats")
+    ap.add_argument("--note", default="")
+    ap.add_argument("--kernel-pattern", help="with --counters: any kernel, by name substring")
+    ap.add_argument("--sources", nargs="+", default=[], help="with --kernel-pattern: its sources")
+    ap.add_argument("--units", type=int, help="with --kernel-pattern: work units per dispatch")
+    ap.add_argument("--unit-name", default="")
     args = ap.parse_args()
+    if args.drive:
+        drive(args.drive, args.steps or 5)
+        return
+    if args.kernels:
+        md = kernels_markdown(args.name, args.stats, args.kernels, args.command, args.note,
+                              last=args.steps)
+        with open(os.path.join(ROOT, "profiles", f"{args.name}.md"), "w") as f:
+            f.write(md)
+        print(md)
+        return
     if args.backward:
         import sys
         sys.path.insert(0, ROOT)
-        md = backward_markdown(args.backward, (3, 4), args.command)
+        md = backward_markdown(args.backward, (4,), args.command, last=args.steps)
         with open(os.path.join(ROOT, "profiles", "attn_bwd_kernels.md"), "w") as f:
             f.write(md)
         print(md)
@@ -333,6 +475,15 @@ def main():
 
     import sys
     sys.path.insert(0, ROOT)
+    if args.counters and args.kernel_pattern:
+        md = f"# {args.name} counters\n\nKernel `{args.kernel_pattern}`; sources hash " \
+             f"{sources_hash(args.sources)} ({', '.join(args.sources)}).\n\n" + \
+             counters_markdown(args.kernel_pattern, None, args.counters, args.command,
+                               units=args.units, unit_name=args.unit_name)
+        with open(os.path.join(ROOT, "profiles", f"{args.name}_counters.md"), "w") as f:
+            f.write(md)
+        print(md)
+        return
     call = CALLS[args.call]
     srcs = call["sources"]
     shash = sources_hash(srcs)
@@ -348,9 +499,11 @@ def main():
         print(md)
         return
     cfg, algo_read, algo_write = algorithmic_bytes(args.workload)
-    calls = call_durations_ns(args.stats, args.call)
+    # the call's dispatches in order: warm-up calls, then the timed ones
+    # (later calls of the same kernel, e.g. other workloads, are not counted)
+    calls = call_durations_ns(args.stats, args.call)[:args.warmup + args.steps]
     durs = [sum(c) for c in calls]
-    timed = calls[-args.steps:]
+    timed = calls[args.warmup:]
     avg_all = sum(durs) / len(durs) / 1e6
     avg_timed = sum(sum(c) for c in timed) / len(timed) / 1e6
     avg_rot = sum(c[0] for c in timed) / len(timed) / 1e6
@@ -386,12 +539,12 @@ Commands (run from /tmp with TMPDIR=/tmp; R = repository root):
 |---|---|
 | calls | {len(durs)} |
 | average duration per call, all calls | {avg_all:.4f} ms |
-| average duration per call, last {args.steps} (the timed calls) | {avg_timed:.4f} ms |
+| average duration per call, calls {args.warmup + 1}-{args.warmup + args.steps} (the timed calls) | {avg_timed:.4f} ms |
 | of which the key rotation pass | {avg_rot:.4f} ms |
 | of which the attention kernel | {avg_attn:.4f} ms |
 | of which the merge kernel | {avg_merge:.4f} ms |
 | min / max per call | {min(durs) / 1e6:.4f} / {max(durs) / 1e6:.4f} ms |
-| bench.py ms per call in the same run | {args.bench_ms if args.bench_ms is not None else 'n/a'} |
+| bench.py ms per call, plain run in the same lease | {args.bench_ms if args.bench_ms is not None else 'n/a'} |
 | attention flops per call (4 B H S^2 D) | {flops:.4e} |
 | TFLOP/s at the timed average | {tflops:.1f} |
 
