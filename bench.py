@@ -5,10 +5,13 @@ One step = one call of the attention library on one batch of the 2048x2048
 text-to-image workload with CFG (cond + uncond batched): B=2, S=16,896
 (512 text + 128x128 image tokens), H=24, D=128, bf16 in/out, inputs resident
 in HBM before timing.  Throughput is attention TFLOP/s = 4*B*H*S^2*D / t.
-The timed call is klein_rope4d_attn_fwd_ws (the split-KV schedule: the
-attention kernel and its merge kernel), its workspace allocated before
-timing; the entry point without a workspace is timed beside it
-(no_workspace_entry_ms).
+The timed call is klein_rope4d_attn_fwd, the attention's own signature: the
+key rotation pass, the attention kernel and its merge kernel (the split-KV
+schedule), in the buffer the library creates on the first (warm-up) call.
+The same schedule with a caller workspace (workspace_entry_ms), with the
+static scratch of the entry point that allocates nothing (noalloc_entry_ms)
+and the per-tile kernels that need no memory (per_tile_kernels_ms) are timed
+beside it.
 
 Prints ONE JSON line.  Fields beyond the common ones:
   roofline      -- the attention kernel against dense bf16 MFMA peak, with the
@@ -160,6 +163,24 @@ def cpu_baseline(inp, cfg, target_s=15.0):
     }
 
 
+def time_per_tile(kl, fn, steps, warmup, torch):
+    """time_gpu of fn with the library's buffer limit at 0, so that the plain
+    entry points run the per-tile kernels that need no memory."""
+    kl.klein_set_buffer_limit(0)
+    try:
+        return time_gpu(fn, steps, warmup, torch)
+    finally:
+        kl.klein_set_buffer_limit(kl.KLEIN_DEFAULT_BUFFER_LIMIT)
+
+
+def plain_call(kl, inp, q, k, v, pos, out):
+    """The timed entry point for a workload: klein_rope4d_attn_fwd (bf16) or
+    klein_rope4d_attn_fwd_fp8 (E4M3 codes with the workload's descales)."""
+    if inp.descale is None:
+        return lambda: kl.klein_rope4d_attn_fwd(q, k, v, pos, out)
+    return lambda: kl.klein_rope4d_attn_fwd_fp8(q, k, v, pos, out, *inp.descale)
+
+
 # kernels whose engine clock the counter run reports
 CLOCK_KERNELS = {"bf16": "attn_fwd_bf16_kernel", "fp8": "attn_fwd_fp8_kernel"}
 
@@ -174,12 +195,12 @@ def clock_child(torch, kl, dev):
         xi = make_inputs(c)
         xq, xk, xv, xp = to_device(xi, dev)
         xo = torch.empty(xq.shape, dtype=torch.bfloat16, device=dev)
-        xw = workspace(kl, torch, c, dev)
+        call = plain_call(kl, xi, xq, xk, xv, xp, xo)
         for _ in range(5):
-            kl.klein_rope4d_attn_fwd_ws(xq, xk, xv, xp, xo, xw, descales=xi.descale or (1.0, 1.0, 1.0))
+            call()
         torch.cuda.synchronize()
         print(f"[clock] {c.dtype}: 5 calls done", file=sys.stderr, flush=True)
-        del xq, xk, xv, xo, xw
+        del xq, xk, xv, xo
 
 
 def observed_clock():
@@ -271,8 +292,7 @@ def next_rows(torch, kl, dev, inp4, steps):
         xi = make_inputs(c)
         xq, xk, xv, xp = to_device(xi, dev)
         xo = torch.empty(xq.shape, dtype=torch.bfloat16, device=dev)
-        xw = workspace(kl, torch, c, dev)
-        call = lambda: kl.klein_rope4d_attn_fwd_ws(xq, xk, xv, xp, xo, xw)
+        call = plain_call(kl, xi, xq, xk, xv, xp, xo)
         _, wper = time_gpu_calls(call, 50, 100, torch)
         cold = []
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -285,12 +305,12 @@ def next_rows(torch, kl, dev, inp4, steps):
             cold.append(e0.elapsed_time(e1))
         wt, ct = c.flops / (med(wper) * 1e-3) / 1e12, c.flops / (med(cold) * 1e-3) / 1e12
         rows.append({"workload": f"{c.name}: B={c.B}, S={c.S}, H={c.H}, D={c.D}, bf16 "
-                                 f"(split-KV entry)",
+                                 f"(klein_rope4d_attn_fwd)",
                      "warm_ms_median": round(med(wper), 4), "cold_ms_median": round(med(cold), 4),
                      "warm_tflops": round(wt, 2), "cold_tflops": round(ct, 2),
                      "peak": PEAK_BF16, "warm_frac": round(wt / PEAK_BF16, 4),
                      "cold_frac": round(ct / PEAK_BF16, 4)})
-        del xq, xk, xv, xo, xw
+        del xq, xk, xv, xo
     del flush
     # a 2048x2048 edit with two reference images (t = 1, 2), bf16
     c = get_config(3, grid=128, refs=2)
@@ -298,14 +318,14 @@ def next_rows(torch, kl, dev, inp4, steps):
     xi = make_inputs(c)
     xq, xk, xv, xp = to_device(xi, dev)
     xo = torch.empty(xq.shape, dtype=torch.bfloat16, device=dev)
-    xw = workspace(kl, torch, c, dev)
-    xms = time_gpu(lambda: kl.klein_rope4d_attn_fwd_ws(xq, xk, xv, xp, xo, xw), 5, 2, torch)
+    xms = time_gpu(plain_call(kl, xi, xq, xk, xv, xp, xo), 5, 2, torch)
     xt = c.flops / (xms * 1e-3) / 1e12
     rows.append({"workload": f"2048x2048 edit with 2 references: B={c.B}, S={c.S} ({c.text} "
-                             f"text + 3 x 128x128), H={c.H}, D={c.D}, bf16 (split-KV entry)",
+                             f"text + 3 x 128x128), H={c.H}, D={c.D}, bf16 "
+                             f"(klein_rope4d_attn_fwd)",
                  "ms_per_call": round(xms, 4), "tflops": round(xt, 2), "peak": PEAK_BF16,
                  "frac": round(xt / PEAK_BF16, 4)})
-    del xq, xk, xv, xo, xw
+    del xq, xk, xv, xo
     return rows
 
 
@@ -349,18 +369,23 @@ def main():
     inp = make_inputs(cfg)
     q, k, v, pos = to_device(inp, dev)
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
-    # the timed call: the split-KV entry point, its workspace allocated (and
-    # inputs resident) before timing; the entry point without a workspace is
-    # timed after it for reference
-    ws = workspace(kl, torch, cfg, dev)
-    ms, per_call = time_gpu_calls(lambda: kl.klein_rope4d_attn_fwd_ws(q, k, v, pos, out, ws),
+    # the timed call: klein_rope4d_attn_fwd, the attention's own signature; its
+    # buffer (keys rotated once, split-KV partials) is created by the first
+    # warm-up call, and the inputs are resident before timing.  The same
+    # schedule with a caller workspace, with the static scratch of the entry
+    # point that allocates nothing, and the per-tile kernels (buffer limit 0)
+    # are timed after it for reference.
+    ms, per_call = time_gpu_calls(lambda: kl.klein_rope4d_attn_fwd(q, k, v, pos, out),
                                   args.steps, args.warmup, torch)
-    dense_ms = time_gpu(lambda: kl.klein_rope4d_attn_fwd(q, k, v, pos, out),
-                        max(3, args.steps // 4), 2, torch)
-    # the same schedule as the timed call with the library's static scratch
-    # instead of a caller workspace (the entry point that allocates nothing)
+    buf_mb = kl.klein_attn_workspace_size(cfg.B, cfg.S, cfg.H, cfg.D) / 1e6
+    n_ref = max(3, args.steps // 4)
+    ws = workspace(kl, torch, cfg, dev)
+    ws_ms = time_gpu(lambda: kl.klein_rope4d_attn_fwd_ws(q, k, v, pos, out, ws), n_ref, 2, torch)
+    del ws
     noalloc_ms = time_gpu(lambda: kl.klein_rope4d_attn_fwd_noalloc(q, k, v, pos, out),
-                          max(3, args.steps // 4), 2, torch)
+                          n_ref, 2, torch)
+    per_tile_ms = time_per_tile(kl, lambda: kl.klein_rope4d_attn_fwd(q, k, v, pos, out), n_ref, 2,
+                                torch)
     tflops = cfg.flops / (ms * 1e-3) / 1e12
     traffic = stored_traffic("attn_fwd_bf16_2048px_t2i_cfg", "attn_fwd_bf16_splitkv")
     rec = {
@@ -385,26 +410,30 @@ def main():
                      "traffic": traffic,
                      "traffic_source": traffic_source("attn_fwd_bf16_2048px_t2i_cfg")
                      if traffic is not None else None},
-        "entry_point": "klein_rope4d_attn_fwd_ws (split-KV schedule, workspace "
-                       f"{0 if ws is None else ws.numel() / 1e6:.1f} MB)",
-        "no_workspace_entry_ms": round(dense_ms, 4),
+        "entry_point": "klein_rope4d_attn_fwd (split-KV schedule in the library's buffer, "
+                       f"{buf_mb:.1f} MB)",
+        "workspace_entry_ms": round(ws_ms, 4),
         "noalloc_entry_ms": round(noalloc_ms, 4),
+        "per_tile_kernels_ms": round(per_tile_ms, 4),
         "ms_per_call_median": round(sorted(per_call)[len(per_call) // 2], 4),
         "ms_per_call_min": round(min(per_call), 4),
     }
-    del q, k, v, out, ws
+    del q, k, v, out
     if not args.no_fp8:
         try:
             cfg5 = get_config(5)
             inp5 = make_inputs(cfg5)
             q5, k5, v5, p5 = to_device(inp5, dev)
             o5 = torch.empty(q5.shape, dtype=torch.bfloat16, device=dev)
-            ws5 = workspace(kl, torch, cfg5, dev)
-            ms5 = time_gpu(lambda: kl.klein_rope4d_attn_fwd_ws(q5, k5, v5, p5, o5, ws5,
-                                                               descales=inp5.descale),
+            ms5 = time_gpu(lambda: kl.klein_rope4d_attn_fwd_fp8(q5, k5, v5, p5, o5,
+                                                                *inp5.descale),
                            max(3, args.steps // 2), max(1, args.warmup // 2), torch)
-            dense5 = time_gpu(lambda: kl.klein_rope4d_attn_fwd_fp8(q5, k5, v5, p5, o5,
-                                                                   *inp5.descale), 3, 1, torch)
+            ws5 = workspace(kl, torch, cfg5, dev)
+            ws5_ms = time_gpu(lambda: kl.klein_rope4d_attn_fwd_ws(q5, k5, v5, p5, o5, ws5,
+                                                                  descales=inp5.descale),
+                              3, 1, torch)
+            per_tile5 = time_per_tile(kl, lambda: kl.klein_rope4d_attn_fwd_fp8(
+                q5, k5, v5, p5, o5, *inp5.descale), 3, 1, torch)
             t5 = cfg5.flops / (ms5 * 1e-3) / 1e12
             rec["fp8"] = {"workload": "2048x2048 edit: B=1, S=33280 (512 text + 2 x 128x128), "
                                       "H=24, D=128, e4m3 in, bf16 out",
@@ -413,8 +442,10 @@ def main():
                           "traffic": stored_traffic("attn_fwd_fp8_2048px_edit",
                                                     "attn_fwd_fp8_splitkv"),
                           "traffic_source": traffic_source("attn_fwd_fp8_2048px_edit"),
-                          "entry_point": "klein_rope4d_attn_fwd_ws",
-                          "no_workspace_entry_ms": round(dense5, 4)}
+                          "entry_point": "klein_rope4d_attn_fwd_fp8 (split-KV schedule in "
+                                         "the library's buffer)",
+                          "workspace_entry_ms": round(ws5_ms, 4),
+                          "per_tile_kernels_ms": round(per_tile5, 4)}
             del q5, k5, v5, o5, ws5
         except kl.KleinError as e:
             rec["fp8"] = {"error": str(e)}
@@ -439,21 +470,16 @@ def main():
             print(f"[extra] timing {c.dtype} S={c.S}", file=sys.stderr, flush=True)
             xq, xk, xv, xp = to_device(xi, dev)
             xo = torch.empty(xq.shape, dtype=torch.bfloat16, device=dev)
-            xw = workspace(kl, torch, c, dev)
-            xms = time_gpu(lambda: kl.klein_rope4d_attn_fwd_ws(
-                xq, xk, xv, xp, xo, xw, descales=xi.descale or (1.0, 1.0, 1.0)), 5, 2, torch)
-            if xi.descale is None:
-                call = lambda: kl.klein_rope4d_attn_fwd(xq, xk, xv, xp, xo)
-            else:
-                call = lambda: kl.klein_rope4d_attn_fwd_fp8(xq, xk, xv, xp, xo, *xi.descale)
-            dms = time_gpu(call, 3, 1, torch)
+            call = plain_call(kl, xi, xq, xk, xv, xp, xo)
+            xms = time_gpu(call, 5, 2, torch)
+            dms = time_per_tile(kl, call, 3, 1, torch)
             xt = c.flops / (xms * 1e-3) / 1e12
             rec["extra"].append({
                 "workload": f"2048x2048 edit with {refs} references: B={c.B}, S={c.S} "
                             f"({c.text} text + {refs + 1} x 128x128), H={c.H}, D={c.D}, {c.dtype}",
                 "ms_per_call": round(xms, 4), "tflops": round(xt, 2), "peak": peak,
-                "frac": round(xt / peak, 4), "no_workspace_entry_ms": round(dms, 4)})
-            del xq, xk, xv, xo, xw
+                "frac": round(xt / peak, 4), "per_tile_kernels_ms": round(dms, 4)})
+            del xq, xk, xv, xo
         # one GPU's share of the 2048x2048 workload under sequence parallelism
         # (heads split over GPUs after an all-to-all): 3 or 4 heads of one CFG
         # branch (8- or 6-way), 6 heads of one branch (4-way), both branches
@@ -464,20 +490,19 @@ def main():
             xi = make_inputs(c)
             xq, xk, xv, xp = to_device(xi, dev)
             xo = torch.empty(xq.shape, dtype=torch.bfloat16, device=dev)
-            xw = workspace(kl, torch, c, dev)
+            call = plain_call(kl, xi, xq, xk, xv, xp, xo)
             # calls of ~0.5-1 ms: ~100 ms of warm-up first, so that the clock has
             # left the idle state of the input generation before timing
-            xms = time_gpu(lambda: kl.klein_rope4d_attn_fwd_ws(xq, xk, xv, xp, xo, xw), 50, 150,
-                           torch)
-            dms = time_gpu(lambda: kl.klein_rope4d_attn_fwd(xq, xk, xv, xp, xo), 50, 150, torch)
+            xms = time_gpu(call, 50, 150, torch)
+            dms = time_per_tile(kl, call, 50, 150, torch)
             xt = c.flops / (xms * 1e-3) / 1e12
             rec["extra"].append({
                 "workload": f"one GPU's share of 2048x2048 t2i: B={B}, S={c.S}, H={H}, D={c.D}, "
                             f"bf16 ({B * H * ((c.S + 255) // 256)} query tiles)",
                 "ms_per_call": round(xms, 4), "tflops": round(xt, 2), "peak": PEAK_BF16,
-                "frac": round(xt / PEAK_BF16, 4), "no_workspace_entry_ms": round(dms, 4),
-                "no_workspace_entry_tflops": round(c.flops / (dms * 1e-3) / 1e12, 2)})
-            del xq, xk, xv, xo, xw
+                "frac": round(xt / PEAK_BF16, 4), "per_tile_kernels_ms": round(dms, 4),
+                "per_tile_kernels_tflops": round(c.flops / (dms * 1e-3) / 1e12, 2)})
+            del xq, xk, xv, xo
         # block-sparse: the bench workloads with a seeded structured mask
         # (text blocks, a band around each query block, 30 % of the rest)
         from workloads import make_block_mask

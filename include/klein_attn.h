@@ -28,7 +28,12 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Pointers to tensors are DEVICE pointers, owned by the caller, 16-byte
- *    aligned.  The library allocates nothing and keeps no per-call state.
+ *    aligned.  The library keeps no per-call state.  It holds device memory
+ *    of its own in two places only: the buffer per GPU that
+ *    klein_rope4d_attn_fwd and klein_rope4d_attn_fwd_fp8 create on first use
+ *    (see there; klein_set_buffer_limit bounds it), and the static scratch
+ *    array of klein_rope4d_attn_fwd_noalloc.  No other entry point
+ *    allocates.
  *  - q, k, v, out are contiguous [B][S][H][D] (D fastest, then heads, then
  *    tokens, then batch).  out is always bfloat16.
  *  - pos_thwl is contiguous int32 [S][4] in the order (t, h, w, l) and is
@@ -44,7 +49,8 @@
  *    stream).  The status reports argument and launch errors only, never
  *    results of device work.  Argument checks run before any HIP call, so an
  *    invalid call touches no device.  No C++ exception crosses this ABI.
- *  - Calls are thread-safe; concurrent calls on different streams are fine.
+ *  - Calls are thread-safe; concurrent calls on different streams are fine,
+ *    except for klein_rope4d_attn_fwd_noalloc (see there).
  */
 #ifndef KLEIN_ATTN_H
 #define KLEIN_ATTN_H
@@ -84,11 +90,46 @@ typedef void* klein_stream_t;
  *   pos_thwl: [S][4] int32 (t, h, w, l)
  *   out     : [B][S][H][D] bfloat16, written completely; must not alias inputs
  * Softmax scale is fixed at 1/sqrt(D).  Accumulation is fp32.
+ *
+ * Schedule and memory.  The call runs the schedule of klein_rope4d_attn_fwd_ws
+ * (keys rotated once, the last round's query tiles split over key chunks)
+ * in a buffer the library owns: one per GPU, created by the first call on
+ * that GPU, replaced by a larger one when a call needs more (its size is
+ * what klein_attn_workspace_size reports, rounded up to 32 MiB), and kept
+ * until klein_set_buffer_limit lowers the limit below it or the process
+ * ends.  Calls that share the buffer are ordered on the GPU: each call's
+ * stream waits for the previous call's kernels, whatever stream they ran on,
+ * so concurrent calls on different streams of one GPU run one after the
+ * other (each fills the GPU).  The call instead runs kernels that need no
+ * memory (each workgroup rotates the key tiles it loads; the last round may
+ * leave compute units idle) when
+ *   - the stream is being captured into a HIP graph (a graph must not hold
+ *     the address of a buffer a later call may free),
+ *   - the shape needs more than the limit (default 2 GiB), or
+ *   - the buffer cannot be allocated for lack of memory (the error is
+ *     cleared).
+ * The two schedules give the same bits for every query tile that no split
+ * touches; split tiles are merged from fp32 partials and agree to rounding.
+ * Growing the buffer waits on the host for the previous call's kernels.
  */
 klein_status_t klein_rope4d_attn_fwd(const void* q, const void* k, const void* v,
                                      const int32_t* pos_thwl, void* out,
                                      int B, int S, int H, int D,
                                      klein_dtype_t dtype, klein_stream_t stream);
+
+/*
+ * Limit, in bytes, of the buffer klein_rope4d_attn_fwd and
+ * klein_rope4d_attn_fwd_fp8 keep per GPU (default KLEIN_DEFAULT_BUFFER_LIMIT).
+ * Shapes whose schedule needs more run the kernels that need no memory; a
+ * limit of 0 makes those calls allocate nothing.  A buffer larger than the
+ * new limit is freed at once, after the host has waited for the kernels
+ * already queued on it (the call then makes HIP calls on each GPU that holds
+ * one and restores the current device).  Thread-safe.
+ * Returns KLEIN_OK, or the error of a HIP call that failed (the limit is set
+ * in any case).
+ */
+#define KLEIN_DEFAULT_BUFFER_LIMIT ((size_t)2 << 30)
+klein_status_t klein_set_buffer_limit(size_t max_bytes);
 
 /*
  * FP8 variant with per-tensor scales: the value of an element is
@@ -108,7 +149,8 @@ klein_status_t klein_rope4d_attn_fwd(const void* q, const void* k, const void* v
  * (9.5 nats) below its row's first max (12.75 below a raised one), as a
  * subnormal about one binade further, and as 0 below that.  On N(0, 1) inputs of
  * the 2048^2 edit workload the result is within 4.5e-2 relative L2 of exact
- * attention of the decoded inputs (bound 6e-2).
+ * attention of the decoded inputs (bound 6e-2).  Schedule and memory as
+ * klein_rope4d_attn_fwd.
  */
 klein_status_t klein_rope4d_attn_fwd_fp8(const void* q, const void* k, const void* v,
                                          const int32_t* pos_thwl, void* out,

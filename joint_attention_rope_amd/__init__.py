@@ -13,7 +13,8 @@ import torch
 from . import _capi
 from ._capi import (KLEIN_DTYPE_BF16, KLEIN_DTYPE_FP8_E4M3, KLEIN_ERR_INVALID_ARG,
                     KLEIN_ERR_LAUNCH, KLEIN_ERR_NO_DEVICE, KLEIN_ERR_UNSUPPORTED, KLEIN_OK,
-                    KLEIN_NOALLOC_SCRATCH_BYTES, KLEIN_SPARSE_KBLOCK, KLEIN_SPARSE_QBLOCK)
+                    KLEIN_DEFAULT_BUFFER_LIMIT, KLEIN_NOALLOC_SCRATCH_BYTES, KLEIN_SPARSE_KBLOCK,
+                    KLEIN_SPARSE_QBLOCK)
 
 __all__ = [
     "KleinError", "klein_rope4d_attn_fwd", "klein_rope4d_attn_fwd_fp8",
@@ -23,7 +24,7 @@ __all__ = [
     "klein_qkv_rope4d_proj", "klein_attn_fwd_prerotated", "klein_rope4d_attn_fwd_ws",
     "klein_attn_workspace_size", "klein_splitkv_plan", "klein_rope4d_attn_fwd_lse",
     "klein_rope4d_attn_bwd", "klein_attn_bwd_workspace_size", "klein_rope4d_attn_fwd_noalloc",
-    "KLEIN_NOALLOC_SCRATCH_BYTES",
+    "KLEIN_NOALLOC_SCRATCH_BYTES", "klein_set_buffer_limit", "KLEIN_DEFAULT_BUFFER_LIMIT",
 ]
 
 
@@ -120,6 +121,12 @@ def klein_rope4d_attn_fwd_fp8(q, k, v, pos_thwl, out, q_descale, k_descale, v_de
         _stream(stream, q.device))
     _check(st, "klein_rope4d_attn_fwd_fp8")
     return out
+
+
+def klein_set_buffer_limit(max_bytes=KLEIN_DEFAULT_BUFFER_LIMIT):
+    """Limit of the buffer klein_rope4d_attn_fwd / _fp8 keep per GPU (0: those
+    calls allocate nothing and run the kernels that need no memory)."""
+    _check(_capi.lib().klein_set_buffer_limit(int(max_bytes)), "klein_set_buffer_limit")
 
 
 def klein_attn_workspace_size(B, S, H, D, dtype=KLEIN_DTYPE_BF16):

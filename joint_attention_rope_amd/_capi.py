@@ -19,6 +19,7 @@ KLEIN_ERR_UNSUPPORTED = 2
 KLEIN_ERR_NO_DEVICE = 3
 KLEIN_ERR_LAUNCH = 4
 KLEIN_NOALLOC_SCRATCH_BYTES = 320 * 1024 * 1024
+KLEIN_DEFAULT_BUFFER_LIMIT = 2 << 30
 KLEIN_SPARSE_QBLOCK = 256
 KLEIN_SPARSE_KBLOCK = 64
 
@@ -39,6 +40,7 @@ SIGNATURES = {
                                         _f32, _f32, _f32, _vp, ctypes.c_size_t, _vp]),
     "klein_rope4d_attn_fwd_noalloc": (_int, [_vp, _vp, _vp, _i32p, _vp, _int, _int, _int, _int,
                                              _int, _f32, _f32, _f32, _vp]),
+    "klein_set_buffer_limit": (_int, [ctypes.c_size_t]),
     "klein_attn_workspace_size": (_int, [_int, _int, _int, _int, _int,
                                          ctypes.POINTER(ctypes.c_size_t)]),
     "klein_splitkv_plan": (_int, [_int, _int, _int, _int, _int, ctypes.POINTER(ctypes.c_int),

@@ -1,9 +1,11 @@
 // C ABI of the RoPE-4D joint-attention library: argument checks, RoPE
 // frequency tables, kernel dispatch, status mapping.  Declarations and the
 // contract of every entry point live in include/klein_attn.h.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/klein_attn.h"
 #include "klein_launch.hpp"
@@ -99,9 +101,178 @@ int current_cu_count(hipError_t* err) {
   return n;
 }
 
+// The checks of the split-KV entry points that need no device.
+klein_status_t check_ws_call(const void* q, const void* k, const void* v,
+                             const int32_t* pos_thwl, const void* out, int B, int S, int H,
+                             int D, klein_dtype_t dtype, float q_descale, float k_descale,
+                             float v_descale) {
+  if (dtype != KLEIN_DTYPE_BF16 && dtype != KLEIN_DTYPE_FP8_E4M3) return KLEIN_ERR_INVALID_ARG;
+  klein_status_t st = check_common(q, k, v, pos_thwl, out, B, S, H, D);
+  if (st != KLEIN_OK) return st;
+  if (dtype == KLEIN_DTYPE_FP8_E4M3)
+    for (float s : {q_descale, k_descale, v_descale})
+      if (!(std::isfinite(s) && s > 0.f)) return KLEIN_ERR_INVALID_ARG;
+  if (klein::attn_fwd_bf16_grid(B, S, H) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
+  return KLEIN_OK;
+}
+
+klein_status_t attn_ws(const void* q, const void* k, const void* v,
+                       const int32_t* pos_thwl, void* out, float* lse, int B, int S, int H,
+                       int D, klein_dtype_t dtype, float q_descale, float k_descale,
+                       float v_descale, void* workspace, size_t workspace_bytes,
+                       klein_stream_t stream) {
+  klein_status_t st = check_ws_call(q, k, v, pos_thwl, out, B, S, H, D, dtype, q_descale,
+                                    k_descale, v_descale);
+  if (st != KLEIN_OK) return st;
+  const bool fp8 = dtype == KLEIN_DTYPE_FP8_E4M3;
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return KLEIN_ERR_INVALID_ARG;
+  try {
+    hipError_t e;
+    const int ncu = current_cu_count(&e);
+    if (e != hipSuccess) return map_hip(e);
+    const WsLayout w = ws_layout(B, S, H, D, dtype, ncu);
+    const klein::SplitPlan& plan = w.plan;
+    if (w.total > 0 && (!workspace || workspace_bytes < (size_t)w.total))
+      return KLEIN_ERR_INVALID_ARG;
+    LaunchArgs a = make_args(q, k, v, pos_thwl, out, B, S, H, D, stream);
+    a.lse = lse;
+    if (w.krot_bytes > 0) a.krot = workspace;
+    if (plan.n_sk > 0) {
+      a.split.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.krot_bytes);
+      a.split.n_dp = plan.n_dp;
+      a.split.n_sk = plan.n_sk;
+      a.split.n_rem = plan.n_rem;
+      a.split.n_chunk = plan.n_chunk;
+    }
+    if (!fp8) return map_hip(klein::launch_attn_fwd_bf16(a));
+    a.descale[0] = q_descale; a.descale[1] = k_descale; a.descale[2] = v_descale;
+    return map_hip(klein::launch_attn_fwd_fp8(a));
+  } catch (...) {
+    return KLEIN_ERR_LAUNCH;
+  }
+}
+
+// The buffer klein_rope4d_attn_fwd and klein_rope4d_attn_fwd_fp8 keep per
+// device for the split-KV schedule (rotated keys, then the split partials).
+// It is created on the first call that needs it and replaced by a larger one
+// when a call needs more, never beyond the limit.  Every call that uses it
+// holds the device's mutex from the look-up to the last launch, makes its
+// stream wait for `done` (the event recorded after the previous user's
+// kernels, on whatever stream they ran) and records `done` again, so uses
+// of the buffer are ordered across streams and threads; a replaced buffer is
+// freed only once `done` has completed.
+constexpr int kMaxDevices = 64;
+constexpr size_t kBufferGrain = size_t(32) << 20;
+
+struct DeviceBuffer {
+  std::mutex mu;
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  hipEvent_t done = nullptr;
+  bool used = false;          // `done` has been recorded
+};
+DeviceBuffer g_buffers[kMaxDevices];
+std::atomic<size_t> g_buffer_limit{KLEIN_DEFAULT_BUFFER_LIMIT};
+
+// Frees b's buffer after its last use has completed.  Caller holds b.mu and
+// has b's device current.
+hipError_t release_buffer(DeviceBuffer& b) {
+  if (!b.ptr) return hipSuccess;
+  hipError_t e = b.used ? hipEventSynchronize(b.done) : hipSuccess;
+  if (e != hipSuccess) return e;
+  e = hipFree(b.ptr);
+  b.ptr = nullptr;
+  b.bytes = 0;
+  return e;
+}
+
+// The split-KV call on the device's buffer.  *ran is false (and nothing is
+// launched) when the call should run the kernels that need no memory: the
+// stream is being captured into a graph (a graph must not hold the address of
+// a buffer that a later call may free), the shape needs more than the limit,
+// or the allocation failed for lack of memory.
+klein_status_t attn_on_buffer(const void* q, const void* k, const void* v, const int32_t* pos,
+                              void* out, int B, int S, int H, int D, klein_dtype_t dtype,
+                              float q_descale, float k_descale, float v_descale,
+                              klein_stream_t stream, bool* ran) {
+  *ran = false;
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(hs, &cap);
+  if (e != hipSuccess) return map_hip(e);
+  if (cap != hipStreamCaptureStatusNone) return KLEIN_OK;
+  int dev = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return map_hip(e);
+  if (dev < 0 || dev >= kMaxDevices) return KLEIN_OK;
+  const int ncu = current_cu_count(&e);
+  if (e != hipSuccess) return map_hip(e);
+  const size_t need = (size_t)ws_layout(B, S, H, D, dtype, ncu).total;
+  const size_t limit = g_buffer_limit.load();
+  if (need > limit) return KLEIN_OK;
+  DeviceBuffer& b = g_buffers[dev];
+  std::lock_guard<std::mutex> lock(b.mu);
+  if (b.bytes < need) {
+    e = release_buffer(b);
+    if (e != hipSuccess) return map_hip(e);
+    const size_t want = std::max(need, std::min((need + kBufferGrain - 1) / kBufferGrain *
+                                                 kBufferGrain, limit));
+    e = hipMalloc(&b.ptr, want);
+    if (e == hipErrorOutOfMemory) {
+      (void)hipGetLastError();
+      b.ptr = nullptr;
+      return KLEIN_OK;
+    }
+    if (e != hipSuccess) {
+      b.ptr = nullptr;
+      return map_hip(e);
+    }
+    b.bytes = want;
+  }
+  if (!b.done) {
+    e = hipEventCreateWithFlags(&b.done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      b.done = nullptr;
+      return map_hip(e);
+    }
+  }
+  if (b.used) {
+    e = hipStreamWaitEvent(hs, b.done, 0);
+    if (e != hipSuccess) return map_hip(e);
+  }
+  const klein_status_t st = attn_ws(q, k, v, pos, out, nullptr, B, S, H, D, dtype, q_descale,
+                                    k_descale, v_descale, b.ptr, b.bytes, stream);
+  if (st != KLEIN_OK) return st;
+  e = hipEventRecord(b.done, hs);
+  if (e != hipSuccess) return map_hip(e);
+  b.used = true;
+  *ran = true;
+  return KLEIN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+klein_status_t klein_set_buffer_limit(size_t max_bytes) {
+  g_buffer_limit.store(max_bytes);
+  klein_status_t st = KLEIN_OK;
+  int cur = -1;
+  for (int d = 0; d < kMaxDevices; ++d) {
+    DeviceBuffer& b = g_buffers[d];
+    std::lock_guard<std::mutex> lock(b.mu);
+    if (!b.ptr || b.bytes <= max_bytes) continue;
+    if (cur < 0 && hipGetDevice(&cur) != hipSuccess) return KLEIN_ERR_NO_DEVICE;
+    hipError_t e = hipSetDevice(d);
+    if (e == hipSuccess) e = release_buffer(b);
+    if (e != hipSuccess && st == KLEIN_OK) st = map_hip(e);
+  }
+  if (cur >= 0) {
+    const hipError_t e = hipSetDevice(cur);
+    if (e != hipSuccess && st == KLEIN_OK) st = map_hip(e);
+  }
+  return st;
+}
 
 klein_status_t klein_rope4d_attn_fwd(const void* q, const void* k, const void* v,
                                      const int32_t* pos_thwl, void* out, int B, int S, int H,
@@ -113,6 +284,10 @@ klein_status_t klein_rope4d_attn_fwd(const void* q, const void* k, const void* v
   if (st != KLEIN_OK) return st;
   if (klein::attn_fwd_bf16_grid(B, S, H) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
   try {
+    bool ran = false;
+    st = attn_on_buffer(q, k, v, pos_thwl, out, B, S, H, D, KLEIN_DTYPE_BF16, 1.f, 1.f, 1.f,
+                        stream, &ran);
+    if (st != KLEIN_OK || ran) return st;
     return map_hip(klein::launch_attn_fwd_bf16(make_args(q, k, v, pos_thwl, out, B, S, H, D, stream)));
   } catch (...) {
     return KLEIN_ERR_LAUNCH;
@@ -129,6 +304,10 @@ klein_status_t klein_rope4d_attn_fwd_fp8(const void* q, const void* k, const voi
     if (!(std::isfinite(s) && s > 0.f)) return KLEIN_ERR_INVALID_ARG;
   if (klein::attn_fwd_fp8_grid(B, S, H) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
   try {
+    bool ran = false;
+    st = attn_on_buffer(q, k, v, pos_thwl, out, B, S, H, D, KLEIN_DTYPE_FP8_E4M3, q_descale,
+                        k_descale, v_descale, stream, &ran);
+    if (st != KLEIN_OK || ran) return st;
     LaunchArgs a = make_args(q, k, v, pos_thwl, out, B, S, H, D, stream);
     a.descale[0] = q_descale; a.descale[1] = k_descale; a.descale[2] = v_descale;
     return map_hip(klein::launch_attn_fwd_fp8(a));
@@ -228,57 +407,6 @@ klein_status_t klein_splitkv_plan(int B, int S, int H, int D, int n_cu, int* pla
   plan[2] = p.n_sk > 0 ? p.n_chunk : 0;
   *partial_bytes = (size_t)p.bytes;
   return KLEIN_OK;
-}
-
-// The checks of the split-KV entry points that need no device.
-static klein_status_t check_ws_call(const void* q, const void* k, const void* v,
-                                    const int32_t* pos_thwl, const void* out, int B, int S, int H,
-                                    int D, klein_dtype_t dtype, float q_descale, float k_descale,
-                                    float v_descale) {
-  if (dtype != KLEIN_DTYPE_BF16 && dtype != KLEIN_DTYPE_FP8_E4M3) return KLEIN_ERR_INVALID_ARG;
-  klein_status_t st = check_common(q, k, v, pos_thwl, out, B, S, H, D);
-  if (st != KLEIN_OK) return st;
-  if (dtype == KLEIN_DTYPE_FP8_E4M3)
-    for (float s : {q_descale, k_descale, v_descale})
-      if (!(std::isfinite(s) && s > 0.f)) return KLEIN_ERR_INVALID_ARG;
-  if (klein::attn_fwd_bf16_grid(B, S, H) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
-  return KLEIN_OK;
-}
-
-static klein_status_t attn_ws(const void* q, const void* k, const void* v,
-                              const int32_t* pos_thwl, void* out, float* lse, int B, int S, int H,
-                              int D, klein_dtype_t dtype, float q_descale, float k_descale,
-                              float v_descale, void* workspace, size_t workspace_bytes,
-                              klein_stream_t stream) {
-  klein_status_t st = check_ws_call(q, k, v, pos_thwl, out, B, S, H, D, dtype, q_descale,
-                                    k_descale, v_descale);
-  if (st != KLEIN_OK) return st;
-  const bool fp8 = dtype == KLEIN_DTYPE_FP8_E4M3;
-  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return KLEIN_ERR_INVALID_ARG;
-  try {
-    hipError_t e;
-    const int ncu = current_cu_count(&e);
-    if (e != hipSuccess) return map_hip(e);
-    const WsLayout w = ws_layout(B, S, H, D, dtype, ncu);
-    const klein::SplitPlan& plan = w.plan;
-    if (w.total > 0 && (!workspace || workspace_bytes < (size_t)w.total))
-      return KLEIN_ERR_INVALID_ARG;
-    LaunchArgs a = make_args(q, k, v, pos_thwl, out, B, S, H, D, stream);
-    a.lse = lse;
-    if (w.krot_bytes > 0) a.krot = workspace;
-    if (plan.n_sk > 0) {
-      a.split.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.krot_bytes);
-      a.split.n_dp = plan.n_dp;
-      a.split.n_sk = plan.n_sk;
-      a.split.n_rem = plan.n_rem;
-      a.split.n_chunk = plan.n_chunk;
-    }
-    if (!fp8) return map_hip(klein::launch_attn_fwd_bf16(a));
-    a.descale[0] = q_descale; a.descale[1] = k_descale; a.descale[2] = v_descale;
-    return map_hip(klein::launch_attn_fwd_fp8(a));
-  } catch (...) {
-    return KLEIN_ERR_LAUNCH;
-  }
 }
 
 klein_status_t klein_rope4d_attn_fwd_ws(const void* q, const void* k, const void* v,

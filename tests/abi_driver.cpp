@@ -150,6 +150,10 @@ int main() {
   CHECK(std::strcmp(klein_status_string(KLEIN_STATUS_SPAN_INT_), "unknown status") == 0);
   CHECK(klein_version() >= 100);
 
+  // ---- the buffer limit: no buffer is held, so no HIP call is made
+  CHECK(klein_set_buffer_limit(0) == KLEIN_OK);
+  CHECK(klein_set_buffer_limit(KLEIN_DEFAULT_BUFFER_LIMIT) == KLEIN_OK);
+
   // ---- without a GPU, every call that reaches the device reports NO_DEVICE
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0) {
@@ -158,6 +162,10 @@ int main() {
     CHECK(klein_attn_workspace_size(1, 4096, 2, 128, KLEIN_DTYPE_BF16, &b) == N);
     CHECK(klein_rope4d_attn_fwd(F, F, F, fpos(), F, 1, 300, 2, 128, KLEIN_DTYPE_BF16, nullptr) == N);
     CHECK(klein_rope4d_attn_fwd(F, F, F, fpos(), F, 1, 300, 2, 64, KLEIN_DTYPE_FP8_E4M3, nullptr) == N);
+    CHECK(klein_set_buffer_limit(0) == KLEIN_OK);   // the per-tile kernels' path
+    CHECK(klein_rope4d_attn_fwd(F, F, F, fpos(), F, 1, 300, 2, 128, KLEIN_DTYPE_BF16, nullptr) == N);
+    CHECK(klein_rope4d_attn_fwd_fp8(F, F, F, fpos(), F, 1, 300, 2, 64, 1, 1, 1, nullptr) == N);
+    CHECK(klein_set_buffer_limit(KLEIN_DEFAULT_BUFFER_LIMIT) == KLEIN_OK);
     CHECK(klein_rope4d_attn_fwd_ws(F, F, F, fpos(), F, 1, 4096, 2, 128, KLEIN_DTYPE_BF16, 1, 1, 1,
                                    F, 1 << 30, nullptr) == N);
     CHECK(klein_rope4d_attn_fwd_noalloc(F, F, F, fpos(), F, 1, 300, 2, 128, KLEIN_DTYPE_BF16, 1, 1,

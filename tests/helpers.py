@@ -10,11 +10,19 @@ inputs, and at 0.08-0.13 on rows that face one dominant key).  A derivation of w
 output, e4m3 Q'/K'/P) is in the design notes.
 """
 
+import contextlib
+
 import numpy as np
 import torch
 
 import joint_attention_rope_amd as kl
 from workloads import Inputs
+
+# The two schedules of klein_rope4d_attn_fwd / _fp8: "buffer" (the default:
+# keys rotated once and the split-KV schedule, in the library's buffer) and
+# "per-tile" (buffer limit 0: the kernels that rotate each key tile they load
+# and need no memory, as under graph capture or above the limit).
+PATHS = ("buffer", "per-tile")
 
 BF16_MAX_ABS = 2e-2
 BF16_REL_L2 = 5e-3
@@ -36,14 +44,31 @@ def bf16_tensor_to_f64(t: torch.Tensor) -> np.ndarray:
         .__lshift__(16).view(np.float32).astype(np.float64)
 
 
-def run_attention(inp: Inputs, dev="cuda:0"):
+@contextlib.contextmanager
+def per_tile_kernels(on=True):
+    """Within the block, klein_rope4d_attn_fwd / _fp8 run the per-tile kernels
+    (buffer limit 0); the default limit is restored after it."""
+    if not on:
+        yield
+        return
+    kl.klein_set_buffer_limit(0)
+    try:
+        yield
+    finally:
+        kl.klein_set_buffer_limit(kl.KLEIN_DEFAULT_BUFFER_LIMIT)
+
+
+def run_attention(inp: Inputs, dev="cuda:0", path="buffer"):
+    """klein_rope4d_attn_fwd (bf16) or klein_rope4d_attn_fwd_fp8 on one of PATHS."""
+    assert path in PATHS
     q, k, v, pos = to_device(inp, dev)
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
-    if inp.descale is None:
-        kl.klein_rope4d_attn_fwd(q, k, v, pos, out)
-    else:
-        kl.klein_rope4d_attn_fwd_fp8(q, k, v, pos, out, *inp.descale)
-    torch.cuda.synchronize()
+    with per_tile_kernels(path == "per-tile"):
+        if inp.descale is None:
+            kl.klein_rope4d_attn_fwd(q, k, v, pos, out)
+        else:
+            kl.klein_rope4d_attn_fwd_fp8(q, k, v, pos, out, *inp.descale)
+        torch.cuda.synchronize()
     return out
 
 

@@ -28,7 +28,25 @@ def test_header_declares_the_entry_points():
         "klein_attn_workspace_size", "klein_splitkv_plan", "klein_rope4d_attn_fwd_lse",
         "klein_rope4d_attn_fwd_lse_ws",
         "klein_rope4d_attn_bwd", "klein_attn_bwd_workspace_size", "klein_rope4d_apply",
-        "klein_rope4d_attn_fwd_noalloc", "klein_status_string", "klein_version"])
+        "klein_rope4d_attn_fwd_noalloc", "klein_set_buffer_limit", "klein_status_string",
+        "klein_version"])
+
+
+def test_header_constants_match_the_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (KLEIN_\w+) (.+)", text))
+    assert eval(consts["KLEIN_DEFAULT_BUFFER_LIMIT"].replace("(size_t)", "")) == \
+        _capi.KLEIN_DEFAULT_BUFFER_LIMIT == 2 << 30
+    assert eval(consts["KLEIN_NOALLOC_SCRATCH_BYTES"].replace("LL", "")) == \
+        _capi.KLEIN_NOALLOC_SCRATCH_BYTES
+
+
+def test_buffer_limit_needs_no_device_while_no_buffer_is_held():
+    # no call has created a buffer in this process, so setting the limit
+    # makes no HIP call
+    lib = _capi.lib()
+    assert lib.klein_set_buffer_limit(0) == _capi.KLEIN_OK
+    assert lib.klein_set_buffer_limit(_capi.KLEIN_DEFAULT_BUFFER_LIMIT) == _capi.KLEIN_OK
 
 
 def test_library_exports_every_declared_symbol():

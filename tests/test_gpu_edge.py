@@ -8,8 +8,8 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import (assert_bf16_close, assert_fp8_close, bf16_tensor_to_f64, oracle_full,
-                     oracle_rows, random_fp8_inputs, random_inputs, run_attention,
+from helpers import (PATHS, assert_bf16_close, assert_fp8_close, bf16_tensor_to_f64,
+                     oracle_full, oracle_rows, random_fp8_inputs, random_inputs, run_attention,
                      sample_rows)
 from workloads import Inputs
 
@@ -20,31 +20,35 @@ def _rows_of(out, rows):
     return bf16_tensor_to_f64(out[:, torch.from_numpy(rows).to(out.device)])
 
 
-def test_long_sequence_bf16_sampled_rows():
-    # S > 65,535 and odd; positions up to 4,000 on every axis, so most keys
-    # take the rotation fallback of the bf16 kernel's table (positions < 256)
+@pytest.mark.parametrize("path", PATHS)
+def test_long_sequence_bf16_sampled_rows(path):
+    # S > 65,535 and odd; positions up to 4,000 on every axis, so on the
+    # per-tile kernels most keys take the rotation fallback of the bf16
+    # kernel's table (positions < 256)
     inp = random_inputs(1, 70001, 2, 64, seed=91, pos_lo=-20, pos_hi=4000)
-    out = run_attention(inp)
+    out = run_attention(inp, path=path)
     rows = sample_rows(70001, 256, n=32, seed=91)
     assert_bf16_close(_rows_of(out, rows), oracle_rows(inp, rows), "S=70001 bf16")
 
 
-def test_long_sequence_fp8_sampled_rows():
+@pytest.mark.parametrize("path", PATHS)
+def test_long_sequence_fp8_sampled_rows(path):
     inp = random_fp8_inputs(1, 70001, 2, 64, seed=92, pos_lo=-20, pos_hi=4000)
-    out = run_attention(inp)
+    out = run_attention(inp, path=path)
     rows = sample_rows(70001, 256, n=32, seed=92)
     assert_fp8_close(_rows_of(out, rows), oracle_rows(inp, rows), "S=70001 fp8")
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("fp8", [False, True])
-def test_odd_batch_and_heads_full(fp8):
+def test_odd_batch_and_heads_full(fp8, path):
     if fp8:
         inp = random_fp8_inputs(3, 300, 5, 128, seed=93)
         check = assert_fp8_close
     else:
         inp = random_inputs(3, 300, 5, 128, seed=93)
         check = assert_bf16_close
-    out = run_attention(inp)
+    out = run_attention(inp, path=path)
     check(bf16_tensor_to_f64(out), oracle_full(inp), f"B=3 H=5 fp8={fp8}")
 
 

@@ -2,7 +2,8 @@
 
 The graded reference is exact attention of what the kernel was given (code x
 descale); the tolerance is relative L2 <= 6e-2 over the compared rows, and
-0.15 per row.
+0.15 per row.  The plain entry runs on both of its schedules (the library's
+buffer and the per-tile kernels).
 """
 
 import numpy as np
@@ -10,27 +11,29 @@ import pytest
 import torch
 
 import joint_attention_rope_amd as kl
-from helpers import (FP8_ROW_REL_L2, assert_fp8_close, bf16_tensor_to_f64, errors, oracle_full,
-                     oracle_rows, random_fp8_inputs, row_rel_l2, run_attention, sample_rows,
-                     to_device)
+from helpers import (FP8_ROW_REL_L2, PATHS, assert_fp8_close, bf16_tensor_to_f64, errors,
+                     oracle_full, oracle_rows, per_tile_kernels, random_fp8_inputs, row_rel_l2,
+                     run_attention, sample_rows, to_device)
 from workloads import get_config, make_inputs
 
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("S", [1, 17, 64, 65, 300, 577])
-def test_fp8_ragged_full(S, D):
+def test_fp8_ragged_full(S, D, path):
     inp = random_fp8_inputs(2, S, 3, D, seed=5000 + 7 * S + D)
-    print("[case] fp8 ragged", S, D, flush=True)
-    out = bf16_tensor_to_f64(run_attention(inp))
+    print("[case] fp8 ragged", S, D, path, flush=True)
+    out = bf16_tensor_to_f64(run_attention(inp, path=path))
     assert_fp8_close(out, oracle_full(inp), f"fp8 S={S} D={D}")
 
 
-def test_fp8_small_edit_workload_full():
+@pytest.mark.parametrize("path", PATHS)
+def test_fp8_small_edit_workload_full(path):
     """The FP8 edit recipe (text + image + reference at t = 1) at 8x8 grids."""
     inp = make_inputs(get_config(5, text=16, grid=8))
-    out = bf16_tensor_to_f64(run_attention(inp))
+    out = bf16_tensor_to_f64(run_attention(inp, path=path))
     assert_fp8_close(out, oracle_full(inp), "fp8 small edit")
 
 
@@ -44,22 +47,24 @@ def test_fp8_dtype_code_path_unit_scales():
     assert_fp8_close(bf16_tensor_to_f64(out), oracle_full(inp), "fp8 unit scales")
 
 
-def test_fp8_edit_workload_sampled_rows():
+@pytest.mark.parametrize("path", PATHS)
+def test_fp8_edit_workload_sampled_rows(path):
     cfg = get_config(5)
     inp = make_inputs(cfg)
-    print("[case] fp8 workload 5", inp.q.shape, flush=True)
-    out = run_attention(inp)
+    print("[case] fp8 workload 5", inp.q.shape, path, flush=True)
+    out = run_attention(inp, path=path)
     rows = sample_rows(cfg.S, cfg.text, n=16, seed=5)
     gpu = bf16_tensor_to_f64(out[:, torch.from_numpy(rows).to(out.device)])
     assert_fp8_close(gpu, oracle_rows(inp, rows), "fp8 workload 5")
 
 
-def test_fp8_multi_reference_sampled_rows():
+@pytest.mark.parametrize("path", PATHS)
+def test_fp8_multi_reference_sampled_rows(path):
     # 1024^2 edit with two references (t = 1, 2) and a prompt padded to 560
     cfg = get_config(5, grid=64, refs=2, text=560)
     inp = make_inputs(cfg)
-    print("[case] fp8 multi-reference", inp.q.shape, flush=True)
-    out = run_attention(inp)
+    print("[case] fp8 multi-reference", inp.q.shape, path, flush=True)
+    out = run_attention(inp, path=path)
     rows = sample_rows(cfg.S, cfg.text, n=24, seed=55)
     gpu = bf16_tensor_to_f64(out[:, torch.from_numpy(rows).to(out.device)])
     assert_fp8_close(gpu, oracle_rows(inp, rows), "fp8 multi-reference")
@@ -72,7 +77,7 @@ def test_fp8_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("entry", ["plain", "workspace"])
+@pytest.mark.parametrize("entry", ["plain", "per-tile", "workspace"])
 @pytest.mark.parametrize("gap,dom", [(11.0, 5), (12.0, 5), (12.0, 4101)])
 def test_fp8_dominant_key_row(entry, gap, dom):
     """Queries 0..63 face one key gap binades above 8,192 others, in the
@@ -91,8 +96,10 @@ def test_fp8_dominant_key_row(entry, gap, dom):
     print(f"[case] fp8 dominant key gap {gap} key {dom} entry {entry}", flush=True)
     q, k, v, p = to_device(inp)
     out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
-    if entry == "plain":
-        kl.klein_rope4d_attn_fwd_fp8(q, k, v, p, out, *descale)
+    if entry in ("plain", "per-tile"):
+        with per_tile_kernels(entry == "per-tile"):
+            kl.klein_rope4d_attn_fwd_fp8(q, k, v, p, out, *descale)
+            torch.cuda.synchronize()
     else:
         ws = torch.empty(max(1, kl.klein_attn_workspace_size(1, S, 1, D, kl.KLEIN_DTYPE_FP8_E4M3)),
                          dtype=torch.uint8, device=q.device)

@@ -1,14 +1,16 @@
 """GPU parity on tensors of 2^31 elements (4 GiB in bf16): element offsets
-past the int32 range, on the plain and the workspace entry (bf16) and the
-FP8 entry.  Inputs are seeded and drawn on the device; the oracle checks three
-whole heads (first, middle and last) from the very bits the kernels read."""
+past the int32 range, on the plain and the workspace entry (bf16; the plain
+entry's schedule needs more than its default buffer limit here, so it runs
+the per-tile kernels) and the FP8 entry on both of its schedules.  Inputs are
+seeded and drawn on the device; the oracle checks three whole heads (first,
+middle and last) from the very bits the kernels read."""
 
 import numpy as np
 import pytest
 import torch
 
 import joint_attention_rope_amd as kl
-from helpers import assert_bf16_close, assert_fp8_close, bf16_tensor_to_f64
+from helpers import assert_bf16_close, assert_fp8_close, bf16_tensor_to_f64, per_tile_kernels
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -38,6 +40,7 @@ def test_bf16_2_pow_31_elements_plain_and_workspace():
     pos_np = positions(2031)
     pos = torch.from_numpy(pos_np).to(DEV)
     out = torch.empty_like(q)
+    assert kl.klein_attn_workspace_size(B, S, H, D) > kl.KLEIN_DEFAULT_BUFFER_LIMIT
     kl.klein_rope4d_attn_fwd(q, k, v, pos, out)
     out_ws = torch.empty_like(q)
     ws = torch.empty(kl.klein_attn_workspace_size(B, S, H, D), dtype=torch.uint8, device=DEV)
@@ -60,12 +63,20 @@ def test_fp8_2_pow_31_elements():
              .view(torch.uint8) for s in scales]
     pos_np = positions(2032)
     pos = torch.from_numpy(pos_np).to(DEV)
-    out = torch.empty(B, S, H, D, dtype=torch.bfloat16, device=DEV)
-    kl.klein_rope4d_attn_fwd_fp8(*codes, pos, out, *scales)
-    torch.cuda.synchronize()
+    outs = []
+    for per_tile in (False, True):
+        out = torch.empty(B, S, H, D, dtype=torch.bfloat16, device=DEV)
+        with per_tile_kernels(per_tile):
+            kl.klein_rope4d_attn_fwd_fp8(*codes, pos, out, *scales)
+            torch.cuda.synchronize()
+        outs.append(out)
     for b, h in HEADS:
         qh, kh, vh = (head64(c, b, h, s) for c, s in zip(codes, scales))
+        ref = oracle.attention(qh, kh, vh, pos_np)
         print(f"[case] fp8 2^31 elements, head ({b}, {h})", flush=True)
-        assert_fp8_close(head64(out, b, h), oracle.attention(qh, kh, vh, pos_np), f"fp8 ({b}, {h})")
-    del codes, out
+        assert_fp8_close(head64(outs[0], b, h), ref, f"fp8 buffer ({b}, {h})")
+        assert_fp8_close(head64(outs[1], b, h), ref, f"fp8 per-tile ({b}, {h})")
+    del codes, outs, out
+    with per_tile_kernels():        # frees the library's buffer
+        pass
     torch.cuda.empty_cache()

@@ -4,9 +4,10 @@ Seeded inputs whose scores grow along the key axis (a ramp: every few tiles
 the softmax mass moves to later keys) or carry one huge key late in the
 sequence (a spike: 2^(s - m) overflows fp32 against the max of the earlier
 tiles).  Positions are zero, so the rotation is the identity and the score
-structure survives it.  Both dtypes, the plain and the workspace entry (the
-latter with the split-KV schedule at S = 4000), against the oracle at the hot
-path's tolerances.
+structure survives it.  Both dtypes; the plain entry on both of its
+schedules (the library's buffer, and the per-tile kernels at buffer limit 0)
+and the workspace entry (the split-KV schedule at S = 4000), against the
+oracle at the hot path's tolerances.
 """
 
 import numpy as np
@@ -14,7 +15,8 @@ import pytest
 import torch
 
 import joint_attention_rope_amd as kl
-from helpers import assert_bf16_close, assert_fp8_close, bf16_tensor_to_f64, oracle_full, to_device
+from helpers import (assert_bf16_close, assert_fp8_close, bf16_tensor_to_f64, oracle_full,
+                     per_tile_kernels, to_device)
 from workloads import Inputs, bf16_bits_from_f32, e4m3_encode, get_config
 
 pytestmark = pytest.mark.gpu
@@ -54,33 +56,36 @@ def make(pattern, dtype, S, H, D, seed):
     return Inputs(get_config(5, B=1, H=H, D=D), *codes, pos, descale=tuple(scales))
 
 
-def run(inp, workspace):
+def run(inp, entry):
     q, k, v, pos = to_device(inp, DEV)
     B, S, H, D = q.shape
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=DEV)
-    if workspace:
+    if entry == "workspace":
         dt = kl.KLEIN_DTYPE_BF16 if inp.descale is None else kl.KLEIN_DTYPE_FP8_E4M3
         ws = torch.empty(kl.klein_attn_workspace_size(B, S, H, D, dt), dtype=torch.uint8, device=DEV)
         kl.klein_rope4d_attn_fwd_ws(q, k, v, pos, out, ws, dtype=dt,
                                     descales=inp.descale or (1.0, 1.0, 1.0))
-    elif inp.descale is None:
-        kl.klein_rope4d_attn_fwd(q, k, v, pos, out)
     else:
-        kl.klein_rope4d_attn_fwd_fp8(q, k, v, pos, out, *inp.descale)
+        with per_tile_kernels(entry == "per-tile"):
+            if inp.descale is None:
+                kl.klein_rope4d_attn_fwd(q, k, v, pos, out)
+            else:
+                kl.klein_rope4d_attn_fwd_fp8(q, k, v, pos, out, *inp.descale)
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     return bf16_tensor_to_f64(out)
 
 
-@pytest.mark.parametrize("workspace", [False, True])
+@pytest.mark.parametrize("entry", ["plain", "per-tile", "workspace"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("pattern", ["ramp", "spike"])
 @pytest.mark.parametrize("S,H,D", [(1000, 2, 128), (4000, 1, 128), (700, 3, 64)])
-def test_running_max_moves(pattern, dtype, workspace, S, H, D):
+def test_running_max_moves(pattern, dtype, entry, S, H, D):
     inp = make(pattern, dtype, S, H, D, seed=S + D)
-    print(f"[case] {pattern} {dtype} ws={workspace} S={S} H={H} D={D}", flush=True)
-    got = run(inp, workspace)
+    print(f"[case] {pattern} {dtype} {entry} S={S} H={H} D={D}", flush=True)
+    got = run(inp, entry)
     ref = oracle_full(inp)
-    what = f"{pattern} {dtype} ws={workspace} S={S} H={H} D={D}"
+    what = f"{pattern} {dtype} {entry} S={S} H={H} D={D}"
     if dtype == "bf16":
         assert_bf16_close(got, ref, what)
     else:

@@ -1,9 +1,10 @@
 """GPU checks of klein_rope4d_attn_fwd_ws, the split-KV schedule.
 
 Query tiles that run whole (the full rounds of the GPU) go through the same
-arithmetic as the dense entry point (the keys are rotated once before the
-call, to the very fp16 values, or e4m3 codes, the dense kernels form per
-tile), so their rows must be bit-identical to it.  Rows of split tiles round P to bf16 relative to each chunk's own
+arithmetic as the per-tile kernels (the keys are rotated once before the
+call, to the very fp16 values, or e4m3 codes, those kernels form per tile),
+so their rows must be bit-identical to them (klein_rope4d_attn_fwd with
+buffer limit 0).  Rows of split tiles round P to bf16 relative to each chunk's own
 running max and merge fp32 partial sums, so they differ from the dense rows
 at the level of the kernel's rounding error; they must match the oracle
 within the hot path's tolerances.  Results must not depend on which
@@ -18,8 +19,8 @@ import torch
 
 import joint_attention_rope_amd as kl
 from helpers import (BF16_MAX_ABS, BF16_REL_L2, assert_bf16_close, assert_fp8_close,
-                     bf16_tensor_to_f64, errors, oracle_full, oracle_rows, random_fp8_inputs, random_inputs, run_attention,
-                     sample_rows, to_device)
+                     bf16_tensor_to_f64, errors, oracle_full, oracle_rows, random_fp8_inputs,
+                     random_inputs, run_attention, sample_rows, to_device)
 from workloads import get_config, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -73,7 +74,7 @@ def test_whole_rounds_bitwise_and_split_close(fp8):
     B, S, H = 2, 4608, 16                      # 576 query tiles
     inp = (random_fp8_inputs if fp8 else random_inputs)(B, S, H, 128, seed=94)
     out, nbytes = run_ws(inp)
-    ref = run_attention(inp)
+    ref = run_attention(inp, path="per-tile")
     split = split_rows_mask(B, S, H)
     a = out.view(torch.int16).cpu().numpy()
     b = ref.view(torch.int16).cpu().numpy()
@@ -93,7 +94,7 @@ def test_workload_4_full_size():
     cfg = get_config(4)
     inp = make_inputs(cfg)
     out, nbytes = run_ws(inp)
-    ref = run_attention(inp)
+    ref = run_attention(inp, path="per-tile")
     assert nbytes > 0
     split = split_rows_mask(cfg.B, cfg.S, cfg.H)
     a = out.view(torch.int16).cpu().numpy()
@@ -127,18 +128,20 @@ def test_repeat_calls_bitwise_identical():
 
 
 @pytest.mark.parametrize("D", [64, 128])
-def test_unsplit_call_equals_dense(D):
+def test_unsplit_call_equals_per_tile_kernels(D):
     # S < 2048: nothing is split; the keys are still rotated once into the
     # workspace (fp16, or e4m3 codes for fp8: the values the kernels' cos/sin
     # tables give), so the result equals the dense entry point bit for bit
     inp = random_inputs(2, 1000, 3, D, seed=98)
     assert kl.klein_attn_workspace_size(2, 1000, 3, D) == 2 * 1000 * 3 * D * 2
     out, _ = run_ws(inp)
-    assert torch.equal(out.view(torch.int16), run_attention(inp).view(torch.int16))
+    assert torch.equal(out.view(torch.int16),
+                       run_attention(inp, path="per-tile").view(torch.int16))
     inp8 = random_fp8_inputs(1, 1000, 2, D, seed=99)
     assert kl.klein_attn_workspace_size(1, 1000, 2, D, kl.KLEIN_DTYPE_FP8_E4M3) == 1000 * 2 * D
     out8, _ = run_ws(inp8)
-    assert torch.equal(out8.view(torch.int16), run_attention(inp8).view(torch.int16))
+    assert torch.equal(out8.view(torch.int16),
+                       run_attention(inp8, path="per-tile").view(torch.int16))
 
 
 def test_workspace_too_small_rejected():
