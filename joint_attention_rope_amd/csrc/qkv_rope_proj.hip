@@ -22,9 +22,9 @@
 // of twice the length).  W and x tiles
 // are double-buffered in LDS (rows padded to 144 bytes, so the 16 rows one
 // 16-lane read phase touches fall on distinct banks) and staged through
-// registers one K step ahead, the stores interleaved with the MFMAs; one
-// barrier per K step.  Rows past N or M read
-// as zeros through the buffer descriptors and are not stored.
+// registers, two K steps ahead (bf16) or one (fp8), with the loads and the
+// stores spread between the MFMAs; one barrier per K step.  Rows past N or M
+// read as zeros through the buffer descriptors and are not stored.
 #include "klein_device.hpp"
 #include "klein_launch.hpp"
 
@@ -77,28 +77,20 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
   const __amdgpu_buffer_rsrc_t rb =
       uniform_rsrc(static_cast<const uint8_t*>(xv) + (size_t)m0 * rowb, nrows_b * rowb);
   u32x4_t stg[NLD];
-  auto load = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int c = tid + 512 * i;
-      const bool isa = c < TN * CPR;
-      const int cc = isa ? c : c - TN * CPR;
-      const int row = cc / CPR, ch = cc % CPR;
-      const int off = row * rowb + kt * KB + 16 * ch;
-      stg[i] = __builtin_bit_cast(u32x4_t, isa ? __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0)
+  // chunk i of a thread: W rows for i < 4, x rows after (TN * CPR = 4 * 512)
+  static_assert(TN * CPR == 4 * 512, "staging split");
+  auto load_one = [&](int kt, int i) {
+    const int cc = tid + 512 * (i & 3);
+    const int row = cc / CPR, ch = cc % CPR;
+    const int off = row * rowb + kt * KB + 16 * ch;
+    stg[i] = __builtin_bit_cast(u32x4_t, i < 4 ? __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0)
                                                : __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
-    }
   };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int c = tid + 512 * i;
-      const bool isa = c < TN * CPR;
-      const int cc = isa ? c : c - TN * CPR;
-      const int row = cc / CPR, ch = cc % CPR;
-      uint16_t* dst = isa ? &a_lds[buf][row * ROW + 8 * ch] : &b_lds[buf][row * ROW + 8 * ch];
-      *reinterpret_cast<u32x4_t*>(dst) = stg[i];
-    }
+  auto store_one = [&](int buf, int i) {
+    const int cc = tid + 512 * (i & 3);
+    const int row = cc / CPR, ch = cc % CPR;
+    uint16_t* dst = i < 4 ? &a_lds[buf][row * ROW + 8 * ch] : &b_lds[buf][row * ROW + 8 * ch];
+    *reinterpret_cast<u32x4_t*>(dst) = stg[i];
   };
 
   f32x16_t acc[4][2];
@@ -108,14 +100,15 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
     for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = (f32x16_t){};
 
   const int nk = C * ES / KB;
-  load(0);
-  store(0);
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) load_one(0, i);
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) store_one(0, i);
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) load_one(1, i);
+  }
   __syncthreads();
-  // K step kt: the loads of step kt+1 go out first (past the last step they
-  // read in-range rows or the descriptors' zeros, and are never used); the
-  // operands of sub-step ks+1 are read during the MFMAs of ks; the stores of
-  // step kt+1 into the other buffer ride along the last two sub-steps (that
-  // buffer was last read before the previous barrier).
   // a lane's operand of k-step ks: 16 bytes (bf16) or 32 bytes (fp8) of its
   // row, the second half-wave taking the next 16 or 32
   typedef uint32_t opnd_t __attribute__((ext_vector_type(FP8 ? 8 : 4)));
@@ -146,9 +139,23 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
       return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                      __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   };
+  // The operands of sub-step ks+1 are read during the MFMAs of ks.  Loads
+  // past the last step read in-range rows or the descriptors' zeros and are
+  // never used.
+  //
+  // bf16: staging slot j of K step kt stores chunk j of step kt+1 (loaded a
+  // step earlier) into the other buffer (last read before the previous
+  // barrier) and reloads its registers with chunk j of step kt+2.  The slots
+  // sit after every fourth MFMA, so a step's loads and stores spread over
+  // it: issued together at the top, the 64 KB of loads of all 8 waves fill
+  // the vector memory queue and hold the waves at issue for 500-1000 cycles
+  // of a ~3,500-cycle step.
+  //
+  // fp8 (operands twice as wide: a register set held across the whole step
+  // would spill): one load of step kt+1 after each MFMA of the first
+  // sub-step, one store of it after each MFMA of the second.
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    load(kt + 1);
     read_ops(buf, 0, 0);
 #pragma unroll
     for (int ks = 0; ks < KSUB; ++ks) {
@@ -157,23 +164,21 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
       for (int i = 0; i < 8; ++i) {
         const int nb = i >> 1, mb = i & 1;
         acc[nb][mb] = mfma(av[ks & 1][nb], bv[ks & 1][mb], acc[nb][mb]);
-        // the 8 stores ride along the second half of the k-steps (on the
-        // last step they fill a buffer no one reads)
-        constexpr int PER = 2 * NLD / KSUB;        // stores per k-step there
-        if (ks >= KSUB / 2) {
-          const int j = PER * (ks - KSUB / 2) + i * PER / 8;
+        if constexpr (FP8) {
+          static_assert(!FP8 || KSUB == 2, "one k-step of loads, one of stores");
+          if (ks == 0) load_one(kt + 1, i);
+          else store_one(buf ^ 1, i);
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+          constexpr int PER = NLD / KSUB;            // staging slots per k-step
           if ((i * PER) % 8 < PER) {
-            const int c = tid + 512 * j;
-            const bool isa = c < TN * CPR;
-            const int cc = isa ? c : c - TN * CPR;
-            const int row = cc / CPR, ch = cc % CPR;
-            uint16_t* dst = isa ? &a_lds[buf ^ 1][row * ROW + 8 * ch]
-                                : &b_lds[buf ^ 1][row * ROW + 8 * ch];
-            *reinterpret_cast<u32x4_t*>(dst) = stg[j];
+            const int j = PER * ks + i * PER / 8;
+            store_one(buf ^ 1, j);
+            load_one(kt + 2, j);
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
   }
