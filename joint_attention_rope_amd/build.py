@@ -1,7 +1,7 @@
 """Build the gfx950 HIP library libklein_attn.so in-tree with hipcc, and the
-measurement harness step_clock (the bf16 attention kernel with per-region
-cycle counters, linked with the library's other objects; not part of the
-library).
+measurement harness step_clock (the bf16 attention kernel and the QKV
+projection with per-part cycle counters, linked with the library's other
+objects; not part of the library).
 
 Usage: python -m joint_attention_rope_amd.build
 """
@@ -14,8 +14,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libklein_attn.so")
 STEP_CLOCK = os.path.join(PKG, "step_clock")
-# the harness replaces this source (it includes it with the cycle counters on)
-STEP_CLOCK_REPLACES = "attn_fwd_bf16.hip"
+# the harness replaces these sources (it includes them with the cycle counters
+# on; it is compiled with the first one's flags, which leave the second's
+# instructions unchanged)
+STEP_CLOCK_REPLACES = ("attn_fwd_bf16.hip", "qkv_rope_proj.hip")
 SOURCES = ["api.cpp", "attn_fwd_bf16.hip", "attn_fwd_fp8.hip", "qkv_rope_proj.hip", "rope_apply.hip",
            "split_schedule.hip", "attn_bwd.hip", "noalloc.hip"]
 # Device kernels never see NaN inputs on purpose (a NaN in q/k/v propagates to
@@ -52,14 +54,14 @@ def build(verbose: bool = False) -> str:
         cflags = [f for f in FLAGS if f != "-shared"]
         for src in SOURCES + ["step_clock.hip"]:
             obj = os.path.join(CSRC, src + ".o" + tag)
-            flags = KERNEL_FLAGS.get(STEP_CLOCK_REPLACES if src == "step_clock.hip" else src, [])
+            flags = KERNEL_FLAGS.get(STEP_CLOCK_REPLACES[0] if src == "step_clock.hip" else src, [])
             _run([HIPCC, *cflags, *flags, "-c", "-o", obj, os.path.join(CSRC, src)], verbose)
             objs[src] = obj
         lib_objs = [objs[s] for s in SOURCES]
         tmp = LIB + ".tmp" + tag
         _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *lib_objs], verbose)
         os.replace(tmp, LIB)
-        clock_objs = [objs[s] for s in SOURCES if s != STEP_CLOCK_REPLACES] + [objs["step_clock.hip"]]
+        clock_objs = [objs[s] for s in SOURCES if s not in STEP_CLOCK_REPLACES] + [objs["step_clock.hip"]]
         tmp = STEP_CLOCK + ".tmp" + tag
         _run([HIPCC, "--offload-arch=gfx950", "-o", tmp, *clock_objs], verbose)
         os.replace(tmp, STEP_CLOCK)

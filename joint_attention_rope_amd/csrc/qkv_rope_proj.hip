@@ -30,6 +30,38 @@
 
 namespace klein {
 
+// Per-part cycle counts of the K step, for a measurement build only: defined
+// by the step_clock.hip harness, never by the library.  Each wave sums, over
+// its K steps, the shader-clock cycles (s_memtime) of each k-sub-step (with
+// the staging slots in it) and of the barrier, and lane 0 writes them, with
+// the K-step count and the cycles of the whole loop, to
+// klein_qkv_clock_out[8 wg + wave][0..7].
+#ifdef KLEIN_STEP_CLOCK
+__device__ unsigned long long* klein_qkv_clock_out;
+#define KLEIN_QKV_CLOCK_START                                                \
+  unsigned long long qclk_sum[5] = {0, 0, 0, 0, 0};                          \
+  unsigned long long qclk_prev = __builtin_amdgcn_s_memtime();               \
+  const unsigned long long qclk_start = qclk_prev;
+#define KLEIN_QKV_CLOCK_MARK(i)                                              \
+  do {                                                                       \
+    const unsigned long long qclk_now = __builtin_amdgcn_s_memtime();        \
+    qclk_sum[i] += qclk_now - qclk_prev;                                     \
+    qclk_prev = qclk_now;                                                    \
+  } while (0)
+#define KLEIN_QKV_CLOCK_STORE(nk)                                            \
+  if (klein_qkv_clock_out != nullptr && lane == 0) {                         \
+    unsigned long long* co = klein_qkv_clock_out + ((size_t)blockIdx.x * 8 + wave) * 8; \
+    for (int i = 0; i < 5; ++i) co[i] = qclk_sum[i];                         \
+    co[5] = (unsigned long long)(nk);                                        \
+    co[6] = qclk_prev - qclk_start;                                          \
+    co[7] = 0;                                                               \
+  }
+#else
+#define KLEIN_QKV_CLOCK_START
+#define KLEIN_QKV_CLOCK_MARK(i) do {} while (0)
+#define KLEIN_QKV_CLOCK_STORE(nk)
+#endif
+
 template <int D, bool FP8>
 __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
     const void* __restrict__ xv, const void* __restrict__ wv,
@@ -154,6 +186,7 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
   // fp8 (operands twice as wide: a register set held across the whole step
   // would spill): one load of step kt+1 after each MFMA of the first
   // sub-step, one store of it after each MFMA of the second.
+  KLEIN_QKV_CLOCK_START
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     read_ops(buf, 0, 0);
@@ -179,9 +212,12 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      KLEIN_QKV_CLOCK_MARK(ks);
     }
     __syncthreads();
+    KLEIN_QKV_CLOCK_MARK(4);
   }
+  KLEIN_QKV_CLOCK_STORE(nk)
 
   // ---- epilogue: lane column = token m, registers 4c..4c+3 = features
   // n0 + 128 wn + 32 nb + 8 c + 4 g + 0..3

@@ -1,26 +1,37 @@
 // Measurement harness (not part of the library): where the cycles of the
-// bf16 attention kernel's pipeline step go.
+// bf16 attention kernel's pipeline step, and of the QKV projection's K
+// step, go.
 //
-// This file compiles attn_fwd_bf16.hip with KLEIN_STEP_CLOCK defined, which
-// makes every wave sum the shader-clock cycles (s_memtime) spent between
-// marks in each step: the step start (key positions, tail mask), region A
-// (the score MFMAs of the next tile with the softmax of this one), the
-// rescale check, region B (the P.V MFMAs with the staging of later tiles),
-// the buffer loads, and the barrier.  It is linked with the library's other
-// objects (everything but attn_fwd_bf16.hip), so the public entry point
-// klein_rope4d_attn_fwd_ws runs the instrumented kernel.  The marks add
+// This file compiles attn_fwd_bf16.hip and qkv_rope_proj.hip with
+// KLEIN_STEP_CLOCK defined, which makes every wave sum the shader-clock
+// cycles (s_memtime) spent between marks.  In the attention kernel's step:
+// the step start (key positions, tail mask), region A (the score MFMAs of
+// the next tile with the softmax of this one), the rescale check, region B
+// (the P.V MFMAs with the staging of later tiles), the buffer loads, and the
+// barrier.  In the projection's K step: each k-sub-step (8 MFMAs with the
+// staging loads and stores placed among them) and the barrier.  The harness
+// is linked with the library's other objects (everything but those two
+// sources), so the public entry points klein_rope4d_attn_fwd_ws and
+// klein_qkv_rope4d_proj(_fp8) run the instrumented kernels.  The marks add
 // waits of their own; the harness reports the instrumented call's time so
 // that the overhead can be read against the plain kernel's.
 //
-// Usage: step_clock [B S H D reps]   (default: the 2048x2048 CFG workload,
-// B=2, S=16896, H=24, D=128).  Inputs are seeded N(0, 1) bf16; positions
-// follow the workload's layout (512 text tokens on the l axis, then a
-// square image grid).  Prints a markdown table: mean cycles per step for
-// the waves 0-3 and 4-7 of the workgroups that run whole tiles (the two
-// waves of a SIMD are w and w + 4), the loop's cycles per step, the clock
-// (cycles over the fixed-rate 100 MHz timestamps) and the call time.
+// Usage: step_clock [B S H D reps]        the attention (default: the
+//                                         2048x2048 CFG workload, B=2,
+//                                         S=16896, H=24, D=128)
+//        step_clock qkv [B S H D reps]    the projection (C = H D), bf16
+//                                         then fp8 operands
+// Inputs are seeded N(0, 1) (W scaled by 1/sqrt(C)); positions follow the
+// workload's layout (512 text tokens on the l axis, then a square image
+// grid).  The attention table gives mean cycles per step for the waves 0-3
+// and 4-7 of the workgroups that run whole tiles (the two waves of a SIMD
+// are w and w + 4), the loop's cycles per step, the clock (cycles over the
+// fixed-rate 100 MHz timestamps) and the call time; the projection table
+// the mean cycles per K step of the same two wave halves over all
+// workgroups.
 #define KLEIN_STEP_CLOCK 1
 #include "attn_fwd_bf16.hip"
+#include "qkv_rope_proj.hip"
 
 #include <cmath>
 #include <cstdio>
@@ -46,7 +57,150 @@ static uint16_t bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+static std::vector<int32_t> workload_positions(int S) {
+  const int text = S >= 512 ? 512 : 0;
+  const int grid = (int)std::lround(std::sqrt((double)(S - text)));
+  std::vector<int32_t> pos((size_t)S * 4, 0);
+  for (int s = 0; s < S; ++s) {
+    if (s < text) {
+      pos[4 * s + 3] = s;
+    } else if (grid > 0) {
+      const int i = s - text;
+      pos[4 * s + 1] = (i / grid) % 4096;
+      pos[4 * s + 2] = i % grid;
+    }
+  }
+  return pos;
+}
+
+// E4M3 code of x (round to nearest even, saturating at 448)
+static uint8_t e4m3_code(float x) {
+  const double a = std::fmin(std::fabs((double)x), 448.0);
+  int c;
+  if (a < std::ldexp(1.0, -6)) {
+    c = (int)std::nearbyint(std::ldexp(a, 9));           // subnormal: m 2^-9 (8 = 2^-6)
+  } else {
+    int E;
+    const double f = std::frexp(a, &E);                   // a = f 2^E, f in [0.5, 1)
+    int m = (int)std::nearbyint((2.0 * f - 1.0) * 8.0);   // a = (1 + m/8) 2^(E-1)
+    int e = E - 1;
+    if (m == 8) {
+      m = 0;
+      ++e;
+    }
+    c = ((e + 7) << 3) | m;
+  }
+  if (c > 126) c = 126;
+  return (uint8_t)(c | (x < 0.f ? 0x80 : 0));
+}
+
+static int qkv_main(int argc, char** argv) {
+  const int B = argc > 2 ? std::atoi(argv[2]) : 2;
+  const int S = argc > 3 ? std::atoi(argv[3]) : 16896;
+  const int H = argc > 4 ? std::atoi(argv[4]) : 24;
+  const int D = argc > 5 ? std::atoi(argv[5]) : 128;
+  const int reps = argc > 6 ? std::atoi(argv[6]) : 10;
+  const int C = H * D, M = B * S, N = 3 * H * D;
+  uint64_t st = 404ull;
+  auto gauss = [&]() {
+    auto uni = [&]() {
+      st = st * 6364136223846793005ull + 1442695040888963407ull;
+      return ((st >> 11) + 0.5) * (1.0 / 9007199254740992.0);
+    };
+    return (float)(std::sqrt(-2.0 * std::log(uni())) * std::cos(6.283185307179586 * uni()));
+  };
+  std::vector<float> xf((size_t)M * C), wf((size_t)N * C);
+  for (auto& e : xf) e = gauss();
+  for (auto& e : wf) e = gauss() / std::sqrt((float)C);
+  std::vector<uint16_t> xb(xf.size()), wb(wf.size()), bias(N, 0);
+  for (size_t i = 0; i < xf.size(); ++i) xb[i] = bf16_rne(xf[i]);
+  for (size_t i = 0; i < wf.size(); ++i) wb[i] = bf16_rne(wf[i]);
+  float xmax = 0.f, wmax = 0.f;
+  for (float e : xf) xmax = std::fmax(xmax, std::fabs(e));
+  for (float e : wf) wmax = std::fmax(wmax, std::fabs(e));
+  const float sx = xmax / 448.f, sw = wmax / 448.f;
+  std::vector<uint8_t> x8(xf.size()), w8(wf.size());
+  for (size_t i = 0; i < xf.size(); ++i) x8[i] = e4m3_code(xf[i] / sx);
+  for (size_t i = 0; i < wf.size(); ++i) w8[i] = e4m3_code(wf[i] / sw);
+  const std::vector<int32_t> pos = workload_positions(S);
+  void *dx, *dw, *dx8, *dw8, *db, *dq, *dk, *dv;
+  int32_t* dpos;
+  CHECK_HIP(hipMalloc(&dx, xb.size() * 2));
+  CHECK_HIP(hipMalloc(&dw, wb.size() * 2));
+  CHECK_HIP(hipMalloc(&dx8, x8.size()));
+  CHECK_HIP(hipMalloc(&dw8, w8.size()));
+  CHECK_HIP(hipMalloc(&db, bias.size() * 2));
+  CHECK_HIP(hipMalloc(&dpos, pos.size() * 4));
+  CHECK_HIP(hipMalloc(&dq, (size_t)M * C * 2));
+  CHECK_HIP(hipMalloc(&dk, (size_t)M * C * 2));
+  CHECK_HIP(hipMalloc(&dv, (size_t)M * C * 2));
+  CHECK_HIP(hipMemcpy(dx, xb.data(), xb.size() * 2, hipMemcpyHostToDevice));
+  CHECK_HIP(hipMemcpy(dw, wb.data(), wb.size() * 2, hipMemcpyHostToDevice));
+  CHECK_HIP(hipMemcpy(dx8, x8.data(), x8.size(), hipMemcpyHostToDevice));
+  CHECK_HIP(hipMemcpy(dw8, w8.data(), w8.size(), hipMemcpyHostToDevice));
+  CHECK_HIP(hipMemcpy(db, bias.data(), bias.size() * 2, hipMemcpyHostToDevice));
+  CHECK_HIP(hipMemcpy(dpos, pos.data(), pos.size() * 4, hipMemcpyHostToDevice));
+  const long long wgs = klein::qkv_rope_proj_grid(B, S, H, D);
+  const size_t nclk = (size_t)wgs * 8 * 8;
+  unsigned long long* clk;
+  CHECK_HIP(hipMalloc(&clk, nclk * 8));
+  CHECK_HIP(hipMemcpyToSymbol(HIP_SYMBOL(klein::klein_qkv_clock_out), &clk, sizeof(clk)));
+  for (int fp8 = 0; fp8 < 2; ++fp8) {
+    auto call = [&]() {
+      const klein_status_t r =
+          fp8 ? klein_qkv_rope4d_proj_fp8(dx8, dw8, db, dpos, dq, dk, dv, B, S, C, H, D, sx, sw, nullptr)
+              : klein_qkv_rope4d_proj(dx, dw, db, dpos, dq, dk, dv, B, S, C, H, D, nullptr);
+      if (r != KLEIN_OK) {
+        std::fprintf(stderr, "call failed: %s\n", klein_status_string(r));
+        std::exit(1);
+      }
+    };
+    CHECK_HIP(hipMemset(clk, 0, nclk * 8));
+    for (int i = 0; i < 10; ++i) call();
+    hipEvent_t e0, e1;
+    CHECK_HIP(hipEventCreate(&e0));
+    CHECK_HIP(hipEventCreate(&e1));
+    CHECK_HIP(hipEventRecord(e0, nullptr));
+    for (int i = 0; i < reps; ++i) call();
+    CHECK_HIP(hipEventRecord(e1, nullptr));
+    CHECK_HIP(hipEventSynchronize(e1));
+    float ms = 0.f;
+    CHECK_HIP(hipEventElapsedTime(&ms, e0, e1));
+    ms /= reps;
+    std::vector<unsigned long long> c(nclk);
+    CHECK_HIP(hipMemcpy(c.data(), clk, nclk * 8, hipMemcpyDeviceToHost));
+    const int ksub = fp8 ? 2 : 4;
+    double sum[2][5] = {}, steps[2] = {0.0, 0.0};
+    for (long long wg = 0; wg < wgs; ++wg)
+      for (int w = 0; w < 8; ++w) {
+        const unsigned long long* r = &c[((size_t)wg * 8 + w) * 8];
+        for (int i = 0; i < 5; ++i) sum[w >= 4][i] += (double)r[i];
+        steps[w >= 4] += (double)r[5];
+      }
+    std::printf("\n%s operands: M=%d N=%d K=%d, %lld workgroups; cycles per K step of one wave\n\n",
+                fp8 ? "FP8 (E4M3)" : "bf16", M, N, C, wgs);
+    std::printf("| part of the K step | waves 0-3 | waves 4-7 |\n|---|---|---|\n");
+    double tot[2] = {0.0, 0.0};
+    for (int i = 0; i < 5; ++i) {
+      if (i >= ksub && i < 4) continue;
+      const double a = sum[0][i] / steps[0], b = sum[1][i] / steps[1];
+      tot[0] += a;
+      tot[1] += b;
+      if (i < 4)
+        std::printf("| k-sub-step %d: 8 MFMAs with their staging slots | %.0f | %.0f |\n", i, a, b);
+      else
+        std::printf("| barrier | %.0f | %.0f |\n", a, b);
+    }
+    std::printf("| the K step | %.0f | %.0f |\n", tot[0], tot[1]);
+    const double flops = 2.0 * M * (double)N * C;
+    std::printf("\nMFMA cycles per K step and SIMD: 2048; instrumented call %.4f ms (%.1f TFLOP/s)\n",
+                ms, flops / (ms * 1e-3) / 1e12);
+  }
+  return 0;
+}
+
 int main(int argc, char** argv) {
+  if (argc > 1 && std::strcmp(argv[1], "qkv") == 0) return qkv_main(argc, argv);
   const int B = argc > 1 ? std::atoi(argv[1]) : 2;
   const int S = argc > 2 ? std::atoi(argv[2]) : 16896;
   const int H = argc > 3 ? std::atoi(argv[3]) : 24;
@@ -68,18 +222,7 @@ int main(int argc, char** argv) {
     CHECK_HIP(hipMalloc(&dev[t], n * 2));
     CHECK_HIP(hipMemcpy(dev[t], host.data(), n * 2, hipMemcpyHostToDevice));
   }
-  const int text = S >= 512 ? 512 : 0;
-  const int grid = (int)std::lround(std::sqrt((double)(S - text)));
-  std::vector<int32_t> pos((size_t)S * 4, 0);
-  for (int s = 0; s < S; ++s) {
-    if (s < text) {
-      pos[4 * s + 3] = s;
-    } else if (grid > 0) {
-      const int i = s - text;
-      pos[4 * s + 1] = (i / grid) % 4096;
-      pos[4 * s + 2] = i % grid;
-    }
-  }
+  const std::vector<int32_t> pos = workload_positions(S);
   int32_t* dpos;
   CHECK_HIP(hipMalloc(&dpos, pos.size() * 4));
   CHECK_HIP(hipMemcpy(dpos, pos.data(), pos.size() * 4, hipMemcpyHostToDevice));
