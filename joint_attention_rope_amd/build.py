@@ -1,6 +1,6 @@
 """Build the gfx950 HIP library libklein_attn.so in-tree with hipcc, and the
-measurement harness step_clock (the bf16 attention kernel and the QKV
-projection with per-part cycle counters, linked with the library's other
+measurement harness step_clock (the bf16 and fp8 attention kernels and the
+QKV projection with per-part cycle counters, linked with the library's other
 objects; not part of the library).
 
 Usage: python -m joint_attention_rope_amd.build
@@ -15,9 +15,9 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libklein_attn.so")
 STEP_CLOCK = os.path.join(PKG, "step_clock")
 # the harness replaces these sources (it includes them with the cycle counters
-# on; it is compiled with the first one's flags, which leave the second's
-# instructions unchanged)
-STEP_CLOCK_REPLACES = ("attn_fwd_bf16.hip", "qkv_rope_proj.hip")
+# on; it is compiled with the attention kernels' flags, which leave the
+# projection's instructions unchanged)
+STEP_CLOCK_REPLACES = ("attn_fwd_bf16.hip", "attn_fwd_fp8.hip", "qkv_rope_proj.hip")
 SOURCES = ["api.cpp", "attn_fwd_bf16.hip", "attn_fwd_fp8.hip", "qkv_rope_proj.hip", "rope_apply.hip",
            "split_schedule.hip", "attn_bwd.hip", "noalloc.hip"]
 # Device kernels never see NaN inputs on purpose (a NaN in q/k/v propagates to

@@ -79,10 +79,46 @@
 
 namespace klein {
 
+// Per-region cycle counts of the pipeline step, for a measurement build
+// only: defined by the step_clock.hip harness, never by the library.  Each
+// wave sums, over its steps, the shader-clock cycles (s_memtime) between
+// marks after the softmax max (with the rare rescale), after region A, after
+// region B, after the buffer loads and after the barrier, and lane 0 writes
+// them, with the step count, the cycles of the whole loop and its
+// fixed-rate timestamps (s_memrealtime), to klein_fp8_clock_out[8 wg +
+// wave][0..9].
+#ifdef KLEIN_STEP_CLOCK
+__device__ unsigned long long* klein_fp8_clock_out;
+#define KLEIN_FP8_CLOCK_START                                                \
+  unsigned long long fclk_sum[6] = {0, 0, 0, 0, 0, 0};                       \
+  const unsigned long long fclk_real0 = __builtin_amdgcn_s_memrealtime();    \
+  unsigned long long fclk_prev = __builtin_amdgcn_s_memtime();               \
+  const unsigned long long fclk_start = fclk_prev;
+#define KLEIN_FP8_CLOCK_MARK(i)                                              \
+  do {                                                                       \
+    const unsigned long long fclk_now = __builtin_amdgcn_s_memtime();        \
+    fclk_sum[i] += fclk_now - fclk_prev;                                     \
+    fclk_prev = fclk_now;                                                    \
+  } while (0)
+#define KLEIN_FP8_CLOCK_STORE(nsteps)                                        \
+  if (klein_fp8_clock_out != nullptr && lane == 0) {                         \
+    unsigned long long* co = klein_fp8_clock_out + ((size_t)blockIdx.x * 8 + wave) * 10; \
+    for (int i = 0; i < 6; ++i) co[i] = fclk_sum[i];                         \
+    co[6] = (unsigned long long)(nsteps);                                    \
+    co[7] = fclk_prev - fclk_start;                                          \
+    co[8] = fclk_real0;                                                      \
+    co[9] = __builtin_amdgcn_s_memrealtime();                                \
+  }
+#else
+#define KLEIN_FP8_CLOCK_START
+#define KLEIN_FP8_CLOCK_MARK(i) do {} while (0)
+#define KLEIN_FP8_CLOCK_STORE(nsteps)
+#endif
+
 namespace {
 
 constexpr float kHalf = 0.5f;
-constexpr int kTabN = 1024;       // positions covered by the cos/sin table
+constexpr int kFp8TabN = 1024;       // positions covered by the cos/sin table
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef short s2_t __attribute__((ext_vector_type(2)));
@@ -151,7 +187,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   constexpr int NJ = D / 8;            // rotation pairs per axis
   constexpr int TROW = NJ + 2;         // cos/sin table row stride (half2)
   constexpr int TSLOT = 10;            // per-thread fallback slot stride
-  constexpr int TAB = kTabN * TROW;    // start of the fallback slots
+  constexpr int TAB = kFp8TabN * TROW;    // start of the fallback slots
   constexpr float YM = 118.0f;         // code of a score equal to the first running max
   constexpr float YR = 110.0f;         // code of the running max after a raise
   constexpr float YMAX = 126.0f;       // largest finite E4M3 code (448)
@@ -161,7 +197,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
 
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][BN * KROW];
   __shared__ __attribute__((aligned(16))) uint8_t v_lds[2][BN * VROW];
-  // fp16 (cos, sin) / 2: table rows for positions [0, kTabN), then 8
+  // fp16 (cos, sin) / 2: table rows for positions [0, kFp8TabN), then 8
   // per-thread slots.  Row and slot strides of 2 (mod 4) dwords spread 32
   // rows over all banks and keep pairs of entries 8-byte aligned.
   __shared__ __attribute__((aligned(16))) h2_t cs_tab[TAB + TSLOT * NT];
@@ -192,7 +228,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
 
   // ---- cos/sin table: entry p * TROW + j = (cos, sin)(p w_j) / 2
   if constexpr (!KPRE) {
-    for (int e = tid; e < kTabN * NJ; e += NT) {
+    for (int e = tid; e < kFp8TabN * NJ; e += NT) {
       const int j = e % NJ, p = e / NJ;
       const float2 c = rope_cs(p, fr.hi[j], fr.lo[j], kHalf);
       cs_tab[p * TROW + j] = (h2_t){(_Float16)c.x, (_Float16)c.y};
@@ -291,7 +327,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   // divergent and skipped by waves whose positions all lie in the table.
   auto key_cs_index = [&](int kp) {
     if constexpr (KPRE) return 0;
-    const bool oob = kst && (unsigned)kp >= (unsigned)kTabN;
+    const bool oob = kst && (unsigned)kp >= (unsigned)kFp8TabN;
     if (oob) {
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
@@ -527,16 +563,22 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   // the positions of K(t+2) and receives those of K(t+4).  The only branches
   // (rare rescale, rare rotation fallback) come first, so that regions A and
   // B form one block whose interleaving the compiler keeps.
+  KLEIN_FP8_CLOCK_START
   auto step = [&](int t, f32x16_t* cur, f32x16_t* nxt, int& kps) {
     const int ci = key_cs_index(kps);
     softmax_max(tl(t), cur);
+    KLEIN_FP8_CLOCK_MARK(0);
     region_a((t + 1) & 1, cur, nxt, pb);
+    KLEIN_FP8_CLOCK_MARK(1);
     // K''(t+2) into buffer t&1 (it held K''(t)); V(t+1) into buffer (t+1)&1
     region_b(t & 1, t & 1, (t + 1) & 1, pb, ci);
+    KLEIN_FP8_CLOCK_MARK(2);
     load_k(tl(t + 3));
     load_pos(tl(t + 4), kps);
     load_v(tl(t + 2));
+    KLEIN_FP8_CLOCK_MARK(3);
     __syncthreads();
+    KLEIN_FP8_CLOCK_MARK(4);
   };
   int t = 0;
   for (; t + 1 < nsteps; t += 2) {
@@ -544,6 +586,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
     step(t + 1, sb, sa, kpos1);
   }
   if (t < nsteps) step(t, sa, sb, kpos0);
+  KLEIN_FP8_CLOCK_STORE(nsteps)
 
   // ---- epilogue: O * dv / l -> bf16; a chunk of a split item stores its
   // partial instead (the merge kernel writes those rows)

@@ -2,13 +2,14 @@
 // bf16 attention kernel's pipeline step, and of the QKV projection's K
 // step, go.
 //
-// This file compiles attn_fwd_bf16.hip and qkv_rope_proj.hip with
-// KLEIN_STEP_CLOCK defined, which makes every wave sum the shader-clock
-// cycles (s_memtime) spent between marks.  In the attention kernel's step:
-// the step start (key positions, tail mask), region A (the score MFMAs of
-// the next tile with the softmax of this one), the rescale check, region B
-// (the P.V MFMAs with the staging of later tiles), the buffer loads, and the
-// barrier.  In the projection's K step: each k-sub-step (8 MFMAs with the
+// This file compiles attn_fwd_bf16.hip, attn_fwd_fp8.hip and
+// qkv_rope_proj.hip with KLEIN_STEP_CLOCK defined, which makes every wave
+// sum the shader-clock cycles (s_memtime) spent between marks.  In the bf16
+// attention kernel's step: the step start (key positions, tail mask), region
+// A (the score MFMAs of the next tile with the softmax of this one), the
+// rescale check, region B (the P.V MFMAs with the staging of later tiles),
+// the buffer loads, and the barrier.  In the fp8 kernel's step: the softmax
+// max with the rare rescale, region A, region B, the loads and the barrier.  In the projection's K step: each k-sub-step (8 MFMAs with the
 // staging loads and stores placed among them) and the barrier.  The harness
 // is linked with the library's other objects (everything but those two
 // sources), so the public entry points klein_rope4d_attn_fwd_ws and
@@ -19,6 +20,9 @@
 // Usage: step_clock [B S H D reps]        the attention (default: the
 //                                         2048x2048 CFG workload, B=2,
 //                                         S=16896, H=24, D=128)
+//        step_clock fp8 [reps]            the FP8 attention on the 2048x2048
+//                                         edit workload (B=1, S=33280:
+//                                         512 text + image + reference)
 //        step_clock qkv [B S H D reps]    the projection (C = H D), bf16
 //                                         then fp8 operands
 // Inputs are seeded N(0, 1) (W scaled by 1/sqrt(C)); positions follow the
@@ -31,6 +35,7 @@
 // workgroups.
 #define KLEIN_STEP_CLOCK 1
 #include "attn_fwd_bf16.hip"
+#include "attn_fwd_fp8.hip"
 #include "qkv_rope_proj.hip"
 
 #include <cmath>
@@ -92,6 +97,123 @@ static uint8_t e4m3_code(float x) {
   }
   if (c > 126) c = 126;
   return (uint8_t)(c | (x < 0.f ? 0x80 : 0));
+}
+
+static int fp8_main(int argc, char** argv) {
+  const int B = 1, H = 24, D = 128, text = 512, grid = 128;
+  const int S = text + 2 * grid * grid;
+  const int reps = argc > 2 ? std::atoi(argv[2]) : 5;
+  const size_t n = (size_t)B * S * H * D;
+  uint64_t st = 20240612ull;
+  auto gauss = [&]() {
+    auto uni = [&]() {
+      st = st * 6364136223846793005ull + 1442695040888963407ull;
+      return ((st >> 11) + 0.5) * (1.0 / 9007199254740992.0);
+    };
+    return (float)(std::sqrt(-2.0 * std::log(uni())) * std::cos(6.283185307179586 * uni()));
+  };
+  // seeded N(0, 1) values as E4M3 codes with per-tensor descales max|x| / 448
+  std::vector<float> f(n);
+  std::vector<uint8_t> codes(n);
+  uint8_t* dev[3];
+  float descale[3];
+  for (int t = 0; t < 3; ++t) {
+    float mx = 0.f;
+    for (auto& e : f) {
+      e = gauss();
+      mx = std::fmax(mx, std::fabs(e));
+    }
+    descale[t] = mx / 448.f;
+    for (size_t i = 0; i < n; ++i) codes[i] = e4m3_code(f[i] / descale[t]);
+    CHECK_HIP(hipMalloc(&dev[t], n));
+    CHECK_HIP(hipMemcpy(dev[t], codes.data(), n, hipMemcpyHostToDevice));
+  }
+  // text on the l axis; the image at t = 0 and the reference at t = 1 share
+  // the (h, w) grid
+  std::vector<int32_t> pos((size_t)S * 4, 0);
+  for (int s = 0; s < S; ++s) {
+    if (s < text) {
+      pos[4 * s + 3] = s;
+    } else {
+      const int i = (s - text) % (grid * grid);
+      pos[4 * s + 0] = (s - text) / (grid * grid);
+      pos[4 * s + 1] = i / grid;
+      pos[4 * s + 2] = i % grid;
+    }
+  }
+  int32_t* dpos;
+  CHECK_HIP(hipMalloc(&dpos, pos.size() * 4));
+  CHECK_HIP(hipMemcpy(dpos, pos.data(), pos.size() * 4, hipMemcpyHostToDevice));
+  uint16_t* out;
+  CHECK_HIP(hipMalloc(&out, n * 2));
+  size_t wsb = 0;
+  if (klein_attn_workspace_size(B, S, H, D, KLEIN_DTYPE_FP8_E4M3, &wsb) != KLEIN_OK) return 1;
+  void* ws = nullptr;
+  CHECK_HIP(hipMalloc(&ws, wsb > 0 ? wsb : 256));
+  int dev_id = 0, ncu = 0;
+  CHECK_HIP(hipGetDevice(&dev_id));
+  CHECK_HIP(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev_id));
+  int plan[3];
+  size_t part = 0;
+  if (klein_splitkv_plan(B, S, H, D, ncu, plan, &part) != KLEIN_OK) return 1;
+  const int whole = plan[0], wgs = plan[0] + plan[1] * plan[2];
+  auto call = [&]() {
+    const klein_status_t r = klein_rope4d_attn_fwd_ws(dev[0], dev[1], dev[2], dpos, out, B, S, H, D,
+                                                      KLEIN_DTYPE_FP8_E4M3, descale[0], descale[1],
+                                                      descale[2], ws, wsb, nullptr);
+    if (r != KLEIN_OK) {
+      std::fprintf(stderr, "call failed: %s\n", klein_status_string(r));
+      std::exit(1);
+    }
+  };
+  unsigned long long* clk;
+  const size_t nclk = (size_t)wgs * 8 * 10;
+  CHECK_HIP(hipMalloc(&clk, nclk * 8));
+  CHECK_HIP(hipMemset(clk, 0, nclk * 8));
+  CHECK_HIP(hipMemcpyToSymbol(HIP_SYMBOL(klein::klein_fp8_clock_out), &clk, sizeof(clk)));
+  for (int i = 0; i < 2; ++i) call();
+  hipEvent_t e0, e1;
+  CHECK_HIP(hipEventCreate(&e0));
+  CHECK_HIP(hipEventCreate(&e1));
+  CHECK_HIP(hipEventRecord(e0, nullptr));
+  for (int i = 0; i < reps; ++i) call();
+  CHECK_HIP(hipEventRecord(e1, nullptr));
+  CHECK_HIP(hipEventSynchronize(e1));
+  float ms = 0.f;
+  CHECK_HIP(hipEventElapsedTime(&ms, e0, e1));
+  ms /= reps;
+  std::vector<unsigned long long> c(nclk);
+  CHECK_HIP(hipMemcpy(c.data(), clk, nclk * 8, hipMemcpyDeviceToHost));
+  double sum[2][7] = {}, realt = 0.0, cyc = 0.0;
+  for (int wg = 0; wg < whole; ++wg)
+    for (int w = 0; w < 8; ++w) {
+      const unsigned long long* r = &c[((size_t)wg * 8 + w) * 10];
+      for (int i = 0; i < 7; ++i) sum[w >= 4][i] += (double)r[i];
+      cyc += (double)r[7];
+      realt += (double)(r[9] - r[8]);
+    }
+  const char* names[5] = {"step start and softmax max (with the rare rescale)",
+                          "region A: Y(t+1) MFMAs with the P8 codes of Y(t)",
+                          "region B: O += V P8 and row-sum MFMAs with the staging of K'', V",
+                          "buffer loads of later tiles", "barrier"};
+  std::printf("| part of the step | waves 0-3: cycles per step | waves 4-7: cycles per step |\n");
+  std::printf("|---|---|---|\n");
+  double tot[2] = {0.0, 0.0};
+  for (int i = 0; i < 5; ++i) {
+    const double a = sum[0][i] / sum[0][6], b = sum[1][i] / sum[1][6];
+    tot[0] += a;
+    tot[1] += b;
+    std::printf("| %s | %.0f | %.0f |\n", names[i], a, b);
+  }
+  std::printf("| the step | %.0f | %.0f |\n", tot[0], tot[1]);
+  const double mhz = cyc / (realt * 1e-8) / 1e6;
+  const double flops = 4.0 * B * H * (double)S * S * D;
+  std::printf("\nB=%d S=%d H=%d D=%d fp8: whole-tile workgroups %d of %d; steps per wave %.0f; "
+              "MFMA cycles per step and SIMD (two waves x 8 MFMAs x 64 cycles, plus two row-sum "
+              "MFMAs of 32 cycles) 1,088; clock %.0f MHz (s_memtime over s_memrealtime); instrumented call %.4f "
+              "ms (%.1f TFLOP/s)\n",
+              B, S, H, D, whole, wgs, sum[0][6] / (4.0 * whole), mhz, ms, flops / (ms * 1e-3) / 1e12);
+  return 0;
 }
 
 static int qkv_main(int argc, char** argv) {
@@ -201,6 +323,7 @@ static int qkv_main(int argc, char** argv) {
 
 int main(int argc, char** argv) {
   if (argc > 1 && std::strcmp(argv[1], "qkv") == 0) return qkv_main(argc, argv);
+  if (argc > 1 && std::strcmp(argv[1], "fp8") == 0) return fp8_main(argc, argv);
   const int B = argc > 1 ? std::atoi(argv[1]) : 2;
   const int S = argc > 2 ? std::atoi(argv[2]) : 16896;
   const int H = argc > 3 ? std::atoi(argv[3]) : 24;
