@@ -23,8 +23,10 @@
 // are double-buffered in LDS (rows padded to 144 bytes, so the 16 rows one
 // 16-lane read phase touches fall on distinct banks) and staged through
 // registers, two K steps ahead (bf16) or one (fp8), with the loads and the
-// stores spread between the MFMAs; one barrier per K step.  Rows past N or M
-// read as zeros through the buffer descriptors and are not stored.
+// stores spread between the MFMAs; one barrier per K step, which bf16 places
+// before the step's last sub-step so that the reads of the next buffer
+// overlap MFMAs.  Rows past N or M read as zeros through the buffer
+// descriptors and are not stored.
 #include "klein_device.hpp"
 #include "klein_launch.hpp"
 
@@ -178,44 +180,69 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
   // bf16: staging slot j of K step kt stores chunk j of step kt+1 (loaded a
   // step earlier) into the other buffer (last read before the previous
   // barrier) and reloads its registers with chunk j of step kt+2.  The slots
-  // sit after every fourth MFMA, so a step's loads and stores spread over
-  // it: issued together at the top, the 64 KB of loads of all 8 waves fill
-  // the vector memory queue and hold the waves at issue for 500-1000 cycles
-  // of a ~3,500-cycle step.
+  // spread a step's loads and stores over it: issued together at the top,
+  // the 64 KB of loads of all 8 waves fill the vector memory queue and hold
+  // the waves at issue for 500-1000 cycles of a ~3,500-cycle step.
   //
   // fp8 (operands twice as wide: a register set held across the whole step
   // would spill): one load of step kt+1 after each MFMA of the first
   // sub-step, one store of it after each MFMA of the second.
   KLEIN_QKV_CLOCK_START
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    read_ops(buf, 0, 0);
+  if constexpr (FP8) {
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      read_ops(buf, 0, 0);
 #pragma unroll
-    for (int ks = 0; ks < KSUB; ++ks) {
-      if (ks + 1 < KSUB) read_ops(buf, ks + 1, (ks + 1) & 1);
+      for (int ks = 0; ks < KSUB; ++ks) {
+        if (ks + 1 < KSUB) read_ops(buf, ks + 1, (ks + 1) & 1);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int nb = i >> 1, mb = i & 1;
-        acc[nb][mb] = mfma(av[ks & 1][nb], bv[ks & 1][mb], acc[nb][mb]);
-        if constexpr (FP8) {
+        for (int i = 0; i < 8; ++i) {
+          const int nb = i >> 1, mb = i & 1;
+          acc[nb][mb] = mfma(av[ks & 1][nb], bv[ks & 1][mb], acc[nb][mb]);
           static_assert(!FP8 || KSUB == 2, "one k-step of loads, one of stores");
           if (ks == 0) load_one(kt + 1, i);
           else store_one(buf ^ 1, i);
           __builtin_amdgcn_sched_barrier(0);
+        }
+        KLEIN_QKV_CLOCK_MARK(ks);
+      }
+      __syncthreads();
+      KLEIN_QKV_CLOCK_MARK(4);
+    }
+  } else {
+    // bf16: the 8 staging slots of step kt sit in its first three
+    // sub-steps (3, 3, 2); the barrier comes before the last sub-step, whose
+    // operands are already in registers, and the operands of the next
+    // step's first sub-step are read while its MFMAs run
+    static_assert(KSUB == 4 && NLD == 8, "slot layout");
+    read_ops(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+#pragma unroll
+      for (int ks = 0; ks < KSUB; ++ks) {
+        if (ks == KSUB - 1) {
+          __syncthreads();
+          KLEIN_QKV_CLOCK_MARK(4);
+          read_ops(buf ^ 1, 0, 0);
         } else {
-          constexpr int PER = NLD / KSUB;            // staging slots per k-step
-          if ((i * PER) % 8 < PER) {
-            const int j = PER * ks + i * PER / 8;
+          read_ops(buf, ks + 1, (ks + 1) & 1);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int nb = i >> 1, mb = i & 1;
+          acc[nb][mb] = mfma(av[ks & 1][nb], bv[ks & 1][mb], acc[nb][mb]);
+          // slots after MFMAs 0, 3, 6 of sub-steps 0 and 1, 0 and 4 of sub-step 2
+          const bool slot = ks < 2 ? (i % 3 == 0) : (ks == 2 && i % 4 == 0);
+          if (slot) {
+            const int j = ks < 2 ? 3 * ks + i / 3 : 6 + i / 4;
             store_one(buf ^ 1, j);
             load_one(kt + 2, j);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+        KLEIN_QKV_CLOCK_MARK(ks);
       }
-      KLEIN_QKV_CLOCK_MARK(ks);
     }
-    __syncthreads();
-    KLEIN_QKV_CLOCK_MARK(4);
   }
   KLEIN_QKV_CLOCK_STORE(nk)
 
