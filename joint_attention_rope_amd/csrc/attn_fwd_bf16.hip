@@ -11,9 +11,11 @@
 //                P(t) = 2^(S(t) - m), row sums, bf16 pack   (VALU)
 //     rare rescale of O, l and P(t) when P(t) came out too large
 //     region B:  O^T += V(t)^T P(t)^T  (16 MFMAs)        interleaved with
-//                staging K'(t+2) (RoPE-4D) and V(t+1)^T into LDS, and the
-//                buffer loads of K(t+3), V(t+2) from HBM
-//     barrier
+//                staging K'(t+2) (RoPE-4D) and V(t+1)^T into LDS; before
+//                its last two MFMAs (operands already in registers) the
+//                buffer loads of K(t+3), V(t+2) from HBM, the barrier, and
+//                the reads of region A's first K'(t+2) operands, which the
+//                two MFMAs then cover
 //
 // Each wave overlaps its own MFMAs with its own VALU work, and both waves of
 // a SIMD issue VALU: measured on this chip, one wave alone issues VALU at
@@ -396,7 +398,14 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   // Returns this lane's sum of P(t).
   constexpr int NA = 2 * KS;                 // MFMAs in region A
   constexpr int SA = 16;                     // softmax slices (2 scores each)
-  auto region_a = [&](int kbuf, const f32x16_t* cur, f32x16_t* nxt, uint32_t (*pw)[8]) {
+  // the K' operand of region A's MFMA i (the first two are read ahead of the
+  // region, right after the barrier that completes the buffer)
+  auto read_k_op = [&](int kbuf, int i) {
+    const int kbk = i / KS, ks = i % KS;
+    return *reinterpret_cast<const f16x8_t*>(&k_lds[kbuf][(32 * kbk + lr) * KROW + 16 * ks + 8 * g]);
+  };
+  auto region_a = [&](int kbuf, const f32x16_t* cur, f32x16_t* nxt, uint32_t (*pw)[8],
+                      const f16x8_t* pre) {
     f16x8_t ka[NA];
     auto read_k = [&](int i) {
       const int kbk = i / KS, ks = i % KS;
@@ -405,8 +414,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     };
     nxt[0] = cinit;
     nxt[1] = cinit;
-    read_k(0);
-    read_k(1);
+    ka[0] = pre[0];
+    ka[1] = pre[1];
     float ls4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
@@ -436,7 +445,12 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   constexpr int NROT = KPRE ? KPT : 4 * KPT;   // RoPE pairs (or K chunks) to stage
   constexpr int NVW = KPT;                   // V chunks to stage
   constexpr int NIT = NROT + NVW;
-  auto region_b = [&](int vbuf, int kdst, int vdst, const uint32_t (*pw)[8], const int* ci) {
+  // `mid` runs before the last two MFMAs (the loads of later tiles, the
+  // barrier, the reads ahead of the next region A); the staging items all
+  // sit in the MFMA slots before it
+  constexpr int NBS = NB - 2;
+  auto region_b = [&](int vbuf, int kdst, int vdst, const uint32_t (*pw)[8], const int* ci,
+                      auto&& mid) {
     float2 kcs[NROT];
     auto read_cs = [&](int item) {
       if constexpr (!KPRE)
@@ -462,6 +476,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     u32x4_t ky;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
+      if (i == NBS) mid();
       if (i + 2 < NB) read_v(i + 2);
       const int mb = i / 4, kbk = (i >> 1) & 1, j = i & 1;
       const u32x4_t pvw = {pw[kbk][4 * j], pw[kbk][4 * j + 1], pw[kbk][4 * j + 2],
@@ -469,7 +484,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
       o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], __builtin_bit_cast(bf16x8_t, pvw),
                                                       o[mb], 0, 0, 0);
 #pragma unroll
-      for (int item = i * NIT / NB; item < (i + 1) * NIT / NB; ++item) {
+      for (int item = i * NIT / NBS; item < (i < NBS ? (i + 1) * NIT / NBS : 0); ++item) {
         read_cs(item + 2);
         if (KPRE && item < NROT) {
           // one pre-rotated K chunk, copied
@@ -553,27 +568,35 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   // `kps` holds the positions of K(t+2) and receives those of K(t+4).  The
   // rare branches (rotation fallback, rescale) sit between the regions.
   KLEIN_CLOCK_START
+  f16x8_t kpre[2] = {read_k_op(1, 0), read_k_op(1, 1)};
   auto step = [&](int t, f32x16_t* cur, f32x16_t* nxt, int* kps) {
     int ci[KPT];
 #pragma unroll
     for (int it = 0; it < KPT; ++it) ci[it] = key_cs_index(kps, it);
     mask_tail(tl(t), cur);
     KLEIN_CLOCK_MARK(0);
-    float lt = region_a((t + 1) & 1, cur, nxt, pw);
+    float lt = region_a((t + 1) & 1, cur, nxt, pw, kpre);
     KLEIN_CLOCK_MARK(1);
     if (__builtin_amdgcn_ballot_w64(lt > kSumLimit)) lt = rescale(cur, nxt, pw);
     l_run += lt;
     KLEIN_CLOCK_MARK(2);
     // K(t+2) into buffer t&1 (it held K(t), consumed last step); V(t+1) into
-    // buffer (t+1)&1 (it held V(t-1), consumed last step)
-    region_b(t & 1, t & 1, (t + 1) & 1, pw, ci);
+    // buffer (t+1)&1 (it held V(t-1), consumed last step).  The barrier comes
+    // before region B's last two MFMAs, whose V operands are already in
+    // registers, and the next region A's first K(t+2) operands are read
+    // while they run.
+    region_b(t & 1, t & 1, (t + 1) & 1, pw, ci, [&]() {
+      KLEIN_CLOCK_MARK(3);
+      load_k(tl(t + 3));
+      load_pos(tl(t + 4), kps);
+      load_v(tl(t + 2));
+      KLEIN_CLOCK_MARK(4);
+      __syncthreads();
+      KLEIN_CLOCK_MARK(5);
+      kpre[0] = read_k_op(t & 1, 0);
+      kpre[1] = read_k_op(t & 1, 1);
+    });
     KLEIN_CLOCK_MARK(3);
-    load_k(tl(t + 3));
-    load_pos(tl(t + 4), kps);
-    load_v(tl(t + 2));
-    KLEIN_CLOCK_MARK(4);
-    __syncthreads();
-    KLEIN_CLOCK_MARK(5);
   };
   int t = 0;
   for (; t + 1 < nsteps; t += 2) {
