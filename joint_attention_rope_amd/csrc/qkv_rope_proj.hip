@@ -36,10 +36,13 @@ namespace klein {
 // by the step_clock.hip harness, never by the library.  Each wave sums, over
 // its K steps, the shader-clock cycles (s_memtime) of each k-sub-step (with
 // the staging slots in it) and of the barrier, and lane 0 writes them, with
-// the K-step count and the cycles of the whole loop, to
-// klein_qkv_clock_out[8 wg + wave][0..7].
+// the K-step count, the cycles of the whole loop, of the prologue before it
+// and of the epilogue after it, to klein_qkv_clock_out[10 (8 wg + wave) +
+// 0..8].
 #ifdef KLEIN_STEP_CLOCK
 __device__ unsigned long long* klein_qkv_clock_out;
+#define KLEIN_QKV_CLOCK_ENTRY                                                \
+  const unsigned long long qclk_entry = __builtin_amdgcn_s_memtime();
 #define KLEIN_QKV_CLOCK_START                                                \
   unsigned long long qclk_sum[5] = {0, 0, 0, 0, 0};                          \
   unsigned long long qclk_prev = __builtin_amdgcn_s_memtime();               \
@@ -52,13 +55,15 @@ __device__ unsigned long long* klein_qkv_clock_out;
   } while (0)
 #define KLEIN_QKV_CLOCK_STORE(nk)                                            \
   if (klein_qkv_clock_out != nullptr && lane == 0) {                         \
-    unsigned long long* co = klein_qkv_clock_out + ((size_t)blockIdx.x * 8 + wave) * 8; \
+    unsigned long long* co = klein_qkv_clock_out + ((size_t)blockIdx.x * 8 + wave) * 10; \
     for (int i = 0; i < 5; ++i) co[i] = qclk_sum[i];                         \
     co[5] = (unsigned long long)(nk);                                        \
     co[6] = qclk_prev - qclk_start;                                          \
-    co[7] = 0;                                                               \
+    co[7] = qclk_start - qclk_entry;                                         \
+    co[8] = __builtin_amdgcn_s_memtime() - qclk_prev;                        \
   }
 #else
+#define KLEIN_QKV_CLOCK_ENTRY
 #define KLEIN_QKV_CLOCK_START
 #define KLEIN_QKV_CLOCK_MARK(i) do {} while (0)
 #define KLEIN_QKV_CLOCK_STORE(nk)
@@ -83,6 +88,7 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][TN * ROW];
   __shared__ __attribute__((aligned(16))) uint16_t b_lds[2][TM * ROW];
 
+  KLEIN_QKV_CLOCK_ENTRY
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lr = lane & 31;
   const int wn = wave & 1, wm = wave >> 1;     // 2 x 4 waves: 128 features x 64 tokens
@@ -244,7 +250,6 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
       }
     }
   }
-  KLEIN_QKV_CLOCK_STORE(nk)
 
   // ---- epilogue: lane column = token m, registers 4c..4c+3 = features
   // n0 + 128 wn + 32 nb + 8 c + 4 g + 0..3
@@ -289,6 +294,7 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
         }
       }
   }
+  KLEIN_QKV_CLOCK_STORE(nk)
 }
 
 template <bool FP8>

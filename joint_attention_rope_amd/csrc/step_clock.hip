@@ -263,7 +263,7 @@ static int qkv_main(int argc, char** argv) {
   CHECK_HIP(hipMemcpy(db, bias.data(), bias.size() * 2, hipMemcpyHostToDevice));
   CHECK_HIP(hipMemcpy(dpos, pos.data(), pos.size() * 4, hipMemcpyHostToDevice));
   const long long wgs = klein::qkv_rope_proj_grid(B, S, H, D);
-  const size_t nclk = (size_t)wgs * 8 * 8;
+  const size_t nclk = (size_t)wgs * 8 * 10;
   unsigned long long* clk;
   CHECK_HIP(hipMalloc(&clk, nclk * 8));
   CHECK_HIP(hipMemcpyToSymbol(HIP_SYMBOL(klein::klein_qkv_clock_out), &clk, sizeof(clk)));
@@ -292,12 +292,16 @@ static int qkv_main(int argc, char** argv) {
     std::vector<unsigned long long> c(nclk);
     CHECK_HIP(hipMemcpy(c.data(), clk, nclk * 8, hipMemcpyDeviceToHost));
     const int ksub = fp8 ? 2 : 4;
-    double sum[2][5] = {}, steps[2] = {0.0, 0.0};
+    double sum[2][5] = {}, steps[2] = {0.0, 0.0}, loop[2] = {0.0, 0.0}, pro[2] = {0.0, 0.0},
+           epi[2] = {0.0, 0.0};
     for (long long wg = 0; wg < wgs; ++wg)
       for (int w = 0; w < 8; ++w) {
-        const unsigned long long* r = &c[((size_t)wg * 8 + w) * 8];
+        const unsigned long long* r = &c[((size_t)wg * 8 + w) * 10];
         for (int i = 0; i < 5; ++i) sum[w >= 4][i] += (double)r[i];
         steps[w >= 4] += (double)r[5];
+        loop[w >= 4] += (double)r[6];
+        pro[w >= 4] += (double)r[7];
+        epi[w >= 4] += (double)r[8];
       }
     std::printf("\n%s operands: M=%d N=%d K=%d, %lld workgroups; cycles per K step of one wave\n\n",
                 fp8 ? "FP8 (E4M3)" : "bf16", M, N, C, wgs);
@@ -314,6 +318,11 @@ static int qkv_main(int argc, char** argv) {
         std::printf("| barrier | %.0f | %.0f |\n", a, b);
     }
     std::printf("| the K step | %.0f | %.0f |\n", tot[0], tot[1]);
+    const double nw = 4.0 * (double)wgs;
+    std::printf("\nPer workgroup and wave, cycles: prologue (entry to the first K step) %.0f / %.0f, "
+                "K loop %.0f / %.0f, epilogue (bias, RoPE, stores) %.0f / %.0f "
+                "(waves 0-3 / 4-7)\n",
+                pro[0] / nw, pro[1] / nw, loop[0] / nw, loop[1] / nw, epi[0] / nw, epi[1] / nw);
     const double flops = 2.0 * M * (double)N * C;
     std::printf("\nMFMA cycles per K step and SIMD: 2048; instrumented call %.4f ms (%.1f TFLOP/s)\n",
                 ms, flops / (ms * 1e-3) / 1e12);
