@@ -87,6 +87,14 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
 
   __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][TN * ROW];
   __shared__ __attribute__((aligned(16))) uint16_t b_lds[2][TM * ROW];
+  // What the epilogue reads besides the accumulators, loaded in the prologue
+  // (its latency hides behind the first staging loads): the tile's token
+  // positions and bias as fp32, and the RoPE frequencies (hi[16], lo[16]),
+  // which a lane reads with one LDS read instead of selecting between kernel
+  // arguments.
+  __shared__ __attribute__((aligned(16))) float ep_pos[TM][4];
+  __shared__ __attribute__((aligned(16))) float ep_bias[TN];
+  __shared__ __attribute__((aligned(16))) float ep_fr[32];
 
   KLEIN_QKV_CLOCK_ENTRY
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -140,6 +148,21 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
     for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = (f32x16_t){};
 
   const int nk = C * ES / KB;
+  if (tid < TM) {
+    // rows past M take the last token's positions; they are not stored
+    const int4 p = *reinterpret_cast<const int4*>(pos + 4 * (min(m0 + tid, M - 1) % S));
+    *reinterpret_cast<f32x4_t*>(ep_pos[tid]) =
+        (f32x4_t){(float)p.x, (float)p.y, (float)p.z, (float)p.w};
+  } else if (tid < TM + TN / 4) {
+    const int i = 4 * (tid - TM), n = n0 + i;  // N is a multiple of 4
+    uint2 b = make_uint2(0, 0);
+    if (bias != nullptr && n < N) b = *reinterpret_cast<const uint2*>(bias + n);
+    *reinterpret_cast<f32x4_t*>(&ep_bias[i]) =
+        (f32x4_t){bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y)};
+  } else if (tid < TM + TN / 4 + 32) {
+    const int i = tid - TM - TN / 4;
+    ep_fr[i] = i < 16 ? fr.hi[i] : fr.lo[i - 16];
+  }
 #pragma unroll
   for (int i = 0; i < NLD; ++i) load_one(0, i);
 #pragma unroll
@@ -251,48 +274,104 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
     }
   }
 
-  // ---- epilogue: lane column = token m, registers 4c..4c+3 = features
-  // n0 + 128 wn + 32 nb + 8 c + 4 g + 0..3
+  // ---- epilogue: lane column = token m0 + tl, tl = 64 wm + 32 mb + lr;
+  // registers 4c..4c+3 = features n0 + 128 wn + 32 nb + 8 c + 4 g + 0..3.
+  // H D is a multiple of 64, so a 32-feature block nb lies in one of q, k, v
+  // and in one head: the output, the head offset and the RoPE axis are
+  // wave-uniform per block, and only the pair index follows the lane half g.
+  // Stores go through a descriptor over the tile's rows of the output, which
+  // drops rows past M: the row is always part of the lane offset (the range
+  // check may leave the scalar offset out), the scalar offset only moves
+  // within a row.  (readfirstlane: the compiler cannot see that wn is
+  // wave-uniform.)
+  const int nw = __builtin_amdgcn_readfirstlane(n0 + 128 * wn);
+  // frequencies of the pairs jb + 2 g + 0..1, jb = (8 c4 mod D/4) / 2
+  f32x2_t fhi[4], flo[4];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int m = m0 + 64 * wm + 32 * mb + lr;
-    if (m >= M) continue;
-    const int s = m % S;
-    const int32_t* pm = pos + 4 * s;
+  for (int c4 = 0; c4 < 4; ++c4) {
+    const int jb = (8 * c4 % DA) / 2;
+    fhi[c4] = *reinterpret_cast<const f32x2_t*>(&ep_fr[jb + 2 * g]);
+    flo[c4] = *reinterpret_cast<const f32x2_t*>(&ep_fr[16 + jb + 2 * g]);
+  }
+  // the 4 outputs of (nb, c4, mb), rounded: bias, then the rotation for q
+  // and k (channel db + 8 c4 + 4 g + 0..3 of a head, db the block's first)
+  auto emit = [&](int nb, int c4, int mb, bool rotate, int db) -> u32x2_t {
+    const f32x4_t bs = *reinterpret_cast<const f32x4_t*>(&ep_bias[128 * wn + 32 * nb + 8 * c4 + 4 * g]);
+    float y[4];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int e = 0; e < 4; ++e) y[e] = acc[nb][mb][4 * c4 + e] * yscale + bs[e];
+    if (!rotate) return (u32x2_t){pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+    // one axis a for both lane halves (D/4 divides 32)
+    const float fp = ep_pos[64 * wm + 32 * mb + lr][(db + 8 * c4) / DA];
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const int n = n0 + 128 * wn + 32 * nb + 8 * c4 + 4 * g;    // multiple of 4
-        if (n >= N) continue;
-        float y[4];
+    for (int pr = 0; pr < 2; ++pr) {
+      const float rev = rope_rev(fp, fhi[c4][pr], flo[c4][pr]);
+      const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+      const f32x2_t r = rope_rot(y[2 * pr], y[2 * pr + 1], cs, sn);
+      y[2 * pr] = r[0];
+      y[2 * pr + 1] = r[1];
+    }
+    return (u32x2_t){pack_f16x2(y[0], y[1]), pack_f16x2(y[2], y[3])};
+  };
+  if (HD % 128 == 0) {
+    // The wave's 128 features are one contiguous segment of one output's
+    // rows.  Each 32-token half goes through the wave's own slice of the LDS
+    // buffer the last K step no longer reads (32 rows of 256 bytes, padded
+    // to 272), and leaves in 8-byte stores of which 16 lanes cover one
+    // 128-byte half of a row: each store writes 4 whole cache lines instead
+    // of 16-byte pieces of 32 rows.  Within one wave, LDS accesses take
+    // effect in program order.  (Not 16-byte stores: the compiler then reused
+    // a store's first data register in the very next instruction, and on
+    // this GPU some lanes stored the new value.)
+    if (nw < N) {
+      const int which = nw / HD, hdw = nw - which * HD;
+      const uint16_t* const obase = which == 0 ? qo : which == 1 ? ko : vo;
+      const __amdgpu_buffer_rsrc_t ro = uniform_rsrc(obase + (size_t)m0 * HD, nrows_b * HD * 2);
+      constexpr int XR = 136;                    // LDS row stride, 16-bit units
+      const int lbuf = (nk - 1) & 1;
+      uint16_t* const xl = (wave < 4 ? a_lds[lbuf] : b_lds[lbuf]) + (wave & 3) * (32 * XR);
+      static_assert(4 * 32 * XR <= TN * ROW, "transpose slices");
+      const int rr = lane >> 4, cc = lane & 15;  // row 4 i + rr, 8-byte chunk cc of a half
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          y[e] = acc[nb][mb][4 * c4 + e] * yscale + (bias ? bf16_lo((uint32_t)bias[n + e]) : 0.f);
-        const int which = n / HD, hd = n % HD, d = hd % D;
-        uint2 outw;
-        if (which < 2) {
-          const int a = d / DA, j0 = (d % DA) / 2;
-          const float fp = (float)pm[a];
+      for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-          for (int pr = 0; pr < 2; ++pr) {
-            const int j = j0 + pr;
-            const float rev = rope_rev(fp, fr.hi[j], fr.lo[j]);
-            const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
-            const f32x2_t r = rope_rot(y[2 * pr], y[2 * pr + 1], cs, sn);
-            y[2 * pr] = r[0];
-            y[2 * pr + 1] = r[1];
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) {
+            const u32x2_t o = emit(nb, c4, mb, which < 2, (hdw + 32 * nb) % D);
+            *reinterpret_cast<u32x2_t*>(xl + lr * XR + 32 * nb + 8 * c4 + 4 * g) = o;
           }
-          outw.x = pack_f16x2(y[0], y[1]);
-          outw.y = pack_f16x2(y[2], y[3]);
-          uint16_t* dst = (which == 0 ? qo : ko) + (size_t)m * HD + hd;
-          *reinterpret_cast<uint2*>(dst) = outw;
-        } else {
-          outw.x = pack_bf16x2(y[0], y[1]);
-          outw.y = pack_bf16x2(y[2], y[3]);
-          *reinterpret_cast<uint2*>(vo + (size_t)m * HD + hd) = outw;
-        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const u32x2_t part =
+                *reinterpret_cast<const u32x2_t*>(xl + (4 * i + rr) * XR + 64 * h + 4 * cc);
+            // the row in the lane offset, which the descriptor's range check
+            // sees; the column (inside the row) in the scalar offset
+            const int vo = ((64 * wm + 32 * mb + 4 * i + rr) * HD + 64 * h + 4 * cc) * 2;
+            __builtin_amdgcn_raw_buffer_store_b64(part, ro, vo, hdw * 2, 0);
+          }
       }
+    }
+  } else {
+    int voff[2];                                // byte offset of (token, 4 g)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) voff[mb] = ((64 * wm + 32 * mb + lr) * HD + 4 * g) * 2;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int nbase = nw + 32 * nb;
+      if (nbase >= N) continue;
+      const int which = nbase / HD, hdb = nbase - which * HD;
+      const uint16_t* const obase = which == 0 ? qo : which == 1 ? ko : vo;
+      const __amdgpu_buffer_rsrc_t ro = uniform_rsrc(obase + (size_t)m0 * HD, nrows_b * HD * 2);
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          __builtin_amdgcn_raw_buffer_store_b64(emit(nb, c4, mb, which < 2, hdb % D), ro, voff[mb],
+                                                (hdb + 8 * c4) * 2, 0);
+    }
   }
   KLEIN_QKV_CLOCK_STORE(nk)
 }
