@@ -18,7 +18,6 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // RoPE-4D frequencies in revolutions per unit of position, w_j = omega_j/(2 pi),
 // omega_j = 10000^(-2j/(D/4)), j < D/8.  Each w_j is split as hi + lo with hi

@@ -32,6 +32,8 @@
 
 namespace klein {
 
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
 // Per-part cycle counts of the K step, for a measurement build only: defined
 // by the step_clock.hip harness, never by the library.  Each wave sums, over
 // its K steps, the shader-clock cycles (s_memtime) of each k-sub-step (with
