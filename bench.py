@@ -253,11 +253,73 @@ def observed_clock():
         shutil.rmtree(out, ignore_errors=True)
 
 
+def qkv_rows(torch, kl, dev, pos):
+    """The QKV projection with the RoPE-4D epilogue at the headline shape
+    (hidden C = H D = 3072, an assumption: the pages give no width), bf16 and
+    E4M3 operands, each against torch's GEMM (hipBLASLt) on the same operands
+    without the rotation."""
+    from workloads import get_config
+    c = get_config(4)
+    C = c.H * c.D
+    print(f"[next] qkv projection M={c.B * c.S} N={3 * C} K={C}", file=sys.stderr, flush=True)
+    g = torch.Generator(device=dev).manual_seed(404)
+    xx = torch.randn(c.B, c.S, C, device=dev, generator=g).to(torch.bfloat16)
+    ww = (torch.randn(3 * C, C, device=dev, generator=g) / C ** 0.5).to(torch.bfloat16)
+    bb = (torch.randn(3 * C, device=dev, generator=g) * 0.1).to(torch.bfloat16)
+    pp = torch.from_numpy(pos).to(dev)
+    qo = torch.empty(c.B, c.S, c.H, c.D, dtype=torch.float16, device=dev)
+    ko = torch.empty_like(qo)
+    vo = torch.empty(c.B, c.S, c.H, c.D, dtype=torch.bfloat16, device=dev)
+    pms = time_gpu(lambda: kl.klein_qkv_rope4d_proj(xx, ww, bb, pp, qo, ko, vo), 10, 3, torch)
+    yy = torch.empty(c.B, c.S, 3 * C, dtype=torch.bfloat16, device=dev)
+    xm = xx.view(-1, C)
+    tms = time_gpu(lambda: torch.addmm(bb, xm, ww.t(), out=yy.view(-1, 3 * C)), 10, 3, torch)
+    gf = 2.0 * c.B * c.S * 3 * C * C
+    rows = [{
+        "workload": f"QKV projection + RoPE-4D epilogue: x [{c.B}, {c.S}, {C}] bf16, "
+                    f"W [{3 * C}, {C}] bf16, bias; q', k' fp16, v bf16",
+        "ms_per_call": round(pms, 4), "tflops": round(gf / (pms * 1e-3) / 1e12, 2),
+        "peak": PEAK_BF16, "frac": round(gf / (pms * 1e-3) / 1e12 / PEAK_BF16, 4),
+        "torch_addmm_ms": round(tms, 4),
+        "torch_addmm_tflops": round(gf / (tms * 1e-3) / 1e12, 2)}]
+    del yy
+    # the same projection on E4M3 operands (per-tensor amax/448 scales),
+    # against torch's fp8 GEMM (torch._scaled_mm, hipBLASLt) on the codes
+    sx = float(xx.float().abs().max()) / 448.0
+    sw = float(ww.float().abs().max()) / 448.0
+    x8 = (xx.float() / sx).to(torch.float8_e4m3fn)
+    w8 = (ww.float() / sw).to(torch.float8_e4m3fn)
+    xq, wq = x8.view(torch.uint8), w8.view(torch.uint8)
+    fms = time_gpu(lambda: kl.klein_qkv_rope4d_proj(xq, wq, bb, pp, qo, ko, vo,
+                                                    descales=(sx, sw)), 10, 3, torch)
+    rec_fp8 = {
+        "workload": f"QKV projection + RoPE-4D epilogue, FP8 operands: x [{c.B}, {c.S}, {C}] "
+                    f"and W [{3 * C}, {C}] E4M3 with per-tensor scales, bf16 bias; "
+                    f"q', k' fp16, v bf16",
+        "ms_per_call": round(fms, 4), "tflops": round(gf / (fms * 1e-3) / 1e12, 2),
+        "peak": PEAK_FP8, "frac": round(gf / (fms * 1e-3) / 1e12 / PEAK_FP8, 4)}
+    try:
+        one = torch.ones((), device=dev)
+        sa_, sb_ = one * sx, one * sw
+        x8m = x8.view(-1, C)
+        yy8 = lambda: torch._scaled_mm(x8m, w8.t(), scale_a=sa_, scale_b=sb_,
+                                       out_dtype=torch.bfloat16)
+        sms = time_gpu(yy8, 10, 3, torch)
+        rec_fp8["torch_scaled_mm_ms"] = round(sms, 4)
+        rec_fp8["torch_scaled_mm_tflops"] = round(gf / (sms * 1e-3) / 1e12, 2)
+    except Exception as e:     # the comparison only; the projection is timed above
+        rec_fp8["torch_scaled_mm"] = f"unavailable: {e}"
+    rows.append(rec_fp8)
+    del xx, ww, bb, qo, ko, vo, x8, w8, xq, wq
+    return rows
+
+
 def next_rows(torch, kl, dev, inp4, steps):
     """The adjacent workloads, each against its MFMA peak: the attention
     backward at the headline shape (LoRA / DreamBooth-style training), the
-    1024x1024 workloads warm and cold, and a 2048x2048 edit with two
-    references (tokens grow by one image grid per reference)."""
+    1024x1024 workloads warm and cold, a 2048x2048 edit with two references
+    (tokens grow by one image grid per reference) and the QKV projection that
+    feeds the attention."""
     from workloads import get_config, make_inputs
     rows = []
     # backward at the 2048x2048 CFG shape: forward with lse once, then the
@@ -326,6 +388,7 @@ def next_rows(torch, kl, dev, inp4, steps):
                  "ms_per_call": round(xms, 4), "tflops": round(xt, 2), "peak": PEAK_BF16,
                  "frac": round(xt / PEAK_BF16, 4)})
     del xq, xk, xv, xo
+    rows.extend(qkv_rows(torch, kl, dev, inp4.pos))
     return rows
 
 
@@ -543,70 +606,28 @@ def main():
                 "keys_rotated_once_effective_tflops": round(weff, 2)})
             del xq, xk, xv, xo, xm, xw
     if args.extra:
-        # QKV projection with the RoPE-4D epilogue at the bench shape (hidden
-        # C = H D = 3072, an assumption: the pages give no width), against
-        # torch's GEMM (hipBLASLt) on the same operands, and the attention on
-        # its pre-rotated output against the fused-rotation attention
+        # the attention on the projection's pre-rotated output, against the
+        # fused-rotation attention
         c = get_config(4)
         C = c.H * c.D
-        print(f"[extra] qkv projection M={c.B * c.S} N={3 * C} K={C}", file=sys.stderr, flush=True)
+        print(f"[extra] attention on pre-rotated q', k' S={c.S}", file=sys.stderr, flush=True)
         g = torch.Generator(device=dev).manual_seed(404)
         xx = torch.randn(c.B, c.S, C, device=dev, generator=g).to(torch.bfloat16)
         ww = (torch.randn(3 * C, C, device=dev, generator=g) / C ** 0.5).to(torch.bfloat16)
-        bb = (torch.randn(3 * C, device=dev, generator=g) * 0.1).to(torch.bfloat16)
         pp = torch.from_numpy(inp.pos).to(dev)
         qo = torch.empty(c.B, c.S, c.H, c.D, dtype=torch.float16, device=dev)
         ko = torch.empty_like(qo)
         vo = torch.empty(c.B, c.S, c.H, c.D, dtype=torch.bfloat16, device=dev)
         oo = torch.empty_like(vo)
-        pms = time_gpu(lambda: kl.klein_qkv_rope4d_proj(xx, ww, bb, pp, qo, ko, vo), 10, 3, torch)
-        yy = torch.empty(c.B, c.S, 3 * C, dtype=torch.bfloat16, device=dev)
-        xm = xx.view(-1, C)
-        tms = time_gpu(lambda: torch.addmm(bb, xm, ww.t(), out=yy.view(-1, 3 * C)), 10, 3, torch)
+        kl.klein_qkv_rope4d_proj(xx, ww, None, pp, qo, ko, vo)
         ams = time_gpu(lambda: kl.klein_attn_fwd_prerotated(qo, ko, vo, oo), 10, 3, torch)
-        gf = 2.0 * c.B * c.S * 3 * C * C
-        rec["extra"].append({
-            "workload": f"QKV projection + RoPE-4D epilogue: x [{c.B}, {c.S}, {C}] bf16, "
-                        f"W [{3 * C}, {C}] bf16, bias; q', k' fp16, v bf16",
-            "ms_per_call": round(pms, 4), "tflops": round(gf / (pms * 1e-3) / 1e12, 2),
-            "peak": PEAK_BF16, "frac": round(gf / (pms * 1e-3) / 1e12 / PEAK_BF16, 4),
-            "torch_addmm_ms": round(tms, 4),
-            "torch_addmm_tflops": round(gf / (tms * 1e-3) / 1e12, 2)})
-        # the same projection on E4M3 operands (per-tensor amax/448 scales),
-        # against torch's fp8 GEMM (torch._scaled_mm, hipBLASLt) on the codes
-        sx = float(xx.float().abs().max()) / 448.0
-        sw = float(ww.float().abs().max()) / 448.0
-        x8 = (xx.float() / sx).to(torch.float8_e4m3fn)
-        w8 = (ww.float() / sw).to(torch.float8_e4m3fn)
-        xq, wq = x8.view(torch.uint8), w8.view(torch.uint8)
-        fms = time_gpu(lambda: kl.klein_qkv_rope4d_proj(xq, wq, bb, pp, qo, ko, vo,
-                                                        descales=(sx, sw)), 10, 3, torch)
-        rec_fp8 = {
-            "workload": f"QKV projection + RoPE-4D epilogue, FP8 operands: x [{c.B}, {c.S}, {C}] "
-                        f"and W [{3 * C}, {C}] E4M3 with per-tensor scales, bf16 bias; "
-                        f"q', k' fp16, v bf16",
-            "ms_per_call": round(fms, 4), "tflops": round(gf / (fms * 1e-3) / 1e12, 2),
-            "peak": PEAK_FP8, "frac": round(gf / (fms * 1e-3) / 1e12 / PEAK_FP8, 4)}
-        try:
-            one = torch.ones((), device=dev)
-            sa_, sb_ = one * sx, one * sw
-            x8m = x8.view(-1, C)
-            yy8 = lambda: torch._scaled_mm(x8m, w8.t(), scale_a=sa_, scale_b=sb_,
-                                           out_dtype=torch.bfloat16)
-            sms = time_gpu(yy8, 10, 3, torch)
-            rec_fp8["torch_scaled_mm_ms"] = round(sms, 4)
-            rec_fp8["torch_scaled_mm_tflops"] = round(gf / (sms * 1e-3) / 1e12, 2)
-        except Exception as e:     # the comparison only; the projection is timed above
-            rec_fp8["torch_scaled_mm"] = f"unavailable: {e}"
-        rec["extra"].append(rec_fp8)
-        del x8, w8, xq, wq
         rec["extra"].append({
             "workload": f"attention on pre-rotated fp16 q', k' (bf16 v): {c.name}, B={c.B}, "
                         f"S={c.S}, H={c.H}, D={c.D}",
             "ms_per_call": round(ams, 4), "tflops": round(c.flops / (ams * 1e-3) / 1e12, 2),
             "peak": PEAK_BF16, "frac": round(c.flops / (ams * 1e-3) / 1e12 / PEAK_BF16, 4),
             "fused_rotation_ms": round(ms, 4)})
-        del xx, ww, bb, qo, ko, vo, oo, yy
+        del xx, ww, qo, ko, vo, oo
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
