@@ -167,3 +167,36 @@ def test_fp8_projection_rejects_bad_descales_and_width():
     with pytest.raises(kl.KleinError) as e:
         kl.klein_qkv_rope4d_proj(x64, w64, None, dev_args[3], q, k, v, descales=(1.0, 1.0))
     assert e.value.status == kl.KLEIN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("B,S,C,H,D", [
+    (2, 300, 128, 2, 64),     # H D = 128: the epilogue's LDS-staged stores, a partial token tile
+    (1, 513, 256, 4, 128),    # the same with D = 128 and a one-token last tile
+    (3, 77, 384, 3, 64),      # H D = 192: the direct per-lane stores
+])
+def test_projection_repeatable(B, S, C, H, D, fp8):
+    # every call writes every output element, and the same bits each time:
+    # outputs start from NaN or from whatever memory held, alternately
+    if fp8:
+        dev_args, descales, _ = fp8_case(B, S, C, H, D, True, seed=900 + S)
+        kw = {"descales": descales}
+    else:
+        dev_args, _ = proj_case(B, S, C, H, D, True, seed=900 + S)
+        kw = {}
+    first = None
+    for i in range(8):
+        print(f"[case] repeat {i} B={B} S={S} C={C} H={H} D={D} fp8={fp8}", flush=True)
+        make = (lambda *a, **k: torch.full(*a, float("nan"), **k)) if i % 2 else torch.empty
+        q = make((B, S, H, D), dtype=torch.float16, device=DEV)
+        k = make((B, S, H, D), dtype=torch.float16, device=DEV)
+        v = make((B, S, H, D), dtype=torch.bfloat16, device=DEV)
+        kl.klein_qkv_rope4d_proj(*dev_args, q, k, v, **kw)
+        torch.cuda.synchronize()
+        got = [t.view(torch.int16).clone() for t in (q, k, v)]
+        assert all(bool(torch.isfinite(t).all()) for t in (q, k, v)), f"call {i}: non-finite output"
+        if first is None:
+            first = got
+        else:
+            for name, a, b in zip("qkv", first, got):
+                assert torch.equal(a, b), f"call {i}: {name} differs from the first call"
