@@ -1,6 +1,6 @@
 // Measurement harness (not part of the library): where the cycles of the
-// bf16 attention kernel's pipeline step, and of the QKV projection's K
-// step, go.
+// bf16 and fp8 attention kernels' pipeline steps, and of the QKV
+// projection, go; and the LDS rates those loops run against.
 //
 // This file compiles attn_fwd_bf16.hip, attn_fwd_fp8.hip and
 // qkv_rope_proj.hip with KLEIN_STEP_CLOCK defined, which makes every wave
@@ -25,6 +25,9 @@
 //                                         512 text + image + reference)
 //        step_clock qkv [B S H D reps]    the projection (C = H D), bf16
 //                                         then fp8 operands
+//        step_clock lds                   LDS rates of this GPU: bytes per
+//                                         shader clock and CU for the access
+//                                         forms the kernels use
 // Inputs are seeded N(0, 1) (W scaled by 1/sqrt(C)); positions follow the
 // workload's layout (512 text tokens on the l axis, then a square image
 // grid).  The attention table gives mean cycles per step for the waves 0-3
@@ -38,6 +41,7 @@
 #include "attn_fwd_fp8.hip"
 #include "qkv_rope_proj.hip"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -330,7 +334,89 @@ static int qkv_main(int argc, char** argv) {
   return 0;
 }
 
+// ---- LDS rates: one workgroup of 512 threads per CU, each thread with a
+// fixed address, 8 accesses per iteration at constant offsets (16 or 8
+// bytes a lane, 16 consecutive lanes on consecutive slots: no bank
+// conflicts), s_memtime around the loop per wave.
+typedef unsigned lds_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned lds_u32x2 __attribute__((ext_vector_type(2)));
+typedef short lds_s16x4 __attribute__((ext_vector_type(4)));
+template <int MODE>
+__global__ __launch_bounds__(512) void lds_rate_kernel(unsigned long long* out, unsigned* sink,
+                                                       int iters) {
+  __shared__ __attribute__((aligned(16))) unsigned lds[16384];     // 64 KB
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 16384; i += 512) lds[i] = i * 2654435761u;
+  __syncthreads();
+  lds_u32x4 acc = {0, 0, 0, 0};
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (MODE == 0) {                 // ds_read_b128: 16 bytes at 16 tid + 8 KB u
+        acc ^= *reinterpret_cast<const lds_u32x4*>(&lds[4 * tid + 2048 * u]);
+      } else if (MODE == 1) {          // ds_write_b128
+        *reinterpret_cast<lds_u32x4*>(&lds[4 * tid + 2048 * u]) = acc;
+        acc.x += 1u;
+      } else {                         // ds_read_b64_tr_b16: 8 bytes at 8 tid + 4 KB u
+        const lds_s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) lds_s16x4*)(reinterpret_cast<short*>(
+                &lds[2 * tid + 1024 * u])));
+        const lds_u32x2 w = __builtin_bit_cast(lds_u32x2, v);
+        acc.x ^= w.x;
+        acc.y ^= w.y;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  if ((tid & 63) == 0) out[blockIdx.x * 8 + (tid >> 6)] = t1 - t0;
+  sink[blockIdx.x * 512 + tid] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
+static int lds_main() {
+  int ncu = 0;
+  CHECK_HIP(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, 0));
+  const int iters = 4096;
+  unsigned long long* d_out = nullptr;
+  unsigned* d_sink = nullptr;
+  CHECK_HIP(hipMalloc(&d_out, (size_t)ncu * 8 * sizeof(unsigned long long)));
+  CHECK_HIP(hipMalloc(&d_sink, (size_t)ncu * 512 * sizeof(unsigned)));
+  const char* names[3] = {"ds_read_b128 (16 bytes a lane)", "ds_write_b128 (16 bytes a lane)",
+                          "ds_read_b64_tr_b16 (8 bytes a lane)"};
+  const int bytes[3] = {16, 16, 8};
+  std::printf("LDS rates, one 512-thread workgroup per CU on %d CUs, %d x 8 accesses per thread\n\n",
+              ncu, iters);
+  std::printf("| access | bytes per shader clock and CU, mean over workgroups | slowest workgroup |\n");
+  std::printf("|---|---|---|\n");
+  for (int mode = 0; mode < 3; ++mode) {
+    for (int rep = 0; rep < 2; ++rep) {
+      if (mode == 0) hipLaunchKernelGGL(lds_rate_kernel<0>, dim3(ncu), dim3(512), 0, 0, d_out, d_sink, iters);
+      if (mode == 1) hipLaunchKernelGGL(lds_rate_kernel<1>, dim3(ncu), dim3(512), 0, 0, d_out, d_sink, iters);
+      if (mode == 2) hipLaunchKernelGGL(lds_rate_kernel<2>, dim3(ncu), dim3(512), 0, 0, d_out, d_sink, iters);
+      CHECK_HIP(hipGetLastError());
+      CHECK_HIP(hipDeviceSynchronize());
+    }
+    std::vector<unsigned long long> h((size_t)ncu * 8);
+    CHECK_HIP(hipMemcpy(h.data(), d_out, h.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost));
+    double sum = 0, mx = 0;
+    for (int b = 0; b < ncu; ++b) {
+      unsigned long long m = 0;
+      for (int w = 0; w < 8; ++w) m = std::max(m, h[(size_t)b * 8 + w]);
+      sum += (double)m;
+      mx = std::max(mx, (double)m);
+    }
+    const double wg_bytes = 512.0 * 8 * iters * bytes[mode];
+    std::printf("| %s | %.1f | %.1f |\n", names[mode], wg_bytes / (sum / ncu), wg_bytes / mx);
+  }
+  CHECK_HIP(hipFree(d_out));
+  CHECK_HIP(hipFree(d_sink));
+  return 0;
+}
+
 int main(int argc, char** argv) {
+  if (argc > 1 && std::strcmp(argv[1], "lds") == 0) return lds_main();
   if (argc > 1 && std::strcmp(argv[1], "qkv") == 0) return qkv_main(argc, argv);
   if (argc > 1 && std::strcmp(argv[1], "fp8") == 0) return fp8_main(argc, argv);
   const int B = argc > 1 ? std::atoi(argv[1]) : 2;
