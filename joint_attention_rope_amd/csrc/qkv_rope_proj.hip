@@ -13,8 +13,9 @@
 // accumulator registers 4c .. 4c+3 of a lane then hold four consecutive
 // channels d of one token (its MFMA column), and the interleaved RoPE pairs
 // (d, d+1) are register pairs of one lane.  The rotation, the bias and the
-// conversions happen in registers before the only store; the angle of each
-// pair is formed once per output element, like the attention kernels' Q.
+// conversions happen in registers (the angle of each pair is formed once per
+// output element, like the attention kernels' Q); the rounded outputs then
+// pass through LDS so that the only stores write whole cache lines.
 //
 // One workgroup of 8 waves computes 256 features x 256 tokens, K in steps of
 // 128 bytes; each wave owns 128 features x 64 tokens (4 x 2 MFMA tiles of
