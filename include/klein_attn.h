@@ -40,7 +40,8 @@
  *    shared by every batch entry.  Angles are formed in fp32; accuracy is
  *    stated for |pos| < 4096 on every axis (larger values are accepted, with
  *    angle error growing like |pos| * 2^-24 revolutions).
- *  - D must be 64 or 128; B, S, H >= 1; B*H*ceil(S/256) < 2^31.
+ *  - D must be 64 or 128; B, S, H >= 1; B*H*ceil(S/256) < 2^31; H*D < 2^22
+ *    (every entry point; larger shapes return UNSUPPORTED).
  *  - bf16 path: the rotated Q (times log2(e)/sqrt(D)) and K are held on chip
  *    as fp16 for the score products (three more mantissa bits than bf16), so
  *    elementwise |k| must stay below ~46000 and |q| below ~360000; larger
@@ -74,7 +75,7 @@ typedef enum {
 typedef enum {
   KLEIN_OK = 0,
   KLEIN_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, size < 1, bad dtype, bad descale */
-  KLEIN_ERR_UNSUPPORTED = 2,  /* D not in {64, 128}, or grid too large */
+  KLEIN_ERR_UNSUPPORTED = 2,  /* D not in {64, 128}, H*D >= 2^22, or grid too large */
   KLEIN_ERR_NO_DEVICE = 3,    /* the HIP runtime found no usable GPU */
   KLEIN_ERR_LAUNCH = 4,       /* the kernel launch itself failed */
   KLEIN_STATUS_SPAN_INT_ = -0x7fffffff - 1

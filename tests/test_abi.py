@@ -184,3 +184,38 @@ def test_backward_argument_checks():
     assert lib.klein_rope4d_attn_fwd_lse(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, 1, 8, 1, 64,
                                          None) == I
     assert lib.klein_rope4d_attn_fwd_lse(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 80, None) == U
+
+
+def test_every_entry_point_rejects_wide_heads():
+    """H D of 2^22 or more (byte offsets within a tile's rows would pass 32
+    bits) is UNSUPPORTED at every entry point, before any HIP call; H D just
+    below the limit passes the check."""
+    lib = _capi.lib()
+    U = _capi.KLEIN_ERR_UNSUPPORTED
+    H, D = 2 ** 15, 128                      # H D = 2^22
+    n = ctypes.c_size_t(0)
+    plan = (ctypes.c_int * 8)()
+    F = FAKE
+    calls = {
+        "klein_rope4d_attn_fwd": (F, F, F, F, F, 1, 1, H, D, 0, None),
+        "klein_rope4d_attn_fwd_fp8": (F, F, F, F, F, 1, 1, H, D, 1.0, 1.0, 1.0, None),
+        "klein_rope4d_attn_fwd_ws": (F, F, F, F, F, 1, 1, H, D, 0, 1.0, 1.0, 1.0, F, 1 << 40, None),
+        "klein_rope4d_attn_fwd_noalloc": (F, F, F, F, F, 1, 1, H, D, 0, 1.0, 1.0, 1.0, None),
+        "klein_rope4d_attn_fwd_lse": (F, F, F, F, F, F, 1, 1, H, D, None),
+        "klein_rope4d_attn_fwd_lse_ws": (F, F, F, F, F, F, 1, 1, H, D, F, 1 << 40, None),
+        "klein_rope4d_attn_fwd_blocksparse": (F, F, F, F, F, 1, 1, H, D, 0, 1.0, 1.0, 1.0, F, None),
+        "klein_rope4d_attn_fwd_blocksparse_ws": (F, F, F, F, F, 1, 1, H, D, 0, 1.0, 1.0, 1.0, F, F,
+                                                 1 << 40, None),
+        "klein_rope4d_attn_bwd": (F, F, F, F, F, F, F, F, F, F, 1, 1, H, D, F, 1 << 40, None),
+        "klein_attn_workspace_size": (1, 1, H, D, 0, ctypes.byref(n)),
+        "klein_attn_bwd_workspace_size": (1, 1, H, D, ctypes.byref(n)),
+        "klein_splitkv_plan": (1, 1, H, D, 256, plan, ctypes.byref(n)),
+        "klein_qkv_rope4d_proj": (F, F, 0, F, F, F, F, 1, 1, 128, H, D, None),
+        "klein_qkv_rope4d_proj_fp8": (F, F, 0, F, F, F, F, 1, 1, 128, H, D, 1.0, 1.0, None),
+        "klein_attn_fwd_prerotated": (F, F, F, F, 1, 1, H, D, None),
+        "klein_rope4d_apply": (F, F, F, 1, 1, H, D, None),
+    }
+    for name, args in calls.items():
+        assert getattr(lib, name)(*args) == U, name
+    # one head fewer is within the limit (this size query needs no device)
+    assert lib.klein_attn_bwd_workspace_size(1, 1, H - 1, D, ctypes.byref(n)) == _capi.KLEIN_OK
