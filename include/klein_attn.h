@@ -41,7 +41,7 @@
  *    stated for |pos| < 4096 on every axis (larger values are accepted, with
  *    angle error growing like |pos| * 2^-24 revolutions).
  *  - D must be 64 or 128; B, S, H >= 1; B*H*ceil(S/256) < 2^31; H*D < 2^22
- *    (every entry point; larger shapes return UNSUPPORTED).
+ *    and S < 2^29 (every entry point; larger shapes return UNSUPPORTED).
  *  - bf16 path: the rotated Q (times log2(e)/sqrt(D)) and K are held on chip
  *    as fp16 for the score products (three more mantissa bits than bf16), so
  *    elementwise |k| must stay below ~46000 and |q| below ~360000; larger
@@ -75,7 +75,7 @@ typedef enum {
 typedef enum {
   KLEIN_OK = 0,
   KLEIN_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, size < 1, bad dtype, bad descale */
-  KLEIN_ERR_UNSUPPORTED = 2,  /* D not in {64, 128}, H*D >= 2^22, or grid too large */
+  KLEIN_ERR_UNSUPPORTED = 2,  /* D not in {64, 128}, H*D >= 2^22, S >= 2^29, or grid too large */
   KLEIN_ERR_NO_DEVICE = 3,    /* the HIP runtime found no usable GPU */
   KLEIN_ERR_LAUNCH = 4,       /* the kernel launch itself failed */
   KLEIN_STATUS_SPAN_INT_ = -0x7fffffff - 1
@@ -388,7 +388,8 @@ klein_status_t klein_rope4d_attn_fwd_blocksparse_ws(const void* q, const void* k
  * NVIDIA Blackwell", section "Method 1"):
  *   y = x W^T (+ bias);  q = y[:, 0:HD], k = y[:, HD:2HD], v = y[:, 2HD:3HD]
  *   q_out = R(pos) q, k_out = R(pos) k  (fp16),  v_out = v  (bfloat16)
- *   x       : [B][S][C] bfloat16 (C % 64 == 0, C <= 65536, else UNSUPPORTED)
+ *   x       : [B][S][C] bfloat16 (C % 64 == 0, C <= 65536, B*S < 2^31, else
+ *             UNSUPPORTED)
  *   w       : [3*H*D][C] bfloat16 (a linear layer's [out, in] layout)
  *   bias    : [3*H*D] bfloat16, 8-byte aligned, or NULL
  *   pos_thwl: [S][4] int32, shared by all batch entries

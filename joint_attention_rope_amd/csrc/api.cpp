@@ -37,16 +37,20 @@ klein::RopeFreqs make_freqs(int D) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // The kernels form byte offsets within a tile's rows in 32-bit integers (up
-// to 256 rows of H D 16-bit elements), so H D stays below 2^22.
+// to 256 rows of H D 16-bit elements), so H D stays below 2^22, and index
+// pos_thwl as 4 s + axis in 32 bits, so S stays below 2^29.
 constexpr long long kMaxHeadWidth = (1LL << 22) - 1;
-bool head_width_ok(int H, int D) { return (long long)H * D <= kMaxHeadWidth; }
+constexpr long long kMaxTokens = (1LL << 29) - 1;
+bool shape_ok(int S, int H, int D) {
+  return (long long)H * D <= kMaxHeadWidth && (long long)S <= kMaxTokens;
+}
 
 klein_status_t check_common(const void* q, const void* k, const void* v, const int32_t* pos,
                             const void* out, int B, int S, int H, int D) {
   if (!q || !k || !v || !pos || !out) return KLEIN_ERR_INVALID_ARG;
   if (B < 1 || S < 1 || H < 1) return KLEIN_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return KLEIN_ERR_UNSUPPORTED;
-  if (!head_width_ok(H, D)) return KLEIN_ERR_UNSUPPORTED;
+  if (!shape_ok(S, H, D)) return KLEIN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(pos))
     return KLEIN_ERR_INVALID_ARG;
   return KLEIN_OK;
@@ -342,7 +346,7 @@ klein_status_t klein_attn_bwd_workspace_size(int B, int S, int H, int D, size_t*
   if (!bytes) return KLEIN_ERR_INVALID_ARG;
   if (B < 1 || S < 1 || H < 1) return KLEIN_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return KLEIN_ERR_UNSUPPORTED;
-  if (!head_width_ok(H, D)) return KLEIN_ERR_UNSUPPORTED;
+  if (!shape_ok(S, H, D)) return KLEIN_ERR_UNSUPPORTED;
   *bytes = (size_t)klein::attn_bwd_workspace(B, S, H, D).total;
   return KLEIN_OK;
 }
@@ -390,7 +394,7 @@ klein_status_t klein_attn_workspace_size(int B, int S, int H, int D, klein_dtype
   if (dtype != KLEIN_DTYPE_BF16 && dtype != KLEIN_DTYPE_FP8_E4M3) return KLEIN_ERR_INVALID_ARG;
   if (B < 1 || S < 1 || H < 1) return KLEIN_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return KLEIN_ERR_UNSUPPORTED;
-  if (!head_width_ok(H, D)) return KLEIN_ERR_UNSUPPORTED;
+  if (!shape_ok(S, H, D)) return KLEIN_ERR_UNSUPPORTED;
   if (klein::attn_fwd_bf16_grid(B, S, H) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
   try {
     hipError_t e;
@@ -408,7 +412,7 @@ klein_status_t klein_splitkv_plan(int B, int S, int H, int D, int n_cu, int* pla
   if (!plan || !partial_bytes) return KLEIN_ERR_INVALID_ARG;
   if (B < 1 || S < 1 || H < 1 || n_cu < 1) return KLEIN_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return KLEIN_ERR_UNSUPPORTED;
-  if (!head_width_ok(H, D)) return KLEIN_ERR_UNSUPPORTED;
+  if (!shape_ok(S, H, D)) return KLEIN_ERR_UNSUPPORTED;
   if (klein::attn_fwd_bf16_grid(B, S, H) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
   const klein::SplitPlan p = klein::plan_split(B, S, H, D, n_cu);
   plan[0] = p.n_sk > 0 ? p.n_dp : (int)klein::attn_fwd_bf16_grid(B, S, H);
@@ -523,7 +527,7 @@ klein_status_t klein_attn_fwd_prerotated(const void* q, const void* k, const voi
   if (!q || !k || !v || !out) return KLEIN_ERR_INVALID_ARG;
   if (B < 1 || S < 1 || H < 1) return KLEIN_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return KLEIN_ERR_UNSUPPORTED;
-  if (!head_width_ok(H, D)) return KLEIN_ERR_UNSUPPORTED;
+  if (!shape_ok(S, H, D)) return KLEIN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return KLEIN_ERR_INVALID_ARG;
   if (klein::attn_fwd_bf16_grid(B, S, H) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
@@ -545,7 +549,7 @@ static klein_status_t qkv_proj(const void* x, const void* w, const void* bias,
                w_descale > 0.f))
     return KLEIN_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return KLEIN_ERR_UNSUPPORTED;
-  if (!head_width_ok(H, D)) return KLEIN_ERR_UNSUPPORTED;
+  if (!shape_ok(S, H, D)) return KLEIN_ERR_UNSUPPORTED;
   if (C % (fp8 ? 128 : 64) != 0 || C > 65536) return KLEIN_ERR_UNSUPPORTED;
   for (const void* p : {x, w, (const void*)q_out, (const void*)k_out, (const void*)v_out,
                         (const void*)pos_thwl})
@@ -553,6 +557,7 @@ static klein_status_t qkv_proj(const void* x, const void* w, const void* bias,
   if (bias && (reinterpret_cast<uintptr_t>(bias) & 7u)) return KLEIN_ERR_INVALID_ARG;
   if (klein::qkv_rope_proj_grid(B, S, H, D) > kMaxGrid) return KLEIN_ERR_UNSUPPORTED;
   if ((long long)B * S * H * D * 3 >= (1LL << 40)) return KLEIN_ERR_UNSUPPORTED;
+  if ((long long)B * S >= (1LL << 31)) return KLEIN_ERR_UNSUPPORTED;   // M = B S in 32 bits
   try {
     klein::QkvArgs a{};
     a.x = x; a.w = w; a.bias = (const uint16_t*)bias;
@@ -590,7 +595,7 @@ klein_status_t klein_rope4d_apply(const void* x, const int32_t* pos_thwl, void* 
   if (!x || !pos_thwl || !y) return KLEIN_ERR_INVALID_ARG;
   if (B < 1 || S < 1 || H < 1) return KLEIN_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return KLEIN_ERR_UNSUPPORTED;
-  if (!head_width_ok(H, D)) return KLEIN_ERR_UNSUPPORTED;
+  if (!shape_ok(S, H, D)) return KLEIN_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(y) || !aligned16(pos_thwl)) return KLEIN_ERR_INVALID_ARG;
   try {
     return map_hip(klein::launch_rope4d_apply(make_args(x, x, x, pos_thwl, y, B, S, H, D, stream)));
@@ -603,7 +608,7 @@ const char* klein_status_string(klein_status_t status) {
   switch (status) {
     case KLEIN_OK: return "ok";
     case KLEIN_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, size < 1, bad dtype or descale)";
-    case KLEIN_ERR_UNSUPPORTED: return "unsupported (head dim must be 64 or 128 and H*D below 2^22; grid or block mask too large; or, for klein_rope4d_attn_fwd_noalloc, the call needs more than its fixed scratch)";
+    case KLEIN_ERR_UNSUPPORTED: return "unsupported (head dim must be 64 or 128, H*D below 2^22 and S below 2^29; grid or block mask too large; or, for klein_rope4d_attn_fwd_noalloc, the call needs more than its fixed scratch)";
     case KLEIN_ERR_NO_DEVICE: return "no usable GPU";
     case KLEIN_ERR_LAUNCH: return "kernel launch failed";
     case KLEIN_STATUS_SPAN_INT_: break;

@@ -188,8 +188,8 @@ def test_backward_argument_checks():
 
 def test_every_entry_point_rejects_wide_heads():
     """H D of 2^22 or more (byte offsets within a tile's rows would pass 32
-    bits) is UNSUPPORTED at every entry point, before any HIP call; H D just
-    below the limit passes the check."""
+    bits) and S of 2^29 or more are UNSUPPORTED at every entry point, before
+    any HIP call; shapes just below the limits pass the check."""
     lib = _capi.lib()
     U = _capi.KLEIN_ERR_UNSUPPORTED
     H, D = 2 ** 15, 128                      # H D = 2^22
@@ -217,5 +217,16 @@ def test_every_entry_point_rejects_wide_heads():
     }
     for name, args in calls.items():
         assert getattr(lib, name)(*args) == U, name
+        # S = 2^29 (pos_thwl's index 4 s + axis would pass 32 bits), H = 1:
+        # S is the argument before H, or before C and H in the projections
+        long_seq = list(args)
+        i = long_seq.index(H)
+        si = i - 2 if name.startswith("klein_qkv") else i - 1
+        assert long_seq[si] == 1, name
+        long_seq[si], long_seq[i] = 2 ** 29, 1
+        assert getattr(lib, name)(*long_seq) == U, (name, "S = 2^29")
     # one head fewer is within the limit (this size query needs no device)
     assert lib.klein_attn_bwd_workspace_size(1, 1, H - 1, D, ctypes.byref(n)) == _capi.KLEIN_OK
+    assert lib.klein_attn_bwd_workspace_size(1, 2 ** 29 - 1, 1, D, ctypes.byref(n)) == _capi.KLEIN_OK
+    # the projection's B S (its token count) in 32 bits
+    assert lib.klein_qkv_rope4d_proj(F, F, 0, F, F, F, F, 8, 2 ** 28, 128, 1, 64, None) == U
