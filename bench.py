@@ -127,8 +127,9 @@ def cpu_baseline(inp, cfg, target_s=15.0):
     import oracle
     from workloads import Inputs
     visible = len(os.sched_getaffinity(0))
-    # a GPU machine gives each GPU a share of 16 host threads, whatever the
-    # affinity mask shows (OMP_NUM_THREADS says the same there)
+    # a shared host may give each GPU a share of its threads (16 on the
+    # MI355X hosts measured), whatever the affinity mask shows;
+    # OMP_NUM_THREADS states that share
     share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
     workers = min(visible, share) if share > 0 else visible
     sub = Inputs(cfg, inp.q[:1], inp.k[:1], inp.v[:1], inp.pos, inp.descale)
@@ -414,7 +415,7 @@ def main():
                          "times (a kernel of known HBM traffic for scaling counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the attention shards by batch entry and head with no exchange; "
               "see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)

@@ -2,7 +2,7 @@
 
 The FP8 attention the pages describe ("How FLUX 3 Image Klein was made 3-4x
 faster on NVIDIA Blackwell", section "Method 2", table of attention methods)
-does not name the format; this build reads it as the OCP 8-bit floating-point
+does not name the format; this library reads it as the OCP 8-bit floating-point
 E4M3 format without infinities (E4M3FN): 1 sign bit, 4 exponent bits with bias
 7, 3 mantissa bits; exponent field 0 is subnormal (m/8 * 2^-6); the pattern
 S.1111.111 is NaN; the largest finite magnitude is 448.

@@ -7,9 +7,9 @@ usual) and linked into tests/abi_driver.cpp, which walks the argument checks
 of every entry point, the split-KV planner over a sweep of shapes, the
 workspace-size arithmetic and the status strings, and -- with no GPU
 visible -- checks that every call that reaches the device reports
-KLEIN_ERR_NO_DEVICE.  A sanitizer finding aborts the driver.  Skipped when a
-GPU is visible: the driver passes fake pointers, which only a machine without
-a device may see past the argument checks.
+KLEIN_ERR_NO_DEVICE.  A sanitizer finding aborts the test program.  Skipped
+when a GPU is visible: the program passes fake pointers, which only a machine
+without a device may see past the argument checks.
 """
 
 import os
