@@ -1,11 +1,10 @@
 """CPU float64 oracle for RoPE-4D joint self-attention -- TEST INFRASTRUCTURE.
 
 This package is the reference the GPU path is tested against, not part of the
-product.  Only the test suite, the smoke
-check of the entry module and the CPU-baseline leg of the benchmark may import
-it.  It shares no code with the HIP library: the only thing both sides consume
-is the seeded input generator in ``workloads``, which holds none of the
-method's arithmetic.
+product.  Only the test suite, the smoke check of the entry module and the
+CPU-baseline leg of the benchmark may import it.  It shares no code with the
+HIP library: the only thing both sides consume is the seeded input generator
+in ``workloads``, which holds none of the method's arithmetic.
 
 What it computes, per batch entry b and head h (sources: "Flux.3 Image Klein
 arrives in Diffusers with a modular architecture", bytechap.com, section "How
