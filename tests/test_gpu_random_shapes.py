@@ -1,6 +1,7 @@
 """GPU parity on a seeded sweep of shapes: batch, sequence length, heads,
 head dim, input format and schedule drawn at random (fixed seed), each
-compared with the oracle over the whole output at the hot path's tolerances.
+compared with the oracle over the whole output at the hot path's tolerances;
+the same for the QKV projection and for the backward.
 
 The fixed-shape tests pick the tile boundaries by hand; this sweep covers the
 combinations between them (ragged S against both tile sizes, odd head counts
@@ -89,3 +90,28 @@ def test_random_projection_shape_matches_oracle(B, S, C, H, D, bias, fp8, seed):
         q, k, v = run_proj(dev_args, B, S, H, D)
     rq, rk, rv = oracle.qkv_rope4d_proj(*host, H, D)
     check_outputs(q, k, v, rq, rk, rv, f"B={B} S={S} C={C} H={H} D={D}", fp8=fp8)
+
+
+def _bwd_cases(n=6, seed=20261205):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 3))
+        H = int(rng.integers(1, 4))
+        S = int(rng.integers(1, 700))
+        D = int(rng.choice([64, 128]))
+        out.append(pytest.param(B, S, H, D, 3000 + i, id=f"B{B}-S{S}-H{H}-D{D}"))
+    return out
+
+
+@pytest.mark.parametrize("B,S,H,D,seed", _bwd_cases())
+def test_random_backward_shape_matches_oracle(B, S, H, D, seed):
+    # the training forward's lse and the backward's dq, dk, dv
+    import oracle
+    from test_gpu_backward import LSE_ABS, check_grads, run_fwd_bwd
+    print(f"[case] backward B={B} S={S} H={H} D={D}", flush=True)
+    inp = random_inputs(B, S, H, D, seed=seed)
+    (_, lse, dq, dk, dv), (q, k, v, dout) = run_fwd_bwd(inp, dout_seed=seed + 1)
+    rq, rk, rv, rlse = oracle.attention_backward(q, k, v, inp.pos, dout)
+    assert float(np.max(np.abs(lse.cpu().numpy() - rlse))) <= LSE_ABS
+    check_grads((dq, dk, dv), (rq, rk, rv), f"B={B} S={S} H={H} D={D}")
