@@ -178,7 +178,11 @@ klein_status_t klein_rope4d_attn_fwd_fp8(const void* q, const void* k, const voi
  * The keys are also rotated once, into `workspace` (fp16 for bf16 inputs,
  * E4M3 codes of R k / 2 for fp8), before the attention kernel; the dense
  * entry points rotate every key tile once per tile of 256 queries.  The
- * values equal those the dense kernels form.
+ * values equal those the dense kernels form.  For bf16 the values are also
+ * regrouped once into key-major tiles (per head and 64-key tile, one row of
+ * 64 keys per channel), which the kernel reads with plain 16-byte LDS reads
+ * instead of transposing ones; this moves data only, so the output bits do
+ * not change.
  *   workspace      : DEVICE pointer, 256-byte aligned, caller-owned, at least
  *                    the size klein_attn_workspace_size reports for the same
  *                    shape on the current device (may be NULL when that is 0).
@@ -197,7 +201,8 @@ klein_status_t klein_rope4d_attn_fwd_ws(const void* q, const void* k, const void
 /*
  * Workspace bytes klein_rope4d_attn_fwd_ws needs for this shape on the
  * current HIP device: the rotated keys (B*S*H*D*2 bytes for bf16, B*S*H*D
- * for fp8, rounded up to a multiple of 256), then the split partials (0 when the
+ * for fp8, rounded up to a multiple of 256), for bf16 the key-major value
+ * tiles (B*H*ceil(S/64)*64*D*2 bytes), then the split partials (0 when the
  * tiles fill whole rounds, or the sequence is shorter than 2048 keys, and
  * nothing is split; at most 4 * (number of compute units) * (256 * D + 1024)
  * * 4 bytes, 138 MB for D = 128 on 256 compute units).  Writes *bytes; INVALID_ARG for a
@@ -240,10 +245,13 @@ klein_status_t klein_splitkv_plan(int B, int S, int H, int D, int n_cu, int* pla
  * allocates nothing and calls no allocating routine.
  *   Scratch: KLEIN_NOALLOC_SCRATCH_BYTES (320 MiB) per GPU, taken when the
  *   process first calls this function on that GPU and held until the
- *   process ends.  A call whose klein_attn_workspace_size is larger returns
- *   UNSUPPORTED before any device work (e.g. B = 4, S = 16,896, H = 24,
- *   D = 128, bf16 needs 517 MB; the 2048^2 shapes with B = 2 bf16 or B = 1
- *   fp8 fit).
+ *   process ends.  Where the bf16 workspace layout (keys, key-major value
+ *   tiles, partials) does not fit, the call keeps the values row-major and
+ *   reads them with transposing LDS reads (same output bits, a few percent
+ *   slower).  A call that does not fit even so returns UNSUPPORTED before
+ *   any device work (e.g. B = 4, S = 16,896, H = 24, D = 128, bf16 needs
+ *   517 MB with the values row-major; the 2048^2 shapes with B = 2 bf16
+ *   (311 MB, values row-major) or B = 1 fp8 fit).
  *   Every call on one GPU uses that GPU's single array: two calls that run
  *   at the same time on one GPU (different streams, threads or processes
  *   sharing a context) race, and their results are undefined; calls in

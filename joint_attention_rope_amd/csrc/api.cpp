@@ -78,18 +78,21 @@ LaunchArgs make_args(const void* q, const void* k, const void* v, const int32_t*
 constexpr long long kMaxGrid = 2147483647LL;
 
 // Workspace of klein_rope4d_attn_fwd_ws: k rotated once (fp16 for bf16
-// inputs, e4m3 codes for fp8, [B][S][H][D]) and the split-KV partials.
+// inputs, e4m3 codes for fp8, [B][S][H][D]), for bf16 with `vt` v in
+// key-major tiles (klein::v_tiles_bytes), and the split-KV partials.
 struct WsLayout {
   long long krot_bytes;
-  klein::SplitPlan plan;      // partials at offset krot_bytes
+  long long vt_bytes;         // at offset krot_bytes
+  klein::SplitPlan plan;      // partials at offset krot_bytes + vt_bytes
   long long total;
 };
-WsLayout ws_layout(int B, int S, int H, int D, klein_dtype_t dtype, int ncu) {
+WsLayout ws_layout(int B, int S, int H, int D, klein_dtype_t dtype, int ncu, bool vt = true) {
   WsLayout w{};
   const int elem = dtype == KLEIN_DTYPE_BF16 ? 2 : 1;      // fp16 or e4m3 rotated keys
   w.krot_bytes = ((long long)B * S * H * D * elem + 255) / 256 * 256;
+  w.vt_bytes = vt && dtype == KLEIN_DTYPE_BF16 ? klein::v_tiles_bytes(B, S, H, D) : 0;
   w.plan = klein::plan_split(B, S, H, D, ncu);
-  w.total = w.krot_bytes + w.plan.bytes;
+  w.total = w.krot_bytes + w.vt_bytes + w.plan.bytes;
   return w;
 }
 
@@ -130,7 +133,7 @@ klein_status_t attn_ws(const void* q, const void* k, const void* v,
                        const int32_t* pos_thwl, void* out, float* lse, int B, int S, int H,
                        int D, klein_dtype_t dtype, float q_descale, float k_descale,
                        float v_descale, void* workspace, size_t workspace_bytes,
-                       klein_stream_t stream) {
+                       klein_stream_t stream, bool vt = true) {
   klein_status_t st = check_ws_call(q, k, v, pos_thwl, out, B, S, H, D, dtype, q_descale,
                                     k_descale, v_descale);
   if (st != KLEIN_OK) return st;
@@ -140,15 +143,17 @@ klein_status_t attn_ws(const void* q, const void* k, const void* v,
     hipError_t e;
     const int ncu = current_cu_count(&e);
     if (e != hipSuccess) return map_hip(e);
-    const WsLayout w = ws_layout(B, S, H, D, dtype, ncu);
+    const WsLayout w = ws_layout(B, S, H, D, dtype, ncu, vt);
     const klein::SplitPlan& plan = w.plan;
     if (w.total > 0 && (!workspace || workspace_bytes < (size_t)w.total))
       return KLEIN_ERR_INVALID_ARG;
     LaunchArgs a = make_args(q, k, v, pos_thwl, out, B, S, H, D, stream);
     a.lse = lse;
     if (w.krot_bytes > 0) a.krot = workspace;
+    if (w.vt_bytes > 0) a.vt = static_cast<char*>(workspace) + w.krot_bytes;
     if (plan.n_sk > 0) {
-      a.split.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.krot_bytes);
+      a.split.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.krot_bytes +
+                                              w.vt_bytes);
       a.split.n_dp = plan.n_dp;
       a.split.n_sk = plan.n_sk;
       a.split.n_rem = plan.n_rem;
@@ -445,13 +450,15 @@ klein_status_t klein_rope4d_attn_fwd_noalloc(const void* q, const void* k, const
     hipError_t e;
     const int ncu = current_cu_count(&e);
     if (e != hipSuccess) return map_hip(e);
-    if (ws_layout(B, S, H, D, dtype, ncu).total > klein::kNoallocScratchBytes)
+    // v in key-major tiles where the scratch holds them too
+    const bool vt = ws_layout(B, S, H, D, dtype, ncu, true).total <= klein::kNoallocScratchBytes;
+    if (!vt && ws_layout(B, S, H, D, dtype, ncu, false).total > klein::kNoallocScratchBytes)
       return KLEIN_ERR_UNSUPPORTED;
     void* scratch = nullptr;
     e = klein::noalloc_scratch(&scratch);
     if (e != hipSuccess) return map_hip(e);
     return attn_ws(q, k, v, pos_thwl, out, nullptr, B, S, H, D, dtype, q_descale, k_descale,
-                   v_descale, scratch, (size_t)klein::kNoallocScratchBytes, stream);
+                   v_descale, scratch, (size_t)klein::kNoallocScratchBytes, stream, vt);
   } catch (...) {
     return KLEIN_ERR_LAUNCH;
   }

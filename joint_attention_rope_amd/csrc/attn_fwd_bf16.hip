@@ -47,17 +47,24 @@
 // to inf); the tile's P is then recomputed from its scores.  The final O / l
 // is the same either way.
 //
-// V stays row-major in LDS ([key][d], staged with plain 16-byte copies) and
-// the V^T operand of O^T += V^T P^T is read with ds_read_b64_tr_b16: inside a
-// 16-lane group, lane i receives element i % 4 of the 8-byte words addressed
-// by lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.  Pointing lane L at
-// V[key0 + L/4][d0 + 4 (L % 4) .. + 3] hands lane i keys key0 .. key0+3 of
-// channel d0 + i; two such reads give the 8 keys of one MFMA operand.
+// V^T operands, two ways.  When v arrives regrouped into key-major tiles (a
+// pass before the kernel writes, per 64-key tile, one row of 64 keys per
+// channel), the tile is staged with plain 16-byte copies and each operand (8
+// keys of one channel) is one 16-byte LDS read.  Otherwise V stays row-major
+// in LDS ([key][d], plain 16-byte copies too) and the operand is read with
+// ds_read_b64_tr_b16: inside a 16-lane group, lane i receives element i % 4
+// of the 8-byte words addressed by lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.
+// Pointing lane L at V[key0 + L/4][d0 + 4 (L % 4) .. + 3] hands lane i keys
+// key0 .. key0+3 of channel d0 + i; two such reads give the 8 keys of one
+// MFMA operand.  The transposing reads move half the bytes per clock of plain
+// 16-byte reads, and the LDS is nearly a second bound of this loop.
 //
 // LDS bank spreading: K rows are padded by 16 bytes (the 16 lanes of one
-// 16-byte read phase hit 16 consecutive rows); V rows by 64 bytes, so the 4
-// rows x 64 bytes a 32-lane transposing read phase touches fall on disjoint
-// banks.  Every operand address is a per-lane base plus a constant.
+// 16-byte read phase hit 16 consecutive rows); row-major V rows by 64 bytes,
+// so the 4 rows x 64 bytes a 32-lane transposing read phase touches fall on
+// disjoint banks; key-major V rows (128 bytes) by 16 bytes, so 16 lanes on
+// consecutive channels hit all 64 banks once.  Every operand address is a
+// per-lane base plus a constant.
 #include "klein_device.hpp"
 #include "klein_launch.hpp"
 
@@ -115,7 +122,10 @@ constexpr int kTabN = 256;        // positions covered by the cos/sin table
 // positions or rotation.
 // SPLIT: the split-KV schedule (SplitArgs): whole items first, then the key
 // chunks of the remaining items, merged through the workspace.
-template <int D, bool SPARSE, int ROT, bool SPLIT>
+// VT: v arrives regrouped into key-major tiles (per (b, h) and 64-key tile, D
+// rows of 64 keys, zero past S; launch_v_tiles), so each V^T operand is one
+// 16-byte LDS read instead of two transposing 8-byte reads.
+template <int D, bool SPARSE, int ROT, bool SPLIT, bool VT>
 __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ pos,
@@ -130,6 +140,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   constexpr int MB = D / 32;           // 32-row blocks of O^T
   constexpr int KROW = D + 8;          // LDS row stride of K' (16-bit), padded
   constexpr int VROW = D + 32;         // LDS row stride of V (bf16), padded
+  constexpr int VTROW = BN + 8;        // LDS row stride of a key-major V tile (bf16), padded
   constexpr int DA = D / 4;            // channels per RoPE axis
   constexpr float kSumLimit = 65536.0f;   // 2^16: the rescale trigger
   constexpr int NJ = D / 8;            // rotation pairs per axis
@@ -139,6 +150,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   static_assert(KPT >= 1 && (BN * CPR) % NT == 0, "tile/thread split");
   static_assert(KPT == 1 || KPT % 2 == 0, "V^T store packs key pairs");
   static_assert(!(SPARSE && SPLIT), "one schedule at a time");
+  static_assert(!VT || (!SPARSE && D * VTROW <= BN * VROW), "key-major V tiles: dense, fit");
   constexpr bool QPRE = ROT == kRotBothPre;     // q arrives rotated (fp16)
   constexpr bool KPRE = ROT != kRotInKernel;    // k arrives rotated (fp16)
 
@@ -185,7 +197,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   // keys, values and key positions from the segment's first tile on; Sk
   // keys remain from there
   const uint16_t* kb = k + base + (size_t)k0 * BN * rs;
-  const uint16_t* vb = v + base + (size_t)k0 * BN * rs;
+  const uint16_t* vb = VT ? v + ((size_t)bh * nkt + k0) * (D * BN) : v + base + (size_t)k0 * BN * rs;
   const int32_t* kposb = pos + (size_t)k0 * BN * 4;
   const int Sk = S - k0 * BN;
 
@@ -274,10 +286,21 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     return pack_f16x2(r[0], r[1]);
   };
   auto load_v = [&](int kt) {
-    const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(vb + (size_t)kt * BN * rs, tile_rows(kt) * rowb);
+    if constexpr (VT) {
+      // the whole key-major tile (its padding is zero), 16-byte chunk tid + NT it;
+      // an empty descriptor past the segment's last tile
+      const __amdgpu_buffer_rsrc_t rv =
+          uniform_rsrc(vb + (size_t)kt * D * BN, tile_rows(kt) > 0 ? D * BN * 2 : 0);
 #pragma unroll
-    for (int it = 0; it < KPT; ++it)
-      vx[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, it * rowb, 0));
+      for (int it = 0; it < KPT; ++it)
+        vx[it] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, 16 * (tid + NT * it), 0, 0));
+    } else {
+      const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(vb + (size_t)kt * BN * rs, tile_rows(kt) * rowb);
+#pragma unroll
+      for (int it = 0; it < KPT; ++it)
+        vx[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, it * rowb, 0));
+    }
   };
   // Registers -> LDS: K rotated (fp16), at its permuted row; V transposed.
   auto stage_k = [&](int buf, const int* kp) {
@@ -297,7 +320,12 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     }
   };
   auto stage_v_chunk = [&](int buf, int it) {
-    *reinterpret_cast<u32x4_t*>(&v_lds[buf][(lk + it) * VROW + 8 * lc]) = vx[it];
+    if constexpr (VT) {
+      const int c = tid + NT * it;     // channel c / 8, keys 8 (c % 8) .. + 7
+      *reinterpret_cast<u32x4_t*>(&v_lds[buf][(c >> 3) * VTROW + 8 * (c & 7)]) = vx[it];
+    } else {
+      *reinterpret_cast<u32x4_t*>(&v_lds[buf][(lk + it) * VROW + 8 * lc]) = vx[it];
+    }
   };
   auto stage_v = [&](int buf) {
 #pragma unroll
@@ -462,6 +490,11 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     auto read_v = [&](int i) {
       const int mb = i / 4, kbk = (i >> 1) & 1, j = i & 1;
       // keys 32 kbk + 16 g + 8 j + [0, 4) and + [4, 8), channel 32 mb + lr
+      if constexpr (VT) {
+        va[i] = *reinterpret_cast<const bf16x8_t*>(
+            &v_lds[vbuf][(32 * mb + lr) * VTROW + 32 * kbk + 16 * g + 8 * j]);
+        return;
+      }
       const uint16_t* src = &v_lds[vbuf][vtr_base + (32 * kbk + 8 * j) * VROW + 32 * mb];
       typedef short s16x4_t __attribute__((ext_vector_type(4)));
       const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -635,14 +668,15 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
   }
 }
 
-template <int D, bool SPARSE, int ROT = kRotInKernel, bool SPLIT = false>
+template <int D, bool SPARSE, int ROT = kRotInKernel, bool SPLIT = false, bool VT = false>
 static hipError_t launch_bf16(const LaunchArgs& a) {
   constexpr int BM = 256;
   const int nqt = (a.S + BM - 1) / BM;
   const long long n = SPLIT ? (long long)a.split.n_dp + a.split.n_sk : (long long)a.B * a.H * nqt;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, SPARSE, ROT, SPLIT>), dim3((unsigned)n), dim3(512),
-                     0, a.stream, (const uint16_t*)a.q,
-                     (const uint16_t*)(ROT == kRotKPre ? a.krot : a.k), (const uint16_t*)a.v,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, SPARSE, ROT, SPLIT, VT>), dim3((unsigned)n),
+                     dim3(512), 0, a.stream, (const uint16_t*)a.q,
+                     (const uint16_t*)(ROT == kRotKPre ? a.krot : a.k),
+                     (const uint16_t*)(VT ? a.vt : a.v),
                      a.pos, (uint16_t*)a.out, a.S, a.H, nqt, a.freqs, a.qscale_log2, a.bmask,
                      a.split, a.lse);
   return hipGetLastError();
@@ -654,6 +688,14 @@ static hipError_t launch_bf16_dense(const LaunchArgs& a) {
     // k rotated once into the workspace, then the kernel without K rotation
     hipError_t e = launch_rope4d_fp16(a.k, a.pos, a.krot, a.B, a.S, a.H, D, a.freqs, 1.0f, a.stream);
     if (e != hipSuccess) return e;
+    if (a.vt) {
+      // and v regrouped into key-major tiles
+      e = launch_v_tiles(a.v, a.vt, a.B, a.S, a.H, D, a.stream);
+      if (e != hipSuccess) return e;
+      if (a.split.n_sk == 0) return launch_bf16<D, false, kRotKPre, false, true>(a);
+      e = launch_bf16<D, false, kRotKPre, true, true>(a);
+      return e != hipSuccess ? e : launch_split_merge(a, 1.0f, a.lse);
+    }
     if (a.split.n_sk == 0) return launch_bf16<D, false, kRotKPre>(a);
     e = launch_bf16<D, false, kRotKPre, true>(a);
     return e != hipSuccess ? e : launch_split_merge(a, 1.0f, a.lse);

@@ -30,6 +30,10 @@ struct LaunchArgs {
   // bf16 dense/split paths: workspace for k rotated once (fp16 [B][S][H][D])
   // before the attention kernel, or null (rotate every K tile in the kernel)
   void* krot = nullptr;
+  // bf16 dense/split paths with krot: workspace for v regrouped into
+  // key-major 64-key tiles (v_tiles_bytes), or null (the kernel reads the
+  // V^T operands transposed out of row-major V tiles)
+  void* vt = nullptr;
 };
 
 // where the attention kernels rotate (see attn_fwd_bf16.hip)
@@ -40,6 +44,12 @@ constexpr int kRotBothPre = 2;
 // y = fp16(R(pos) x * scale) for bf16 x [B][S][H][D] (the kernels' rotation routine)
 hipError_t launch_rope4d_fp16(const void* x, const int32_t* pos, void* y, int B, int S, int H,
                               int D, const RopeFreqs& fr, float scale, hipStream_t stream);
+
+// v [B][S][H][D] bf16 -> per (b, h) and 64-key tile, D rows of 64 keys
+// (zero past S), for the bf16 attention kernel's V^T operands
+long long v_tiles_bytes(int B, int S, int H, int D);
+hipError_t launch_v_tiles(const void* v, void* vt, int B, int S, int H, int D,
+                          hipStream_t stream);
 
 // Split-KV cut of a dense call for a GPU of n_cu compute units (n_sk == 0:
 // whole items only, no workspace).  The workspace holds the partial slots.

@@ -131,9 +131,12 @@ def test_repeat_calls_bitwise_identical():
 def test_unsplit_call_equals_per_tile_kernels(D):
     # S < 2048: nothing is split; the keys are still rotated once into the
     # workspace (fp16, or e4m3 codes for fp8: the values the kernels' cos/sin
-    # tables give), so the result equals the dense entry point bit for bit
+    # tables give), and for bf16 the values regrouped into key-major tiles of
+    # 64 keys (16 tiles, the last one zero past key 1000), so the result
+    # equals the dense entry point bit for bit
     inp = random_inputs(2, 1000, 3, D, seed=98)
-    assert kl.klein_attn_workspace_size(2, 1000, 3, D) == 2 * 1000 * 3 * D * 2
+    assert kl.klein_attn_workspace_size(2, 1000, 3, D) == \
+        2 * 1000 * 3 * D * 2 + 2 * 3 * 16 * 64 * D * 2
     out, _ = run_ws(inp)
     assert torch.equal(out.view(torch.int16),
                        run_attention(inp, path="per-tile").view(torch.int16))
@@ -181,11 +184,13 @@ def test_graph_capture_replays():
 @pytest.mark.parametrize("B,S,H,D,fp8", [(2, 16896, 24, 128, False), (1, 33280, 24, 128, True),
                                          (1, 16896, 4, 128, False), (1, 1000, 3, 64, False)])
 def test_workspace_size_is_keys_plus_planned_partials(B, S, H, D, fp8):
-    # the size query on this GPU = the rotated keys (256-aligned) + the
+    # the size query on this GPU = the rotated keys (256-aligned), for bf16
+    # the key-major value tiles (64 keys each, the last one padded), + the
     # partials of the plan for this GPU's compute-unit count
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
     dtype = kl.KLEIN_DTYPE_FP8_E4M3 if fp8 else kl.KLEIN_DTYPE_BF16
     keys = B * S * H * D * (1 if fp8 else 2)
     keys = (keys + 255) // 256 * 256
+    values = 0 if fp8 else B * H * -(-S // 64) * 64 * D * 2
     assert kl.klein_attn_workspace_size(B, S, H, D, dtype) == \
-        keys + kl.klein_splitkv_plan(B, S, H, D, ncu)[3]
+        keys + values + kl.klein_splitkv_plan(B, S, H, D, ncu)[3]

@@ -61,7 +61,7 @@ def test_noalloc_equals_workspace_entry_on_two_calls(kind):
 
 
 def test_noalloc_refuses_shapes_beyond_its_scratch():
-    B, S, H, D = 4, 16896, 24, 128                   # workspace ~517 MB > 320 MiB
+    B, S, H, D = 4, 16896, 24, 128      # 517 MB even with the values row-major
     need = kl.klein_attn_workspace_size(B, S, H, D)
     assert need > kl.KLEIN_NOALLOC_SCRATCH_BYTES
     x = torch.zeros(16, dtype=torch.uint8, device=DEV)   # never read: refused first
@@ -70,7 +70,34 @@ def test_noalloc_refuses_shapes_beyond_its_scratch():
                                                    kl.KLEIN_DTYPE_BF16, 1.0, 1.0, 1.0, None)
     assert st == _capi.KLEIN_ERR_UNSUPPORTED
     assert "scratch" in kl.klein_status_string(st)
-    # the largest headline shapes fit
-    assert kl.klein_attn_workspace_size(2, 16896, 24, 128) <= kl.KLEIN_NOALLOC_SCRATCH_BYTES
+    # the largest fp8 headline shape fits the workspace layout as it is
     assert kl.klein_attn_workspace_size(1, 33280, 24, 128, kl.KLEIN_DTYPE_FP8_E4M3) \
         <= kl.KLEIN_NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_runs_the_bf16_headline_shape():
+    # 2048^2 text-to-image with CFG: the workspace entry's layout (rotated keys,
+    # values regrouped into key-major tiles, partials) needs more than the
+    # scratch, so the call keeps the values row-major and fits; the kernels
+    # differ only in how they read V^T, so the outputs are equal bit for bit
+    B, S, H, D = 2, 16896, 24, 128
+    assert kl.klein_attn_workspace_size(B, S, H, D) > kl.KLEIN_NOALLOC_SCRATCH_BYTES
+    print(f"[case] noalloc bf16 B={B} S={S} H={H} D={D}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(905)
+    q, k, v = (torch.randn(B, S, H, D, device=DEV, generator=g, dtype=torch.bfloat16)
+               for _ in range(3))
+    rng = np.random.default_rng(905)
+    pos = torch.from_numpy(rng.integers(-50, 600, size=(S, 4)).astype(np.int32)).to(DEV)
+    a = torch.full_like(q, float("nan"))
+    stream = torch.cuda.current_stream().cuda_stream
+    st = _capi.lib().klein_rope4d_attn_fwd_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), pos.data_ptr(), a.data_ptr(),
+        B, S, H, D, kl.KLEIN_DTYPE_BF16, 1.0, 1.0, 1.0, stream)
+    assert st == _capi.KLEIN_OK, kl.klein_status_string(st)
+    ws = torch.empty(kl.klein_attn_workspace_size(B, S, H, D), dtype=torch.uint8, device=DEV)
+    b = torch.empty_like(q)
+    kl.klein_rope4d_attn_fwd_ws(q, k, v, pos, b, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    del q, k, v, a, b, ws
+    torch.cuda.empty_cache()
