@@ -6,8 +6,9 @@ text-to-image workload with CFG (cond + uncond batched): B=2, S=16,896
 (512 text + 128x128 image tokens), H=24, D=128, bf16 in/out, inputs resident
 in HBM before timing.  Throughput is attention TFLOP/s = 4*B*H*S^2*D / t.
 The timed call is klein_rope4d_attn_fwd, the attention's own signature: the
-key rotation pass, the attention kernel and its merge kernel (the split-KV
-schedule), in the buffer the library creates on the first (warm-up) call.
+key rotation pass, the pass that regroups the values into key-major tiles,
+the attention kernel and its merge kernel (the split-KV schedule), in the
+buffer the library creates on the first (warm-up) call.
 The same schedule with a caller workspace (workspace_entry_ms), with the
 static scratch of the entry point that allocates nothing (noalloc_entry_ms)
 and the per-tile kernels that need no memory (per_tile_kernels_ms) are timed
@@ -434,11 +435,11 @@ def main():
     q, k, v, pos = to_device(inp, dev)
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     # the timed call: klein_rope4d_attn_fwd, the attention's own signature; its
-    # buffer (keys rotated once, split-KV partials) is created by the first
-    # warm-up call, and the inputs are resident before timing.  The same
-    # schedule with a caller workspace, with the static scratch of the entry
-    # point that allocates nothing, and the per-tile kernels (buffer limit 0)
-    # are timed after it for reference.
+    # buffer (keys rotated once, values in key-major tiles, split-KV partials)
+    # is created by the first warm-up call, and the inputs are resident before
+    # timing.  The same schedule with a caller workspace, with the static
+    # scratch of the entry point that allocates nothing, and the per-tile
+    # kernels (buffer limit 0) are timed after it for reference.
     ms, per_call = time_gpu_calls(lambda: kl.klein_rope4d_attn_fwd(q, k, v, pos, out),
                                   args.steps, args.warmup, torch)
     buf_mb = kl.klein_attn_workspace_size(cfg.B, cfg.S, cfg.H, cfg.D) / 1e6

@@ -30,28 +30,28 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 COPY_KERNEL = "MulFunctor"
 
-# A profiled call of an entry point: the elementwise pass that rotates the
-# keys once (dispatched before the attention kernel), the attention kernel
-# (matched on the demangled name, template arguments included) and, on the
-# split-KV path, the merge kernel dispatched after it; and the sources the
-# measurement depends on.
+# A profiled call of an entry point: the elementwise passes dispatched before
+# the attention kernel (the keys rotated once; for bf16 the values regrouped
+# into key-major tiles), the attention kernel (matched on the demangled name,
+# template arguments included) and, on the split-KV path, the merge kernel
+# dispatched after it; and the sources the measurement depends on.
 CALLS = {
     "attn_fwd_bf16_splitkv": {
-        "before": "rope4d_fp16_kernel<128>",
-        "kernel": "attn_fwd_bf16_kernel<128, false, 1, true>",
+        "before": ["rope4d_fp16_kernel<128>", "v_tiles_kernel<128>"],
+        "kernel": "attn_fwd_bf16_kernel<128, false, 1, true, true>",
         "merge": "split_merge_kernel<128>",
         "sources": ["klein_device.hpp", "attn_fwd_bf16.hip", "split_schedule.hip",
                     "rope_apply.hip"]},
     "attn_fwd_fp8_splitkv": {
-        "before": "rope4d_fp8_kernel<128>",
+        "before": ["rope4d_fp8_kernel<128>"],
         "kernel": "attn_fwd_fp8_kernel<128, false, true, true>",
         "merge": "split_merge_kernel<128>",
         "sources": ["klein_device.hpp", "attn_fwd_fp8.hip", "split_schedule.hip"]},
     "attn_fwd_bf16_dense": {
-        "before": None, "kernel": "attn_fwd_bf16_kernel<128, false, 0, false>", "merge": None,
-        "sources": ["klein_device.hpp", "attn_fwd_bf16.hip"]},
+        "before": [], "kernel": "attn_fwd_bf16_kernel<128, false, 0, false, false>",
+        "merge": None, "sources": ["klein_device.hpp", "attn_fwd_bf16.hip"]},
     "attn_fwd_fp8_dense": {
-        "before": None, "kernel": "attn_fwd_fp8_kernel<128, false, false, false>", "merge": None,
+        "before": [], "kernel": "attn_fwd_fp8_kernel<128, false, false, false>", "merge": None,
         "sources": ["klein_device.hpp", "attn_fwd_fp8.hip"]},
 }
 
@@ -101,16 +101,16 @@ def _ids(rows, name):
 
 
 def call_durations_ns(stats_dir, call):
-    """Per call, in dispatch order: (rotation pass ns, attention kernel ns,
-    merge kernel ns)."""
+    """Per call, in dispatch order: (passes before the kernel ns, attention
+    kernel ns, merge kernel ns)."""
     c = CALLS[call]
     rows = _rows(_find(stats_dir, "kernel_trace.csv"))
     dur = {int(r["Dispatch_Id"]): int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows}
     ks = _ids(rows, c["kernel"])
     pm = _pair(ks, _ids(rows, c["merge"]))
-    pb = _pair(ks, _ids(rows, c["before"]), after=False)
+    pbs = [_pair(ks, _ids(rows, b), after=False) for b in c["before"]]
     get = lambda d: dur[d] if d is not None else 0
-    return [(get(pb[k]), dur[k], get(pm[k])) for k in sorted(ks)]
+    return [(sum(get(pb[k]) for pb in pbs), dur[k], get(pm[k])) for k in sorted(ks)]
 
 
 def counter_per_dispatch(pmc_dir, kernel, counter):
@@ -124,16 +124,18 @@ def counter_per_dispatch(pmc_dir, kernel, counter):
 
 
 def call_counter(pmc_dir, call, counter):
-    """Per call: the counter of the attention kernel plus those of its
-    rotation pass and merge."""
+    """Per call: the counter of the attention kernel plus those of the
+    passes before it and of its merge."""
     c = CALLS[call]
     ks = counter_per_dispatch(pmc_dir, c["kernel"], counter)
     ms = counter_per_dispatch(pmc_dir, c["merge"], counter) if c["merge"] else {}
-    bs = counter_per_dispatch(pmc_dir, c["before"], counter) if c["before"] else {}
     pm = _pair(list(ks), list(ms))
-    pb = _pair(list(ks), list(bs), after=False)
-    return [ks[k] + (ms[pm[k]] if pm[k] is not None else 0.0) + (bs[pb[k]] if pb[k] is not None else 0.0)
-            for k in sorted(ks)]
+    out = [ks[k] + (ms[pm[k]] if pm[k] is not None else 0.0) for k in sorted(ks)]
+    for b in c["before"]:
+        bs = counter_per_dispatch(pmc_dir, b, counter)
+        pb = _pair(list(ks), list(bs), after=False)
+        out = [o + (bs[pb[k]] if pb[k] is not None else 0.0) for o, k in zip(out, sorted(ks))]
+    return out
 
 
 # Counter passes (8 SQ counters and one GRBM counter per pass at most).
@@ -487,7 +489,7 @@ def main():
     call = CALLS[args.call]
     srcs = call["sources"]
     shash = sources_hash(srcs)
-    kinds = (f"`{call['before']}` + " if call["before"] else "") + f"`{call['kernel']}`" + \
+    kinds = "".join(f"`{b}` + " for b in call["before"]) + f"`{call['kernel']}`" + \
         (f" + `{call['merge']}`" if call["merge"] else "")
     if args.counters:
         from workloads import get_config
@@ -540,7 +542,7 @@ Commands (run from /tmp with TMPDIR=/tmp; R = repository root):
 | calls | {len(durs)} |
 | average duration per call, all calls | {avg_all:.4f} ms |
 | average duration per call, calls {args.warmup + 1}-{args.warmup + args.steps} (the timed calls) | {avg_timed:.4f} ms |
-| of which the key rotation pass | {avg_rot:.4f} ms |
+| of which the passes before the kernel ({', '.join(b.split('<')[0] for b in call['before']) or 'none'}) | {avg_rot:.4f} ms |
 | of which the attention kernel | {avg_attn:.4f} ms |
 | of which the merge kernel | {avg_merge:.4f} ms |
 | min / max per call | {min(durs) / 1e6:.4f} / {max(durs) / 1e6:.4f} ms |
