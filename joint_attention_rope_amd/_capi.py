@@ -9,6 +9,9 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libklein_attn.so")
+# the race check copy: the attention kernels with a full wait and a workgroup
+# barrier at every stage boundary (tests compare it with the library)
+SYNC_LIB_PATH = os.path.join(PKG, "libklein_attn_sync.so")
 
 KLEIN_DTYPE_BF16 = 0
 KLEIN_DTYPE_FP8_E4M3 = 1
@@ -64,18 +67,23 @@ SIGNATURES = {
 }
 
 
+def load(path):
+    """A build of the library at `path` (ctypes.CDLL) with the ABI's signatures."""
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build the HIP library first "
+            "(python -m joint_attention_rope_amd.build)")
+    l = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(l, name)
+        fn.restype = res
+        fn.argtypes = args
+    return l
+
+
 def lib():
     """The loaded library (ctypes.CDLL), loading it on first use."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(
-                f"{LIB_PATH} is missing: build the HIP library first "
-                "(python -m joint_attention_rope_amd.build)")
-        l = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(l, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = l
+        _lib = load(LIB_PATH)
     return _lib

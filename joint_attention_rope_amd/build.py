@@ -1,7 +1,11 @@
-"""Build the gfx950 HIP library libklein_attn.so in-tree with hipcc, and the
-measurement harness step_clock (the bf16 and fp8 attention kernels and the
-QKV projection with per-part cycle counters, linked with the library's other
-objects; not part of the library).
+"""Build the gfx950 HIP library libklein_attn.so in-tree with hipcc; its race
+check copy libklein_attn_sync.so (the attention kernels compiled with
+KLEIN_SYNC_CHECK: a full wait and a workgroup barrier at every stage
+boundary of their pipeline step, otherwise the same objects), which the GPU
+tests compare with the library bit for bit; and the measurement harness
+step_clock (the bf16 and fp8 attention kernels and the QKV projection with
+per-part cycle counters, linked with the library's other objects; not part
+of the library).
 
 Usage: python -m joint_attention_rope_amd.build
 """
@@ -13,11 +17,14 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libklein_attn.so")
+SYNC_LIB = os.path.join(PKG, "libklein_attn_sync.so")
 STEP_CLOCK = os.path.join(PKG, "step_clock")
 # the harness replaces these sources (it includes them with the cycle counters
 # on; it is compiled with the attention kernels' flags, which leave the
 # projection's instructions unchanged)
 STEP_CLOCK_REPLACES = ("attn_fwd_bf16.hip", "attn_fwd_fp8.hip", "qkv_rope_proj.hip")
+# sources compiled a second time, with KLEIN_SYNC_CHECK, for the race check copy
+SYNC_CHECKED = ("attn_fwd_bf16.hip", "attn_fwd_fp8.hip")
 SOURCES = ["api.cpp", "attn_fwd_bf16.hip", "attn_fwd_fp8.hip", "qkv_rope_proj.hip", "rope_apply.hip",
            "split_schedule.hip", "attn_bwd.hip", "noalloc.hip"]
 # Device kernels never see NaN inputs on purpose (a NaN in q/k/v propagates to
@@ -47,7 +54,8 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source (always) and link libklein_attn.so."""
+    """Compile every source (always) and link libklein_attn.so, its race
+    check copy and the step_clock harness."""
     tag = "%d" % os.getpid()
     objs = {}
     try:
@@ -57,10 +65,19 @@ def build(verbose: bool = False) -> str:
             flags = KERNEL_FLAGS.get(STEP_CLOCK_REPLACES[0] if src == "step_clock.hip" else src, [])
             _run([HIPCC, *cflags, *flags, "-c", "-o", obj, os.path.join(CSRC, src)], verbose)
             objs[src] = obj
+        for src in SYNC_CHECKED:
+            obj = os.path.join(CSRC, src + ".sync.o" + tag)
+            _run([HIPCC, *cflags, *KERNEL_FLAGS.get(src, []), "-DKLEIN_SYNC_CHECK", "-c", "-o", obj,
+                  os.path.join(CSRC, src)], verbose)
+            objs[src + ".sync"] = obj
         lib_objs = [objs[s] for s in SOURCES]
         tmp = LIB + ".tmp" + tag
         _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *lib_objs], verbose)
         os.replace(tmp, LIB)
+        sync_objs = [objs[s + ".sync"] if s in SYNC_CHECKED else objs[s] for s in SOURCES]
+        tmp = SYNC_LIB + ".tmp" + tag
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *sync_objs], verbose)
+        os.replace(tmp, SYNC_LIB)
         clock_objs = [objs[s] for s in SOURCES if s not in STEP_CLOCK_REPLACES] + [objs["step_clock.hip"]]
         tmp = STEP_CLOCK + ".tmp" + tag
         _run([HIPCC, "--offload-arch=gfx950", "-o", tmp, *clock_objs], verbose)

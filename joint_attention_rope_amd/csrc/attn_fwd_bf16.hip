@@ -106,6 +106,24 @@ __device__ unsigned long long* klein_step_clock_out;
 #define KLEIN_CLOCK_STORE(nsteps)
 #endif
 
+// Race check build: KLEIN_SYNC_CHECK is defined only for the library's
+// synchronised copy (libklein_attn_sync.so), never for the library itself.
+// At every stage boundary of the pipeline step each wave then waits for all
+// of its outstanding memory operations (s_waitcnt 0) and for the whole
+// workgroup, so no LDS hand-off between waves can overlap the next stage.
+// The arithmetic is unchanged, so both builds must give the same bits; a
+// difference means the fast build reads LDS data before it is written or
+// overwrites it before it is read.
+#ifdef KLEIN_SYNC_CHECK
+#define KLEIN_SYNC_POINT()                                                   \
+  do {                                                                       \
+    __builtin_amdgcn_s_waitcnt(0);                                           \
+    __syncthreads();                                                         \
+  } while (0)
+#else
+#define KLEIN_SYNC_POINT() do {} while (0)
+#endif
+
 constexpr int kTabN = 256;        // positions covered by the cos/sin table
 
 // SPARSE: block-sparse variant; bmask holds one byte per (batch, head, query
@@ -607,11 +625,14 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int it = 0; it < KPT; ++it) ci[it] = key_cs_index(kps, it);
     mask_tail(tl(t), cur);
+    KLEIN_SYNC_POINT();
     KLEIN_CLOCK_MARK(0);
     float lt = region_a((t + 1) & 1, cur, nxt, pw, kpre);
+    KLEIN_SYNC_POINT();
     KLEIN_CLOCK_MARK(1);
     if (__builtin_amdgcn_ballot_w64(lt > kSumLimit)) lt = rescale(cur, nxt, pw);
     l_run += lt;
+    KLEIN_SYNC_POINT();
     KLEIN_CLOCK_MARK(2);
     // K(t+2) into buffer t&1 (it held K(t), consumed last step); V(t+1) into
     // buffer (t+1)&1 (it held V(t-1), consumed last step).  The barrier comes
@@ -619,6 +640,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     // registers, and the next region A's first K(t+2) operands are read
     // while they run.
     region_b(t & 1, t & 1, (t + 1) & 1, pw, ci, [&]() {
+      KLEIN_SYNC_POINT();
       KLEIN_CLOCK_MARK(3);
       load_k(tl(t + 3));
       load_pos(tl(t + 4), kps);
@@ -629,6 +651,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
       kpre[0] = read_k_op(t & 1, 0);
       kpre[1] = read_k_op(t & 1, 1);
     });
+    KLEIN_SYNC_POINT();
     KLEIN_CLOCK_MARK(3);
   };
   int t = 0;

@@ -115,6 +115,24 @@ __device__ unsigned long long* klein_fp8_clock_out;
 #define KLEIN_FP8_CLOCK_STORE(nsteps)
 #endif
 
+// Race check build: KLEIN_SYNC_CHECK is defined only for the library's
+// synchronised copy (libklein_attn_sync.so), never for the library itself.
+// At every stage boundary of the pipeline step each wave then waits for all
+// of its outstanding memory operations (s_waitcnt 0) and for the whole
+// workgroup, so no LDS hand-off between waves can overlap the next stage.
+// The arithmetic is unchanged, so both builds must give the same bits; a
+// difference means the fast build reads LDS data before it is written or
+// overwrites it before it is read.
+#ifdef KLEIN_SYNC_CHECK
+#define KLEIN_SYNC_POINT()                                                   \
+  do {                                                                       \
+    __builtin_amdgcn_s_waitcnt(0);                                           \
+    __syncthreads();                                                         \
+  } while (0)
+#else
+#define KLEIN_SYNC_POINT() do {} while (0)
+#endif
+
 namespace {
 
 constexpr float kHalf = 0.5f;
@@ -567,15 +585,19 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   auto step = [&](int t, f32x16_t* cur, f32x16_t* nxt, int& kps) {
     const int ci = key_cs_index(kps);
     softmax_max(tl(t), cur);
+    KLEIN_SYNC_POINT();
     KLEIN_FP8_CLOCK_MARK(0);
     region_a((t + 1) & 1, cur, nxt, pb);
+    KLEIN_SYNC_POINT();
     KLEIN_FP8_CLOCK_MARK(1);
     // K''(t+2) into buffer t&1 (it held K''(t)); V(t+1) into buffer (t+1)&1
     region_b(t & 1, t & 1, (t + 1) & 1, pb, ci);
+    KLEIN_SYNC_POINT();
     KLEIN_FP8_CLOCK_MARK(2);
     load_k(tl(t + 3));
     load_pos(tl(t + 4), kps);
     load_v(tl(t + 2));
+    KLEIN_SYNC_POINT();
     KLEIN_FP8_CLOCK_MARK(3);
     __syncthreads();
     KLEIN_FP8_CLOCK_MARK(4);
