@@ -500,13 +500,14 @@ def main():
             per_tile5 = time_per_tile(kl, lambda: kl.klein_rope4d_attn_fwd_fp8(
                 q5, k5, v5, p5, o5, *inp5.descale), 3, 1, torch)
             t5 = cfg5.flops / (ms5 * 1e-3) / 1e12
+            traffic5 = stored_traffic("attn_fwd_fp8_2048px_edit", "attn_fwd_fp8_splitkv")
             rec["fp8"] = {"workload": "2048x2048 edit: B=1, S=33280 (512 text + 2 x 128x128), "
                                       "H=24, D=128, e4m3 in, bf16 out",
                           "ms_per_call": round(ms5, 4), "tflops": round(t5, 2),
                           "peak": PEAK_FP8, "frac": round(t5 / PEAK_FP8, 4),
-                          "traffic": stored_traffic("attn_fwd_fp8_2048px_edit",
-                                                    "attn_fwd_fp8_splitkv"),
-                          "traffic_source": traffic_source("attn_fwd_fp8_2048px_edit"),
+                          "traffic": traffic5,
+                          "traffic_source": traffic_source("attn_fwd_fp8_2048px_edit")
+                          if traffic5 is not None else None,
                           "entry_point": "klein_rope4d_attn_fwd_fp8 (split-KV schedule in "
                                          "the library's buffer)",
                           "workspace_entry_ms": round(ws5_ms, 4),
