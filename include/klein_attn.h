@@ -178,11 +178,12 @@ klein_status_t klein_rope4d_attn_fwd_fp8(const void* q, const void* k, const voi
  * The keys are also rotated once, into `workspace` (fp16 for bf16 inputs,
  * E4M3 codes of R k / 2 for fp8), before the attention kernel; the dense
  * entry points rotate every key tile once per tile of 256 queries.  The
- * values equal those the dense kernels form.  For bf16 the values are also
- * regrouped once into key-major tiles (per head and 64-key tile, one row of
- * 64 keys per channel), which the kernel reads with plain 16-byte LDS reads
- * instead of transposing ones; this moves data only, so the output bits do
- * not change.
+ * values equal those the dense kernels form.  For bf16 with S >= 12,288 the
+ * values are also regrouped once into key-major tiles (per head and 64-key
+ * tile, one row of 64 keys per channel), which the kernel reads with plain
+ * 16-byte LDS reads instead of transposing ones; this moves data only, so
+ * the output bits do not change (shorter sequences gain less than the pass
+ * costs).
  *   workspace      : DEVICE pointer, 256-byte aligned, caller-owned, at least
  *                    the size klein_attn_workspace_size reports for the same
  *                    shape on the current device (may be NULL when that is 0).
@@ -201,13 +202,13 @@ klein_status_t klein_rope4d_attn_fwd_ws(const void* q, const void* k, const void
 /*
  * Workspace bytes klein_rope4d_attn_fwd_ws needs for this shape on the
  * current HIP device: the rotated keys (B*S*H*D*2 bytes for bf16, B*S*H*D
- * for fp8, rounded up to a multiple of 256), for bf16 the key-major value
- * tiles (B*H*ceil(S/64)*64*D*2 bytes), then the split partials (0 when the
- * tiles fill whole rounds, or the sequence is shorter than 2048 keys, and
- * nothing is split; at most 4 * (number of compute units) * (256 * D + 1024)
- * * 4 bytes, 138 MB for D = 128 on 256 compute units).  Writes *bytes; INVALID_ARG for a
- * null `bytes`, sizes < 1 or a bad dtype, UNSUPPORTED for D not in {64, 128},
- * NO_DEVICE without a usable GPU.
+ * for fp8, rounded up to a multiple of 256), for bf16 with S >= 12,288 the
+ * key-major value tiles (B*H*ceil(S/64)*64*D*2 bytes), then the split
+ * partials (0 when the tiles fill whole rounds, or the sequence is shorter
+ * than 2048 keys, and nothing is split; at most 4 * (number of compute
+ * units) * (256 * D + 1024) * 4 bytes, 138 MB for D = 128 on 256 compute
+ * units).  Writes *bytes; INVALID_ARG for a null `bytes`, sizes < 1 or a bad
+ * dtype, UNSUPPORTED for D not in {64, 128}, NO_DEVICE without a usable GPU.
  */
 klein_status_t klein_attn_workspace_size(int B, int S, int H, int D, klein_dtype_t dtype,
                                          size_t* bytes);

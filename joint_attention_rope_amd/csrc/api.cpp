@@ -77,9 +77,17 @@ LaunchArgs make_args(const void* q, const void* k, const void* v, const int32_t*
 
 constexpr long long kMaxGrid = 2147483647LL;
 
+// Sequences from which the bf16 workspace schedule also regroups v into
+// key-major tiles.  The pass costs a read and a write of V per call; the
+// kernel saves LDS time per key tile and query tile, so the gain grows with S.
+// Measured (same process, MI355X): +1.9 % at S = 16,896 (B = 2, H = 24),
+// -1.3 % at S = 8,704 and -1.7 % at S = 4,608 (B = 1, H = 24).
+constexpr int kVTilesMinS = 12288;
+
 // Workspace of klein_rope4d_attn_fwd_ws: k rotated once (fp16 for bf16
-// inputs, e4m3 codes for fp8, [B][S][H][D]), for bf16 with `vt` v in
-// key-major tiles (klein::v_tiles_bytes), and the split-KV partials.
+// inputs, e4m3 codes for fp8, [B][S][H][D]), for bf16 with `vt` and S of at
+// least kVTilesMinS v in key-major tiles (klein::v_tiles_bytes), and the
+// split-KV partials.
 struct WsLayout {
   long long krot_bytes;
   long long vt_bytes;         // at offset krot_bytes
@@ -90,7 +98,8 @@ WsLayout ws_layout(int B, int S, int H, int D, klein_dtype_t dtype, int ncu, boo
   WsLayout w{};
   const int elem = dtype == KLEIN_DTYPE_BF16 ? 2 : 1;      // fp16 or e4m3 rotated keys
   w.krot_bytes = ((long long)B * S * H * D * elem + 255) / 256 * 256;
-  w.vt_bytes = vt && dtype == KLEIN_DTYPE_BF16 ? klein::v_tiles_bytes(B, S, H, D) : 0;
+  w.vt_bytes = vt && dtype == KLEIN_DTYPE_BF16 && S >= kVTilesMinS
+                   ? klein::v_tiles_bytes(B, S, H, D) : 0;
   w.plan = klein::plan_split(B, S, H, D, ncu);
   w.total = w.krot_bytes + w.vt_bytes + w.plan.bytes;
   return w;

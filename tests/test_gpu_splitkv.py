@@ -110,6 +110,26 @@ def test_workload_4_full_size():
     assert_bf16_close(got, oracle_rows(inp, rows), "workload 4 split-KV")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_value_tiles_ragged_tail(D):
+    # 12,345 keys: the bf16 schedule regroups the values into key-major tiles,
+    # the last one holding 57 keys and zeros; rows of whole query tiles equal
+    # the per-tile kernels (row-major values) bit for bit, split rows and the
+    # last rows match the oracle
+    B, S, H = 1, 12345, 3
+    inp = random_inputs(B, S, H, D, seed=990 + D)
+    out, nbytes = run_ws(inp)
+    assert nbytes >= B * S * H * D * 2 + B * H * 193 * 64 * D * 2
+    ref = run_attention(inp, path="per-tile")
+    split = split_rows_mask(B, S, H)
+    a = out.view(torch.int16).cpu().numpy()
+    b = ref.view(torch.int16).cpu().numpy()
+    assert np.array_equal(a[~split], b[~split]), "whole tiles must equal the dense kernel"
+    rows = np.unique(np.r_[0, 1, 255, 256, S - 57, S - 2, S - 1, np.arange(5, S, 811)])
+    got = bf16_tensor_to_f64(out[:, torch.from_numpy(rows).to(DEV)])
+    assert_bf16_close(got, oracle_rows(inp, rows), f"value tiles D={D}")
+
+
 def test_workload_5_fp8_full_size():
     cfg = get_config(5)
     inp = make_inputs(cfg)
@@ -131,12 +151,10 @@ def test_repeat_calls_bitwise_identical():
 def test_unsplit_call_equals_per_tile_kernels(D):
     # S < 2048: nothing is split; the keys are still rotated once into the
     # workspace (fp16, or e4m3 codes for fp8: the values the kernels' cos/sin
-    # tables give), and for bf16 the values regrouped into key-major tiles of
-    # 64 keys (16 tiles, the last one zero past key 1000), so the result
-    # equals the dense entry point bit for bit
+    # tables give), so the result equals the dense entry point bit for bit
+    # (the values stay row-major below 12,288 keys)
     inp = random_inputs(2, 1000, 3, D, seed=98)
-    assert kl.klein_attn_workspace_size(2, 1000, 3, D) == \
-        2 * 1000 * 3 * D * 2 + 2 * 3 * 16 * 64 * D * 2
+    assert kl.klein_attn_workspace_size(2, 1000, 3, D) == 2 * 1000 * 3 * D * 2
     out, _ = run_ws(inp)
     assert torch.equal(out.view(torch.int16),
                        run_attention(inp, path="per-tile").view(torch.int16))
@@ -182,15 +200,16 @@ def test_graph_capture_replays():
 
 
 @pytest.mark.parametrize("B,S,H,D,fp8", [(2, 16896, 24, 128, False), (1, 33280, 24, 128, True),
-                                         (1, 16896, 4, 128, False), (1, 1000, 3, 64, False)])
+                                         (1, 16896, 4, 128, False), (1, 1000, 3, 64, False),
+                                         (1, 12287, 2, 64, False), (1, 12288, 2, 64, False)])
 def test_workspace_size_is_keys_plus_planned_partials(B, S, H, D, fp8):
     # the size query on this GPU = the rotated keys (256-aligned), for bf16
-    # the key-major value tiles (64 keys each, the last one padded), + the
-    # partials of the plan for this GPU's compute-unit count
+    # from 12,288 keys on the key-major value tiles (64 keys each, the last
+    # one padded), + the partials of the plan for this GPU's compute-unit count
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
     dtype = kl.KLEIN_DTYPE_FP8_E4M3 if fp8 else kl.KLEIN_DTYPE_BF16
     keys = B * S * H * D * (1 if fp8 else 2)
     keys = (keys + 255) // 256 * 256
-    values = 0 if fp8 else B * H * -(-S // 64) * 64 * D * 2
+    values = 0 if fp8 or S < 12288 else B * H * -(-S // 64) * 64 * D * 2
     assert kl.klein_attn_workspace_size(B, S, H, D, dtype) == \
         keys + values + kl.klein_splitkv_plan(B, S, H, D, ncu)[3]

@@ -7,10 +7,11 @@ differs.  A stage that read LDS data before another wave had written it, or
 overwrote a buffer another wave still read, would give different bits in the
 fast build, so every entry point that runs these kernels must return the same
 bits from both: the split-KV schedule (keys rotated once; bf16 values in
-key-major tiles), the per-tile kernels with the rotation in the kernel, the
-block-sparse kernels, the attention on pre-rotated inputs and the training
-forward with lse, on ragged shapes, both head sizes and both formats.  Each
-call also runs twice on the fast build (repeat runs must agree too).
+key-major tiles from 12,288 keys on), the per-tile kernels with the rotation
+in the kernel, the block-sparse kernels, the attention on pre-rotated inputs
+and the training forward with lse, on ragged shapes, both head sizes and both
+formats.  Each call also runs twice on the fast build (repeat runs must agree
+too).
 """
 
 import contextlib
@@ -62,8 +63,9 @@ def dtype_of(inp):
     return kl.KLEIN_DTYPE_BF16 if inp.descale is None else kl.KLEIN_DTYPE_FP8_E4M3
 
 
-CASES = [((2, 2500, 5, 128), False), ((1, 1000, 3, 64), False), ((1, 2100, 3, 64), True),
-         ((2, 1300, 2, 128), True)]
+# the bf16 cases of 12,288 keys or more take the key-major value tiles
+CASES = [((2, 2500, 5, 128), False), ((1, 1000, 3, 64), False), ((1, 12500, 2, 128), False),
+         ((1, 13001, 1, 64), False), ((1, 2100, 3, 64), True), ((2, 1300, 2, 128), True)]
 
 
 @pytest.mark.parametrize("shape,fp8", CASES)
