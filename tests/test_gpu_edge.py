@@ -1,8 +1,9 @@
 """GPU edge cases beyond the workloads: a sequence longer than 65,535 tokens
 with positions outside the kernels' cos/sin tables, odd batch and head
-counts, and FP8 descales whose product is moderate while each factor is
-extreme (the score scale then leaves one E8M0 operand's range and is split)
-or whose product is tiny (the softmax must come out uniform)."""
+counts, bf16 inputs at the edge of the range the fp16 score operands hold,
+and FP8 descales whose product is moderate while each factor is extreme (the
+score scale then leaves one E8M0 operand's range and is split) or whose
+product is tiny (the softmax must come out uniform)."""
 
 import numpy as np
 import pytest
@@ -50,6 +51,30 @@ def test_odd_batch_and_heads_full(fp8, path):
         check = assert_bf16_close
     out = run_attention(inp, path=path)
     check(bf16_tensor_to_f64(out), oracle_full(inp), f"B=3 H=5 fp8={fp8}")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_bf16_magnitudes_at_the_stated_range(path):
+    # |k| up to 40,000 and |q| up to 300,000 (the stated limits are ~46,000
+    # and ~360,000): the rotated, scaled q and k still fit fp16.  The large
+    # values sit in channel pairs where the other operand is zero, so the
+    # scores stay moderate and the softmax is not one-hot; the result must
+    # match the oracle as ordinary inputs do.
+    from workloads import bf16_bits_from_f32
+    rng = np.random.default_rng(94)
+    B, S, H, D = 1, 700, 2, 128
+    q = rng.standard_normal((B, S, H, D)).astype(np.float32)
+    k = rng.standard_normal((B, S, H, D)).astype(np.float32)
+    v = rng.standard_normal((B, S, H, D)).astype(np.float32)
+    q[..., 0:2] = 0.0
+    k[..., 0:2] = rng.choice([-40000.0, 40000.0], size=(B, S, H, 2))
+    k[..., 34:36] = 0.0
+    q[..., 34:36] = rng.choice([-300000.0, 300000.0], size=(B, S, H, 2))
+    base = random_inputs(B, S, H, D, seed=94)
+    inp = Inputs(base.cfg, bf16_bits_from_f32(q), bf16_bits_from_f32(k), bf16_bits_from_f32(v),
+                 base.pos)
+    out = run_attention(inp, path=path)
+    assert_bf16_close(bf16_tensor_to_f64(out), oracle_full(inp), f"large magnitudes {path}")
 
 
 def _with_descales(inp, dq, dk, dv):
