@@ -403,7 +403,8 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   auto score_mfma = [&](i32x8_t a, int ks, f32x16_t c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qreg[ks], c, 0, 0, 0, sc_a, 0, sc_b);
   };
-  auto rowmax32 = [&](const f32x16_t* sc) {
+  // largest of the 32 values a lane holds (rowmax32: of its row, both lanes)
+  auto lanemax32 = [&](const f32x16_t* sc) {
     float m[12];
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
@@ -416,8 +417,9 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
     float n[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) n[i] = __builtin_fmaxf(m[3 * i], __builtin_fmaxf(m[3 * i + 1], m[3 * i + 2]));
-    return pair_max(__builtin_fmaxf(n[0], __builtin_fmaxf(n[1], __builtin_fmaxf(n[2], n[3]))));
+    return __builtin_fmaxf(n[0], __builtin_fmaxf(n[1], __builtin_fmaxf(n[2], n[3])));
   };
+  auto rowmax32 = [&](const f32x16_t* sc) { return pair_max(lanemax32(sc)); };
   f32x16_t cinit;
   auto set_cinit = [&]() {
 #pragma unroll
@@ -434,8 +436,11 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(
   };
   auto softmax_max = [&](int t, f32x16_t* sc) {
     mask_tail(t, sc);
-    const float mx = rowmax32(sc);              // code of the row's largest score
-    if (__builtin_amdgcn_ballot_w64(mx > YMAX)) {
+    // a row passes YMAX exactly when one of its two lanes does, so the test
+    // needs no exchange; the rare rescale takes the row max
+    const float lm = lanemax32(sc);
+    if (__builtin_amdgcn_ballot_w64(lm > YMAX)) {
+      const float mx = pair_max(lm);            // code of the row's largest score
       const float delta = __builtin_fmaxf(mx - YR, 0.f);
       const float alpha = __builtin_amdgcn_exp2f(-0.125f * delta);
       m8 += delta;
