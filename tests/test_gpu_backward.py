@@ -137,10 +137,11 @@ def test_repeat_bitwise_identical():
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
-@pytest.mark.parametrize("B,S,H", [(1, 2500, 4), (2, 900, 3)])
+@pytest.mark.parametrize("B,S,H", [(1, 2500, 4), (2, 900, 3), (1, 12300, 1)])
 def test_forward_with_lse_on_the_split_schedule(B, S, H):
     # the workspace variant: tiles that run whole give the same bits as the
-    # plain training forward, split tiles match the oracle (out and lse)
+    # plain training forward, split tiles match the oracle (out and lse); at
+    # 12,300 keys the workspace variant reads the values as key-major tiles
     import oracle
     inp = random_inputs(B, S, H, 128, seed=S + H)
     q, k, v, pos = to_device(inp)
