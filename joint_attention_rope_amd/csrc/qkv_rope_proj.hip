@@ -28,6 +28,8 @@
 // before the step's last sub-step so that the reads of the next buffer
 // overlap MFMAs.  Rows past N or M read as zeros through the buffer
 // descriptors and are not stored.
+#include <type_traits>
+
 #include "klein_device.hpp"
 #include "klein_launch.hpp"
 
@@ -298,23 +300,28 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
   }
   // the 4 outputs of (nb, c4, mb), rounded: bias, then the rotation for q
   // and k (channel db + 8 c4 + 4 g + 0..3 of a head, db the block's first)
-  auto emit = [&](int nb, int c4, int mb, bool rotate, int db) -> u32x2_t {
+  // (`rot` is a compile-time flag, so that the caller's loops over the
+  // outputs hold no branch and their LDS reads can be issued together)
+  auto emit = [&](int nb, int c4, int mb, auto rot, int db) -> u32x2_t {
     const f32x4_t bs = *reinterpret_cast<const f32x4_t*>(&ep_bias[128 * wn + 32 * nb + 8 * c4 + 4 * g]);
     float y[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) y[e] = acc[nb][mb][4 * c4 + e] * yscale + bs[e];
-    if (!rotate) return (u32x2_t){pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-    // one axis a for both lane halves (D/4 divides 32)
-    const float fp = ep_pos[64 * wm + 32 * mb + lr][(db + 8 * c4) / DA];
+    if constexpr (!decltype(rot)::value) {
+      return (u32x2_t){pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+    } else {
+      // one axis a for both lane halves (D/4 divides 32)
+      const float fp = ep_pos[64 * wm + 32 * mb + lr][(db + 8 * c4) / DA];
 #pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-      const float rev = rope_rev(fp, fhi[c4][pr], flo[c4][pr]);
-      const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
-      const f32x2_t r = rope_rot(y[2 * pr], y[2 * pr + 1], cs, sn);
-      y[2 * pr] = r[0];
-      y[2 * pr + 1] = r[1];
+      for (int pr = 0; pr < 2; ++pr) {
+        const float rev = rope_rev(fp, fhi[c4][pr], flo[c4][pr]);
+        const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+        const f32x2_t r = rope_rot(y[2 * pr], y[2 * pr + 1], cs, sn);
+        y[2 * pr] = r[0];
+        y[2 * pr + 1] = r[1];
+      }
+      return (u32x2_t){pack_f16x2(y[0], y[1]), pack_f16x2(y[2], y[3])};
     }
-    return (u32x2_t){pack_f16x2(y[0], y[1]), pack_f16x2(y[2], y[3])};
   };
   if (HD % 128 == 0) {
     // The wave's 128 features are one contiguous segment of one output's
@@ -335,15 +342,22 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
       uint16_t* const xl = (wave < 4 ? a_lds[lbuf] : b_lds[lbuf]) + (wave & 3) * (32 * XR);
       static_assert(4 * 32 * XR <= TN * ROW, "transpose slices");
       const int rr = lane >> 4, cc = lane & 15;  // row 4 i + rr, 8-byte chunk cc of a half
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      // one straight-line copy of the output loop for q and k (rotated), one for v
+      auto out_half = [&](int mb, auto rot) {
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
           for (int c4 = 0; c4 < 4; ++c4) {
-            const u32x2_t o = emit(nb, c4, mb, which < 2, (hdw + 32 * nb) % D);
+            const u32x2_t o = emit(nb, c4, mb, rot, (hdw + 32 * nb) % D);
             *reinterpret_cast<u32x2_t*>(xl + lr * XR + 32 * nb + 8 * c4 + 4 * g) = o;
           }
+      };
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        if (which < 2)
+          out_half(mb, std::true_type{});
+        else
+          out_half(mb, std::false_type{});
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -372,8 +386,10 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
       for (int c4 = 0; c4 < 4; ++c4)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
-          __builtin_amdgcn_raw_buffer_store_b64(emit(nb, c4, mb, which < 2, hdb % D), ro, voff[mb],
-                                                (hdb + 8 * c4) * 2, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(
+              which < 2 ? emit(nb, c4, mb, std::true_type{}, hdb % D)
+                        : emit(nb, c4, mb, std::false_type{}, hdb % D),
+              ro, voff[mb], (hdb + 8 * c4) * 2, 0);
     }
   }
   KLEIN_QKV_CLOCK_STORE(nk)
