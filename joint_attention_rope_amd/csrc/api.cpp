@@ -582,6 +582,9 @@ static klein_status_t qkv_proj(const void* x, const void* w, const void* bias,
     a.q = (uint16_t*)q_out; a.k = (uint16_t*)k_out; a.v = (uint16_t*)v_out;
     a.B = B; a.S = S; a.C = C; a.H = H; a.D = D;
     a.freqs = make_freqs(D);
+    hipError_t e = hipSuccess;
+    a.ncu = current_cu_count(&e);
+    if (e != hipSuccess) return map_hip(e);
     a.stream = reinterpret_cast<hipStream_t>(stream);
     return map_hip(klein::launch_qkv_rope_proj(a));
   } catch (...) {

@@ -123,6 +123,7 @@ struct QkvArgs {
   uint16_t* v;
   int B, S, C, H, D;
   RopeFreqs freqs;
+  int ncu;                 // compute units of the device (the persistent grid)
   hipStream_t stream;
 };
 hipError_t launch_qkv_rope_proj(const QkvArgs& a);

@@ -28,6 +28,13 @@
 // before the step's last sub-step so that the reads of the next buffer
 // overlap MFMAs.  Rows past N or M read as zeros through the buffer
 // descriptors and are not stored.
+//
+// The grid is persistent: one workgroup per compute unit, each looping over
+// its share of the tiles.  The last K steps of a tile load the next tile's
+// first steps (into the LDS buffer its epilogue leaves alone, and for bf16
+// its second step into the staging registers), and its epilogue loads the
+// next tile's positions and bias into a second LDS copy, so a tile after the
+// first starts with its first K step in place.
 #include <type_traits>
 
 #include "klein_device.hpp"
@@ -39,39 +46,51 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // Per-part cycle counts of the K step, for a measurement build only: defined
 // by the step_clock.hip harness, never by the library.  Each wave sums, over
-// its K steps, the shader-clock cycles (s_memtime) of each k-sub-step (with
-// the staging slots in it) and of the barrier, and lane 0 writes them, with
-// the K-step count, the cycles of the whole loop, of the prologue before it
-// and of the epilogue after it, to klein_qkv_clock_out[10 (8 wg + wave) +
-// 0..8].
+// the K steps of all its tiles, the shader-clock cycles (s_memtime) of each
+// k-sub-step (with the staging slots in it) and of the barrier, and lane 0
+// writes them, with the K-step count and the cycles of the K loops, of what
+// precedes each (kernel entry or the previous tile's end) and of the
+// epilogues, to klein_qkv_clock_out[10 (8 wg + wave) + 0..8].
 #ifdef KLEIN_STEP_CLOCK
 __device__ unsigned long long* klein_qkv_clock_out;
 #define KLEIN_QKV_CLOCK_ENTRY                                                \
-  const unsigned long long qclk_entry = __builtin_amdgcn_s_memtime();
-#define KLEIN_QKV_CLOCK_START                                                \
   unsigned long long qclk_sum[5] = {0, 0, 0, 0, 0};                          \
+  unsigned long long qclk_pro = 0, qclk_loop = 0, qclk_epi = 0, qclk_nk = 0; \
   unsigned long long qclk_prev = __builtin_amdgcn_s_memtime();               \
-  const unsigned long long qclk_start = qclk_prev;
+  unsigned long long qclk_start = qclk_prev, qclk_tile_end = qclk_prev;
+#define KLEIN_QKV_CLOCK_START                                                \
+  qclk_prev = __builtin_amdgcn_s_memtime();                                  \
+  qclk_start = qclk_prev;                                                    \
+  qclk_pro += qclk_start - qclk_tile_end;
 #define KLEIN_QKV_CLOCK_MARK(i)                                              \
   do {                                                                       \
     const unsigned long long qclk_now = __builtin_amdgcn_s_memtime();        \
     qclk_sum[i] += qclk_now - qclk_prev;                                     \
     qclk_prev = qclk_now;                                                    \
   } while (0)
-#define KLEIN_QKV_CLOCK_STORE(nk)                                            \
+#define KLEIN_QKV_CLOCK_TILE_END(nk)                                         \
+  do {                                                                       \
+    const unsigned long long qclk_now = __builtin_amdgcn_s_memtime();        \
+    qclk_loop += qclk_prev - qclk_start;                                     \
+    qclk_epi += qclk_now - qclk_prev;                                        \
+    qclk_nk += (unsigned long long)(nk);                                     \
+    qclk_tile_end = qclk_now;                                                \
+  } while (0)
+#define KLEIN_QKV_CLOCK_STORE                                                \
   if (klein_qkv_clock_out != nullptr && lane == 0) {                         \
     unsigned long long* co = klein_qkv_clock_out + ((size_t)blockIdx.x * 8 + wave) * 10; \
     for (int i = 0; i < 5; ++i) co[i] = qclk_sum[i];                         \
-    co[5] = (unsigned long long)(nk);                                        \
-    co[6] = qclk_prev - qclk_start;                                          \
-    co[7] = qclk_start - qclk_entry;                                         \
-    co[8] = __builtin_amdgcn_s_memtime() - qclk_prev;                        \
+    co[5] = qclk_nk;                                                         \
+    co[6] = qclk_loop;                                                       \
+    co[7] = qclk_pro;                                                        \
+    co[8] = qclk_epi;                                                        \
   }
 #else
 #define KLEIN_QKV_CLOCK_ENTRY
 #define KLEIN_QKV_CLOCK_START
 #define KLEIN_QKV_CLOCK_MARK(i) do {} while (0)
-#define KLEIN_QKV_CLOCK_STORE(nk)
+#define KLEIN_QKV_CLOCK_TILE_END(nk) do {} while (0)
+#define KLEIN_QKV_CLOCK_STORE
 #endif
 
 template <int D, bool FP8>
@@ -92,13 +111,13 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
 
   __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][TN * ROW];
   __shared__ __attribute__((aligned(16))) uint16_t b_lds[2][TM * ROW];
-  // What the epilogue reads besides the accumulators, loaded in the prologue
-  // (its latency hides behind the first staging loads): the tile's token
-  // positions and bias as fp32, and the RoPE frequencies (hi[16], lo[16]),
+  // What the epilogue reads besides the accumulators: the tile's token
+  // positions and bias as fp32 (two copies: the next tile's are loaded while
+  // this tile's epilogue runs), and the RoPE frequencies (hi[16], lo[16]),
   // which a lane reads with one LDS read instead of selecting between kernel
   // arguments.
-  __shared__ __attribute__((aligned(16))) float ep_pos[TM][4];
-  __shared__ __attribute__((aligned(16))) float ep_bias[TN];
+  __shared__ __attribute__((aligned(16))) float ep_pos[2][TM][4];
+  __shared__ __attribute__((aligned(16))) float ep_bias[2][TN];
   __shared__ __attribute__((aligned(16))) float ep_fr[32];
 
   KLEIN_QKV_CLOCK_ENTRY
@@ -113,63 +132,105 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
   // of W.
   constexpr int kGroupM = 8;
   const int ntile_m = (M + TM - 1) / TM;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int ntiles = ntile_m * ntile_n;
   const int gsz = kGroupM * ntile_n;
-  const int m_first = (L / gsz) * kGroupM;
-  const int gm = min(ntile_m - m_first, kGroupM);
-  const int tmi = m_first + (L % gsz) % gm, tn = (L % gsz) / gm;
-  const int n0 = tn * TN, m0 = tmi * TM;
   const int HD = H * D;
+  const int rowb = C * ES;
+  const int nk = C * ES / KB;
+  // Persistent: workgroup b computes the tiles of the virtual workgroups
+  // b, b + G, b + 2G, ... (G = gridDim.x, a multiple of 8, so virtual
+  // workgroup v runs on XCD v mod 8 as xcd_remap assumes); (n0, m0) of the
+  // tile of virtual workgroup v:
+  auto tile_origin = [&](int v, int& n0o, int& m0o) {
+    const int L = xcd_remap(v, ntiles);
+    const int m_first = (L / gsz) * kGroupM;
+    const int gm = min(ntile_m - m_first, kGroupM);
+    m0o = (m_first + (L % gsz) % gm) * TM;
+    n0o = ((L % gsz) / gm) * TN;
+  };
+  auto rsrc_w = [&](int n0o) {
+    return uniform_rsrc(static_cast<const uint8_t*>(wv) + (size_t)n0o * rowb,
+                        min(TN, N - n0o) * rowb);
+  };
+  auto rsrc_x = [&](int m0o) {
+    return uniform_rsrc(static_cast<const uint8_t*>(xv) + (size_t)m0o * rowb,
+                        min(TM, M - m0o) * rowb);
+  };
+  int v = blockIdx.x, n0, m0;
+  tile_origin(v, n0, m0);
+  __amdgpu_buffer_rsrc_t ra = rsrc_w(n0), rb = rsrc_x(m0);
+  // the next tile (the same one again after the last: its loads are then
+  // valid and unused)
+  int n0n = n0, m0n = m0;
+  __amdgpu_buffer_rsrc_t ran = ra, rbn = rb;
+  auto next_tile = [&]() {
+    if (v + (int)gridDim.x < ntiles) {
+      tile_origin(v + gridDim.x, n0n, m0n);
+      ran = rsrc_w(n0n);
+      rbn = rsrc_x(m0n);
+    } else {
+      n0n = n0; m0n = m0; ran = ra; rbn = rb;
+    }
+  };
+  next_tile();
 
   // ---- staging: chunk c = tid + 512 i; the first TN*CPR chunks are W rows,
-  // the rest x rows
-  const int rowb = C * ES;
-  const int nrows_a = min(TN, N - n0), nrows_b = min(TM, M - m0);
-  const __amdgpu_buffer_rsrc_t ra =
-      uniform_rsrc(static_cast<const uint8_t*>(wv) + (size_t)n0 * rowb, nrows_a * rowb);
-  const __amdgpu_buffer_rsrc_t rb =
-      uniform_rsrc(static_cast<const uint8_t*>(xv) + (size_t)m0 * rowb, nrows_b * rowb);
+  // the rest x rows.  Step s of this tile, s >= nk reading step s - nk of the
+  // next tile (so the last steps' loads bring the next tile's first steps).
   u32x4_t stg[NLD];
+  // The staging addresses derive from tid_t, a copy of tid that each tile
+  // makes opaque again, so that the compiler recomputes them per tile instead
+  // of keeping them in registers through the epilogue.
+  int tid_t = tid;
   // chunk i of a thread: W rows for i < 4, x rows after (TN * CPR = 4 * 512)
   static_assert(TN * CPR == 4 * 512, "staging split");
-  auto load_one = [&](int kt, int i) {
-    const int cc = tid + 512 * (i & 3);
+  auto load_one = [&](int s, int i) {
+    const int cc = tid_t + 512 * (i & 3);
     const int row = cc / CPR, ch = cc % CPR;
-    const int off = row * rowb + kt * KB + 16 * ch;
-    stg[i] = __builtin_bit_cast(u32x4_t, i < 4 ? __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0)
-                                               : __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+    const bool nx = s >= nk;
+    const int off = row * rowb + (nx ? s - nk : s) * KB + 16 * ch;
+    stg[i] = __builtin_bit_cast(
+        u32x4_t, i < 4 ? __builtin_amdgcn_raw_buffer_load_b128(nx ? ran : ra, off, 0, 0)
+                       : __builtin_amdgcn_raw_buffer_load_b128(nx ? rbn : rb, off, 0, 0));
   };
   auto store_one = [&](int buf, int i) {
-    const int cc = tid + 512 * (i & 3);
+    const int cc = tid_t + 512 * (i & 3);
     const int row = cc / CPR, ch = cc % CPR;
     uint16_t* dst = i < 4 ? &a_lds[buf][row * ROW + 8 * ch] : &b_lds[buf][row * ROW + 8 * ch];
     *reinterpret_cast<u32x4_t*>(dst) = stg[i];
   };
 
   f32x16_t acc[4][2];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = (f32x16_t){};
-
-  const int nk = C * ES / KB;
-  if (tid < TM) {
-    // rows past M take the last token's positions; they are not stored
-    const int4 p = *reinterpret_cast<const int4*>(pos + 4 * (min(m0 + tid, M - 1) % S));
-    *reinterpret_cast<f32x4_t*>(ep_pos[tid]) =
-        (f32x4_t){(float)p.x, (float)p.y, (float)p.z, (float)p.w};
-  } else if (tid < TM + TN / 4) {
-    const int i = 4 * (tid - TM), n = n0 + i;  // N is a multiple of 4
-    uint2 b = make_uint2(0, 0);
-    if (bias != nullptr && n < N) b = *reinterpret_cast<const uint2*>(bias + n);
-    *reinterpret_cast<f32x4_t*>(&ep_bias[i]) =
-        (f32x4_t){bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y)};
-  } else if (tid < TM + TN / 4 + 32) {
+  // the epilogue inputs of the tile at (n0o, m0o): thread tid < TM loads a
+  // token's positions, TM <= tid < TM + TN / 4 four bias words
+  int4 ep_p = make_int4(0, 0, 0, 0);
+  uint2 ep_b = make_uint2(0, 0);
+  auto ep_load = [&](int n0o, int m0o) {
+    if (tid < TM) {
+      // rows past M take the last token's positions; they are not stored
+      ep_p = *reinterpret_cast<const int4*>(pos + 4 * (min(m0o + tid, M - 1) % S));
+    } else if (tid < TM + TN / 4) {
+      const int n = n0o + 4 * (tid - TM);     // N is a multiple of 4
+      ep_b = make_uint2(0, 0);
+      if (bias != nullptr && n < N) ep_b = *reinterpret_cast<const uint2*>(bias + n);
+    }
+  };
+  auto ep_store = [&](int eb) {
+    if (tid < TM)
+      *reinterpret_cast<f32x4_t*>(ep_pos[eb][tid]) =
+          (f32x4_t){(float)ep_p.x, (float)ep_p.y, (float)ep_p.z, (float)ep_p.w};
+    else if (tid < TM + TN / 4)
+      *reinterpret_cast<f32x4_t*>(&ep_bias[eb][4 * (tid - TM)]) =
+          (f32x4_t){bf16_lo(ep_b.x), bf16_hi(ep_b.x), bf16_lo(ep_b.y), bf16_hi(ep_b.y)};
+  };
+  ep_load(n0, m0);
+  if (tid >= TM + TN / 4 && tid < TM + TN / 4 + 32) {
     const int i = tid - TM - TN / 4;
     ep_fr[i] = i < 16 ? fr.hi[i] : fr.lo[i - 16];
   }
 #pragma unroll
   for (int i = 0; i < NLD; ++i) load_one(0, i);
+  ep_store(0);
 #pragma unroll
   for (int i = 0; i < NLD; ++i) store_one(0, i);
   if constexpr (!FP8) {
@@ -221,10 +282,20 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
   // fp8 (operands twice as wide: a register set held across the whole step
   // would spill): one load of step kt+1 after each MFMA of the first
   // sub-step, one store of it after each MFMA of the second.
+  // gb: K steps of the earlier tiles; step kt of this tile uses LDS buffer
+  // (gb + kt) & 1, which at the tile's start holds its first step.
+  int gb = 0;
+  for (int tile = 0;; ++tile) {
+  const int eb = tile & 1;
+  __asm__ volatile("" : "+v"(tid_t));
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = (f32x16_t){};
   KLEIN_QKV_CLOCK_START
   if constexpr (FP8) {
     for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
+      const int buf = (gb + kt) & 1;
       read_ops(buf, 0, 0);
 #pragma unroll
       for (int ks = 0; ks < KSUB; ++ks) {
@@ -249,9 +320,9 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
     // operands are already in registers, and the operands of the next
     // step's first sub-step are read while its MFMAs run
     static_assert(KSUB == 4 && NLD == 8, "slot layout");
-    read_ops(0, 0, 0);
+    read_ops(gb & 1, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
+      const int buf = (gb + kt) & 1;
 #pragma unroll
       for (int ks = 0; ks < KSUB; ++ks) {
         if (ks == KSUB - 1) {
@@ -289,6 +360,14 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
   // check may leave the scalar offset out), the scalar offset only moves
   // within a row.  (readfirstlane: the compiler cannot see that wn is
   // wave-uniform.)
+  ep_load(n0n, m0n);     // the next tile's epilogue inputs, stored after this epilogue
+  int lane_e = lane;
+  __asm__ volatile("" : "+v"(lane_e));
+  {
+  // the epilogue's lane indices from an opaque copy, so that its addresses
+  // are formed here rather than kept in registers through the K loop
+  const int lane = lane_e, g = lane_e >> 5, lr = lane_e & 31;
+  const int nrows_b = min(TM, M - m0);
   const int nw = __builtin_amdgcn_readfirstlane(n0 + 128 * wn);
   // frequencies of the pairs jb + 2 g + 0..1, jb = (8 c4 mod D/4) / 2
   f32x2_t fhi[4], flo[4];
@@ -303,7 +382,7 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
   // (`rot` is a compile-time flag, so that the caller's loops over the
   // outputs hold no branch and their LDS reads can be issued together)
   auto emit = [&](int nb, int c4, int mb, auto rot, int db) -> u32x2_t {
-    const f32x4_t bs = *reinterpret_cast<const f32x4_t*>(&ep_bias[128 * wn + 32 * nb + 8 * c4 + 4 * g]);
+    const f32x4_t bs = *reinterpret_cast<const f32x4_t*>(&ep_bias[eb][128 * wn + 32 * nb + 8 * c4 + 4 * g]);
     float y[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) y[e] = acc[nb][mb][4 * c4 + e] * yscale + bs[e];
@@ -311,7 +390,7 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
       return (u32x2_t){pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
     } else {
       // one axis a for both lane halves (D/4 divides 32)
-      const float fp = ep_pos[64 * wm + 32 * mb + lr][(db + 8 * c4) / DA];
+      const float fp = ep_pos[eb][64 * wm + 32 * mb + lr][(db + 8 * c4) / DA];
 #pragma unroll
       for (int pr = 0; pr < 2; ++pr) {
         const float rev = rope_rev(fp, fhi[c4][pr], flo[c4][pr]);
@@ -338,7 +417,7 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
       const uint16_t* const obase = which == 0 ? qo : which == 1 ? ko : vo;
       const __amdgpu_buffer_rsrc_t ro = uniform_rsrc(obase + (size_t)m0 * HD, nrows_b * HD * 2);
       constexpr int XR = 136;                    // LDS row stride, 16-bit units
-      const int lbuf = (nk - 1) & 1;
+      const int lbuf = (gb + nk - 1) & 1;
       uint16_t* const xl = (wave < 4 ? a_lds[lbuf] : b_lds[lbuf]) + (wave & 3) * (32 * XR);
       static_assert(4 * 32 * XR <= TN * ROW, "transpose slices");
       const int rr = lane >> 4, cc = lane & 15;  // row 4 i + rr, 8-byte chunk cc of a half
@@ -392,14 +471,32 @@ __global__ __launch_bounds__(512) void qkv_rope_proj_kernel(
               ro, voff[mb], (hdb + 8 * c4) * 2, 0);
     }
   }
-  KLEIN_QKV_CLOCK_STORE(nk)
+  }
+  KLEIN_QKV_CLOCK_TILE_END(nk);
+  v += gridDim.x;
+  if (v >= ntiles) break;
+  ep_store(eb ^ 1);
+  gb += nk;
+  n0 = n0n; m0 = m0n; ra = ran; rb = rbn;
+  next_tile();
+  // this epilogue's LDS reads (its slices of buffer (gb - 1) & 1, the inputs
+  // copy eb) end before the next tile stores into them
+  __syncthreads();
+  }
+  KLEIN_QKV_CLOCK_STORE
 }
 
 template <bool FP8>
 static hipError_t launch_qkv(const QkvArgs& a) {
   const int M = a.B * a.S, N = 3 * a.H * a.D;
   const int ntn = (N + 255) / 256, ntm = (M + 255) / 256;
-  const dim3 grid((unsigned)(ntn * ntm));
+  // persistent: one workgroup per compute unit (it needs most of a CU's LDS),
+  // a multiple of 8 so that each keeps to one XCD's share of the tile list
+  const long long ntiles = (long long)ntn * ntm;
+  long long nwg = a.ncu > 0 ? a.ncu : ntiles;
+  if (nwg >= 8) nwg -= nwg % 8;
+  if (nwg > ntiles) nwg = ntiles;
+  const dim3 grid((unsigned)nwg);
   const float ys = FP8 ? a.x_descale * a.w_descale : 1.0f;
   if (a.D == 128)
     hipLaunchKernelGGL((qkv_rope_proj_kernel<128, FP8>), grid, dim3(512), 0, a.stream, a.x, a.w,
