@@ -307,7 +307,7 @@ static int qkv_main(int argc, char** argv) {
         pro[w >= 4] += (double)r[7];
         epi[w >= 4] += (double)r[8];
       }
-    std::printf("\n%s operands: M=%d N=%d K=%d, %lld workgroups; cycles per K step of one wave\n\n",
+    std::printf("\n%s operands: M=%d N=%d K=%d, %lld tiles; cycles per K step of one wave\n\n",
                 fp8 ? "FP8 (E4M3)" : "bf16", M, N, C, wgs);
     std::printf("| part of the K step | waves 0-3 | waves 4-7 |\n|---|---|---|\n");
     double tot[2] = {0.0, 0.0};
@@ -323,7 +323,8 @@ static int qkv_main(int argc, char** argv) {
     }
     std::printf("| the K step | %.0f | %.0f |\n", tot[0], tot[1]);
     const double nw = 4.0 * (double)wgs;
-    std::printf("\nPer workgroup and wave, cycles: prologue (entry to the first K step) %.0f / %.0f, "
+    std::printf("\nPer tile and wave, cycles: before its K loop (kernel entry, or the end of the "
+                "wave's previous tile) %.0f / %.0f, "
                 "K loop %.0f / %.0f, epilogue (bias, RoPE, stores) %.0f / %.0f "
                 "(waves 0-3 / 4-7)\n",
                 pro[0] / nw, pro[1] / nw, loop[0] / nw, loop[1] / nw, epi[0] / nw, epi[1] / nw);
