@@ -320,6 +320,11 @@ klein_status_t klein_rope4d_attn_fwd_lse_ws(const void* q, const void* k, const 
  *   exponents, in fp32); contents on entry do not matter.
  * Two calls sharing one workspace on different streams race.  A smaller
  * workspace is INVALID_ARG.
+ * Ordering: the call is ordered on `stream` as one unit.  Inside, the dq
+ * kernel runs on a second stream the library creates once per device
+ * (non-blocking, default priority), forked from `stream` and joined back
+ * into it with events, so it overlaps the dk/dv kernel; under graph capture
+ * of `stream` that stream joins the capture.
  */
 klein_status_t klein_rope4d_attn_bwd(const void* q, const void* k, const void* v,
                                      const int32_t* pos_thwl, const void* out, const void* dout,

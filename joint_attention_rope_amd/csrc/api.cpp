@@ -196,6 +196,31 @@ struct DeviceBuffer {
   bool used = false;          // `done` has been recorded
 };
 DeviceBuffer g_buffers[kMaxDevices];
+
+// Per device, the backward's second stream (non-blocking, default priority)
+// and its fork/join events, created on first use and kept until the process
+// ends.  The lock covers one call's records and waits.
+struct BwdSide {
+  std::mutex mu;
+  bool tried = false;
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+BwdSide g_bwd_side[kMaxDevices];
+
+// Creates the device's side stream and events once; on failure the backward
+// runs on the caller's stream alone (same kernels, one after the other).
+void bwd_side_init(BwdSide& s) {
+  if (s.tried) return;
+  s.tried = true;
+  if (hipStreamCreateWithFlags(&s.side, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess) {
+    (void)hipGetLastError();
+    s.side = nullptr;
+    s.fork = s.join = nullptr;
+  }
+}
 std::atomic<size_t> g_buffer_limit{KLEIN_DEFAULT_BUFFER_LIMIT};
 
 // Frees b's buffer after its last use has completed.  Caller holds b.mu and
@@ -396,6 +421,16 @@ klein_status_t klein_rope4d_attn_bwd(const void* q, const void* k, const void* v
     a.qscale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
     a.freqs = make_freqs(D);
     a.stream = reinterpret_cast<hipStream_t>(stream);
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return map_hip(e);
+    if (dev < 0 || dev >= kMaxDevices) return map_hip(klein::launch_attn_bwd(a));
+    BwdSide& side = g_bwd_side[dev];
+    std::lock_guard<std::mutex> lock(side.mu);
+    bwd_side_init(side);
+    a.side = side.side;
+    a.fork = side.fork;
+    a.join = side.join;
     return map_hip(klein::launch_attn_bwd(a));
   } catch (...) {
     return KLEIN_ERR_LAUNCH;

@@ -544,6 +544,18 @@ static hipError_t launch_bwd(const BwdArgs& a) {
                      a.norm2, a.escale, a.S, (long long)a.B * a.H * a.S);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // dK/dV and dQ read the same inputs and write disjoint outputs.  Given a
+  // second stream, dQ runs on it beside dK/dV, so that the workgroups of
+  // each fill the compute units the other's last, partial round leaves idle.
+  const bool two = a.side != nullptr && a.fork != nullptr && a.join != nullptr;
+  hipStream_t sq = a.stream;
+  if (two) {
+    e = hipEventRecord(a.fork, a.stream);
+    if (e != hipSuccess) return e;
+    e = hipStreamWaitEvent(a.side, a.fork, 0);
+    if (e != hipSuccess) return e;
+    sq = a.side;
+  }
   const int nb = (a.S + 255) / 256;
   const dim3 grid((unsigned)(a.B * a.H * nb));
   hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, grid, dim3(512), 0, a.stream, a.qr, a.kr, a.v,
@@ -551,10 +563,14 @@ static hipError_t launch_bwd(const BwdArgs& a) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqb = (a.S + 255) / 256;
-  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3((unsigned)(a.B * a.H * nqb)), dim3(512), 0, a.stream,
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3((unsigned)(a.B * a.H * nqb)), dim3(512), 0, sq,
                      a.qr, a.kr, a.v, a.dout, a.lse, a.delta, a.escale, a.pos, a.dq, a.S, a.H, nqb,
                      a.freqs, (float)(1.0 / std::sqrt((double)D)));
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess || !two) return e;
+  e = hipEventRecord(a.join, a.side);
+  if (e != hipSuccess) return e;
+  return hipStreamWaitEvent(a.stream, a.join, 0);
 }
 
 hipError_t launch_attn_bwd(const BwdArgs& a) {

@@ -94,6 +94,10 @@ struct BwdArgs {
   float qscale_log2;
   RopeFreqs freqs;
   hipStream_t stream;
+  // a second stream for the dq kernel, forked from and joined back into
+  // `stream` with these two events (all null: everything on `stream`)
+  hipStream_t side;
+  hipEvent_t fork, join;
 };
 hipError_t launch_attn_bwd(const BwdArgs& a);
 // byte offsets of the backward's workspace parts (qr at 0) and its size

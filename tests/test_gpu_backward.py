@@ -137,6 +137,35 @@ def test_repeat_bitwise_identical():
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
+def test_graph_capture_replays():
+    # the backward runs dq on a second stream, forked from and joined back into
+    # the caller's: captured on a side stream, every replay (with eager calls
+    # of the backward in between) writes the eager result bit for bit
+    inp = random_inputs(1, 2100, 3, 128, seed=47)
+    (out, lse, dq0, dk0, dv0), _ = run_fwd_bwd(inp, dout_seed=9)
+    q, k, v, pos = to_device(inp)
+    B, S, H, D = q.shape
+    rng = np.random.default_rng(9)
+    dout, _ = bf16_from_f64(rng.standard_normal(q.shape))
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(kl.klein_attn_bwd_workspace_size(B, S, H, D), dtype=torch.uint8, device=DEV)
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            kl.klein_rope4d_attn_bwd(q, k, v, pos, out, dout, lse, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    for i in range(4):
+        for t in (dq, dk, dv):
+            t.zero_()
+        ws.fill_(0xAB)                       # stale workspace contents between replays
+        run_fwd_bwd(inp, dout_seed=9)        # eager backward work in between
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, ref in ((dq, dq0), (dk, dk0), (dv, dv0)):
+            assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {i}"
+
+
 @pytest.mark.parametrize("B,S,H", [(1, 2500, 4), (2, 900, 3), (1, 12300, 1)])
 def test_forward_with_lse_on_the_split_schedule(B, S, H):
     # the workspace variant: tiles that run whole give the same bits as the
