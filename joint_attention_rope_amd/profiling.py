@@ -304,6 +304,21 @@ def backward_markdown(stats_dir, workloads, command, last=None):
                       f"{rate} |\n")
         md.append(f"| the backward (sum of the means) | | {total:.4f} | 10 (algorithmic) | "
                   f"{10 * unit / (total * 1e-3) / 1e12:.1f} |\n")
+        # dQ runs beside dK/dV on a second stream, so a call's time is its
+        # span: the i-th prep's start to the end of the i-th call's last kernel
+        span = {label: [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
+                        if name in r["Kernel_Name"] and size(r) == grids[label]]
+                for label, name in BWD_KERNELS}
+        if last:
+            span = {k: v[-last:] for k, v in span.items()}
+        n = min(len(v) for v in span.values())
+        spans = [(max(span[k][i][1] for k in span) - min(span[k][i][0] for k in span)) / 1e6
+                 for i in range(n)]
+        if spans:
+            ms = sum(spans) / len(spans)
+            md.append(f"| the backward per call (first start to last end; dK/dV and dQ overlap) | "
+                      f"{len(spans)} | {ms:.4f} | 10 (algorithmic) | "
+                      f"{10 * unit / (ms * 1e-3) / 1e12:.1f} |\n")
     return "".join(md)
 
 
